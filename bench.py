@@ -1,0 +1,511 @@
+#!/usr/bin/env python3
+"""Cold-cache benchmark of the skinny decode GEMV on one MI355X (gfx950).
+
+Headline: bf16 weights x bf16 activation, M=1, K=4096, N=12288 (100.7 MB of
+weights per launch), the decode shape of "The Shape That Actually Matters"
+(The shape a decode step actually runs).  Following its instrument (The
+instrument came first): enough distinct weight buffers rotate per launch that
+the working set (>= 2 GB) is far past the 256 MB Infinity Cache, so every
+launch streams its weights from HBM; warm-up on the same rotation; then the
+timed launches in repeats of 200, and no ratio is claimed unless the
+run-to-run spread of the repeats is under 5%.
+
+One step = one GEMV launch on the next rotation buffer.  `value` is achieved
+HBM GB/s = algorithmic bytes (weights + x + y) per launch / time per launch.
+Times come from HIP events recorded on the stream the kernels run on.
+
+Further arms (same protocol, shorter): the streaming-read ceiling, q8_0 / q4_0
+x fp32 and q4_0 x Q8_1 at M=1..8 (K=4096, N=14336), the Llama-2-7B-shaped
+q4_0 x Q8_1 decode layer over 32 distinct layers, the q8_0 M=1 K=256 N=512
+launch-bound case, and the M=512 MFMA prefill tile.  The CPU oracle is timed
+on a bounded sample of the headline workload on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 60000] [--arms all|none|a,b]
+Prints one JSON line on stdout; details go to --details (default
+gpurun_out/bench_details.json when that directory exists).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+ROTATION_BYTES = 2 * 1000**3   # >= 2 GB working set per arm
+METRIC = "achieved HBM GB/s (% of peak) + µs per M=1 GEMV, cold-cache rotation"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# timing helpers
+# --------------------------------------------------------------------------
+
+class Timer:
+    """Times `launch(i)` calls on torch's current stream with HIP events."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, launch, n_rot: int, steps: int, warmup: int, per_repeat: int = 200, warm_s: float | None = None):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        i = 0
+        if warm_s is not None:
+            t_end = time.time() + warm_s
+            while time.time() < t_end:
+                for _ in range(per_repeat):
+                    launch(i % n_rot)
+                    i += 1
+                torch.cuda.synchronize()
+        for _ in range(warmup):
+            launch(i % n_rot)
+            i += 1
+        torch.cuda.synchronize()
+        reps = []
+        left = steps
+        while left > 0:
+            n = min(per_repeat, left)
+            reps.append(n)
+            left -= n
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(len(reps) + 1)]
+        torch.cuda.synchronize()
+        events[0].record(stream)
+        for r, n in enumerate(reps):
+            for _ in range(n):
+                launch(i % n_rot)
+                i += 1
+            events[r + 1].record(stream)
+        torch.cuda.synchronize()
+        rep_us = [events[r].elapsed_time(events[r + 1]) * 1000.0 / reps[r] for r in range(len(reps))]
+        total_ms = events[0].elapsed_time(events[-1])
+        return summarize(rep_us, total_ms, steps)
+
+
+def summarize(rep_us, total_ms, steps):
+    mean = statistics.fmean(rep_us)
+    spread = (max(rep_us) - min(rep_us)) / mean if mean > 0 else 0.0
+    return {
+        "us_per_launch": total_ms * 1000.0 / steps,
+        "us_median": statistics.median(rep_us),
+        "us_min": min(rep_us),
+        "us_max": max(rep_us),
+        "spread": spread,
+        "spread_ok": spread < 0.05,
+        "repeats_us": [round(v, 4) for v in rep_us],
+        "total_ms": total_ms,
+    }
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def rotation_count(bytes_per_buffer: int, minimum: int = 1) -> int:
+    return max(minimum, -(-ROTATION_BYTES // bytes_per_buffer))
+
+
+def make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0, keep_rows=None):
+    """n_rot packed weight buffers generated on the device; optionally keeps
+    host copies of a few canonical rows per buffer (for the oracle sample)."""
+    bufs, kept = [], []
+    idx = None if keep_rows is None else torch.as_tensor(keep_rows, device="cuda")
+    for b in range(n_rot):
+        W = si.torch_weights(kind, N, K, seed0 + b, "cuda")
+        P = skg.pack_weights(fmt, N, K, W)
+        if idx is not None and b < 4:
+            kept.append(W[idx].cpu().numpy())
+        bufs.append(P)
+        del W
+    torch.cuda.synchronize()
+    return bufs, kept
+
+
+def check_outputs_sane(torch, ys):
+    """Pre-timing gate that needs no reference: outputs are finite, and two
+    launches on the same buffer agree bit for bit (checked by the caller)."""
+    for y in ys:
+        if not bool(torch.isfinite(y).all()):
+            raise RuntimeError("non-finite GEMV output; refusing to time")
+
+
+def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmup, warm_s, x_host, keep_rows=None,
+                   graph=False):
+    import ctypes
+    wbytes = skg.packed_size(fmt, N, K)
+    n_rot = rotation_count(wbytes)
+    log(f"[{name}] {n_rot} rotation buffers x {wbytes / 1e6:.1f} MB")
+    bufs, kept = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=1000 * (fmt + 1) + 10 * M,
+                                      keep_rows=keep_rows)
+    x = torch.from_numpy(x_host).cuda()
+    if fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1):
+        xin = skg.quantize_act_q8_1(x)
+        xbytes = xin.numel()
+    else:
+        xin = x
+        xbytes = x.numel() * x.element_size()
+    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(2)]
+    wp = [b.data_ptr() for b in bufs]
+    xp, yp = xin.data_ptr(), [y.data_ptr() for y in ys]
+    lib = skg.lib
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[i & 1], sh)
+
+    # gate: finite and deterministic on every rotation buffer
+    outs = []
+    for i in range(n_rot):
+        skg.check(lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[0], sh))
+        a = ys[0].clone()
+        skg.check(lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[1], sh))
+        if not torch.equal(a, ys[1]):
+            raise RuntimeError(f"[{name}] GEMV not deterministic on buffer {i}")
+        outs.append(a)
+    check_outputs_sane(torch, outs)
+    res = timer.run(launch, n_rot, steps, warmup, warm_s=warm_s)
+    alg = wbytes + xbytes + M * N * 4
+    res.update(name=name, fmt=skg.FMT_NAMES[fmt], M=M, N=N, K=K, rotation_buffers=n_rot,
+               working_set_bytes=n_rot * wbytes, algorithmic_bytes=alg,
+               gbs=alg / (res["us_per_launch"] * 1e-6) / 1e9)
+    res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
+    if graph:
+        res["graph"] = bench_graph(torch, launch, n_rot)
+        res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
+    idx = None if keep_rows is None else torch.as_tensor(keep_rows, device="cuda")
+    extra = {"outputs": [o[:, idx].cpu().numpy() if idx is not None else None for o in outs[:4]],
+             "kept_rows": kept, "x": x_host}
+    del bufs
+    torch.cuda.empty_cache()
+    return res, extra
+
+
+def bench_graph(torch, launch, n_rot, per_graph=200, repeats=10):
+    """Same launches captured into a HIP graph of 200 and replayed: removes
+    host launch overhead, so back-to-back kernel time shows."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            launch(i % n_rot)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(per_graph):
+            launch(i % n_rot)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(repeats + 1)]
+    cur = torch.cuda.current_stream()
+    ev[0].record(cur)
+    for r in range(repeats):
+        g.replay()
+        ev[r + 1].record(cur)
+    torch.cuda.synchronize()
+    rep_us = [ev[r].elapsed_time(ev[r + 1]) * 1000.0 / per_graph for r in range(repeats)]
+    return summarize(rep_us, ev[0].elapsed_time(ev[-1]), per_graph * repeats)
+
+
+def bench_ceiling(skg, torch, timer, steps, warm_s):
+    """Streaming-read ceiling over a >= 2 GB rotation of 100.7 MB buffers."""
+    nbytes = 12288 * 4096 * 2
+    n_rot = rotation_count(nbytes)
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(n_rot)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bp = [b.data_ptr() for b in bufs]
+    sp = sink.data_ptr()
+    sh = torch.cuda.current_stream().cuda_stream
+    lib = skg.lib
+
+    def launch(i):
+        lib.skg_stream_read(bp[i], nbytes, sp, sh)
+
+    skg.check(lib.skg_stream_read(bp[0], nbytes, sp, sh))
+    res = timer.run(launch, n_rot, steps, 0, warm_s=warm_s)
+    res.update(name="stream_read_ceiling", bytes=nbytes, rotation_buffers=n_rot,
+               gbs=nbytes / (res["us_per_launch"] * 1e-6) / 1e9)
+    res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_layer(skg, si, torch, timer, steps, warm_s):
+    """Llama-2-7B-shaped q4_0 x Q8_1 decode layer, M=1, 32 distinct layers:
+    quantize(x) -> QKV (one launch) -> gate/up + SwiGLU (one launch) ->
+    quantize(h) -> down (K=11008).  One step = one layer."""
+    D, F = 4096, 11008
+    fmt = skg.Q4_0_Q8_1
+    layers = []
+    for l in range(32):
+        q, k, v = (si.torch_weights("q4_0", D, D, 50_000 + 10 * l + j, "cuda") for j in range(3))
+        g, u = (si.torch_weights("q4_0", F, D, 50_005 + 10 * l + j, "cuda") for j in range(2))
+        d = si.torch_weights("q4_0", D, F, 50_009 + 10 * l, "cuda")
+        layers.append((skg.pack_weights_multi(fmt, [D, D, D], D, [q, k, v]),
+                       skg.pack_weights_multi(fmt, [F, F], D, [g, u]),
+                       skg.pack_weights(fmt, D, F, d)))
+        del q, k, v, g, u, d
+    torch.cuda.synchronize()
+    x = torch.from_numpy(si.activations_f32(si.rng_for(0, 3, 7), 1, D)).cuda()
+    xq = torch.empty((1, D // 32, 36), dtype=torch.uint8, device="cuda")
+    yq, yk, yv = (torch.empty((1, D), dtype=torch.float32, device="cuda") for _ in range(3))
+    h = torch.empty((1, F), dtype=torch.float32, device="cuda")
+    hq = torch.empty((1, F // 32, 36), dtype=torch.uint8, device="cuda")
+    yo = torch.empty((1, D), dtype=torch.float32, device="cuda")
+    import ctypes
+    lib = skg.lib
+    sh = torch.cuda.current_stream().cuda_stream
+    N3 = (ctypes.c_int64 * 3)(D, D, D)
+    N2 = (ctypes.c_int64 * 2)(F, F)
+    Y3 = (ctypes.c_void_p * 3)(yq.data_ptr(), yk.data_ptr(), yv.data_ptr())
+    Y1 = (ctypes.c_void_p * 1)(h.data_ptr())
+    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in layers]
+    xp, xqp, hp, hqp, yop = x.data_ptr(), xq.data_ptr(), h.data_ptr(), hq.data_ptr(), yo.data_ptr()
+
+    def launch(i):
+        pq, pg, pd = ptrs[i]
+        lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
+        lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
+        lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, 1, sh)
+        lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
+        lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+
+    launch(0)
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(yo).all()):
+        raise RuntimeError("layer chain produced non-finite output")
+    res = timer.run(launch, 32, steps, 0, per_repeat=32, warm_s=warm_s)
+    wbytes = (skg.packed_size_multi(fmt, [D, D, D], D) + skg.packed_size_multi(fmt, [F, F], D)
+              + skg.packed_size(fmt, D, F))
+    alg = wbytes + 2 * (D // 32 * 36) + 2 * (F // 32 * 36) + 4 * (3 * D + F + D) + 4 * (D + F)
+    res.update(name="llama2_7b_q4_0_q8_1_layer", layers=32, working_set_bytes=32 * wbytes,
+               algorithmic_bytes=alg, launches_per_layer=5)
+    res["us_per_layer"] = res.pop("us_per_launch")
+    res["gbs"] = alg / (res["us_per_layer"] * 1e-6) / 1e9
+    res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
+    res["graph"] = bench_graph(torch, launch, 32, per_graph=32)
+    res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(skg, si, torch, timer, steps, warm_s):
+    M, N, K = 512, 14336, 4096
+    fmt = skg.Q4_0_BF16
+    wbytes = skg.packed_size(fmt, N, K)
+    n_rot = rotation_count(wbytes)
+    bufs, _ = make_packed_rotation(skg, si, torch, "q4_0", fmt, N, K, n_rot, seed0=70_000)
+    A = torch.from_numpy(si.activations_bf16(si.rng_for(0, 5, 9), M, K).view("int16")).cuda()
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    lib = skg.lib
+    sh = torch.cuda.current_stream().cuda_stream
+    wp = [b.data_ptr() for b in bufs]
+    ap, yp = A.data_ptr(), y.data_ptr()
+
+    def launch(i):
+        lib.skg_gemm_tiled(fmt, M, K, N, wp[i], ap, yp, sh)
+
+    skg.check(lib.skg_gemm_tiled(fmt, M, K, N, wp[0], ap, yp, sh))
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(y).all()):
+        raise RuntimeError("prefill tile produced non-finite output")
+    res = timer.run(launch, n_rot, steps, 0, per_repeat=50, warm_s=warm_s)
+    flops = 2.0 * M * N * K
+    res.update(name="prefill_q4_0_bf16_m512", M=M, N=N, K=K, rotation_buffers=n_rot, flop=flops,
+               tflops=flops / (res["us_per_launch"] * 1e-6) / 1e12)
+    res["frac_peak_mfma_bf16"] = res["tflops"] / PEAK_BF16_TFLOPS
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle itself, on a bounded sample of the headline workload
+# --------------------------------------------------------------------------
+
+def cpu_baseline(si, gpu_sample, budget_s=15.0):
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    N, K = 12288, 4096
+    x = gpu_sample["x"]
+    done, t0 = 0, time.perf_counter()
+    Ws = []
+    while time.perf_counter() - t0 < budget_s or done == 0:
+        W = si.bf16_weights(si.rng_for(0, 2, 100 + done), N, K)   # generation is not timed
+        t1 = time.perf_counter()
+        y, bound = oracle.gemv_ref_fmt("bf16", W, x, x_kind="bf16")
+        Ws.append(time.perf_counter() - t1)
+        done += 1
+        if done >= 64:
+            break
+    per = sum(Ws) / len(Ws)
+    alg = N * K * 2 + K * 2 + N * 4
+    # parity of the GPU's sampled rows on the timed rotation buffers
+    worst = 0.0
+    for rows_w, y_gpu in zip(gpu_sample["kept_rows"], gpu_sample["outputs"]):
+        y_ref, b = oracle.gemv_ref_fmt("bf16", rows_w.view(np.uint16), x, x_kind="bf16")
+        ok, w = oracle.check_close(y_gpu, y_ref, oracle.tolerance(b))
+        worst = max(worst, w)
+        if not ok:
+            raise RuntimeError(f"GPU output outside tolerance on a timed buffer (worst {w})")
+    return {
+        "value": alg / per / 1e9,
+        "unit": "GB/s",
+        "cores": blas_threads if blas_threads else os.cpu_count(),
+        "kind": "oracle",
+        "sample": (f"{len(Ws)} full bf16 GEMVs M=1 K=4096 N=12288 (oracle: exact decode to fp64 + numpy "
+                   f"fp64 matvec), {sum(Ws):.1f} s of CPU work; host has {os.cpu_count()} logical CPUs; "
+                   f"decode single-threaded, BLAS threads as given in cores"),
+        "us_per_gemv": per * 1e6,
+        "gpu_parity_worst_err_over_tol": worst,
+    }
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000, help="timed launches (repeats of 200)")
+    ap.add_argument("--warmup", type=int, default=60000, help="untimed warm-up launches (~1 s)")
+    ap.add_argument("--arms", default="all", help="all, none, or a comma list of: ceiling,q8_0,q4_0,q8_1,"
+                                                  "multi_m,layer,small,prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--details", default=None, help="write the full results JSON here")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path is single-GPU "
+              f"by design: no sharding or collectives).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import skinny_gemm_decode_amd as skg
+    from synth import inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    timer = Timer(torch)
+    arms = set() if args.arms == "none" else (
+        {"ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "prefill"} if args.arms == "all"
+        else set(args.arms.split(",")))
+
+    # ---- headline: bf16 M=1 K=4096 N=12288 ----
+    N, K = 12288, 4096
+    x_host = si.activations_bf16(si.rng_for(0, 2, 0), 1, K)
+    keep = np.array(sorted({0, 1, N - 1, N - 2} | set(np.random.default_rng(0).choice(N, 60, replace=False).tolist())))
+    head, sample = bench_gemv_arm(skg, si, torch, timer, "bf16_m1_k4096_n12288", "bf16", skg.BF16_BF16, 1, N, K,
+                                  args.steps, args.warmup, None, x_host.view(np.int16), keep_rows=keep, graph=True)
+    sample["x"] = x_host
+    log(f"[headline] {head['us_per_launch']:.2f} us/launch  {head['gbs']:.0f} GB/s  "
+        f"({100 * head['frac_peak']:.1f}% of 8 TB/s)  spread {100 * head['spread']:.2f}%  "
+        f"graph {head['graph']['us_per_launch']:.2f} us")
+
+    details = {"headline": head, "arms": {}}
+    short = dict(steps=2000, warmup=0, warm_s=0.3)
+    if "ceiling" in arms:
+        details["arms"]["ceiling"] = bench_ceiling(skg, torch, timer, short["steps"], short["warm_s"])
+        log(f"[ceiling] {details['arms']['ceiling']['gbs']:.0f} GB/s")
+    for kind, fmt, key in (("q8_0", skg.Q8_0_F32, "q8_0"), ("q4_0", skg.Q4_0_F32, "q4_0"),
+                           ("q4_0", skg.Q4_0_Q8_1, "q8_1")):
+        if key not in arms:
+            continue
+        Ms = (1, 2, 4, 8) if ("multi_m" in arms and key != "q8_1") else (1,)
+        for M in Ms:
+            xh = si.activations_f32(si.rng_for(0, 4, M), M, 4096)
+            r, _ = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
+                                  14336, 4096, short["steps"], 0, short["warm_s"], xh, graph=True)
+            details["arms"][r["name"]] = r
+            log(f"[{r['name']}] {r['us_per_launch']:.2f} us  {r['gbs']:.0f} GB/s  graph "
+                f"{r['graph']['us_per_launch']:.2f} us ({r['graph']['gbs']:.0f} GB/s)")
+    if "small" in arms:
+        xh = si.activations_f32(si.rng_for(0, 1, 0), 1, 256)
+        r, _ = bench_gemv_arm(skg, si, torch, timer, "q8_0_f32_m1_k256_n512", "q8_0", skg.Q8_0_F32, 1, 512, 256,
+                              short["steps"], 0, short["warm_s"], xh, graph=True)
+        details["arms"][r["name"]] = r
+        log(f"[{r['name']}] {r['us_per_launch']:.2f} us (graph {r['graph']['us_per_launch']:.2f} us)")
+    if "layer" in arms:
+        r = bench_layer(skg, si, torch, timer, 640, 0.3)
+        details["arms"]["layer"] = r
+        log(f"[layer] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
+            f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
+    if "prefill" in arms:
+        r = bench_prefill(skg, si, torch, timer, 500, 0.3)
+        details["arms"]["prefill"] = r
+        log(f"[prefill] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "
+            f"({100 * r['frac_peak_mfma_bf16']:.1f}% of bf16 peak)")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(si, sample)
+    if cpu:
+        log(f"[cpu oracle] {cpu['value']:.2f} GB/s ({cpu['us_per_gemv']:.0f} us per GEMV, {cpu['cores']} threads)")
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_launch"] / 1000.0,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: bf16 weights N(0,0.02), bf16 activation N(0,1), seeded; generated on device",
+        "config": {
+            "workload": "bf16 GEMV M=1 K=4096 N=12288, cold-cache rotation",
+            "M": 1, "K": 4096, "N": 12288,
+            "rotation_buffers": head["rotation_buffers"],
+            "working_set_bytes": head["working_set_bytes"],
+            "us_per_launch": round(head["us_per_launch"], 3),
+            "frac_of_8TBs": round(head["frac_peak"], 4),
+            "spread": round(head["spread"], 4),
+            "spread_ok": head["spread_ok"],
+            "timer": "HIP events on the launch stream, eager launches, 200 per repeat",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["gbs"], 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(head["frac_peak"], 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+    }
+    details["line"] = line
+    details["cpu_baseline"] = cpu
+    path = args.details or (os.path.join(ROOT, "gpurun_out", "bench_details.json")
+                            if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else None)
+    if path:
+        with open(path, "w") as f:
+            json.dump(details, f, indent=1, default=lambda o: o.tolist() if hasattr(o, "tolist") else str(o))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

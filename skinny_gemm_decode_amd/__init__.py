@@ -1,0 +1,247 @@
+"""Python binding of libskg, the MI355X (gfx950) skinny decode GEMM / GEMV library.
+
+Argument marshalling only: every function here checks that its tensors live on
+the GPU, passes raw device pointers and the current HIP stream to the C ABI
+declared in ``include/skg.h``, and raises ``SkgError`` on a nonzero status.
+All arithmetic happens in the library's HIP kernels; there is no CPU fallback.
+Importing this module fails with ImportError when ``libskg.so`` has not been
+built (``python -m skinny_gemm_decode_amd.build``).
+
+PyTorch is used for device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskg.so")
+
+# skg_fmt
+BF16_BF16 = 0
+Q8_0_F32 = 1
+Q4_0_F32 = 2
+Q4_0_Q8_1 = 3
+Q8_0_Q8_1 = 4
+Q4_0_BF16 = 5
+FMT_NAMES = {BF16_BF16: "bf16_bf16", Q8_0_F32: "q8_0_f32", Q4_0_F32: "q4_0_f32",
+             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16"}
+# skg_epi
+EPI_NONE = 0
+EPI_SWIGLU = 1
+# skg_status
+OK, E_INVALID_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_DEVICE, E_HIP = range(7)
+
+Q8_1_BLOCK_BYTES = 36
+
+
+class SkgError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_str(status)}: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m skinny_gemm_decode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sigs = {
+        "skg_abi_version": (i32, []),
+        "skg_status_str": (ctypes.c_char_p, [i32]),
+        "skg_last_error": (ctypes.c_char_p, []),
+        "skg_packed_size": (sz, [i32, i64, i64]),
+        "skg_pack_weights": (i32, [i32, i64, i64, vp, vp, vp]),
+        "skg_packed_size_multi": (sz, [i32, i32, ctypes.POINTER(i64), i64]),
+        "skg_pack_weights_multi": (i32, [i32, i32, ctypes.POINTER(i64), i64, ctypes.POINTER(vp), vp, vp]),
+        "skg_quantize_act_q8_1": (i32, [i64, i64, vp, vp, vp]),
+        "skg_gemv": (i32, [i32, i64, i64, i64, vp, vp, vp, vp]),
+        "skg_gemv_multi": (i32, [i32, i64, i64, i32, ctypes.POINTER(i64), vp, vp, ctypes.POINTER(vp), i32, vp]),
+        "skg_gemm_tiled": (i32, [i32, i64, i64, i64, vp, vp, vp, vp]),
+        "skg_debug_block_dots": (i32, [i32, i64, i64, i64, i64, vp, vp, vp, vp]),
+        "skg_stream_read": (i32, [vp, sz, vp, vp]),
+        "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32]),
+        "skg_gemv_variants": (i32, [ctypes.POINTER(i32), i32]),
+        "skg_set_lds_pad": (i32, [i64]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def abi_version() -> int:
+    return lib.skg_abi_version()
+
+
+def status_str(status: int) -> str:
+    return lib.skg_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib.skg_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != OK:
+        raise SkgError(status, last_error())
+
+
+def _dev_ptr(t) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ---- packing -----------------------------------------------------------
+
+def packed_size(fmt: int, N: int, K: int) -> int:
+    return int(lib.skg_packed_size(fmt, N, K))
+
+
+def packed_size_multi(fmt: int, Ns: Sequence[int], K: int) -> int:
+    arr = (ctypes.c_int64 * len(Ns))(*Ns)
+    return int(lib.skg_packed_size_multi(fmt, len(Ns), arr, K))
+
+
+def pack_weights(fmt: int, N: int, K: int, src, dst=None, stream=None):
+    """Pack canonical weights (device tensor) into a new or given uint8 buffer."""
+    import torch
+
+    size = packed_size(fmt, N, K)
+    if size == 0:
+        check(lib.skg_pack_weights(fmt, N, K, None, None, None))
+    if dst is None:
+        dst = torch.empty(size, dtype=torch.uint8, device=src.device)
+    elif _nbytes(dst) < size:
+        raise ValueError(f"dst holds {_nbytes(dst)} bytes, packing needs {size}")
+    check(lib.skg_pack_weights(fmt, N, K, _dev_ptr(src), _dev_ptr(dst), _stream(stream)))
+    return dst
+
+
+def pack_weights_multi(fmt: int, Ns: Sequence[int], K: int, srcs, dst=None, stream=None):
+    """Pack several canonical matrices sharing K into one buffer (QKV, gate/up)."""
+    import torch
+
+    n = len(Ns)
+    size = packed_size_multi(fmt, Ns, K)
+    arr = (ctypes.c_int64 * n)(*Ns)
+    if size == 0:
+        check(lib.skg_pack_weights_multi(fmt, n, arr, K, None, None, None))
+    if dst is None:
+        dst = torch.empty(size, dtype=torch.uint8, device=srcs[0].device)
+    elif _nbytes(dst) < size:
+        raise ValueError(f"dst holds {_nbytes(dst)} bytes, packing needs {size}")
+    ptrs = (ctypes.c_void_p * n)(*[_dev_ptr(s) for s in srcs])
+    check(lib.skg_pack_weights_multi(fmt, n, arr, K, ptrs, _dev_ptr(dst), _stream(stream)))
+    return dst
+
+
+# ---- activation quantisation -------------------------------------------
+
+def quantize_act_q8_1(x, xq=None, stream=None):
+    """float32 [M, K] device tensor -> uint8 [M, K/32, 36] Q8_1 blocks."""
+    import torch
+
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K // 32, Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    check(lib.skg_quantize_act_q8_1(M, K, _dev_ptr(x), _dev_ptr(xq), _stream(stream)))
+    return xq
+
+
+# ---- products -------------------------------------------------------------
+
+def gemv(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
+    """y[M, N] = x W^T on packed weights W (skinny GEMM, 1 <= M <= 8)."""
+    import torch
+
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=W.device)
+    check(lib.skg_gemv(fmt, M, K, N, _dev_ptr(W), _dev_ptr(x), _dev_ptr(y), _stream(stream)))
+    return y
+
+
+def gemv_multi(fmt: int, M: int, K: int, Ns: Sequence[int], W, x, ys=None, epi: int = EPI_NONE, stream=None):
+    """Several packed matrices sharing x in one launch; SwiGLU writes one output."""
+    import torch
+
+    n = len(Ns)
+    nout = 1 if epi == EPI_SWIGLU else n
+    if ys is None:
+        ys = [torch.empty((M, Ns[i]), dtype=torch.float32, device=W.device) for i in range(nout)]
+    arr = (ctypes.c_int64 * n)(*Ns)
+    yp = (ctypes.c_void_p * nout)(*[_dev_ptr(t) for t in ys])
+    check(lib.skg_gemv_multi(fmt, M, K, n, arr, _dev_ptr(W), _dev_ptr(x), yp, epi, _stream(stream)))
+    return ys
+
+
+def gemm_tiled(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
+    """y[M, N] = x W^T on MFMA for large M (q4_0 weights, bf16 x)."""
+    import torch
+
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=W.device)
+    check(lib.skg_gemm_tiled(fmt, M, K, N, _dev_ptr(W), _dev_ptr(x), _dev_ptr(y), _stream(stream)))
+    return y
+
+
+def debug_block_dots(fmt: int, N: int, K: int, n0: int, nr: int, W, xq, out=None, stream=None):
+    """int32 [nr, K/32] integer block dots of rows [n0, n0+nr) (test hook)."""
+    import torch
+
+    if out is None:
+        out = torch.empty((nr, K // 32), dtype=torch.int32, device=W.device)
+    check(lib.skg_debug_block_dots(fmt, N, K, n0, nr, _dev_ptr(W), _dev_ptr(xq), _dev_ptr(out), _stream(stream)))
+    return out
+
+
+def stream_read(buf, nbytes: int | None = None, out=None, stream=None):
+    """Read nbytes of buf once (bandwidth ceiling); returns the sink tensor."""
+    import torch
+
+    if out is None:
+        out = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    nbytes = _nbytes(buf) if nbytes is None else nbytes
+    check(lib.skg_stream_read(_dev_ptr(buf), nbytes, _dev_ptr(out), _stream(stream)))
+    return out
+
+
+# ---- tuning hooks ------------------------------------------------------
+
+def gemv_variants():
+    """List of compiled GEMV variants as dicts (first per (fmt, M, epi) = default)."""
+    n = lib.skg_gemv_variants(None, 0)
+    buf = (ctypes.c_int * (7 * n))()
+    lib.skg_gemv_variants(buf, n)
+    keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves")
+    return [dict(zip(keys, buf[7 * i: 7 * i + 7])) for i in range(n)]
+
+
+def gemv_set_variant(fmt: int, M: int, epi: int = EPI_NONE, ro: int = 0, j: int = 0, x_lds: int = 0,
+                     waves: int = 4) -> None:
+    check(lib.skg_gemv_set_variant(fmt, M, epi, ro, j, x_lds, waves))
+
+
+def set_lds_pad(nbytes: int) -> None:
+    check(lib.skg_set_lds_pad(nbytes))

@@ -1,0 +1,396 @@
+// C ABI of the skinny decode GEMM / GEMV library: host-side validation,
+// device check, kernel selection and launch.  Every argument is validated on
+// the host before any HIP call, so every error path can be exercised without
+// a GPU; nothing falls back to another code path when validation fails.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "gemv_instances.h"
+#include "kernels.h"
+
+using namespace skg;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+skg_status fail(skg_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+skg_status ok() {
+  g_err[0] = '\0';
+  return SKG_OK;
+}
+
+constexpr int MAX_DEV = 64;
+std::atomic<int> g_dev_state[MAX_DEV];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[MAX_DEV];
+
+skg_status check_device(int* cus = nullptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SKG_E_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEV) return fail(SKG_E_DEVICE, "device index %d out of range", dev);
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(SKG_E_DEVICE, "hipGetDeviceProperties failed (%s)", hipGetErrorString(e));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return fail(SKG_E_DEVICE, "device %d is not gfx950; this library is built for gfx950 only", dev);
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return SKG_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_gemv_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1; }
+bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q4_0_BF16; }
+
+// K and N rules shared by packing and products.
+skg_status check_nk(int fmt, int64_t N, int64_t K) {
+  const int wk = wkind_of(fmt);
+  if (wk == WK_INVALID) return fail(SKG_E_INVALID_ARG, "unknown fmt %d", fmt);
+  if (N < 1) return fail(SKG_E_SHAPE, "N must be >= 1 (got %lld)", (long long)N);
+  if (wk == WK_BF16) {
+    if (K < 8 || K % 8) return fail(SKG_E_SHAPE, "bf16 needs K >= 8 and K %% 8 == 0 (got %lld)", (long long)K);
+  } else {
+    if (K < 32 || K % 32) return fail(SKG_E_SHAPE, "q8_0/q4_0 need K >= 32 and K %% 32 == 0 (got %lld)", (long long)K);
+  }
+  if (K > (int64_t(1) << 30) || N > (int64_t(1) << 31))
+    return fail(SKG_E_SHAPE, "N=%lld K=%lld exceed the supported range", (long long)N, (long long)K);
+  return SKG_OK;
+}
+
+// ---- GEMV variant registry ------------------------------------------------
+
+std::once_flag g_reg_once;
+std::vector<GemvEntry>* g_reg = nullptr;
+std::mutex g_sel_mu;
+// selected registry index per (fmt, M, epi); -1 = default (first registered)
+int g_sel[5][9][2];
+std::atomic<int64_t> g_lds_pad{0};
+
+void init_registry() {
+  std::call_once(g_reg_once, [] {
+    auto* v = new std::vector<GemvEntry>();
+    register_gemv_bf16(*v);
+    register_gemv_q8_0_f32(*v);
+    register_gemv_q8_0_f32_m38(*v);
+    register_gemv_q4_0_f32(*v);
+    register_gemv_q4_0_f32_m35(*v);
+    register_gemv_q4_0_f32_m68(*v);
+    register_gemv_q8_1(*v);
+    for (auto& a : g_sel)
+      for (auto& b : a)
+        for (int& c : b) c = -1;
+    if (const char* e = std::getenv("SKG_LDS_PAD_BYTES")) g_lds_pad.store(std::atoll(e));
+    g_reg = v;
+  });
+}
+
+const GemvEntry* find_variant(int fmt, int M, int epi) {
+  init_registry();
+  int sel;
+  {
+    std::lock_guard<std::mutex> lk(g_sel_mu);
+    sel = g_sel[fmt][M][epi];
+  }
+  if (sel >= 0) return &(*g_reg)[size_t(sel)];
+  for (const GemvEntry& e : *g_reg)
+    if (e.fmt == fmt && e.M == M && e.epi == epi) return &e;
+  return nullptr;
+}
+
+size_t packed_size_multi(int fmt, int n, const int64_t* Ns, int64_t K) {
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) total += layout_of(wkind_of(fmt), Ns[i], K).total;
+  return total;
+}
+
+skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const int64_t* Ns, const void* W,
+                                const void* x, float* const* ys, int epi, hipStream_t stream) {
+  const GemvEntry* v = find_variant(fmt, int(M), epi);
+  if (!v) return fail(SKG_E_UNSUPPORTED, "no compiled kernel for fmt=%d M=%lld epi=%d", fmt, (long long)M, epi);
+  const int wk = wkind_of(fmt);
+  GemvArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.K = K;
+  a.nu = uint32_t(wk == WK_BF16 ? K / 8 : K / 32);
+  a.x = static_cast<const uint8_t*>(x);
+  const int rows_per_block = v->waves * v->ro;
+  int64_t blocks = 0;
+  const uint8_t* base = static_cast<const uint8_t*>(W);
+  if (epi == SKG_EPI_SWIGLU) {
+    const Layout L = layout_of(wk, Ns[0], K);
+    a.nseg = 1;
+    a.seg[0].w0 = packed_view(base, L);
+    a.seg[0].w1 = packed_view(base + L.total, L);
+    a.seg[0].y = ys[0];
+    a.seg[0].N = Ns[0];
+    a.seg[0].blk_begin = 0;
+    blocks = (Ns[0] + rows_per_block - 1) / rows_per_block;
+  } else {
+    a.nseg = nseg;
+    size_t off = 0;
+    for (int i = 0; i < nseg; ++i) {
+      const Layout L = layout_of(wk, Ns[i], K);
+      a.seg[i].w0 = packed_view(base + off, L);
+      a.seg[i].w1 = a.seg[i].w0;
+      a.seg[i].y = ys[i];
+      a.seg[i].N = Ns[i];
+      a.seg[i].blk_begin = int(blocks);
+      blocks += (Ns[i] + rows_per_block - 1) / rows_per_block;
+      off += L.total;
+    }
+  }
+  if (blocks > 0x7FFFFFFF) return fail(SKG_E_SHAPE, "too many rows");
+  size_t lds = gemv_lds_bytes(fmt, int(M), v->j, v->xlds) + size_t(g_lds_pad.load());
+  if (lds > 160 * 1024) return fail(SKG_E_UNSUPPORTED, "variant needs %zu bytes of LDS", lds);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+  }
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(v->fn, dim3(unsigned(blocks)), dim3(unsigned(v->waves * 64)), args, lds, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "gemv launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status check_gemv_common(int fmt, int64_t M, int64_t K, const void* W, const void* x) {
+  if (!is_gemv_fmt(fmt)) {
+    if (is_any_fmt(fmt)) return fail(SKG_E_UNSUPPORTED, "fmt %d is not a gemv format (use skg_gemm_tiled)", fmt);
+    return fail(SKG_E_INVALID_ARG, "unknown fmt %d", fmt);
+  }
+  if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "gemv needs 1 <= M <= 8 (got %lld)", (long long)M);
+  if (!W || !x) return fail(SKG_E_INVALID_ARG, "null W or x");
+  if (!aligned(W, 16)) return fail(SKG_E_ALIGN, "W must be 16-byte aligned");
+  const bool q8 = (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1);
+  if (!aligned(x, q8 ? 4 : 16)) return fail(SKG_E_ALIGN, "x must be %d-byte aligned", q8 ? 4 : 16);
+  (void)K;
+  return SKG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int skg_abi_version(void) { return SKG_ABI_VERSION; }
+
+const char* skg_status_str(int status) {
+  switch (status) {
+    case SKG_OK: return "SKG_OK";
+    case SKG_E_INVALID_ARG: return "SKG_E_INVALID_ARG";
+    case SKG_E_SHAPE: return "SKG_E_SHAPE";
+    case SKG_E_ALIGN: return "SKG_E_ALIGN";
+    case SKG_E_UNSUPPORTED: return "SKG_E_UNSUPPORTED";
+    case SKG_E_DEVICE: return "SKG_E_DEVICE";
+    case SKG_E_HIP: return "SKG_E_HIP";
+    default: return "SKG_E_UNKNOWN";
+  }
+}
+
+const char* skg_last_error(void) { return g_err; }
+
+size_t skg_packed_size(skg_fmt fmt, int64_t N, int64_t K) {
+  if (check_nk(fmt, N, K) != SKG_OK) return 0;
+  return layout_of(wkind_of(fmt), N, K).total;
+}
+
+size_t skg_packed_size_multi(skg_fmt fmt, int n, const int64_t* Ns, int64_t K) {
+  if (n < 1 || n > MAX_SEGS || !Ns) return 0;
+  for (int i = 0; i < n; ++i)
+    if (check_nk(fmt, Ns[i], K) != SKG_OK) return 0;
+  return packed_size_multi(fmt, n, Ns, K);
+}
+
+skg_status skg_pack_weights(skg_fmt fmt, int64_t N, int64_t K, const void* src, void* dst, hipStream_t stream) {
+  skg_status st = check_nk(fmt, N, K);
+  if (st != SKG_OK) return st;
+  if (!src || !dst) return fail(SKG_E_INVALID_ARG, "null src or dst");
+  if (!aligned(src, 2)) return fail(SKG_E_ALIGN, "src must be 2-byte aligned");
+  if (!aligned(dst, 16)) return fail(SKG_E_ALIGN, "dst must be 16-byte aligned");
+  if ((st = check_device()) != SKG_OK) return st;
+  hipError_t e = launch_pack(wkind_of(fmt), N, K, src, dst, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "pack: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_pack_weights_multi(skg_fmt fmt, int n, const int64_t* Ns, int64_t K, const void* const* srcs,
+                                  void* dst, hipStream_t stream) {
+  if (n < 1 || n > MAX_SEGS) return fail(SKG_E_INVALID_ARG, "n must be 1..%d (got %d)", MAX_SEGS, n);
+  if (!Ns || !srcs || !dst) return fail(SKG_E_INVALID_ARG, "null Ns, srcs or dst");
+  for (int i = 0; i < n; ++i) {
+    skg_status st = check_nk(fmt, Ns[i], K);
+    if (st != SKG_OK) return st;
+    if (!srcs[i]) return fail(SKG_E_INVALID_ARG, "null srcs[%d]", i);
+    if (!aligned(srcs[i], 2)) return fail(SKG_E_ALIGN, "srcs[%d] must be 2-byte aligned", i);
+  }
+  if (!aligned(dst, 16)) return fail(SKG_E_ALIGN, "dst must be 16-byte aligned");
+  skg_status st = check_device();
+  if (st != SKG_OK) return st;
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = launch_pack(wkind_of(fmt), Ns[i], K, srcs[i], static_cast<uint8_t*>(dst) + off, stream);
+    if (e != hipSuccess) return fail(SKG_E_HIP, "pack: %s", hipGetErrorString(e));
+    off += layout_of(wkind_of(fmt), Ns[i], K).total;
+  }
+  return ok();
+}
+
+skg_status skg_quantize_act_q8_1(int64_t M, int64_t K, const float* x, void* xq, hipStream_t stream) {
+  if (M < 1) return fail(SKG_E_SHAPE, "M must be >= 1 (got %lld)", (long long)M);
+  if (K < 32 || K % 32) return fail(SKG_E_SHAPE, "K must be >= 32 and a multiple of 32 (got %lld)", (long long)K);
+  if (M * (K / 32) > (int64_t(1) << 36)) return fail(SKG_E_SHAPE, "too many blocks");
+  if (!x || !xq) return fail(SKG_E_INVALID_ARG, "null x or xq");
+  if (!aligned(x, 16)) return fail(SKG_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(xq, 4)) return fail(SKG_E_ALIGN, "xq must be 4-byte aligned");
+  skg_status st = check_device();
+  if (st != SKG_OK) return st;
+  hipError_t e = launch_quantize_q8_1(M, K, x, xq, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "quantize: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_gemv(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x, float* y,
+                    hipStream_t stream) {
+  skg_status st = check_gemv_common(fmt, M, K, W, x);
+  if (st != SKG_OK) return st;
+  if ((st = check_nk(fmt, N, K)) != SKG_OK) return st;
+  if (!y) return fail(SKG_E_INVALID_ARG, "null y");
+  if (!aligned(y, 4)) return fail(SKG_E_ALIGN, "y must be 4-byte aligned");
+  if ((st = check_device()) != SKG_OK) return st;
+  return launch_gemv_segments(fmt, M, K, 1, &N, W, x, &y, SKG_EPI_NONE, stream);
+}
+
+skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_t* Ns, const void* W,
+                          const void* x, float* const* ys, skg_epi epi, hipStream_t stream) {
+  skg_status st = check_gemv_common(fmt, M, K, W, x);
+  if (st != SKG_OK) return st;
+  if (!Ns || !ys) return fail(SKG_E_INVALID_ARG, "null Ns or ys");
+  if (epi == SKG_EPI_NONE) {
+    if (n < 1 || n > MAX_SEGS) return fail(SKG_E_INVALID_ARG, "n must be 1..%d (got %d)", MAX_SEGS, n);
+  } else if (epi == SKG_EPI_SWIGLU) {
+    if (n != 2) return fail(SKG_E_INVALID_ARG, "SwiGLU needs n == 2 (gate, up), got %d", n);
+    if (Ns[0] != Ns[1]) return fail(SKG_E_SHAPE, "SwiGLU needs Ns[0] == Ns[1]");
+  } else {
+    return fail(SKG_E_INVALID_ARG, "unknown epilogue %d", int(epi));
+  }
+  for (int i = 0; i < n; ++i)
+    if ((st = check_nk(fmt, Ns[i], K)) != SKG_OK) return st;
+  const int nout = (epi == SKG_EPI_SWIGLU) ? 1 : n;
+  for (int i = 0; i < nout; ++i) {
+    if (!ys[i]) return fail(SKG_E_INVALID_ARG, "null ys[%d]", i);
+    if (!aligned(ys[i], 4)) return fail(SKG_E_ALIGN, "ys[%d] must be 4-byte aligned", i);
+  }
+  if ((st = check_device()) != SKG_OK) return st;
+  return launch_gemv_segments(fmt, M, K, n, Ns, W, x, ys, epi, stream);
+}
+
+skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x, float* y,
+                          hipStream_t stream) {
+  if (!is_any_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown fmt %d", int(fmt));
+  if (fmt != SKG_Q4_0_BF16) return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16 only");
+  skg_status st = check_nk(fmt, N, K);
+  if (st != SKG_OK) return st;
+  if (M < 1 || M > (int64_t(1) << 31)) return fail(SKG_E_SHAPE, "M must be >= 1 (got %lld)", (long long)M);
+  if (!W || !x || !y) return fail(SKG_E_INVALID_ARG, "null W, x or y");
+  if (!aligned(W, 16) || !aligned(x, 16)) return fail(SKG_E_ALIGN, "W and x must be 16-byte aligned");
+  if (!aligned(y, 4)) return fail(SKG_E_ALIGN, "y must be 4-byte aligned");
+  if ((st = check_device()) != SKG_OK) return st;
+  const Layout L = layout_of(WK_Q4_0, N, K);
+  hipError_t e = launch_gemm_tiled(M, K, N, W, L, x, y, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "gemm_tiled: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_debug_block_dots(skg_fmt fmt, int64_t N, int64_t K, int64_t n0, int64_t nr, const void* W,
+                                const void* xq, int32_t* out, hipStream_t stream) {
+  if (fmt != SKG_Q4_0_Q8_1 && fmt != SKG_Q8_0_Q8_1) {
+    if (is_any_fmt(fmt)) return fail(SKG_E_UNSUPPORTED, "block dots exist for the Q8_1 formats only");
+    return fail(SKG_E_INVALID_ARG, "unknown fmt %d", int(fmt));
+  }
+  skg_status st = check_nk(fmt, N, K);
+  if (st != SKG_OK) return st;
+  if (n0 < 0 || nr < 1 || n0 + nr > N) return fail(SKG_E_SHAPE, "rows [n0, n0+nr) must lie in [0, N)");
+  if (!W || !xq || !out) return fail(SKG_E_INVALID_ARG, "null W, xq or out");
+  if (!aligned(W, 16) || !aligned(xq, 4) || !aligned(out, 4)) return fail(SKG_E_ALIGN, "misaligned pointer");
+  if ((st = check_device()) != SKG_OK) return st;
+  hipError_t e = launch_block_dots(fmt, W, layout_of(wkind_of(fmt), N, K), n0, nr, xq, out, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "block dots: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream) {
+  if (!buf || !out) return fail(SKG_E_INVALID_ARG, "null buf or out");
+  if (bytes == 0 || bytes % 16) return fail(SKG_E_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned(buf, 16) || !aligned(out, 4)) return fail(SKG_E_ALIGN, "buf must be 16-byte aligned");
+  int cus = 0;
+  skg_status st = check_device(&cus);
+  if (st != SKG_OK) return st;
+  hipError_t e = launch_stream_read(buf, bytes, out, cus * 8, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "stream read: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves) {
+  if (!is_gemv_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown gemv fmt %d", int(fmt));
+  if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "M must be 1..8");
+  if (epi != SKG_EPI_NONE && epi != SKG_EPI_SWIGLU) return fail(SKG_E_INVALID_ARG, "unknown epilogue");
+  init_registry();
+  int idx = -1;
+  if (ro != 0) {
+    for (size_t i = 0; i < g_reg->size(); ++i) {
+      const GemvEntry& e = (*g_reg)[i];
+      if (e.fmt == fmt && e.M == M && e.epi == epi && e.ro == ro && e.j == j && e.xlds == x_lds && e.waves == waves) {
+        idx = int(i);
+        break;
+      }
+    }
+    if (idx < 0) return fail(SKG_E_UNSUPPORTED, "no compiled variant ro=%d j=%d x_lds=%d waves=%d", ro, j, x_lds, waves);
+  }
+  std::lock_guard<std::mutex> lk(g_sel_mu);
+  g_sel[fmt][M][epi] = idx;
+  return ok();
+}
+
+int skg_gemv_variants(int* out, int max_entries) {
+  init_registry();
+  const int n = int(g_reg->size());
+  if (out) {
+    for (int i = 0; i < n && i < max_entries; ++i) {
+      const GemvEntry& e = (*g_reg)[size_t(i)];
+      int* o = out + 7 * i;
+      o[0] = e.fmt;
+      o[1] = e.M;
+      o[2] = e.epi;
+      o[3] = e.ro;
+      o[4] = e.j;
+      o[5] = e.xlds;
+      o[6] = e.waves;
+    }
+  }
+  return n;
+}
+
+skg_status skg_set_lds_pad(int64_t bytes) {
+  if (bytes < 0 || bytes > 64 * 1024) return fail(SKG_E_INVALID_ARG, "LDS pad must be 0..65536 bytes");
+  init_registry();
+  g_lds_pad.store(bytes);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal definitions shared by the library's HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "skg.h"
+
+namespace skg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QK = 32;  // elements per quantisation block along K
+
+enum WKind { WK_BF16 = 0, WK_Q8_0 = 1, WK_Q4_0 = 2, WK_INVALID = -1 };
+
+__host__ __device__ inline int wkind_of(int fmt) {
+  switch (fmt) {
+    case SKG_BF16_BF16: return WK_BF16;
+    case SKG_Q8_0_F32:
+    case SKG_Q8_0_Q8_1: return WK_Q8_0;
+    case SKG_Q4_0_F32:
+    case SKG_Q4_0_Q8_1:
+    case SKG_Q4_0_BF16: return WK_Q4_0;
+    default: return WK_INVALID;
+  }
+}
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Packed weight layout (opaque to callers, version 1):
+//   payload: row-major, row n at n * row_bytes.  Within a row, 16-byte units
+//     in K order: bf16 -> 8 elements per unit (the canonical row unchanged);
+//     q4_0 -> one unit per block (its 16 code bytes);
+//     q8_0 -> two planes of nb units: plane 0 holds codes 0..15 of every
+//             block, plane 1 codes 16..31, so each plane streams contiguously.
+//   scales (q8_0, q4_0): fp16 [N][nb] at scale_off (256-byte aligned).
+struct Layout {
+  int64_t N = 0, K = 0, nb = 0;
+  int wk = WK_INVALID;
+  size_t row_bytes = 0, payload_bytes = 0, scale_off = 0, total = 0;
+};
+
+__host__ __device__ inline Layout layout_of(int wk, int64_t N, int64_t K) {
+  Layout L;
+  L.N = N;
+  L.K = K;
+  L.wk = wk;
+  L.nb = K / QK;
+  if (wk == WK_BF16) {
+    L.row_bytes = size_t(K) * 2;
+    L.payload_bytes = size_t(N) * L.row_bytes;
+    L.scale_off = align256(L.payload_bytes);
+    L.total = L.scale_off;
+  } else {
+    L.row_bytes = size_t(L.nb) * (wk == WK_Q8_0 ? 32 : 16);
+    L.payload_bytes = size_t(N) * L.row_bytes;
+    L.scale_off = align256(L.payload_bytes);
+    L.total = align256(L.scale_off + size_t(N) * size_t(L.nb) * 2);
+  }
+  return L;
+}
+
+// A packed matrix as the kernels see it.
+struct PackedW {
+  const uint8_t* payload;
+  const uint16_t* scales;
+  uint32_t row_bytes;
+  uint32_t nb;
+};
+
+inline PackedW packed_view(const void* base, const Layout& L) {
+  PackedW p;
+  p.payload = static_cast<const uint8_t*>(base);
+  p.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(base) + L.scale_off);
+  p.row_bytes = uint32_t(L.row_bytes);
+  p.nb = uint32_t(L.nb);
+  return p;
+}
+
+__device__ inline u32x4 ld_u32x4(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ inline float h2f(uint32_t bits16) {
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
+}
+
+// DPP row operations (gfx9 encodings).
+#define SKG_DPP_QUAD_XOR1 0xB1   // quad_perm [1,0,3,2]
+#define SKG_DPP_QUAD_XOR2 0x4E   // quad_perm [2,3,0,1]
+#define SKG_DPP_ROW_HALF_MIRROR 0x141
+#define SKG_DPP_ROW_MIRROR 0x140
+
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the same total.
+// Quads first (two quad_perm swaps), then 8 and 16 lanes by mirroring, then
+// the 16-lane rows by swapping across the two 32-lane halves and across rows.
+__device__ inline float wave_sum(float v) {
+  v += dpp_f<SKG_DPP_QUAD_XOR1>(v);
+  v += dpp_f<SKG_DPP_QUAD_XOR2>(v);
+  v += dpp_f<SKG_DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f<SKG_DPP_ROW_MIRROR>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+}  // namespace skg

@@ -1,0 +1,408 @@
+// Skinny GEMM / GEMV kernels: y[m][n] = sum_k W[n][k] x[m][k], 1 <= M <= 8.
+//
+// The decode product streams every weight once from HBM ("The Shape That
+// Actually Matters", The shape a decode step actually runs), so the kernel is
+// organised around the weight stream:
+//
+// * A wave owns RO output rows (2*RO weight rows for the SwiGLU epilogue).
+//   Its 64 lanes split K into 16-byte units: lane l takes units l, l+64, ...
+//   so each wave-wide 16-byte load reads 1 KB of one row contiguously, and a
+//   lane always owns whole q4_0 / q8_0 blocks ("Six hypotheses, four
+//   refutations", What the failure left behind: a full data block per lane
+//   through wide loads, several output rows per workgroup).
+// * K is walked in chunks of 64*J units per lane-row; all RT*J weight loads of
+//   a chunk are issued before any of them is consumed.
+// * The activation is fetched once per wave per chunk and reused for every
+//   row the wave owns: from global memory into registers (XLDS = false), or
+//   staged once per workgroup in LDS (XLDS = true) for larger M.  Re-fetching
+//   an already cached activation per row is exactly the waste the MI50 case
+//   study found (Hypothesis ledger: 3 of 5 memory instructions per iteration).
+// * Products accumulate in fp32 (int32 within a block for the Q8_1 formats),
+//   then one DPP/shuffle reduction per output over the 64 lanes.
+#pragma once
+
+#include "common.h"
+
+namespace skg {
+
+template <int FMT>
+struct Fmt;
+
+template <>
+struct Fmt<SKG_BF16_BF16> {
+  static constexpr int E = 8, WV = 4, XB = 16, XF = 8;
+  static constexpr bool SCALE = false, XQ8 = false, XSUM = false;
+};
+template <>
+struct Fmt<SKG_Q8_0_F32> {
+  static constexpr int E = 32, WV = 8, XB = 128, XF = 32;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
+};
+template <>
+struct Fmt<SKG_Q4_0_F32> {
+  static constexpr int E = 32, WV = 4, XB = 128, XF = 32;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
+};
+template <>
+struct Fmt<SKG_Q4_0_Q8_1> {
+  static constexpr int E = 32, WV = 4, XB = 36, XF = 0;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
+};
+template <>
+struct Fmt<SKG_Q8_0_Q8_1> {
+  static constexpr int E = 32, WV = 8, XB = 36, XF = 0;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
+};
+
+// One 16-byte (bf16, q4_0) or 2x16-byte (q8_0) weight unit and its scale.
+template <int FMT>
+struct WUnit {
+  uint32_t w[Fmt<FMT>::WV];
+  float d;
+};
+
+// One activation unit in compute form.
+template <int FMT, bool Q8 = Fmt<FMT>::XQ8>
+struct XUnit;
+template <int FMT>
+struct XUnit<FMT, false> {
+  float v[Fmt<FMT>::XF];
+  float sum;
+};
+template <int FMT>
+struct XUnit<FMT, true> {
+  uint32_t q[8];
+  float d, s;
+};
+
+template <int FMT>
+__device__ inline void zero_w(WUnit<FMT>& u) {
+#pragma unroll
+  for (int k = 0; k < Fmt<FMT>::WV; ++k) u.w[k] = 0;
+  u.d = 0.f;
+}
+
+// rowp: start of the row's payload; srow: the row's fp16 scales.
+template <int FMT>
+__device__ inline void load_w(WUnit<FMT>& u, const uint8_t* rowp, const uint16_t* srow, uint32_t nb,
+                              uint32_t unit) {
+  const u32x4 p = ld_u32x4(rowp + size_t(unit) * 16);
+  u.w[0] = p.x;
+  u.w[1] = p.y;
+  u.w[2] = p.z;
+  u.w[3] = p.w;
+  if constexpr (Fmt<FMT>::WV == 8) {
+    const u32x4 q = ld_u32x4(rowp + (size_t(nb) + unit) * 16);
+    u.w[4] = q.x;
+    u.w[5] = q.y;
+    u.w[6] = q.z;
+    u.w[7] = q.w;
+  }
+  if constexpr (Fmt<FMT>::SCALE) {
+    u.d = h2f(srow[unit]);
+  } else {
+    u.d = 0.f;
+  }
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ inline float ubyte(uint32_t w, int i) { return float((w >> (8 * i)) & 0xFFu); }
+
+template <int FMT>
+__device__ inline void zero_x(XUnit<FMT>& x) {
+  if constexpr (Fmt<FMT>::XQ8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.q[k] = 0;
+    x.d = 0.f;
+    x.s = 0.f;
+  } else {
+#pragma unroll
+    for (int k = 0; k < Fmt<FMT>::XF; ++k) x.v[k] = 0.f;
+    x.sum = 0.f;
+  }
+}
+
+// Activation unit from raw 16-byte pieces (bf16 / fp32 layouts).
+template <int FMT>
+__device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
+  if constexpr (FMT == SKG_BF16_BF16) {
+    const u32x4 p = pc[0];
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x.v[2 * k] = bf16_lo(w[k]);
+      x.v[2 * k + 1] = bf16_hi(w[k]);
+    }
+    x.sum = 0.f;
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const u32x4 v = pc[p];
+      x.v[4 * p + 0] = __uint_as_float(v.x);
+      x.v[4 * p + 1] = __uint_as_float(v.y);
+      x.v[4 * p + 2] = __uint_as_float(v.z);
+      x.v[4 * p + 3] = __uint_as_float(v.w);
+    }
+    // The block sum is accumulated in the same element order as the code x
+    // activation chain of unit_acc, so that a block whose codes are all equal
+    // (all 8 for q4_0, all 0 for q8_0) cancels to exactly zero: scaling every
+    // term by a power of two commutes with each rounding.
+    if constexpr (FMT == SKG_Q4_0_F32) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += x.v[4 * k + i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += x.v[16 + 4 * k + i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s += x.v[i];
+    }
+    x.sum = s;
+  }
+}
+
+// Activation unit straight from global memory (row m, unit index u).
+template <int FMT>
+__device__ inline void fetch_x_global(XUnit<FMT>& x, const uint8_t* xb, int64_t K, uint32_t nb, int m,
+                                      uint32_t u) {
+  if constexpr (Fmt<FMT>::XQ8) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(xb + (size_t(m) * nb + u) * 36);
+    const uint32_t ds = p[0];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.q[k] = p[1 + k];
+    x.d = h2f(ds & 0xFFFFu);
+    x.s = h2f(ds >> 16);
+  } else {
+    constexpr int PP = Fmt<FMT>::XB / 16;
+    constexpr int ESZ = Fmt<FMT>::XB / Fmt<FMT>::E;
+    const u32x4* src = reinterpret_cast<const u32x4*>(xb + (size_t(m) * size_t(K) + size_t(u) * Fmt<FMT>::E) * ESZ);
+    u32x4 pc[PP];
+#pragma unroll
+    for (int p = 0; p < PP; ++p) pc[p] = src[p];
+    x_from_pieces<FMT>(x, pc);
+  }
+}
+
+// Integer block dot of the Q8_1 formats (exact int32).
+template <int FMT>
+__device__ inline int unit_idot(const WUnit<FMT>& w, const XUnit<FMT, true>& x) {
+  int si = 0;
+  if constexpr (FMT == SKG_Q4_0_Q8_1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      si = __builtin_amdgcn_sdot4(int(w.w[k] & 0x0F0F0F0Fu), int(x.q[k]), si, false);
+      si = __builtin_amdgcn_sdot4(int((w.w[k] >> 4) & 0x0F0F0F0Fu), int(x.q[4 + k]), si, false);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) si = __builtin_amdgcn_sdot4(int(w.w[k]), int(x.q[k]), si, false);
+  }
+  return si;
+}
+
+// acc + (contribution of one weight unit against one activation unit).
+template <int FMT>
+__device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float acc) {
+  if constexpr (FMT == SKG_BF16_BF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc = fmaf(bf16_lo(w.w[k]), x.v[2 * k], acc);
+      acc = fmaf(bf16_hi(w.w[k]), x.v[2 * k + 1], acc);
+    }
+    return acc;
+  } else if constexpr (FMT == SKG_Q4_0_F32) {
+    // sum_i (c_i - 8) x_i = sum_i c_i x_i - 8 sum_i x_i
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = w.w[k] & 0x0F0F0F0Fu;
+      const uint32_t hi = (w.w[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(ubyte(lo, i), x.v[4 * k + i], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(ubyte(hi, i), x.v[16 + 4 * k + i], s);
+    }
+    return fmaf(w.d, fmaf(-8.f, x.sum, s), acc);
+  } else if constexpr (FMT == SKG_Q8_0_F32) {
+    // int8 q + 128 is the unsigned byte of q ^ 0x80: sum_i q_i x_i =
+    // sum_i (q_i + 128) x_i - 128 sum_i x_i
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b = w.w[k] ^ 0x80808080u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(ubyte(b, i), x.v[4 * k + i], s);
+    }
+    return fmaf(w.d, fmaf(-128.f, x.sum, s), acc);
+  } else if constexpr (FMT == SKG_Q4_0_Q8_1) {
+    const int si = unit_idot<FMT>(w, x);
+    return fmaf(w.d, fmaf(x.d, float(si), -8.f * x.s), acc);
+  } else {
+    const int si = unit_idot<FMT>(w, x);
+    return fmaf(w.d * x.d, float(si), acc);
+  }
+}
+
+__device__ inline float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// One output segment of a launch: a matrix (two for SwiGLU) and its output.
+struct Seg {
+  PackedW w0, w1;
+  float* y;
+  int64_t N;
+  int blk_begin;
+};
+
+constexpr int MAX_SEGS = 4;
+
+struct GemvArgs {
+  Seg seg[MAX_SEGS];
+  int nseg;
+  int64_t K;
+  uint32_t nu;  // 16-byte weight units per row (K/8 bf16, K/32 quantised)
+  const uint8_t* x;
+};
+
+template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
+  using F = Fmt<FMT>;
+  constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
+  constexpr int RT = RO * NR;
+  constexpr int UC = 64 * J;
+  constexpr int PP = F::XB / 16;
+  extern __shared__ u32x4 xlds[];
+
+  const int blk = blockIdx.x;
+  // Segment of this workgroup; selected with compile-time indices so the
+  // argument block is read with scalar loads, never copied to scratch.
+  Seg sg = a.seg[0];
+#pragma unroll
+  for (int i = 1; i < MAX_SEGS; ++i)
+    if (i < a.nseg && blk >= a.seg[i].blk_begin) sg = a.seg[i];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t n0 = (int64_t(blk - sg.blk_begin) * WAVES + wave) * RO;
+
+  const uint8_t* rowp[RT];
+  const uint16_t* srow[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const PackedW& P = (r < RO) ? sg.w0 : sg.w1;
+    const int64_t n = n0 + (r % RO);
+    const int64_t nn = (n < sg.N) ? n : 0;
+    rowp[r] = P.payload + size_t(nn) * P.row_bytes;
+    srow[r] = P.scales + size_t(nn) * P.nb;
+  }
+  const uint32_t nb = sg.w0.nb;
+  const uint32_t nu = a.nu;
+
+  float acc[RT][M];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+
+  const int nchunks = int((nu + UC - 1) / UC);
+  for (int c = 0; c < nchunks; ++c) {
+    const uint32_t ub = uint32_t(c) * UC;
+    // Loads are unconditional: a unit past the end of the row reads unit 0
+    // of the row (its activation is zeroed below, so it adds exactly 0), and
+    // a row past N reads row 0 (its output is never stored).
+    WUnit<FMT> w[RT][J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t u = ub + uint32_t(j * 64 + lane);
+      const uint32_t uc = (u < nu) ? u : 0u;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) load_w<FMT>(w[r][j], rowp[r], srow[r], nb, uc);
+    }
+    if constexpr (XLDS) {
+      // Stage this chunk's activation for all M rows: piece-planar layout
+      // [m][piece][unit] so that lanes reading consecutive units hit
+      // consecutive 16-byte LDS words (no bank conflicts).
+      if (c > 0) __syncthreads();
+      constexpr int ESZ = F::XB / F::E;
+      const int total = M * UC * PP;
+      for (int i = threadIdx.x; i < total; i += WAVES * 64) {
+        const int p = i % PP;
+        const int t = i / PP;
+        const int uu = t % UC;
+        const int m = t / UC;
+        const uint32_t gu = ub + uint32_t(uu);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (gu < nu)
+          v = ld_u32x4(a.x + (size_t(m) * size_t(a.K) + size_t(gu) * F::E) * ESZ + size_t(p) * 16);
+        xlds[(m * PP + p) * UC + uu] = v;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t u = ub + uint32_t(j * 64 + lane);
+      const bool uok = u < nu;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        XUnit<FMT> xu;
+        if constexpr (XLDS) {
+          u32x4 pc[PP];
+#pragma unroll
+          for (int p = 0; p < PP; ++p) pc[p] = xlds[(m * PP + p) * UC + j * 64 + lane];
+          x_from_pieces<FMT>(xu, pc);
+        } else {
+          fetch_x_global<FMT>(xu, a.x, a.K, nb, m, uok ? u : 0u);
+          if (!uok) zero_x<FMT>(xu);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r][m] = unit_acc<FMT>(w[r][j], xu, acc[r][m]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+
+  float out = 0.f;
+#pragma unroll
+  for (int ro = 0; ro < RO; ++ro)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (lane == ro * M + m) {
+        if constexpr (EPI == SKG_EPI_SWIGLU)
+          out = silu_f32(acc[ro][m]) * acc[RO + ro][m];
+        else
+          out = acc[ro][m];
+      }
+  if (lane < RO * M) {
+    const int ro = lane / M;
+    const int m = lane % M;
+    const int64_t n = n0 + ro;
+    if (n < sg.N) sg.y[size_t(m) * size_t(sg.N) + size_t(n)] = out;
+  }
+}
+
+// Registry entry of one compiled kernel instance.
+struct GemvEntry {
+  const void* fn;
+  int fmt, M, epi, ro, j, xlds, waves;
+};
+
+template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI>
+inline GemvEntry gemv_entry() {
+  return GemvEntry{reinterpret_cast<const void*>(&gemv_kernel<FMT, M, RO, J, XLDS, WAVES, EPI>),
+                   FMT, M, EPI, RO, J, XLDS ? 1 : 0, WAVES};
+}
+
+// LDS bytes an instance needs (0 when the activation lives in registers).
+inline size_t gemv_lds_bytes(int fmt, int M, int J, int xlds) {
+  if (!xlds) return 0;
+  const int xb = (fmt == SKG_BF16_BF16) ? 16 : 128;
+  return size_t(M) * size_t(64 * J) * size_t(xb);
+}
+
+}  // namespace skg

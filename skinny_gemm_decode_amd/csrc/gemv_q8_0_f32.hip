@@ -1,0 +1,15 @@
+// q8_0 weights x fp32 activations, M = 1, 2 and measurement variants.
+#include "gemv_instances.h"
+
+namespace skg {
+void register_gemv_q8_0_f32(std::vector<GemvEntry>& out) {
+  SKG_M12(SKG_Q8_0_F32, 4, 2, 4, 1, 2, 2)
+  SKG_I(SKG_Q8_0_F32, 1, 2, 2, false, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 1, 8, 2, false, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 1, 4, 1, false, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 1, 8, 1, false, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 1, 4, 2, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 1, 8, 2, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 2, 4, 1, true, 4, SKG_EPI_NONE)
+}
+}  // namespace skg

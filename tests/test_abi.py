@@ -1,0 +1,155 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any HIP
+call (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skg.h")
+
+
+@pytest.fixture(scope="module")
+def skg():
+    import skinny_gemm_decode_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skg_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["skg_pack_weights", "skg_pack_weights_multi", "skg_packed_size", "skg_packed_size_multi",
+                     "skg_quantize_act_q8_1", "skg_gemv", "skg_gemv_multi", "skg_gemm_tiled",
+                     "skg_status_str", "skg_last_error", "skg_debug_block_dots", "skg_stream_read"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(skg):
+    lib = ctypes.CDLL(skg.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings(skg):
+    assert skg.abi_version() == 1
+    assert skg.status_str(0) == "SKG_OK"
+    assert skg.status_str(2) == "SKG_E_SHAPE"
+    assert skg.status_str(99) == "SKG_E_UNKNOWN"
+
+
+def test_packed_sizes(skg):
+    # q4_0 at K=4096, N=14336: 16-byte payload + 2-byte scale per block
+    assert skg.packed_size(skg.Q4_0_F32, 14336, 4096) == 14336 * 128 * 18
+    assert skg.packed_size(skg.Q8_0_F32, 14336, 4096) == 14336 * 128 * 34
+    assert skg.packed_size(skg.BF16_BF16, 12288, 4096) == 12288 * 4096 * 2
+    assert skg.packed_size(skg.Q4_0_Q8_1, 4096, 11008) == 4096 * 344 * 18
+    assert skg.packed_size(skg.Q4_0_F32, 1, 33) == 0        # K not a multiple of 32
+    assert skg.packed_size(skg.BF16_BF16, 0, 64) == 0       # N < 1
+    assert skg.packed_size(17, 4, 64) == 0                  # unknown format
+    assert skg.packed_size_multi(skg.Q4_0_Q8_1, [4096, 4096, 4096], 4096) == 3 * 4096 * 128 * 18
+    # three 4096x4096 + two 11008x4096 + one 4096x11008 q4_0 matrices: one decode layer
+    layer = (skg.packed_size_multi(3, [4096] * 3, 4096) + skg.packed_size_multi(3, [11008] * 2, 4096)
+             + skg.packed_size(3, 4096, 11008))
+    assert layer == 104_398_848
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+
+# The calls below pass fake device pointers and rely on host validation to
+# reject them.  Where a GPU is visible, a mistaken "invalid" case would launch
+# a kernel on those pointers, so these tests run only where there is none.
+no_gpu = pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                            reason="fake-pointer validation tests run only without a GPU")
+
+
+def call(skg, name, *args):
+    return getattr(skg.lib, name)(*args)
+
+
+@no_gpu
+@pytest.mark.parametrize("args,status", [
+    ((99, 1, 4096, 4096), 1),            # unknown fmt
+    ((5, 1, 4096, 4096), 4),             # gemm format is not a gemv format
+    ((2, 0, 4096, 4096), 2),             # M = 0
+    ((2, 9, 4096, 4096), 2),             # M > 8
+    ((2, 1, 4008, 4096), 2),             # K % 32 != 0
+    ((0, 1, 4, 4096), 2),                # bf16 K < 8
+    ((2, 1, 4096, 0), 2),                # N = 0
+])
+def test_gemv_shape_and_fmt_errors(skg, args, status):
+    fmt, M, K, N = args
+    assert call(skg, "skg_gemv", fmt, M, K, N, FAKE, FAKE, FAKE, None) == status
+    assert skg.last_error() != ""
+
+
+@no_gpu
+def test_gemv_pointer_errors(skg):
+    assert call(skg, "skg_gemv", 2, 1, 4096, 4096, None, FAKE, FAKE, None) == skg.E_INVALID_ARG
+    assert call(skg, "skg_gemv", 2, 1, 4096, 4096, FAKE, FAKE, None, None) == skg.E_INVALID_ARG
+    assert call(skg, "skg_gemv", 2, 1, 4096, 4096, MISALIGNED, FAKE, FAKE, None) == skg.E_ALIGN
+    assert call(skg, "skg_gemv", 2, 1, 4096, 4096, FAKE, MISALIGNED, FAKE, None) == skg.E_ALIGN
+    # Q8_1 activations need only 4-byte alignment; y needs 4
+    assert call(skg, "skg_gemv", 3, 1, 4096, 4096, FAKE, ctypes.c_void_p((1 << 20) + 4), MISALIGNED,
+                None) == skg.E_ALIGN
+
+
+@no_gpu
+def test_gemv_multi_errors(skg):
+    Ns = (ctypes.c_int64 * 4)(64, 64, 64, 64)
+    ys = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    g = skg.lib.skg_gemv_multi
+    assert g(2, 1, 64, 0, Ns, FAKE, FAKE, ys, 0, None) == skg.E_INVALID_ARG        # n = 0
+    assert g(2, 1, 64, 5, Ns, FAKE, FAKE, ys, 0, None) == skg.E_INVALID_ARG        # n > 4
+    assert g(2, 1, 64, 3, Ns, FAKE, FAKE, ys, 1, None) == skg.E_INVALID_ARG        # swiglu needs n = 2
+    Ns2 = (ctypes.c_int64 * 2)(64, 65)
+    assert g(2, 1, 64, 2, Ns2, FAKE, FAKE, ys, 1, None) == skg.E_SHAPE             # gate/up differ
+    assert g(2, 1, 64, 2, Ns, FAKE, FAKE, ys, 7, None) == skg.E_INVALID_ARG        # unknown epilogue
+    ysn = (ctypes.c_void_p * 2)(FAKE, None)
+    assert g(2, 1, 64, 2, Ns, FAKE, FAKE, ysn, 0, None) == skg.E_INVALID_ARG       # null output
+
+
+@no_gpu
+def test_other_entry_point_errors(skg):
+    L = skg.lib
+    assert L.skg_quantize_act_q8_1(0, 64, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_quantize_act_q8_1(1, 48, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_quantize_act_q8_1(1, 64, MISALIGNED, FAKE, None) == skg.E_ALIGN
+    assert L.skg_quantize_act_q8_1(1, 64, FAKE, None, None) == skg.E_INVALID_ARG
+    assert L.skg_gemm_tiled(2, 512, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED
+    assert L.skg_gemm_tiled(5, 0, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_gemm_tiled(5, 512, 4100, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_pack_weights(2, 4, 64, FAKE, MISALIGNED, None) == skg.E_ALIGN
+    assert L.skg_pack_weights(2, 4, 64, ctypes.c_void_p((1 << 20) + 1), FAKE, None) == skg.E_ALIGN
+    assert L.skg_pack_weights(2, 4, 60, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_debug_block_dots(2, 8, 64, 0, 1, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED
+    assert L.skg_debug_block_dots(3, 8, 64, 6, 3, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_stream_read(FAKE, 17, FAKE, None) == skg.E_SHAPE
+    assert L.skg_set_lds_pad(1 << 20) == skg.E_INVALID_ARG
+    assert L.skg_gemv_set_variant(2, 1, 0, 3, 3, 0, 4) == skg.E_UNSUPPORTED
+
+
+def test_variant_registry(skg):
+    vs = skg.gemv_variants()
+    seen = {(v["fmt"], v["M"], v["epi"]) for v in vs}
+    for fmt in range(5):
+        for M in range(1, 9):
+            for epi in (0, 1):
+                assert (fmt, M, epi) in seen, (fmt, M, epi)
+    skg.gemv_set_variant(2, 1, 0, 16, 2, 0, 4)
+    skg.gemv_set_variant(2, 1, 0, 0)
+
+
+@no_gpu
+def test_valid_call_without_gpu_reports_device_error(skg):
+    # Arguments are valid, so only the device check can reject the call.
+    assert skg.lib.skg_gemv(2, 1, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_DEVICE
+    assert "device" in skg.last_error().lower()

@@ -1,0 +1,171 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (default kernel variants).  Where the oracle would take long,
+it computes a sample of output rows (always including the first and last row
+and rows of the last, ragged workgroup)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import inputs as si
+from tests._gpu import assert_close, dev, host, note, poisoned
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def skg():
+    import skinny_gemm_decode_amd as m
+    return m
+
+
+def sample_rows(N, n=256, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    rows |= {0, 1, N - 2, N - 1} | set(range(max(0, N - 40), N))
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+def test_q8_0_m1_k256_n512(skg):
+    N, K = 512, 256
+    rng = si.rng_for(0, 1, 0)
+    W = si.q8_0_weights(rng, N, K)
+    x = si.activations_f32(rng, 1, K)
+    note("q8_0 M=1 K=256 N=512")
+    Wp = skg.pack_weights(skg.Q8_0_F32, N, K, dev(W))
+    y = poisoned((1, N))
+    skg.gemv(skg.Q8_0_F32, 1, K, N, Wp, dev(x), y)
+    y_ref, bound = oracle.gemv_ref_fmt("q8_0", W, x)
+    assert_close(host(y), y_ref, bound, "q8_0 M=1 K=256 N=512")
+
+
+def test_bf16_m1_k4096_n12288(skg):
+    N, K = 12288, 4096
+    rng = si.rng_for(0, 2, 0)
+    W = si.bf16_weights(rng, N, K)
+    x = si.activations_bf16(rng, 1, K)
+    note("bf16 M=1 K=4096 N=12288")
+    Wp = skg.pack_weights(skg.BF16_BF16, N, K, dev(W))
+    y = poisoned((1, N))
+    skg.gemv(skg.BF16_BF16, 1, K, N, Wp, dev(x), y)
+    y_ref, bound = oracle.gemv_ref_fmt("bf16", W, x, x_kind="bf16")
+    assert_close(host(y), y_ref, bound, "bf16 M=1 K=4096 N=12288")
+
+
+@pytest.mark.parametrize("kind,fmt", [("q8_0", 1), ("q4_0", 2)])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_skinny_k4096_n14336(skg, kind, fmt, M):
+    N, K = 14336, 4096
+    rng = si.rng_for(0, 4, 10 * fmt + M)
+    W = si.weights(kind, rng, N, K)
+    x = si.activations_f32(rng, M, K)
+    note(f"{kind} x f32 M={M} K=4096 N=14336")
+    Wp = skg.pack_weights(fmt, N, K, dev(W))
+    y = poisoned((M, N))
+    skg.gemv(fmt, M, K, N, Wp, dev(x), y)
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+    rows = sample_rows(N, seed=M)
+    y_ref, bound = oracle.gemv_ref_fmt(kind, W[rows], x)
+    assert_close(yh[:, rows], y_ref, bound, f"{kind} M={M}")
+
+
+def test_llama2_7b_q4_0_q8_1_layer_chain(skg):
+    """One Llama-2-7B-shaped decode layer, M=1: quantize(x) -> fused QKV ->
+    fused gate/up + SwiGLU -> quantize(h) -> down.  Each stage is checked where
+    it acts; the chain end to end against the oracle's own chain."""
+    import torch
+    D, F = 4096, 11008
+    rng = si.rng_for(0, 3, 0)
+    Wq, Wk, Wv = (si.q4_0_weights(rng, D, D) for _ in range(3))
+    Wg, Wu = si.q4_0_weights(rng, F, D), si.q4_0_weights(rng, F, D)
+    Wd = si.q4_0_weights(rng, D, F)
+    x = si.activations_f32(rng, 1, D)
+    fmt = skg.Q4_0_Q8_1
+    note("layer chain: pack")
+    Pqkv = skg.pack_weights_multi(fmt, [D, D, D], D, [dev(Wq), dev(Wk), dev(Wv)])
+    Pgu = skg.pack_weights_multi(fmt, [F, F], D, [dev(Wg), dev(Wu)])
+    Pd = skg.pack_weights(fmt, D, F, dev(Wd))
+
+    note("layer chain: quantize x")
+    xq = skg.quantize_act_q8_1(dev(x))
+    xq_ref = oracle.quantize_q8_1(x)
+    assert np.array_equal(host(xq), xq_ref)
+
+    note("layer chain: qkv")
+    ys = [poisoned((1, D)) for _ in range(3)]
+    skg.gemv_multi(fmt, 1, D, [D, D, D], Pqkv, xq, ys)
+    rows = sample_rows(D, seed=3)
+    for name, W, y in zip("qkv", (Wq, Wk, Wv), ys):
+        y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(W[rows], xq_ref)
+        assert_close(host(y)[:, rows], y_ref, bound, f"{name} projection")
+
+    note("layer chain: gate/up + swiglu")
+    h = poisoned((1, F))
+    skg.gemv_multi(fmt, 1, D, [F, F], Pgu, xq, [h], epi=skg.EPI_SWIGLU)
+    hh = host(h)
+    frows = sample_rows(F, seed=4)
+    g_ref, _, bg = oracle.gemv_q4_0_q8_1_ref(Wg[frows], xq_ref)
+    u_ref, _, bu = oracle.gemv_q4_0_q8_1_ref(Wu[frows], xq_ref)
+    tol = oracle.swiglu_tolerance(g_ref, u_ref, oracle.tolerance(bg), oracle.tolerance(bu))
+    ok, worst = oracle.check_close(hh[:, frows], oracle.swiglu_ref(g_ref, u_ref), tol)
+    assert ok, f"swiglu worst {worst}"
+
+    note("layer chain: down projection stage on a generated h")
+    h_in = si.activations_f32(si.rng_for(0, 3, 1), 1, F) * np.float32(0.05)
+    hq = skg.quantize_act_q8_1(dev(h_in))
+    hq_ref = oracle.quantize_q8_1(h_in)
+    assert np.array_equal(host(hq), hq_ref)
+    yd = poisoned((1, D))
+    skg.gemv(fmt, 1, F, D, Pd, hq, yd)
+    yd_ref, _, bd = oracle.gemv_q4_0_q8_1_ref(Wd[rows], hq_ref)
+    assert_close(host(yd)[:, rows], yd_ref, bd, "down projection (K=11008)")
+
+    note("layer chain: end to end")
+    hq_gpu = skg.quantize_act_q8_1(h)
+    yo = poisoned((1, D))
+    skg.gemv(fmt, 1, F, D, Pd, hq_gpu, yo)
+    g_all, _, _ = oracle.gemv_q4_0_q8_1_ref(Wg, xq_ref)
+    u_all, _, _ = oracle.gemv_q4_0_q8_1_ref(Wu, xq_ref)
+    h_ref32 = oracle.swiglu_ref(g_all, u_all).astype(np.float32)
+    y_end, _, b_end = oracle.gemv_q4_0_q8_1_ref(Wd[rows], oracle.quantize_q8_1(h_ref32))
+    assert_close(host(yo)[:, rows], y_end, b_end, "layer end to end")
+    del torch
+
+
+def test_prefill_tile_m512_k4096_n14336(skg):
+    M, N, K = 512, 14336, 4096
+    rng = si.rng_for(0, 5, 0)
+    W = si.q4_0_weights(rng, N, K)
+    A = si.activations_bf16(rng, M, K)
+    note("gemm_tiled M=512 K=4096 N=14336")
+    Wp = skg.pack_weights(skg.Q4_0_BF16, N, K, dev(W))
+    y = poisoned((M, N))
+    skg.gemm_tiled(skg.Q4_0_BF16, M, K, N, Wp, dev(A), y)
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+    mrows = sample_rows(M, n=48, seed=5)
+    ncols = sample_rows(N, n=2048, seed=6)
+    y_ref, bound, y_b = oracle.gemm_tiled_ref(W[ncols], A[mrows])
+    assert_close(yh[np.ix_(mrows, ncols)], y_ref, bound, "tile vs exact weights")
+    # the bf16-rounded-weight reference classifies what deviation remains
+    assert_close(yh[np.ix_(mrows, ncols)], y_b, bound, "tile vs bf16 weights", rel=1e-4)
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 256, 2048), (300, 250, 2080), (1, 1, 32), (17, 129, 96), (257, 113, 4096)])
+def test_prefill_tile_ragged_shapes(skg, M, N, K):
+    """Ragged tiles, odd block counts (K tail inside a 64-wide step), and the
+    m=2048, n=256, k=2048 attention-projection shape on which the pages'
+    Metal tile returned -inf."""
+    rng = si.rng_for(0, 5, M + N + K)
+    W = si.q4_0_weights(rng, N, K)
+    A = si.activations_bf16(rng, M, K)
+    note(f"gemm_tiled M={M} N={N} K={K}")
+    Wp = skg.pack_weights(skg.Q4_0_BF16, N, K, dev(W))
+    y = poisoned((M, N))
+    skg.gemm_tiled(skg.Q4_0_BF16, M, K, N, Wp, dev(A), y)
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+    mrows = sample_rows(M, n=64, seed=7)
+    y_ref, bound, _ = oracle.gemm_tiled_ref(W, A[mrows])
+    assert_close(yh[mrows], y_ref, bound, f"tile M={M} N={N} K={K}")

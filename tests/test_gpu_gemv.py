@@ -1,0 +1,231 @@
+"""GPU parity of the skinny GEMM / GEMV entry points against the CPU oracle.
+
+Small shapes span several K chunks, ragged row groups and K tails; every
+compiled kernel variant is checked; outputs are NaN-poisoned first so rows a
+kernel fails to write show up.  Float outputs must satisfy
+|y - y_ref| <= 2e-3 * sum|w x| + 1e-6; integer block dots and the Q8_1
+quantiser must match exactly."""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import inputs as si
+from tests._gpu import assert_close, dev, host, note, poisoned
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def skg():
+    import skinny_gemm_decode_amd as m
+    return m
+
+
+def wkind(skg, fmt):
+    return {skg.BF16_BF16: "bf16", skg.Q8_0_F32: "q8_0", skg.Q4_0_F32: "q4_0",
+            skg.Q4_0_Q8_1: "q4_0", skg.Q8_0_Q8_1: "q8_0"}[fmt]
+
+
+def is_q8_1(skg, fmt):
+    return fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+
+
+def make_inputs(skg, fmt, M, N, K, seed):
+    rng = si.rng_for(0, 99, seed)
+    W = si.weights(wkind(skg, fmt), rng, N, K)
+    x = si.activations_bf16(rng, M, K) if fmt == skg.BF16_BF16 else si.activations_f32(rng, M, K)
+    return W, x
+
+
+def gpu_activation(skg, fmt, x):
+    """Device activation in the format the kernel reads (Q8_1 quantised on the
+    GPU and checked bit-exactly against the oracle's quantiser first)."""
+    xd = dev(x)
+    if not is_q8_1(skg, fmt):
+        return xd, None
+    import torch
+    xq = poisoned((x.shape[0], x.shape[1] // 32, 36), dtype=torch.uint8)
+    skg.quantize_act_q8_1(xd, xq)
+    ref = oracle.quantize_q8_1(x)
+    assert np.array_equal(host(xq), ref), "Q8_1 activation differs from the oracle"
+    return xq, ref
+
+
+def reference(skg, fmt, W, x, xq_ref):
+    kind = wkind(skg, fmt)
+    if fmt == skg.Q4_0_Q8_1:
+        y, _, bound = oracle.gemv_q4_0_q8_1_ref(W, xq_ref)
+        return y, bound
+    if fmt == skg.Q8_0_Q8_1:
+        return oracle.gemv_q8_0_q8_1_ref(W, xq_ref)
+    return oracle.gemv_ref_fmt(kind, W, x, x_kind="bf16" if fmt == skg.BF16_BF16 else "f32")
+
+
+def run_gemv(skg, fmt, M, N, K, W, x):
+    note(f"gemv fmt={skg.FMT_NAMES[fmt]} M={M} N={N} K={K}")
+    Wp = skg.pack_weights(fmt, N, K, dev(W))
+    xin, xq_ref = gpu_activation(skg, fmt, x)
+    y = poisoned((M, N))
+    skg.gemv(fmt, M, K, N, Wp, xin, y)
+    return host(y), xq_ref
+
+
+GEMV_FMTS = [0, 1, 2, 3, 4]
+
+
+def shapes_for(fmt):
+    if fmt == 0:
+        return [(1, 8), (5, 40), (17, 520), (131, 4104)]
+    return [(1, 32), (3, 96), (17, 288), (131, 4128)]
+
+
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_gemv_small_shapes(skg, fmt, M):
+    for i, (N, K) in enumerate(shapes_for(fmt)):
+        W, x = make_inputs(skg, fmt, M, N, K, seed=1000 + 100 * fmt + 10 * M + i)
+        y, xq_ref = run_gemv(skg, fmt, M, N, K, W, x)
+        y_ref, bound = reference(skg, fmt, W, x, xq_ref)
+        assert_close(y, y_ref, bound, f"fmt={fmt} M={M} N={N} K={K}")
+
+
+def test_every_compiled_variant(skg):
+    """Each compiled kernel variant, selected through the tuning hook, on a
+    shape with ragged row groups and a K tail."""
+    variants = skg.gemv_variants()
+    assert variants
+    cache = {}
+    try:
+        for v in variants:
+            fmt, M, epi = v["fmt"], v["M"], v["epi"]
+            N = 300
+            K = 4104 if fmt == skg.BF16_BF16 else 4128
+            key = (fmt, M, epi)
+            if key not in cache:
+                W0, x = make_inputs(skg, fmt, M, N, K, seed=5000 + 10 * fmt + M)
+                W1, _ = make_inputs(skg, fmt, 1, N, K, seed=6000 + 10 * fmt + M)
+                cache[key] = (W0, W1, x)
+            W0, W1, x = cache[key]
+            skg.gemv_set_variant(fmt, M, epi, v["ro"], v["j"], v["x_lds"], v["waves"])
+            note(f"variant {v}")
+            xin, xq_ref = gpu_activation(skg, fmt, x)
+            if epi == skg.EPI_NONE:
+                Wp = skg.pack_weights(fmt, N, K, dev(W0))
+                y = poisoned((M, N))
+                skg.gemv(fmt, M, K, N, Wp, xin, y)
+                y_ref, bound = reference(skg, fmt, W0, x, xq_ref)
+                assert_close(host(y), y_ref, bound, f"variant {v}")
+            else:
+                Wp = skg.pack_weights_multi(fmt, [N, N], K, [dev(W0), dev(W1)])
+                h = poisoned((M, N))
+                skg.gemv_multi(fmt, M, K, [N, N], Wp, xin, [h], epi=skg.EPI_SWIGLU)
+                g_ref, bg = reference(skg, fmt, W0, x, xq_ref)
+                u_ref, bu = reference(skg, fmt, W1, x, xq_ref)
+                tol = oracle.swiglu_tolerance(g_ref, u_ref, oracle.tolerance(bg), oracle.tolerance(bu))
+                ok, worst = oracle.check_close(host(h), oracle.swiglu_ref(g_ref, u_ref), tol)
+                assert ok, f"variant {v}: worst {worst}"
+            skg.gemv_set_variant(fmt, M, epi, 0)
+    finally:
+        for v in variants:
+            skg.gemv_set_variant(v["fmt"], v["M"], v["epi"], 0)
+
+
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
+def test_gemv_multi_qkv_three_outputs(skg, fmt):
+    K = 4104 if fmt == skg.BF16_BF16 else 4128
+    Ns = [96, 33, 130]
+    Ws = [make_inputs(skg, fmt, 1, n, K, seed=7000 + 10 * fmt + i)[0] for i, n in enumerate(Ns)]
+    _, x = make_inputs(skg, fmt, 2, 1, K, seed=7100 + fmt)
+    note(f"gemv_multi qkv fmt={fmt}")
+    Wp = skg.pack_weights_multi(fmt, Ns, K, [dev(w) for w in Ws])
+    xin, xq_ref = gpu_activation(skg, fmt, x)
+    ys = [poisoned((2, n)) for n in Ns]
+    skg.gemv_multi(fmt, 2, K, Ns, Wp, xin, ys)
+    for i, (w, y) in enumerate(zip(Ws, ys)):
+        y_ref, bound = reference(skg, fmt, w, x, xq_ref)
+        assert_close(host(y), y_ref, bound, f"qkv output {i}")
+
+
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
+@pytest.mark.parametrize("M", [1, 2, 5])
+def test_gemv_multi_swiglu_and_its_halves(skg, fmt, M):
+    K = 4104 if fmt == skg.BF16_BF16 else 4128
+    N = 257
+    Wg, x = make_inputs(skg, fmt, M, N, K, seed=8000 + 10 * fmt + M)
+    Wu, _ = make_inputs(skg, fmt, M, N, K, seed=8100 + 10 * fmt + M)
+    note(f"gemv_multi swiglu fmt={fmt} M={M}")
+    Wp = skg.pack_weights_multi(fmt, [N, N], K, [dev(Wg), dev(Wu)])
+    xin, xq_ref = gpu_activation(skg, fmt, x)
+    h = poisoned((M, N))
+    skg.gemv_multi(fmt, M, K, [N, N], Wp, xin, [h], epi=skg.EPI_SWIGLU)
+    # the same packed pair without the epilogue: each half on its own
+    g, u = poisoned((M, N)), poisoned((M, N))
+    skg.gemv_multi(fmt, M, K, [N, N], Wp, xin, [g, u], epi=skg.EPI_NONE)
+    g_ref, bg = reference(skg, fmt, Wg, x, xq_ref)
+    u_ref, bu = reference(skg, fmt, Wu, x, xq_ref)
+    assert_close(host(g), g_ref, bg, "gate")
+    assert_close(host(u), u_ref, bu, "up")
+    tol = oracle.swiglu_tolerance(g_ref, u_ref, oracle.tolerance(bg), oracle.tolerance(bu))
+    ok, worst = oracle.check_close(host(h), oracle.swiglu_ref(g_ref, u_ref), tol)
+    assert ok, f"swiglu worst {worst}"
+
+
+@pytest.mark.parametrize("fmt", [3, 4])
+def test_block_dots_bit_exact(skg, fmt):
+    N, K = 37, 4128
+    W, x = make_inputs(skg, fmt, 1, N, K, seed=9000 + fmt)
+    Wp = skg.pack_weights(fmt, N, K, dev(W))
+    xq, xq_ref = gpu_activation(skg, fmt, x)
+    note(f"block dots fmt={fmt}")
+    import torch
+    out = poisoned((N - 3, K // 32), dtype=torch.int32)
+    skg.debug_block_dots(fmt, N, K, 3, N - 3, Wp, xq, out)
+    ref = (oracle.block_dots_q4_0_q8_1 if fmt == 3 else oracle.block_dots_q8_0_q8_1)(W[3:], xq_ref[0])
+    assert np.array_equal(host(out), ref)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_one_hot_activation_is_bit_exact(skg, fmt):
+    N, K = 70, 4096 if fmt else 4104
+    W, _ = make_inputs(skg, fmt, 1, N, K, seed=9100 + fmt)
+    Wd = oracle.dequantize(wkind(skg, fmt), W)
+    Wp = skg.pack_weights(fmt, N, K, dev(W))
+    for k in (0, 31, 33, K - 1):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        if fmt == skg.BF16_BF16:
+            x = np.zeros((1, K), np.uint16)
+            x[0, k] = 0x3F80
+        note(f"one-hot fmt={fmt} k={k}")
+        y = poisoned((1, N))
+        skg.gemv(fmt, 1, K, N, Wp, dev(x), y)
+        assert np.array_equal(host(y)[0].astype(np.float64), Wd[:, k]), f"k={k}"
+
+
+def test_q4_0_all_codes_eight(skg):
+    """Blocks whose codes are all 8 decode to zero: exactly zero on the float
+    path, and the second reference (stored block sum) on the Q8_1 path."""
+    N, K = 40, 4096
+    W, x = make_inputs(skg, skg.Q4_0_F32, 1, N, K, seed=9200)
+    W[..., 2:] = 0x88
+    y, _ = run_gemv(skg, skg.Q4_0_F32, 1, N, K, W, x)
+    assert np.all(y == 0.0)
+    y8, xq_ref = run_gemv(skg, skg.Q4_0_Q8_1, 1, N, K, W, x)
+    y_ref, y_ref_s, _ = oracle.gemv_q4_0_q8_1_ref(W, xq_ref)
+    assert np.all(y_ref == 0.0)
+    dW = oracle.fp16_bits_to_f64(W[..., 0].astype(np.uint16) | (W[..., 1].astype(np.uint16) << 8))
+    dA, sA, qa = oracle.q8_1_fields(xq_ref[0])
+    bound_s = np.sum(np.abs(dW) * (np.abs(dA) * 8 * np.abs(qa).sum(-1) + 8 * np.abs(sA)), axis=1)[None, :]
+    assert_close(y8, y_ref_s, bound_s, "all-8 vs stored-sum reference")
+
+
+def test_bf16_scale_boundaries(skg):
+    """bf16 weights and activations spanning many binades, K = 8 (one unit)."""
+    N, K = 9, 8
+    W = np.array([[0x3F80, 0xBF80, 0x7F7F, 0x0080, 0x8001, 0x4000, 0x3E00, 0xC2C8]] * N, np.uint16)
+    W[:, 2] = 0x4700   # keep products finite
+    x = np.array([[0x3F80, 0x3F80, 0x3F00, 0x7000, 0x0000, 0xC000, 0x4100, 0x3C00]], np.uint16)
+    y, _ = run_gemv(skg, skg.BF16_BF16, 1, N, K, W, x)
+    y_ref, bound = oracle.gemv_ref_fmt("bf16", W, x, x_kind="bf16")
+    assert_close(y, y_ref, bound, "bf16 boundaries")
