@@ -60,16 +60,17 @@ class Timer:
     def run(self, launch, n_rot: int, steps: int, warmup: int, per_repeat: int = 200, warm_s: float | None = None):
         torch = self.torch
         stream = torch.cuda.current_stream()
+        sh = stream.cuda_stream
         i = 0
         if warm_s is not None:
             t_end = time.time() + warm_s
             while time.time() < t_end:
                 for _ in range(per_repeat):
-                    launch(i % n_rot)
+                    launch(i % n_rot, sh)
                     i += 1
                 torch.cuda.synchronize()
         for _ in range(warmup):
-            launch(i % n_rot)
+            launch(i % n_rot, sh)
             i += 1
         torch.cuda.synchronize()
         reps = []
@@ -83,7 +84,7 @@ class Timer:
         events[0].record(stream)
         for r, n in enumerate(reps):
             for _ in range(n):
-                launch(i % n_rot)
+                launch(i % n_rot, sh)
                 i += 1
             events[r + 1].record(stream)
         torch.cuda.synchronize()
@@ -160,7 +161,7 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
     lib = skg.lib
     sh = torch.cuda.current_stream().cuda_stream
 
-    def launch(i):
+    def launch(i, sh):
         lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[i & 1], sh)
 
     # gate: finite and deterministic on every rotation buffer
@@ -179,6 +180,17 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
                working_set_bytes=n_rot * wbytes, algorithmic_bytes=alg,
                gbs=alg / (res["us_per_launch"] * 1e-6) / 1e9)
     res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
+    # achievable reference: the streaming-read kernel over the same buffers
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    skp = sink.data_ptr()
+
+    def read(i, sh):
+        lib.skg_stream_read(wp[i], wbytes, skp, sh)
+
+    ceil = timer.run(read, n_rot, steps, 0, warm_s=0.1)
+    res["ceiling_us"] = ceil["us_per_launch"]
+    res["ceiling_gbs"] = wbytes / (ceil["us_per_launch"] * 1e-6) / 1e9
+    res["frac_ceiling"] = ceil["us_per_launch"] / res["us_per_launch"]
     if graph:
         res["graph"] = bench_graph(torch, launch, n_rot)
         res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
@@ -198,12 +210,12 @@ def bench_graph(torch, launch, n_rot, per_graph=200, repeats=10):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for i in range(3):
-            launch(i % n_rot)
+            launch(i % n_rot, s.cuda_stream)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
         for i in range(per_graph):
-            launch(i % n_rot)
+            launch(i % n_rot, s.cuda_stream)
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
@@ -229,7 +241,7 @@ def bench_ceiling(skg, torch, timer, steps, warm_s):
     sh = torch.cuda.current_stream().cuda_stream
     lib = skg.lib
 
-    def launch(i):
+    def launch(i, sh):
         lib.skg_stream_read(bp[i], nbytes, sp, sh)
 
     skg.check(lib.skg_stream_read(bp[0], nbytes, sp, sh))
@@ -274,7 +286,7 @@ def bench_layer(skg, si, torch, timer, steps, warm_s):
     ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in layers]
     xp, xqp, hp, hqp, yop = x.data_ptr(), xq.data_ptr(), h.data_ptr(), hq.data_ptr(), yo.data_ptr()
 
-    def launch(i):
+    def launch(i, sh):
         pq, pg, pd = ptrs[i]
         lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
         lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
@@ -282,7 +294,7 @@ def bench_layer(skg, si, torch, timer, steps, warm_s):
         lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
         lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
 
-    launch(0)
+    launch(0, sh)
     torch.cuda.synchronize()
     if not bool(torch.isfinite(yo).all()):
         raise RuntimeError("layer chain produced non-finite output")
@@ -315,7 +327,7 @@ def bench_prefill(skg, si, torch, timer, steps, warm_s):
     wp = [b.data_ptr() for b in bufs]
     ap, yp = A.data_ptr(), y.data_ptr()
 
-    def launch(i):
+    def launch(i, sh):
         lib.skg_gemm_tiled(fmt, M, K, N, wp[i], ap, yp, sh)
 
     skg.check(lib.skg_gemm_tiled(fmt, M, K, N, wp[0], ap, yp, sh))
@@ -423,7 +435,7 @@ def main():
     sample["x"] = x_host
     log(f"[headline] {head['us_per_launch']:.2f} us/launch  {head['gbs']:.0f} GB/s  "
         f"({100 * head['frac_peak']:.1f}% of 8 TB/s)  spread {100 * head['spread']:.2f}%  "
-        f"graph {head['graph']['us_per_launch']:.2f} us")
+        f"graph {head['graph']['us_per_launch']:.2f} us  read-ceiling {head['ceiling_us']:.2f} us")
 
     details = {"headline": head, "arms": {}}
     short = dict(steps=2000, warmup=0, warm_s=0.3)
@@ -441,7 +453,8 @@ def main():
                                   14336, 4096, short["steps"], 0, short["warm_s"], xh, graph=True)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_launch']:.2f} us  {r['gbs']:.0f} GB/s  graph "
-                f"{r['graph']['us_per_launch']:.2f} us ({r['graph']['gbs']:.0f} GB/s)")
+                f"{r['graph']['us_per_launch']:.2f} us ({r['graph']['gbs']:.0f} GB/s)  read-ceiling "
+                f"{r['ceiling_us']:.2f} us")
     if "small" in arms:
         xh = si.activations_f32(si.rng_for(0, 1, 0), 1, 256)
         r, _ = bench_gemv_arm(skg, si, torch, timer, "q8_0_f32_m1_k256_n512", "q8_0", skg.Q8_0_F32, 1, 512, 256,
@@ -485,6 +498,8 @@ def main():
             "frac_of_8TBs": round(head["frac_peak"], 4),
             "spread": round(head["spread"], 4),
             "spread_ok": head["spread_ok"],
+            "stream_read_ceiling_us": round(head["ceiling_us"], 3),
+            "frac_of_stream_read_ceiling": round(head["frac_ceiling"], 4),
             "timer": "HIP events on the launch stream, eager launches, 200 per repeat",
         },
         "roofline": {

@@ -215,20 +215,23 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
  * is a cliff; the hardware maximum is a cliff).
  *
  * skg_gemv_set_variant: use the compiled variant with `ro` output rows per
- *   wave, `j` 16-byte units per lane per K chunk, activation staged in LDS
- *   (x_lds = 1) or registers (0) and `waves` waves per workgroup for every
- *   later gemv / gemv_multi call with this (fmt, M, epi); ro = 0 restores
- *   the default.  SKG_E_UNSUPPORTED if that variant is not compiled.
- * skg_gemv_variants: writes up to max_entries records of 7 ints
- *   {fmt, M, epi, ro, j, x_lds, waves} to out (host) and returns the number of
- *   compiled variants; the first record of each (fmt, M, epi) is its default.
+ *   row group, `j` 16-byte units per lane per K chunk, activation staged in
+ *   LDS (x_lds = 1) or registers (0), `waves` waves per workgroup and `kw`
+ *   waves sharing each row group (each takes every kw-th K chunk; partial sums
+ *   meet in LDS) for every later gemv / gemv_multi call with this
+ *   (fmt, M, epi); ro = 0 restores the default.  SKG_E_UNSUPPORTED if that
+ *   variant is not compiled.
+ * skg_gemv_variants: writes up to max_entries records of 8 ints
+ *   {fmt, M, epi, ro, j, x_lds, waves, kw} to out (host) and returns the
+ *   number of compiled variants; the first record of each (fmt, M, epi) is its
+ *   default.
  * skg_set_lds_pad: extra dynamic LDS bytes (0..65536) requested by every gemv
  *   launch, which lowers occupancy without changing the code (the MI50 case
  *   study's diagnostic control).  Initial value: $SKG_LDS_PAD_BYTES or 0.
  * These settings are process-wide and must not change while another thread
  * is launching gemv work.
  */
-skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves);
+skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw);
 int skg_gemv_variants(int* out, int max_entries);
 skg_status skg_set_lds_pad(int64_t bytes);
 

@@ -62,7 +62,7 @@ def _load() -> ctypes.CDLL:
         "skg_gemm_tiled": (i32, [i32, i64, i64, i64, vp, vp, vp, vp]),
         "skg_debug_block_dots": (i32, [i32, i64, i64, i64, i64, vp, vp, vp, vp]),
         "skg_stream_read": (i32, [vp, sz, vp, vp]),
-        "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32]),
+        "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "skg_gemv_variants": (i32, [ctypes.POINTER(i32), i32]),
         "skg_set_lds_pad": (i32, [i64]),
     }
@@ -232,15 +232,15 @@ def stream_read(buf, nbytes: int | None = None, out=None, stream=None):
 def gemv_variants():
     """List of compiled GEMV variants as dicts (first per (fmt, M, epi) = default)."""
     n = lib.skg_gemv_variants(None, 0)
-    buf = (ctypes.c_int * (7 * n))()
+    buf = (ctypes.c_int * (8 * n))()
     lib.skg_gemv_variants(buf, n)
-    keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves")
-    return [dict(zip(keys, buf[7 * i: 7 * i + 7])) for i in range(n)]
+    keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves", "kw")
+    return [dict(zip(keys, buf[8 * i: 8 * i + 8])) for i in range(n)]
 
 
 def gemv_set_variant(fmt: int, M: int, epi: int = EPI_NONE, ro: int = 0, j: int = 0, x_lds: int = 0,
-                     waves: int = 4) -> None:
-    check(lib.skg_gemv_set_variant(fmt, M, epi, ro, j, x_lds, waves))
+                     waves: int = 4, kw: int = 1) -> None:
+    check(lib.skg_gemv_set_variant(fmt, M, epi, ro, j, x_lds, waves, kw))
 
 
 def set_lds_pad(nbytes: int) -> None:

@@ -131,7 +131,7 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
   a.K = K;
   a.nu = uint32_t(wk == WK_BF16 ? K / 8 : K / 32);
   a.x = static_cast<const uint8_t*>(x);
-  const int rows_per_block = v->waves * v->ro;
+  const int rows_per_block = (v->waves / v->kw) * v->ro;
   int64_t blocks = 0;
   const uint8_t* base = static_cast<const uint8_t*>(W);
   if (epi == SKG_EPI_SWIGLU) {
@@ -346,7 +346,7 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
   return ok();
 }
 
-skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves) {
+skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw) {
   if (!is_gemv_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown gemv fmt %d", int(fmt));
   if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "M must be 1..8");
   if (epi != SKG_EPI_NONE && epi != SKG_EPI_SWIGLU) return fail(SKG_E_INVALID_ARG, "unknown epilogue");
@@ -355,12 +355,15 @@ skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, 
   if (ro != 0) {
     for (size_t i = 0; i < g_reg->size(); ++i) {
       const GemvEntry& e = (*g_reg)[i];
-      if (e.fmt == fmt && e.M == M && e.epi == epi && e.ro == ro && e.j == j && e.xlds == x_lds && e.waves == waves) {
+      if (e.fmt == fmt && e.M == M && e.epi == epi && e.ro == ro && e.j == j && e.xlds == x_lds && e.waves == waves &&
+          e.kw == kw) {
         idx = int(i);
         break;
       }
     }
-    if (idx < 0) return fail(SKG_E_UNSUPPORTED, "no compiled variant ro=%d j=%d x_lds=%d waves=%d", ro, j, x_lds, waves);
+    if (idx < 0)
+      return fail(SKG_E_UNSUPPORTED, "no compiled variant ro=%d j=%d x_lds=%d waves=%d kw=%d", ro, j, x_lds, waves,
+                  kw);
   }
   std::lock_guard<std::mutex> lk(g_sel_mu);
   g_sel[fmt][M][epi] = idx;
@@ -373,7 +376,7 @@ int skg_gemv_variants(int* out, int max_entries) {
   if (out) {
     for (int i = 0; i < n && i < max_entries; ++i) {
       const GemvEntry& e = (*g_reg)[size_t(i)];
-      int* o = out + 7 * i;
+      int* o = out + 8 * i;
       o[0] = e.fmt;
       o[1] = e.M;
       o[2] = e.epi;
@@ -381,6 +384,7 @@ int skg_gemv_variants(int* out, int max_entries) {
       o[4] = e.j;
       o[5] = e.xlds;
       o[6] = e.waves;
+      o[7] = e.kw;
     }
   }
   return n;

@@ -82,24 +82,31 @@ __device__ inline void zero_w(WUnit<FMT>& u) {
   u.d = 0.f;
 }
 
+// Weights are read exactly once per launch, so they are loaded non-temporally
+// (streamed past the caches that hold the reused activation); measured on
+// MI355X this moves the bf16 M=1 GEMV from 17.1 to 15.9 us.
+__device__ inline u32x4 ld_u32x4_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // rowp: start of the row's payload; srow: the row's fp16 scales.
 template <int FMT>
 __device__ inline void load_w(WUnit<FMT>& u, const uint8_t* rowp, const uint16_t* srow, uint32_t nb,
                               uint32_t unit) {
-  const u32x4 p = ld_u32x4(rowp + size_t(unit) * 16);
+  const u32x4 p = ld_u32x4_stream(rowp + size_t(unit) * 16);
   u.w[0] = p.x;
   u.w[1] = p.y;
   u.w[2] = p.z;
   u.w[3] = p.w;
   if constexpr (Fmt<FMT>::WV == 8) {
-    const u32x4 q = ld_u32x4(rowp + (size_t(nb) + unit) * 16);
+    const u32x4 q = ld_u32x4_stream(rowp + (size_t(nb) + unit) * 16);
     u.w[4] = q.x;
     u.w[5] = q.y;
     u.w[6] = q.z;
     u.w[7] = q.w;
   }
   if constexpr (Fmt<FMT>::SCALE) {
-    u.d = h2f(srow[unit]);
+    u.d = h2f(__builtin_nontemporal_load(srow + unit));
   } else {
     u.d = 0.f;
   }
@@ -165,26 +172,61 @@ __device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
   }
 }
 
-// Activation unit straight from global memory (row m, unit index u).
+// Raw activation unit as loaded from global memory: 16-byte pieces (bf16,
+// fp32) or the nine dwords of a Q8_1 block.
+template <int FMT, bool Q8 = Fmt<FMT>::XQ8>
+struct XRaw;
 template <int FMT>
-__device__ inline void fetch_x_global(XUnit<FMT>& x, const uint8_t* xb, int64_t K, uint32_t nb, int m,
-                                      uint32_t u) {
+struct XRaw<FMT, false> {
+  u32x4 pc[Fmt<FMT>::XB / 16];
+};
+template <int FMT>
+struct XRaw<FMT, true> {
+  uint32_t w[9];
+};
+
+// Loads activation unit u of row m (u must be in range).
+template <int FMT>
+__device__ inline void load_x_raw(XRaw<FMT>& r, const uint8_t* xb, int64_t K, uint32_t nb, int m, uint32_t u) {
   if constexpr (Fmt<FMT>::XQ8) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(xb + (size_t(m) * nb + u) * 36);
-    const uint32_t ds = p[0];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x.q[k] = p[1 + k];
-    x.d = h2f(ds & 0xFFFFu);
-    x.s = h2f(ds >> 16);
+    for (int k = 0; k < 9; ++k) r.w[k] = p[k];
   } else {
     constexpr int PP = Fmt<FMT>::XB / 16;
     constexpr int ESZ = Fmt<FMT>::XB / Fmt<FMT>::E;
     const u32x4* src = reinterpret_cast<const u32x4*>(xb + (size_t(m) * size_t(K) + size_t(u) * Fmt<FMT>::E) * ESZ);
+#pragma unroll
+    for (int p = 0; p < PP; ++p) r.pc[p] = src[p];
+  }
+}
+
+// Compute form of a raw unit; ok == false yields the all-zero unit (selects,
+// no branch).
+template <int FMT>
+__device__ inline void x_from_raw(XUnit<FMT>& x, const XRaw<FMT>& r, bool ok) {
+  if constexpr (Fmt<FMT>::XQ8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.q[k] = ok ? r.w[1 + k] : 0u;
+    const uint32_t ds = ok ? r.w[0] : 0u;
+    x.d = h2f(ds & 0xFFFFu);
+    x.s = h2f(ds >> 16);
+  } else {
+    constexpr int PP = Fmt<FMT>::XB / 16;
     u32x4 pc[PP];
 #pragma unroll
-    for (int p = 0; p < PP; ++p) pc[p] = src[p];
+    for (int p = 0; p < PP; ++p) pc[p] = ok ? r.pc[p] : u32x4{0u, 0u, 0u, 0u};
     x_from_pieces<FMT>(x, pc);
   }
+}
+
+// Activation unit straight from global memory (row m, unit index u).
+template <int FMT>
+__device__ inline void fetch_x_global(XUnit<FMT>& x, const uint8_t* xb, int64_t K, uint32_t nb, int m,
+                                      uint32_t u) {
+  XRaw<FMT> r;
+  load_x_raw<FMT>(r, xb, K, nb, m, u);
+  x_from_raw<FMT>(x, r, true);
 }
 
 // Integer block dot of the Q8_1 formats (exact int32).
@@ -267,14 +309,18 @@ struct GemvArgs {
   const uint8_t* x;
 };
 
-template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI>
+template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI, int KW>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   using F = Fmt<FMT>;
   constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
   constexpr int RT = RO * NR;
   constexpr int UC = 64 * J;
   constexpr int PP = F::XB / 16;
+  constexpr int GROUPS = WAVES / KW;  // row groups per workgroup
+  static_assert(WAVES % KW == 0, "KW must divide WAVES");
+  static_assert(KW == 1 || !XLDS, "K split across waves keeps the activation in registers");
   extern __shared__ u32x4 xlds[];
+  __shared__ float red[KW > 1 ? WAVES : 1][KW > 1 ? RT * M : 1];
 
   const int blk = blockIdx.x;
   // Segment of this workgroup; selected with compile-time indices so the
@@ -285,7 +331,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     if (i < a.nseg && blk >= a.seg[i].blk_begin) sg = a.seg[i];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t n0 = (int64_t(blk - sg.blk_begin) * WAVES + wave) * RO;
+  // Waves g*KW .. g*KW+KW-1 share row group g and take its K chunks in turn.
+  const int kw = wave % KW;
+  const int64_t n0 = (int64_t(blk - sg.blk_begin) * GROUPS + wave / KW) * RO;
 
   const uint8_t* rowp[RT];
   const uint16_t* srow[RT];
@@ -307,10 +355,46 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
   const int nchunks = int((nu + UC - 1) / UC);
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = kw; c < nchunks; c += KW) {
     const uint32_t ub = uint32_t(c) * UC;
-    // Loads are unconditional: a unit past the end of the row reads unit 0
-    // of the row (its activation is zeroed below, so it adds exactly 0), and
+    // Issue order matters: the vector-memory counter retires loads in order,
+    // so the activation (small, mostly L2 hits) is requested first and the
+    // weight stream second; the first wait then covers only the activation
+    // and every weight load stays in flight until it is consumed.
+    XRaw<FMT> xr[XLDS ? 1 : J][XLDS ? 1 : M];
+    u32x4 stage[XLDS ? (M * UC * PP + WAVES * 64 - 1) / (WAVES * 64) : 1];
+    if constexpr (!XLDS) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const uint32_t u = ub + uint32_t(j * 64 + lane);
+#pragma unroll
+        for (int m = 0; m < M; ++m) load_x_raw<FMT>(xr[j][m], a.x, a.K, nb, m, (u < nu) ? u : 0u);
+      }
+    } else {
+      // Cooperative staging of this chunk's activation, all M rows, into a
+      // piece-planar LDS layout [m][piece][unit]: lanes reading consecutive
+      // units then hit consecutive 16-byte LDS words (no bank conflicts).
+      if (c > 0) __syncthreads();
+      constexpr int ESZ = F::XB / F::E;
+      constexpr int NS = sizeof(stage) / sizeof(stage[0]);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const int i = int(threadIdx.x) + t * WAVES * 64;
+        const int p = i % PP;
+        const int uu = (i / PP) % UC;
+        const int m = i / (PP * UC);
+        const uint32_t gu = ub + uint32_t(uu);
+        const bool ok = (m < M) && (gu < nu);
+        const u32x4 v = ld_u32x4(a.x + (size_t(ok ? m : 0) * size_t(a.K) + size_t(ok ? gu : 0u) * F::E) * ESZ +
+                                 size_t(p) * 16);
+        stage[t] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // Keep the scheduler from sinking the activation loads below the weight
+    // loads (a later wait for them would then drain the weight stream too).
+    __builtin_amdgcn_sched_barrier(0);
+    // Weight loads are unconditional: a unit past the end of the row reads
+    // unit 0 of the row (its activation is zeroed, so it adds exactly 0), and
     // a row past N reads row 0 (its output is never stored).
     WUnit<FMT> w[RT][J];
 #pragma unroll
@@ -320,23 +404,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) load_w<FMT>(w[r][j], rowp[r], srow[r], nb, uc);
     }
+    // Every load of the chunk is issued before any result is used.
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (XLDS) {
-      // Stage this chunk's activation for all M rows: piece-planar layout
-      // [m][piece][unit] so that lanes reading consecutive units hit
-      // consecutive 16-byte LDS words (no bank conflicts).
-      if (c > 0) __syncthreads();
-      constexpr int ESZ = F::XB / F::E;
-      const int total = M * UC * PP;
-      for (int i = threadIdx.x; i < total; i += WAVES * 64) {
-        const int p = i % PP;
-        const int t = i / PP;
-        const int uu = t % UC;
-        const int m = t / UC;
-        const uint32_t gu = ub + uint32_t(uu);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (gu < nu)
-          v = ld_u32x4(a.x + (size_t(m) * size_t(a.K) + size_t(gu) * F::E) * ESZ + size_t(p) * 16);
-        xlds[(m * PP + p) * UC + uu] = v;
+      constexpr int NS = sizeof(stage) / sizeof(stage[0]);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const int i = int(threadIdx.x) + t * WAVES * 64;
+        if (i < M * UC * PP) {
+          const int p = i % PP;
+          const int uu = (i / PP) % UC;
+          const int m = i / (PP * UC);
+          xlds[(m * PP + p) * UC + uu] = stage[t];
+        }
       }
       __syncthreads();
     }
@@ -353,8 +433,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
           for (int p = 0; p < PP; ++p) pc[p] = xlds[(m * PP + p) * UC + j * 64 + lane];
           x_from_pieces<FMT>(xu, pc);
         } else {
-          fetch_x_global<FMT>(xu, a.x, a.K, nb, m, uok ? u : 0u);
-          if (!uok) zero_x<FMT>(xu);
+          x_from_raw<FMT>(xu, xr[j][m], uok);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r][m] = unit_acc<FMT>(w[r][j], xu, acc[r][m]);
@@ -366,6 +445,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   for (int r = 0; r < RT; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+
+  if constexpr (KW > 1) {
+    // Partial sums of the KW waves of a row group meet in LDS; the group's
+    // first wave adds them (in a fixed order) and writes the outputs.
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) red[wave][r * M + m] = acc[r][m];
+    }
+    __syncthreads();
+    if (kw != 0) return;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float t = red[wave][r * M + m];
+#pragma unroll
+        for (int k = 1; k < KW; ++k) t += red[wave + k][r * M + m];
+        acc[r][m] = t;
+      }
+  }
 
   float out = 0.f;
 #pragma unroll
@@ -389,13 +490,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 // Registry entry of one compiled kernel instance.
 struct GemvEntry {
   const void* fn;
-  int fmt, M, epi, ro, j, xlds, waves;
+  int fmt, M, epi, ro, j, xlds, waves, kw;
 };
 
-template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI>
+template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI, int KW>
 inline GemvEntry gemv_entry() {
-  return GemvEntry{reinterpret_cast<const void*>(&gemv_kernel<FMT, M, RO, J, XLDS, WAVES, EPI>),
-                   FMT, M, EPI, RO, J, XLDS ? 1 : 0, WAVES};
+  return GemvEntry{reinterpret_cast<const void*>(&gemv_kernel<FMT, M, RO, J, XLDS, WAVES, EPI, KW>),
+                   FMT, M, EPI, RO, J, XLDS ? 1 : 0, WAVES, KW};
 }
 
 // LDS bytes an instance needs (0 when the activation lives in registers).

@@ -7,8 +7,10 @@
 
 #include "gemv_impl.h"
 
-// I(FMT, M, RO, J, XLDS, WAVES, EPI)
-#define SKG_I(F, M, RO, J, X, W, E) out.push_back(skg::gemv_entry<F, M, RO, J, X, W, E>());
+// I(FMT, M, RO, J, XLDS, WAVES, EPI): one row group per wave.
+#define SKG_I(F, M, RO, J, X, W, E) out.push_back(skg::gemv_entry<F, M, RO, J, X, W, E, 1>());
+// IK(..., KW): KW waves share each row group and split its K chunks.
+#define SKG_IK(F, M, RO, J, W, E, KW) out.push_back(skg::gemv_entry<F, M, RO, J, false, W, E, KW>());
 
 // Default instances, split by M so translation units compile in parallel.
 // Arguments: format; rows per wave and units per lane for M = 1, for M = 2,

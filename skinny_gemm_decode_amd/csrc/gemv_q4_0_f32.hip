@@ -3,12 +3,17 @@
 
 namespace skg {
 void register_gemv_q4_0_f32(std::vector<GemvEntry>& out) {
+  // The first instance of each (format, M, epilogue) is its default, chosen
+  // by measurement on MI355X under cold-cache rotation.
+  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 4, SKG_EPI_NONE)
   SKG_M12(SKG_Q4_0_F32, 8, 2, 8, 1, 4, 4)
+  SKG_IK(SKG_Q4_0_F32, 1, 8, 1, 4, SKG_EPI_NONE, 2)
+  SKG_IK(SKG_Q4_0_F32, 1, 4, 1, 4, SKG_EPI_NONE, 2)
+  SKG_IK(SKG_Q4_0_F32, 1, 4, 1, 4, SKG_EPI_NONE, 4)
   SKG_I(SKG_Q4_0_F32, 1, 4, 2, false, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 16, 2, false, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 8, 1, false, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 16, 1, false, 4, SKG_EPI_NONE)
-  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 16, 2, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 2, 8, 1, true, 4, SKG_EPI_NONE)
 }

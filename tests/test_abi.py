@@ -134,7 +134,7 @@ def test_other_entry_point_errors(skg):
     assert L.skg_debug_block_dots(3, 8, 64, 6, 3, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_stream_read(FAKE, 17, FAKE, None) == skg.E_SHAPE
     assert L.skg_set_lds_pad(1 << 20) == skg.E_INVALID_ARG
-    assert L.skg_gemv_set_variant(2, 1, 0, 3, 3, 0, 4) == skg.E_UNSUPPORTED
+    assert L.skg_gemv_set_variant(2, 1, 0, 3, 3, 0, 4, 1) == skg.E_UNSUPPORTED
 
 
 def test_variant_registry(skg):
@@ -144,7 +144,7 @@ def test_variant_registry(skg):
         for M in range(1, 9):
             for epi in (0, 1):
                 assert (fmt, M, epi) in seen, (fmt, M, epi)
-    skg.gemv_set_variant(2, 1, 0, 16, 2, 0, 4)
+    skg.gemv_set_variant(2, 1, 0, 16, 2, 0, 4, 1)
     skg.gemv_set_variant(2, 1, 0, 0)
 
 

@@ -107,7 +107,7 @@ def test_every_compiled_variant(skg):
                 W1, _ = make_inputs(skg, fmt, 1, N, K, seed=6000 + 10 * fmt + M)
                 cache[key] = (W0, W1, x)
             W0, W1, x = cache[key]
-            skg.gemv_set_variant(fmt, M, epi, v["ro"], v["j"], v["x_lds"], v["waves"])
+            skg.gemv_set_variant(fmt, M, epi, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
             note(f"variant {v}")
             xin, xq_ref = gpu_activation(skg, fmt, x)
             if epi == skg.EPI_NONE:
