@@ -47,6 +47,25 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_bf16_m1_k4096_n12288_hbm_traffic.md")
+
+
+def counter_traffic():
+    """HBM bytes per headline launch from the committed hardware-counter
+    summary, or None when that summary is missing or was taken on GEMV sources
+    other than the ones built now (the counters would describe another kernel)."""
+    from skinny_gemm_decode_amd.rocprof_summary import gemv_source_hash
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.strip().split(": ", 1) for line in text.splitlines() if line.strip().startswith(
+        ("traffic_bytes_per_launch:", "gemv_source_sha256:")))
+    if fields.get("gemv_source_sha256") != gemv_source_hash():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 # --------------------------------------------------------------------------
 # timing helpers
 # --------------------------------------------------------------------------
@@ -348,7 +367,11 @@ def bench_prefill(skg, si, torch, timer, steps, warm_s):
 # CPU baseline: the oracle itself, on a bounded sample of the headline workload
 # --------------------------------------------------------------------------
 
-def cpu_baseline(si, gpu_sample, budget_s=15.0):
+def cpu_baseline(si, gpu_sample, budget_s=12.0):
+    """The oracle as it stands, timed on this host's cores on a bounded
+    sample of the headline workload: whole bf16 GEMVs (exact decode to fp64,
+    numpy fp64 matvec) over two generated weight buffers, repeated until about
+    budget_s seconds of oracle time; generation is not timed."""
     import numpy as np
 
     import oracle
@@ -359,17 +382,14 @@ def cpu_baseline(si, gpu_sample, budget_s=15.0):
         blas_threads = None
     N, K = 12288, 4096
     x = gpu_sample["x"]
-    done, t0 = 0, time.perf_counter()
-    Ws = []
-    while time.perf_counter() - t0 < budget_s or done == 0:
-        W = si.bf16_weights(si.rng_for(0, 2, 100 + done), N, K)   # generation is not timed
+    Ws = [si.bf16_weights(si.rng_for(0, 2, 100 + b), N, K) for b in range(2)]
+    times = []
+    while sum(times) < budget_s and len(times) < 400:
+        W = Ws[len(times) % 2]
         t1 = time.perf_counter()
-        y, bound = oracle.gemv_ref_fmt("bf16", W, x, x_kind="bf16")
-        Ws.append(time.perf_counter() - t1)
-        done += 1
-        if done >= 64:
-            break
-    per = sum(Ws) / len(Ws)
+        oracle.gemv_ref_fmt("bf16", W, x, x_kind="bf16")
+        times.append(time.perf_counter() - t1)
+    per = sum(times) / len(times)
     alg = N * K * 2 + K * 2 + N * 4
     # parity of the GPU's sampled rows on the timed rotation buffers
     worst = 0.0
@@ -384,9 +404,9 @@ def cpu_baseline(si, gpu_sample, budget_s=15.0):
         "unit": "GB/s",
         "cores": blas_threads if blas_threads else os.cpu_count(),
         "kind": "oracle",
-        "sample": (f"{len(Ws)} full bf16 GEMVs M=1 K=4096 N=12288 (oracle: exact decode to fp64 + numpy "
-                   f"fp64 matvec), {sum(Ws):.1f} s of CPU work; host has {os.cpu_count()} logical CPUs; "
-                   f"decode single-threaded, BLAS threads as given in cores"),
+        "sample": (f"{len(times)} whole bf16 GEMVs M=1 K=4096 N=12288 over 2 generated weight buffers "
+                   f"({sum(times):.1f} s of oracle time: exact decode to fp64, single-threaded, then numpy "
+                   f"fp64 matvec on the BLAS threads given in cores); host has {os.cpu_count()} logical CPUs"),
         "us_per_gemv": per * 1e6,
         "gpu_parity_worst_err_over_tol": worst,
     }
@@ -403,6 +423,9 @@ def main():
                                                   "multi_m,layer,small,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run 5 plain 256 MiB device-to-device copies (a known-size reference for "
+                         "hardware traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -472,10 +495,21 @@ def main():
         log(f"[prefill] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "
             f"({100 * r['frac_peak_mfma_bf16']:.1f}% of bf16 peak)")
 
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[calibration] 5 x 256 MiB device copies")
+        del src, dst
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(si, sample)
     if cpu:
         log(f"[cpu oracle] {cpu['value']:.2f} GB/s ({cpu['us_per_gemv']:.0f} us per GEMV, {cpu['cores']} threads)")
 
+    traffic = counter_traffic()
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -508,7 +542,9 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(head["frac_peak"], 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": head["algorithmic_bytes"],
         },
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
     }
