@@ -234,6 +234,10 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
 skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw);
 int skg_gemv_variants(int* out, int max_entries);
 skg_status skg_set_lds_pad(int64_t bytes);
+/* skg_gemm_tiled_set_variant: prefill kernel organisation, 0 = every wave
+ * decodes weights and runs MFMAs, 1 = producer waves decode, consumer waves
+ * run MFMAs (default).  Process-wide. */
+skg_status skg_gemm_tiled_set_variant(int variant);
 
 #ifdef __cplusplus
 }

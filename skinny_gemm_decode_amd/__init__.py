@@ -5,7 +5,7 @@ the GPU, passes raw device pointers and the current HIP stream to the C ABI
 declared in ``include/skg.h``, and raises ``SkgError`` on a nonzero status.
 All arithmetic happens in the library's HIP kernels; there is no CPU fallback.
 Importing this module fails with ImportError when ``libskg.so`` has not been
-built (``python -m skinny_gemm_decode_amd.build``).
+built (``python skinny_gemm_decode_amd/build.py``).
 
 PyTorch is used for device memory and streams only.
 """
@@ -45,7 +45,7 @@ class SkgError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m skinny_gemm_decode_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python skinny_gemm_decode_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sigs = {
@@ -65,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "skg_gemv_variants": (i32, [ctypes.POINTER(i32), i32]),
         "skg_set_lds_pad": (i32, [i64]),
+        "skg_gemm_tiled_set_variant": (i32, [i32]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -245,3 +246,7 @@ def gemv_set_variant(fmt: int, M: int, epi: int = EPI_NONE, ro: int = 0, j: int 
 
 def set_lds_pad(nbytes: int) -> None:
     check(lib.skg_set_lds_pad(nbytes))
+
+
+def gemm_tiled_set_variant(variant: int) -> None:
+    check(lib.skg_gemm_tiled_set_variant(variant))

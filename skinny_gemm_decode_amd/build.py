@@ -1,7 +1,8 @@
 """Build libskg.so (gfx950 only) in-tree with hipcc.
 
 Every HIP source is compiled to an object in parallel, then linked into one
-shared library next to this file.  Usage: ``python -m skinny_gemm_decode_amd.build``.
+shared library next to this file.  Usage: ``python skinny_gemm_decode_amd/build.py``
+(run as a file: importing the package would load the library being rebuilt).
 """
 
 from __future__ import annotations
@@ -40,7 +41,7 @@ SOURCES = [
 CFLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",

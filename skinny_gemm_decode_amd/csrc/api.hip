@@ -390,6 +390,12 @@ int skg_gemv_variants(int* out, int max_entries) {
   return n;
 }
 
+skg_status skg_gemm_tiled_set_variant(int variant) {
+  if (variant < 0 || variant > 1) return fail(SKG_E_INVALID_ARG, "prefill variant must be 0 or 1");
+  g_gemm_variant = variant;
+  return ok();
+}
+
 skg_status skg_set_lds_pad(int64_t bytes) {
   if (bytes < 0 || bytes > 64 * 1024) return fail(SKG_E_INVALID_ARG, "LDS pad must be 0..65536 bytes");
   init_registry();

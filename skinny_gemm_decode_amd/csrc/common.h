@@ -82,6 +82,19 @@ inline PackedW packed_view(const void* base, const Layout& L) {
 
 __device__ inline u32x4 ld_u32x4(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Byte i of v as a float, one v_cvt_f32_ubyte<i> instruction.  Written as
+// asm because the compiler otherwise narrows the byte mask it can prove and
+// emits a bit-field extract plus a conversion (two VALU ops per element).
+template <int I>
+__device__ inline float cvt_ubyte(uint32_t v) {
+  float r;
+  if constexpr (I == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+  if constexpr (I == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+  if constexpr (I == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+  if constexpr (I == 3) asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 __device__ inline float h2f(uint32_t bits16) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }

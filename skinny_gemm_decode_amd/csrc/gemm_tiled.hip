@@ -21,6 +21,7 @@
 // 8*(l/16)..+7; B supplies column l%16, the same k; the 16x16 result gives
 // lane l rows 4*(l/16)..+3 of column l%16.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -34,17 +35,27 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int GT_BM = 256;
 constexpr int GT_BK = 64;
 constexpr int GT_LDS_ROW = GT_BK + 8;  // bf16 per LDS row: 128 data bytes + 16 pad bytes
+constexpr int GT_PW = 4;              // weight prefetch distance in K steps
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   const f32x2 f = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-template <int NB16>
+// Workgroup barrier for the LDS tile only: waits for this wave's LDS
+// accesses, not for its outstanding global loads (the weight prefetch ring
+// must stay in flight across the barrier).
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int NB16, int PW>
 __global__ __launch_bounds__(256) void gemm_q4_0_bf16_kernel(PackedW P, const uint16_t* __restrict__ A,
                                                              float* __restrict__ y, int M, int N, int K) {
   constexpr int BN = 16 * NB16;
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * GT_LDS_ROW];
+  // 128 LDS rows whatever BN: threads past the tile's 2*BN blocks decode a
+  // clamped duplicate into rows that are never read, so no thread branches.
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * GT_LDS_ROW];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -55,31 +66,32 @@ __global__ __launch_bounds__(256) void gemm_q4_0_bf16_kernel(PackedW P, const ui
   const int nbk = int(P.nb);  // q4_0 blocks per row
   const int steps = (K + GT_BK - 1) / GT_BK;
 
-  // ---- weight decode: thread t < 2*BN owns (tile row t/2, block t%2) ----
-  const bool dec = tid < 2 * BN;
+  // ---- weight decode: thread t owns (tile row t/2, block t%2 of the step) ----
   const int drow = tid >> 1;
   const int dblk = tid & 1;
   const int dn = min(n0 + drow, N - 1);
   const uint8_t* dpay = P.payload + size_t(dn) * P.row_bytes;
   const uint16_t* dsc = P.scales + size_t(dn) * P.nb;
 
-  u32x4 wraw = {0u, 0u, 0u, 0u};
-  uint32_t wsc = 0;
-  auto load_w = [&](int s) {
+  // Ring of PW raw blocks: the block of step s is requested PW steps before
+  // it is decoded, which covers HBM latency with one wave per SIMD.  A block
+  // past the end of K reads the last block and decodes with scale 0.
+  u32x4 wraw[PW];
+  uint32_t wsc[PW];
+  bool wok[PW];
+  auto load_w = [&](auto slot_c, int s) {
+    constexpr int SL = decltype(slot_c)::value;
     const int kb = s * 2 + dblk;
-    if (dec && kb < nbk) {
-      wraw = ld_u32x4(dpay + size_t(kb) * 16);
-      wsc = dsc[kb];
-    } else {
-      wraw = u32x4{0u, 0u, 0u, 0u};
-      wsc = 0;  // d = 0: the block decodes to zeros
-    }
+    const int kc = min(kb, nbk - 1);
+    wraw[SL] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dpay + size_t(kc) * 16));
+    wsc[SL] = __builtin_nontemporal_load(dsc + kc);
+    wok[SL] = kb < nbk;
   };
-  auto store_w = [&](int buf) {
-    if (!dec) return;
-    const float d = h2f(wsc);
+  auto store_w = [&](auto slot_c, int buf) {
+    constexpr int SL = decltype(slot_c)::value;
+    const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
     const float nd8 = -8.0f * d;
-    const uint32_t pw[4] = {wraw.x, wraw.y, wraw.z, wraw.w};
+    const uint32_t pw[4] = {wraw[SL].x, wraw[SL].y, wraw[SL].z, wraw[SL].w};
     uint32_t o[16];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -98,20 +110,20 @@ __global__ __launch_bounds__(256) void gemm_q4_0_bf16_kernel(PackedW P, const ui
   };
 
   // ---- activation fragments: lane supplies row l%16, k 8*(l/16)..+7 ----
+  // Past the end of K the fragment reads the last 8 columns; the weights
+  // there decode to zero, so it contributes exactly 0.
   const int arow_base = m0 + wave * 64 + (lane & 15);
   const int akoff = (lane >> 4) * 8;
   u32x4 afr[2][4][2];  // [buffer][mi][kk]
-  auto load_a = [&](int buf, int s) {
+  auto load_a = [&](auto buf_c, int s) {
+    constexpr int BUF = decltype(buf_c)::value;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int m = min(arow_base + mi * 16, M - 1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int k = s * GT_BK + kk * 32 + akoff;
-        if (k < K)
-          afr[buf][mi][kk] = ld_u32x4(A + size_t(m) * size_t(K) + size_t(k));
-        else
-          afr[buf][mi][kk] = u32x4{0u, 0u, 0u, 0u};
+        const int k = min(s * GT_BK + kk * 32 + akoff, K - 8);
+        afr[BUF][mi][kk] = ld_u32x4(A + size_t(m) * size_t(K) + size_t(k));
       }
     }
   };
@@ -122,42 +134,52 @@ __global__ __launch_bounds__(256) void gemm_q4_0_bf16_kernel(PackedW P, const ui
 #pragma unroll
     for (int nj = 0; nj < NB16; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_w(0);
-  load_a(0, 0);
-  store_w(0);
-  __syncthreads();
+  // prologue: fill the ring, decode step 0, refill its slot
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (load_w(std::integral_constant<int, I>{}, I), ...);
+  }(std::make_integer_sequence<int, PW>{});
+  load_a(std::integral_constant<int, 0>{}, 0);
+  store_w(std::integral_constant<int, 0>{}, 0);
+  load_w(std::integral_constant<int, 0>{}, PW);
+  lds_barrier();
 
-  // One step: prefetch step s+1 (weights raw, activation fragments), run the
-  // MFMAs of step s from LDS buffer CUR, decode step s+1 into the other
-  // buffer, barrier.  CUR is a compile-time constant so the fragment double
-  // buffer stays in registers.
-  auto step = [&](auto cur_c, int s) {
+  // Step s: activation fragments of s+1 requested; the B fragments of s read
+  // from LDS; the MFMAs of s; the raw block of s+1 (requested PW steps ago)
+  // decoded into the other LDS buffer and its ring slot refilled with s+1+PW;
+  // one barrier.  CUR and SLOT are compile-time constants.
+  auto step = [&](auto cur_c, auto slot_c, int s) {
     constexpr int CUR = decltype(cur_c)::value;
-    const bool more = s + 1 < steps;
-    if (more) {
-      load_w(s + 1);
-      load_a(CUR ^ 1, s + 1);
-    }
+    constexpr int SLOT = decltype(slot_c)::value;  // ring slot of step s+1
+    load_a(std::integral_constant<int, CUR ^ 1>{}, s + 1);
+    u32x4 bfr[2][NB16];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nj = 0; nj < NB16; ++nj)
+        bfr[kk][nj] = *reinterpret_cast<const u32x4*>(&Bs[CUR][(nj * 16 + (lane & 15)) * GT_LDS_ROW + kk * 32 + akoff]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int nj = 0; nj < NB16; ++nj) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(
-            &Bs[CUR][(nj * 16 + (lane & 15)) * GT_LDS_ROW + kk * 32 + akoff]);
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, bfr[kk][nj]);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
           const bf16x8 av = __builtin_bit_cast(bf16x8, afr[CUR][mi][kk]);
           acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mi][nj], 0, 0, 0);
         }
       }
-    }
-    if (more) store_w(CUR ^ 1);
-    __syncthreads();
+    store_w(slot_c, CUR ^ 1);
+    load_w(slot_c, s + 1 + PW);
+    lds_barrier();
   };
-  for (int s = 0; s < steps; s += 2) {
-    step(std::integral_constant<int, 0>{}, s);
-    if (s + 1 < steps) step(std::integral_constant<int, 1>{}, s + 1);
+  constexpr int U = (PW % 2 == 0) ? PW : 2 * PW;  // steps per unrolled iteration
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((s0 + I < steps ? step(std::integral_constant<int, I % 2>{}, std::integral_constant<int, (I + 1) % PW>{},
+                              s0 + I)
+                       : void()),
+       ...);
+    }(std::make_integer_sequence<int, U>{});
   }
 
   // ---- store: lane holds rows 4*(l/16)..+3 of column l%16 of each tile ----
@@ -176,6 +198,178 @@ __global__ __launch_bounds__(256) void gemm_q4_0_bf16_kernel(PackedW P, const ui
   }
 }
 
+// Producer/consumer variant: 8 waves per workgroup.  Waves 0-3 own the
+// output rows exactly as above (activation fragments from global memory, B
+// fragments from LDS, MFMAs); waves 4-7 own the weight stream (the PW-deep
+// ring of raw blocks and the decode into LDS).  Each SIMD then runs one wave
+// of each kind, so decode VALU work and MFMAs overlap, and either wave covers
+// the other's memory waits.
+template <int NB16, int PW>
+__global__ __launch_bounds__(512) void gemm_q4_0_bf16_pc_kernel(PackedW P, const uint16_t* __restrict__ A,
+                                                                float* __restrict__ y, int M, int N, int K) {
+  constexpr int BN = 16 * NB16;
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * GT_LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t As_raw[4 * 2 * 64 * 8 * 16];  // 4 waves x 2 x 64 rows x 128 B
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int mtiles = (M + GT_BM - 1) / GT_BM;
+  const int m0 = (blockIdx.x % mtiles) * GT_BM;
+  const int n0 = (blockIdx.x / mtiles) * BN;
+  const int nbk = int(P.nb);
+  const int steps = (K + GT_BK - 1) / GT_BK;
+  constexpr int U = (PW % 2 == 0) ? PW : 2 * PW;
+
+  if (wave >= 4) {
+    // ---------------- producer: weight ring + decode ----------------
+    const int ptid = tid - 256;
+    const int drow = ptid >> 1;
+    const int dblk = ptid & 1;
+    const int dn = min(n0 + drow, N - 1);
+    const uint8_t* dpay = P.payload + size_t(dn) * P.row_bytes;
+    const uint16_t* dsc = P.scales + size_t(dn) * P.nb;
+    u32x4 wraw[PW];
+    uint32_t wsc[PW];
+    bool wok[PW];
+    auto load_w = [&](auto slot_c, int s) {
+      constexpr int SL = decltype(slot_c)::value;
+      const int kb = s * 2 + dblk;
+      const int kc = min(kb, nbk - 1);
+      wraw[SL] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dpay + size_t(kc) * 16));
+      wsc[SL] = __builtin_nontemporal_load(dsc + kc);
+      wok[SL] = kb < nbk;
+    };
+    auto store_w = [&](auto slot_c, int buf) {
+      constexpr int SL = decltype(slot_c)::value;
+      const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
+      const float nd8 = -8.0f * d;
+      const uint32_t pw[4] = {wraw[SL].x, wraw[SL].y, wraw[SL].z, wraw[SL].w};
+      uint32_t o[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = pw[k] & 0x0F0F0F0Fu;
+        const uint32_t hi = (pw[k] >> 4) & 0x0F0F0F0Fu;
+        o[2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(lo), d, nd8), fmaf(cvt_ubyte<1>(lo), d, nd8));
+        o[2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(lo), d, nd8), fmaf(cvt_ubyte<3>(lo), d, nd8));
+        o[8 + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(hi), d, nd8), fmaf(cvt_ubyte<1>(hi), d, nd8));
+        o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(hi), d, nd8), fmaf(cvt_ubyte<3>(hi), d, nd8));
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(&Bs[buf][drow * GT_LDS_ROW + dblk * 32]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (load_w(std::integral_constant<int, I>{}, I), ...);
+    }(std::make_integer_sequence<int, PW>{});
+    store_w(std::integral_constant<int, 0>{}, 0);
+    load_w(std::integral_constant<int, 0>{}, PW);
+    lds_barrier();
+    auto pstep = [&](auto cur_c, auto slot_c, int s) {
+      constexpr int CUR = decltype(cur_c)::value;
+      store_w(slot_c, CUR ^ 1);
+      load_w(slot_c, s + 1 + PW);
+      lds_barrier();
+    };
+    for (int s0 = 0; s0 < steps; s0 += U) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((s0 + I < steps ? pstep(std::integral_constant<int, I % 2>{}, std::integral_constant<int, (I + 1) % PW>{},
+                                 s0 + I)
+                         : void()),
+         ...);
+      }(std::make_integer_sequence<int, U>{});
+    }
+    return;
+  }
+
+  // ---------------- consumer: activation slice + MFMA ----------------
+  // Each consumer wave loads its own 64 rows x 64 columns of x per step with
+  // full-cache-line loads (instruction i: rows 8i..8i+7, 128 contiguous bytes
+  // each), parks them in a wave-private LDS slice, and reads the MFMA
+  // fragments from there.  Slot of (row r, 16-byte chunk c) = 8r + (c ^ (r & 7)):
+  // the 16 rows of a fragment read land on distinct banks.  Only the owning
+  // wave touches its slice, and a wave's LDS operations complete in order, so
+  // the slice needs no barrier.  Rows past M read row M-1; columns past K read
+  // the last 8 (their weights decode to zero).
+  u32x4* As = reinterpret_cast<u32x4*>(As_raw) + wave * (2 * 64 * 8);
+  const int mw = m0 + wave * 64;
+  u32x4 araw[8];
+  auto load_a = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      const int m = min(mw + r, M - 1);
+      const int k = min(s * GT_BK + (lane & 7) * 8, K - 8);
+      araw[i] = ld_u32x4(A + size_t(m) * size_t(K) + size_t(k));
+    }
+  };
+  auto park_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      const int c = lane & 7;
+      As[buf * 512 + r * 8 + (c ^ (r & 7))] = araw[i];
+    }
+  };
+  f32x4 acc[4][NB16];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NB16; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load_a(0);
+  park_a(0);
+  load_a(1);
+  lds_barrier();
+  auto cstep = [&](auto cur_c, int s) {
+    constexpr int CUR = decltype(cur_c)::value;
+    park_a(CUR ^ 1);  // slice of step s+1 (loaded one step ago)
+    load_a(s + 2);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 afr[4], bfr[NB16];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = mi * 16 + (lane & 15);
+        const int c = kk * 4 + (lane >> 4);
+        afr[mi] = As[CUR * 512 + r * 8 + (c ^ (r & 7))];
+      }
+#pragma unroll
+      for (int nj = 0; nj < NB16; ++nj)
+        bfr[nj] = *reinterpret_cast<const u32x4*>(&Bs[CUR][(nj * 16 + (lane & 15)) * GT_LDS_ROW + kk * 32 + (lane >> 4) * 8]);
+#pragma unroll
+      for (int nj = 0; nj < NB16; ++nj) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, bfr[nj]);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, afr[mi]);
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mi][nj], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();
+  };
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((s0 + I < steps ? cstep(std::integral_constant<int, I % 2>{}, s0 + I) : void()), ...);
+    }(std::make_integer_sequence<int, U>{});
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int nj = 0; nj < NB16; ++nj) {
+      const int n = n0 + nj * 16 + (lane & 15);
+      const float v[4] = {acc[mi][nj].x, acc[mi][nj].y, acc[mi][nj].z, acc[mi][nj].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wave * 64 + mi * 16 + (lane >> 4) * 4 + r;
+        if (m < M && n < N) y[size_t(m) * size_t(N) + size_t(n)] = v[r];
+      }
+    }
+  }
+}
+
+int g_gemm_variant = 1;  // 0: one role per wave, 1: producer/consumer waves
+
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,
                              float* y, hipStream_t stream) {
   const PackedW P = packed_view(W, L);
@@ -186,12 +380,19 @@ hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, con
   const int cus = 256;
   const double e7 = double(t7) / double(((t7 + cus - 1) / cus) * cus);
   const double e8 = double(t8) / double(((t8 + cus - 1) / cus) * cus);
-  if (e7 > e8) {
-    hipLaunchKernelGGL(gemm_q4_0_bf16_kernel<7>, dim3(unsigned(t7)), dim3(256), 0, stream, P,
-                       static_cast<const uint16_t*>(x), y, int(M), int(N), int(K));
+  const bool seven = e7 > e8;
+  const unsigned grid = unsigned(seven ? t7 : t8);
+  const uint16_t* xa = static_cast<const uint16_t*>(x);
+  if (g_gemm_variant == 0) {
+    if (seven)
+      hipLaunchKernelGGL((gemm_q4_0_bf16_kernel<7, GT_PW>), dim3(grid), dim3(256), 0, stream, P, xa, y, int(M), int(N), int(K));
+    else
+      hipLaunchKernelGGL((gemm_q4_0_bf16_kernel<8, GT_PW>), dim3(grid), dim3(256), 0, stream, P, xa, y, int(M), int(N), int(K));
   } else {
-    hipLaunchKernelGGL(gemm_q4_0_bf16_kernel<8>, dim3(unsigned(t8)), dim3(256), 0, stream, P,
-                       static_cast<const uint16_t*>(x), y, int(M), int(N), int(K));
+    if (seven)
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<7, GT_PW>), dim3(grid), dim3(512), 0, stream, P, xa, y, int(M), int(N), int(K));
+    else
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<8, GT_PW>), dim3(grid), dim3(512), 0, stream, P, xa, y, int(M), int(N), int(K));
   }
   return hipGetLastError();
 }
