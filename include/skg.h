@@ -220,11 +220,18 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
  *   waves sharing each row group (each takes every kw-th K chunk; partial sums
  *   meet in LDS) for every later gemv / gemv_multi call with this
  *   (fmt, M, epi); ro = 0 restores the default.  SKG_E_UNSUPPORTED if that
- *   variant is not compiled.
+ *   variant is not compiled; a later call returns SKG_E_UNSUPPORTED if the
+ *   selected variant does not take its K.
+ *   x_lds = 2 names the matrix-core kernel of the fp32-activation quantised
+ *   formats (SKG_Q8_0_F32, SKG_Q4_0_F32): ro = 16 output rows per tile, j =
+ *   fp16 terms carrying each activation (2: ~22 bits; 1: one rounding to
+ *   fp16, relative error 2^-11), waves = most waves per workgroup, kw =
+ *   quantisation blocks per wave; it takes K with (K / 32) % kw == 0 and
+ *   K / 32 <= waves * kw.
  * skg_gemv_variants: writes up to max_entries records of 8 ints
  *   {fmt, M, epi, ro, j, x_lds, waves, kw} to out (host) and returns the
- *   number of compiled variants; the first record of each (fmt, M, epi) is its
- *   default.
+ *   number of compiled variants.  For each (fmt, M, epi) and K the default is
+ *   the first record whose variant takes that K.
  * skg_set_lds_pad: extra dynamic LDS bytes (0..65536) requested by every gemv
  *   launch, which lowers occupancy without changing the code (the MI50 case
  *   study's diagnostic control).  Initial value: $SKG_LDS_PAD_BYTES or 0.

@@ -46,6 +46,11 @@ class SkgError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python skinny_gemm_decode_amd/build.py`")
+    # PyTorch's HIP runtime must be loaded first: the library then binds to it
+    # by soname, so one process never holds two HIP runtimes (a second copy,
+    # loaded through the library's own runpath, does not see the device once
+    # PyTorch has initialised it).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sigs = {

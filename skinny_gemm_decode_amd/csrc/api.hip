@@ -8,9 +8,11 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "gemv_instances.h"
+#include "gemv_mfma.h"
 #include "kernels.h"
 
 using namespace skg;
@@ -87,6 +89,10 @@ std::atomic<int64_t> g_lds_pad{0};
 void init_registry() {
   std::call_once(g_reg_once, [] {
     auto* v = new std::vector<GemvEntry>();
+    // Matrix-core defaults first (M >= 2 for q4_0, M >= 4 for q8_0, where
+    // they measure faster); their measurement variants last.
+    register_gemv_mfma_q4_0(*v);
+    register_gemv_mfma_q8_0(*v);
     register_gemv_bf16(*v);
     register_gemv_q8_0_f32(*v);
     register_gemv_q8_0_f32_m38(*v);
@@ -94,6 +100,8 @@ void init_registry() {
     register_gemv_q4_0_f32_m35(*v);
     register_gemv_q4_0_f32_m68(*v);
     register_gemv_q8_1(*v);
+    register_gemv_mfma_q4_0_alt(*v);
+    register_gemv_mfma_q8_0_alt(*v);
     for (auto& a : g_sel)
       for (auto& b : a)
         for (int& c : b) c = -1;
@@ -102,17 +110,92 @@ void init_registry() {
   });
 }
 
-const GemvEntry* find_variant(int fmt, int M, int epi) {
+// The matrix-core kernel runs nb / kw waves of kw blocks each.
+bool variant_supports(const GemvEntry& e, int64_t K) {
+  if (e.xlds != 2) return true;
+  const int64_t nb = K / 32;
+  return nb % e.kw == 0 && nb >= e.kw && nb <= e.max_nb;
+}
+
+// The selected variant, else the first registered one that supports K.
+const GemvEntry* find_variant(int fmt, int M, int epi, int64_t K) {
   init_registry();
   int sel;
   {
     std::lock_guard<std::mutex> lk(g_sel_mu);
     sel = g_sel[fmt][M][epi];
   }
-  if (sel >= 0) return &(*g_reg)[size_t(sel)];
+  if (sel >= 0) {
+    const GemvEntry& e = (*g_reg)[size_t(sel)];
+    return variant_supports(e, K) ? &e : nullptr;
+  }
   for (const GemvEntry& e : *g_reg)
-    if (e.fmt == fmt && e.M == M && e.epi == epi) return &e;
+    if (e.fmt == fmt && e.M == M && e.epi == epi && variant_supports(e, K)) return &e;
   return nullptr;
+}
+
+// Workgroups of a persistent launch that fit on one CU at once.
+int blocks_per_cu(const void* fn, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::vector<std::tuple<const void*, int, size_t, int>> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  for (auto& c : cache)
+    if (std::get<0>(c) == fn && std::get<1>(c) == threads && std::get<2>(c) == lds) return std::get<3>(c);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess || n < 1) n = 1;
+  cache.emplace_back(fn, threads, lds, n);
+  return n;
+}
+
+skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64_t* Ns, const void* W,
+                            const void* x, float* const* ys, int epi, hipStream_t stream) {
+  const int wk = wkind_of(v.fmt);
+  MfArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.K = K;
+  a.nb = uint32_t(K / 32);
+  a.x = static_cast<const float*>(x);
+  const uint8_t* base = static_cast<const uint8_t*>(W);
+  int64_t tiles = 0;
+  if (epi == SKG_EPI_SWIGLU) {
+    const Layout L = layout_of(wk, Ns[0], K);
+    a.nseg = 1;
+    a.seg[0].w0 = packed_view(base, L);
+    a.seg[0].w1 = packed_view(base + L.total, L);
+    a.seg[0].y = ys[0];
+    a.seg[0].N = Ns[0];
+    tiles = (Ns[0] + MF_ROWS - 1) / MF_ROWS;
+  } else {
+    a.nseg = nseg;
+    size_t off = 0;
+    for (int i = 0; i < nseg; ++i) {
+      const Layout L = layout_of(wk, Ns[i], K);
+      a.seg[i].w0 = packed_view(base + off, L);
+      a.seg[i].w1 = a.seg[i].w0;
+      a.seg[i].y = ys[i];
+      a.seg[i].N = Ns[i];
+      a.seg[i].tile_begin = int(tiles);
+      tiles += (Ns[i] + MF_ROWS - 1) / MF_ROWS;
+      off += L.total;
+    }
+  }
+  if (tiles > 0x7FFFFFFF) return fail(SKG_E_SHAPE, "too many rows");
+  a.ntiles = int(tiles);
+  int cus = 0;
+  skg_status st = check_device(&cus);
+  if (st != SKG_OK) return st;
+  const int threads = int(a.nb / uint32_t(v.kw)) * 64;
+  const size_t lds = size_t(v.lds);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+  }
+  const int64_t resident = int64_t(cus) * blocks_per_cu(v.fn, threads, lds);
+  const int grid = int(tiles < resident ? tiles : resident);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(v.fn, dim3(unsigned(grid)), dim3(unsigned(threads)), args, lds, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "gemv launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 size_t packed_size_multi(int fmt, int n, const int64_t* Ns, int64_t K) {
@@ -123,8 +206,11 @@ size_t packed_size_multi(int fmt, int n, const int64_t* Ns, int64_t K) {
 
 skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const int64_t* Ns, const void* W,
                                 const void* x, float* const* ys, int epi, hipStream_t stream) {
-  const GemvEntry* v = find_variant(fmt, int(M), epi);
-  if (!v) return fail(SKG_E_UNSUPPORTED, "no compiled kernel for fmt=%d M=%lld epi=%d", fmt, (long long)M, epi);
+  const GemvEntry* v = find_variant(fmt, int(M), epi, K);
+  if (!v)
+    return fail(SKG_E_UNSUPPORTED, "no compiled kernel (or the selected variant does not take K=%lld) for fmt=%d "
+                "M=%lld epi=%d", (long long)K, fmt, (long long)M, epi);
+  if (v->xlds == 2) return launch_gemv_mfma(*v, K, nseg, Ns, W, x, ys, epi, stream);
   const int wk = wkind_of(fmt);
   GemvArgs a;
   std::memset(&a, 0, sizeof a);

@@ -487,10 +487,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   }
 }
 
-// Registry entry of one compiled kernel instance.
+// Registry entry of one compiled kernel instance.  xlds: 0 = activation in
+// registers, 1 = staged in LDS, 2 = matrix-core kernel (activation held as
+// fp16 MFMA operands; j is then the number of fp16 terms per element).
+// lds: fixed LDS bytes (matrix-core kernel); max_nb: largest number of
+// quantisation blocks per row it handles (0 = any).
 struct GemvEntry {
   const void* fn;
   int fmt, M, epi, ro, j, xlds, waves, kw;
+  int lds = 0;
+  int max_nb = 0;
 };
 
 template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI, int KW>

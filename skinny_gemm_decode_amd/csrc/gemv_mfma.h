@@ -1,0 +1,470 @@
+// Small-batch GEMV on the matrix cores: y[m][n] = sum_k W[n][k] x[m][k] for
+// q4_0 / q8_0 weights and fp32 activations, 1 <= M <= 8.
+//
+// With fp32 activations every weight element costs M fused multiply-adds on
+// the vector ALU, so the vector kernel stops being bound by HBM as soon as
+// M > 1 ("The Shape That Actually Matters": the 8-row kernel that keeps 64
+// accumulators per thread loses to the one-row kernel at M = 1).  Here the
+// products run on v_mfma_f32_16x16x32_f16 instead, and the vector ALU only
+// decodes weights:
+//
+// * One MFMA takes one 32-element quantisation block of 16 weight rows (the
+//   B operand, one column per row) against the same 32 activation elements of
+//   up to 16 activation rows (the A operand; rows m >= M are don't-care, their
+//   outputs are never read).  Its fp32 result is scaled by the block's fp16
+//   scale and accumulated; so no two blocks share an MFMA accumulator.
+// * Weights decode exactly to fp16: a q4_0 nibble n becomes 1024 + n (or
+//   1024 + 16 n for a high nibble) by OR-ing it into the mantissa of 1024.0
+//   (one v_and_or_b32 per two elements), and one packed fp16 add (or fma by
+//   1/16) makes that n - 8; a q8_0 code q becomes 1024 + (q + 128) by a byte
+//   permute with 0x64, then q.  Every weight value is a small integer, exact
+//   in fp16, and a zero weight contributes exactly zero.
+// * The activation is split into two fp16 terms, hi = fp16(x s) and
+//   lo = fp16(x s - hi), where s is a power of two chosen per activation row
+//   and per wave so that the largest |x| of the row in the wave's span of K
+//   maps into [2^14, 2^15).  The pair carries ~22 significant bits for every
+//   element within 2^-28 of that largest magnitude; smaller elements keep an
+//   absolute error below 2^-39 of it.  Every product is exact in fp32.  Each
+//   block takes two MFMAs (hi, then lo accumulated on top).
+// * Loads keep the row-major packed layout of the vector kernels: lane
+//   (g, c) of a wave (g = lane / 16, c = lane % 16) reads the 16-byte unit of
+//   block 4 q + g of row c, i.e. four consecutive blocks per row per load.
+//   A 4 x 4 transpose across the four 16-lane rows (two v_permlane32_swap and
+//   two v_permlane16_swap per four dwords) then leaves dword g of every block
+//   in lane (g, c): exactly the B operand layout, where lane (g, c) holds
+//   k = 8 g .. 8 g + 7 of column c.
+// * Waves split K: wave w owns blocks BPW w .. BPW w + BPW - 1 and keeps their A
+//   operands in registers for the whole launch.  Workgroups are persistent:
+//   each stages the activation once (through wave-private LDS, in the A
+//   operand order) and then walks tiles of 16 output rows, loading tile t + 1
+//   before decoding tile t.  Partial sums of the waves meet in LDS.
+#pragma once
+
+#include "common.h"
+#include "gemv_impl.h"
+
+#include <type_traits>
+
+namespace skg {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int MF_ROWS = 16;  // output rows per tile (MFMA N dimension)
+
+struct MfSeg {
+  PackedW w0, w1;
+  float* y;
+  int64_t N;
+  int tile_begin;
+};
+
+struct MfArgs {
+  MfSeg seg[MAX_SEGS];
+  int nseg;
+  int ntiles;
+  int64_t K;
+  uint32_t nb;
+  const float* x;
+};
+
+__device__ inline uint32_t bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ inline f16x2 half2_of(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f<SKG_DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<SKG_DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f<SKG_DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<SKG_DPP_ROW_MIRROR>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// In-register 4 x 4 transpose across the four 16-lane rows of a wave: on
+// entry v[q] in row r holds element (r, q); on exit v[q] in row r holds
+// element (q, r).
+__device__ inline void transpose_rows4(uint32_t (&v)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  v[0] = c[0];
+  v[1] = c[1];
+  v[2] = d[0];
+  v[3] = d[1];
+}
+
+// No inline asm in this kernel: the compiler inserts the wait states an
+// in-flight MFMA needs before another instruction writes or reads its
+// registers only for instructions it can see.
+// B operand of one block from dword g of its q4_0 unit (bytes 4g..4g+3: low
+// nibbles are elements 4g..4g+3, high nibbles 16+4g..16+4g+3) as n - 8.
+// Slot order: elements 4g, 4g+2, 4g+1, 4g+3, then the same plus 16.
+__device__ inline f16x8 decode_q4_0(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic) {
+  const uint32_t w8 = w >> 8;
+  const f16x2 e0 = half2_of((w & mlo) | magic);   // 1024 + n
+  const f16x2 e1 = half2_of((w8 & mlo) | magic);
+  const f16x2 e2 = half2_of((w & mhi) | magic);   // 1024 + 16 n
+  const f16x2 e3 = half2_of((w8 & mhi) | magic);
+  const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const f16x2 r0 = e0 + off, r1 = e1 + off;
+  const f16x2 r2 = __builtin_elementwise_fma(e2, sixteenth, off16);
+  const f16x2 r3 = __builtin_elementwise_fma(e3, sixteenth, off16);
+  return f16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// B operand of one block from dword g of each q8_0 plane (codes 4g..4g+3 and
+// 16+4g..16+4g+3) as q, same slot order as decode_q4_0.
+__device__ inline f16x8 decode_q8_0(uint32_t p0, uint32_t p1) {
+  const uint32_t u0 = p0 ^ 0x80808080u, u1 = p1 ^ 0x80808080u;  // q + 128 as unsigned bytes
+  const uint32_t hi = 0x64646464u;
+  // bytes {u.b0, 0x64, u.b2, 0x64} and {u.b1, 0x64, u.b3, 0x64}: 1024 + q + 128
+  const f16x2 e0 = half2_of(__builtin_amdgcn_perm(hi, u0, 0x04020400u));
+  const f16x2 e1 = half2_of(__builtin_amdgcn_perm(hi, u0, 0x04030401u));
+  const f16x2 e2 = half2_of(__builtin_amdgcn_perm(hi, u1, 0x04020400u));
+  const f16x2 e3 = half2_of(__builtin_amdgcn_perm(hi, u1, 0x04030401u));
+  const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const f16x2 r0 = e0 + off, r1 = e1 + off, r2 = e2 + off, r3 = e3 + off;
+  return f16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Weight registers of one tile for one matrix: NP planes x BPW/4 quads of 16
+// bytes and the fp16 scales of the wave's BPW blocks (aligned 16-byte loads:
+// the kernel requires nb % BPW == 0).
+template <int NP, int BPW>
+struct MfW {
+  u32x4 u[BPW / 4][NP];
+  u32x4 sc[BPW / 8];
+};
+
+template <int NP, int BPW>
+__device__ inline void mf_load_quad(MfW<NP, BPW>& r, int q, const uint8_t* rowp, uint32_t nb, uint32_t blk0,
+                                    int g) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    r.u[q][p] = ld_u32x4_stream(rowp + (size_t(p) * nb + blk0 + uint32_t(4 * q + g)) * 16);
+}
+
+template <int NP, int BPW>
+__device__ inline void mf_load_scales(MfW<NP, BPW>& r, const uint16_t* srow, uint32_t blk0) {
+  const u32x4* sp = reinterpret_cast<const u32x4*>(srow + blk0);
+#pragma unroll
+  for (int i = 0; i < BPW / 8; ++i) r.sc[i] = __builtin_nontemporal_load(sp + i);
+}
+
+// Where the next tile of one matrix lives, for the rolling prefetch.
+struct MfNext {
+  const uint8_t* rowp;
+  const uint16_t* srow;
+  uint32_t nb;
+};
+
+// One tile of one matrix.  With RELOAD, each quad's registers are refilled
+// with the same quad of the next tile as soon as they have been transposed,
+// and the scales after their last use, so about one tile of loads stays in
+// flight with a single register set.
+template <int NP, int BPW, int RR, int XT, bool RELOAD>
+__device__ inline void mf_tile(MfW<NP, BPW>& r, const f16x8 (&ah)[BPW], const f16x8 (&al)[BPW], float (&acc)[4],
+                               uint32_t mlo, uint32_t mhi, uint32_t magic, const MfNext& nx, uint32_t blk0, int g) {
+  uint32_t scw[BPW / 2];
+#pragma unroll
+  for (int i = 0; i < BPW / 8; ++i) {
+    scw[4 * i + 0] = r.sc[i].x;
+    scw[4 * i + 1] = r.sc[i].y;
+    scw[4 * i + 2] = r.sc[i].z;
+    scw[4 * i + 3] = r.sc[i].w;
+  }
+  if constexpr (RELOAD) {
+    mf_load_scales<NP, BPW>(r, nx.srow, blk0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < BPW / 4; ++q) {
+    uint32_t t[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      t[p][0] = r.u[q][p].x;
+      t[p][1] = r.u[q][p].y;
+      t[p][2] = r.u[q][p].z;
+      t[p][3] = r.u[q][p].w;
+      transpose_rows4(t[p]);
+    }
+    if constexpr (RELOAD) {
+      mf_load_quad<NP, BPW>(r, q, nx.rowp, nx.nb, blk0, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * q + jj;
+      f16x8 bw;
+      if constexpr (NP == 1)
+        bw = decode_q4_0(t[0][jj], mlo, mhi, magic);
+      else
+        bw = decode_q8_0(t[0][jj], t[1][jj]);
+      f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j], bw, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      if constexpr (XT == 2) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[j], bw, d, 0, 0, 0);
+      const uint32_t sw = scw[j >> 1];
+      const float s = h2f((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+#pragma unroll
+      for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, d[i], acc[i]);
+    }
+  }
+}
+
+// LDS bytes of one launch with up to WAVES waves: per-wave activation
+// staging, reused afterwards for the two reduction buffers.
+template <int M, int WAVES, int BPW, int XT, int NR>
+struct MfLds {
+  // one pass of 8 blocks (hi and lo A entries)
+  static constexpr int WAVE_STAGE = XT * 8 * 4 * M * 16;
+  static constexpr int STAGE = WAVES * WAVE_STAGE;
+  static constexpr int RED = 2 * WAVES * NR * MF_ROWS * M * 4;
+  static constexpr int BYTES = STAGE > RED ? STAGE : RED;
+};
+
+// Launched with nb / BPW waves (at most WAVES), so every wave owns BPW
+// blocks; requires nb % BPW == 0.
+template <int FMT, int M, int WAVES, int BPW, int XT, int EPI, int PD>
+__global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
+  static_assert(PD == 1 || PD == 2, "prefetch depth: tiles in flight per wave");
+  static_assert(BPW % 8 == 0, "whole 16-byte scale loads");
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32, "fp32-activation quantised formats only");
+  constexpr int NP = (FMT == SKG_Q8_0_F32) ? 2 : 1;
+  constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
+  constexpr int RR = M < 4 ? M : 4;  // accumulator rows a lane can own
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  // The nibble masks (SGPRs) and fp16 1024.0 in both halves (a VGPR) are
+  // made opaque here, before any MFMA, so each q4_0 pair decodes in one
+  // v_and_or_b32 (two literals do not fit one instruction).  The empty asm
+  // statements emit nothing.
+  uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+  asm volatile("" : "+s"(mlo));
+  asm volatile("" : "+s"(mhi));
+  asm volatile("" : "+v"(magic));
+  const int nw = int(blockDim.x) >> 6;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const uint32_t blk0 = uint32_t(wave) * BPW;
+
+  const int t0 = blockIdx.x;
+  const int step = int(gridDim.x);
+  if (t0 >= a.ntiles) return;  // uniform per workgroup: no barrier is skipped by part of it
+  const int nmine = (a.ntiles - t0 + step - 1) / step;
+
+  auto seg_of = [&](int t) {
+    MfSeg sg = a.seg[0];
+#pragma unroll
+    for (int i = 1; i < MAX_SEGS; ++i)
+      if (i < a.nseg && t >= a.seg[i].tile_begin) sg = a.seg[i];
+    return sg;
+  };
+  auto next_of = [&](MfNext (&nx)[NR], int t) {
+    const MfSeg sg = seg_of(t);
+    int64_t n = int64_t(t - sg.tile_begin) * MF_ROWS + c;
+    n = (n < sg.N) ? n : sg.N - 1;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const PackedW& P = (r == 0) ? sg.w0 : sg.w1;
+      nx[r].rowp = P.payload + size_t(n) * P.row_bytes;
+      nx[r].srow = P.scales + size_t(n) * P.nb;
+      nx[r].nb = P.nb;
+    }
+  };
+  // ---- activation staging: A operands of this wave's BPW blocks ----
+  // The activation is loaded once into registers, the first tile's weight
+  // loads are issued right behind it, and the staging arithmetic runs while
+  // the weights are in flight.
+  MfW<NP, BPW> w[NR], w2[NR];
+  MfNext nx[NR];
+  f16x8 ah[BPW], al[BPW];
+  float unscale[4];  // 2^e of the activation rows this lane's outputs belong to
+  {
+    using L = MfLds<M, WAVES, BPW, XT, 1>;
+    uint8_t* hi_base = lds + size_t(wave) * L::WAVE_STAGE;
+    uint8_t* lo_base = hi_base + 8 * 4 * M * 16;
+    const int mr = (c < M) ? c : c % M;
+    f32x4 xv[M][BPW / 8];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int e = 0; e < BPW / 8; ++e)
+        xv[m][e] =
+            *reinterpret_cast<const f32x4*>(a.x + size_t(m) * size_t(a.K) + size_t(blk0) * 32 + 256 * e + 4 * lane);
+    __builtin_amdgcn_sched_barrier(0);
+    next_of(nx, t0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int q = 0; q < BPW / 4; ++q) mf_load_quad<NP, BPW>(w[r], q, nx[r].rowp, nx[r].nb, blk0, g);
+      mf_load_scales<NP, BPW>(w[r], nx[r].srow, blk0);
+    }
+    if constexpr (PD == 2) {
+      // second tile (the first again when there is none: unconditional
+      // loads keep the compiler's waits exact)
+      next_of(nx, nmine > 1 ? t0 + step : t0);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int q = 0; q < BPW / 4; ++q) mf_load_quad<NP, BPW>(w2[r], q, nx[r].rowp, nx[r].nb, blk0, g);
+        mf_load_scales<NP, BPW>(w2[r], nx[r].srow, blk0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // per activation row: the largest |x| in this wave's span of K
+    float sc[M], us[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < BPW / 8; ++e)
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][e].x), fabsf(xv[m][e].y)), fmaxf(fabsf(xv[m][e].z), fabsf(xv[m][e].w))));
+      mx = wave_max(mx);
+      // mx = f 2^e with f in [0.5, 1): |x| 2^(15-e) < 2^15; both factors stay
+      // normal floats
+      int se = 15 - __builtin_amdgcn_frexp_expf(mx);
+      se = se > 126 ? 126 : (se < -126 ? -126 : se);
+      sc[m] = __builtin_ldexpf(1.0f, se);
+      us[m] = __builtin_ldexpf(1.0f, -se);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m0 = i, m1 = 4 + i;
+      unscale[i] = (m0 < M) ? us[m0 < M ? m0 : 0] : 1.f;
+      if (m1 < M && g == 1) unscale[i] = us[m1 < M ? m1 : 0];
+    }
+    // Passes of 8 blocks through one wave-private area: a wave's LDS accesses
+    // complete in order, so its own writes are visible to its reads without
+    // a barrier, and a pass's reads finish before the next pass overwrites.
+#pragma unroll
+    for (int e = 0; e < BPW / 8; ++e) {
+      // element 256 e + 4 lane + i of the wave lies in block 8 e + bl,
+      // quarter gq, half h; slots 4h .. 4h+3 of A entry (bl, gq, m) hold
+      // elements 0, 2, 1, 3.
+      const int bl = lane >> 3, h = (lane >> 2) & 1, gq = lane & 3;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const f32x4 v = xv[m][e] * sc[m];
+        const f16x2 h02 = __builtin_convertvector((f32x2{v.x, v.z}), f16x2);
+        const f16x2 h13 = __builtin_convertvector((f32x2{v.y, v.w}), f16x2);
+        const size_t off = size_t(((bl * 4 + gq) * M + m) * 16 + 8 * h);
+        *reinterpret_cast<u32x2*>(hi_base + off) = u32x2{bits(h02), bits(h13)};
+        if constexpr (XT == 2) {
+          const f32x2 r02 = f32x2{v.x, v.z} - __builtin_convertvector(h02, f32x2);
+          const f32x2 r13 = f32x2{v.y, v.w} - __builtin_convertvector(h13, f32x2);
+          *reinterpret_cast<u32x2*>(lo_base + off) =
+              u32x2{bits(__builtin_convertvector(r02, f16x2)), bits(__builtin_convertvector(r13, f16x2))};
+        }
+      }
+#pragma unroll
+      for (int jl = 0; jl < 8; ++jl) {
+        const size_t off = size_t(((jl * 4 + g) * M + mr) * 16);
+        ah[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hi_base + off));
+        if constexpr (XT == 2)
+          al[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lo_base + off));
+        else
+          al[8 * e + jl] = ah[8 * e + jl];
+      }
+    }
+  }
+  __syncthreads();  // the staging area becomes the reduction buffers
+
+  float* red = reinterpret_cast<float*>(lds);
+  int parity = 0;
+
+  auto process = [&](MfW<NP, BPW>(&w)[NR], int t, auto reload, const MfNext (&nx)[NR]) {
+    constexpr bool RELOAD = decltype(reload)::value;
+    float acc[NR][4];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
+      mf_tile<NP, BPW, RR, XT, RELOAD>(w[r], ah, al, acc[r], mlo, mhi, magic, nx[r], blk0, g);
+    }
+    // partial sums: lane (g, c) holds rows m = 4g + i of output row c
+    float* rb = red + size_t(parity) * (WAVES * NR * MF_ROWS * M);
+    parity ^= 1;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < RR; ++i) {
+        const int m = 4 * g + i;
+        if (m < M) rb[((wave * NR + r) * MF_ROWS + c) * M + m] = acc[r][i] * unscale[i];
+      }
+    // One barrier per tile: the buffer written here is rewritten two tiles
+    // later, after the next tile's barrier, which its readers pass only once
+    // they are done.
+    __syncthreads();
+    // 16 M outputs; a launch may have a single wave (K = 32 BPW)
+    for (int o = int(threadIdx.x); o < MF_ROWS * M; o += int(blockDim.x)) {
+      const int cc = o / M, m = o % M;
+      float v[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float s = 0.f;
+        for (int ww = 0; ww < nw; ++ww) s += rb[((ww * NR + r) * MF_ROWS + cc) * M + m];
+        v[r] = s;
+      }
+      const MfSeg sg = seg_of(t);
+      const int64_t n = int64_t(t - sg.tile_begin) * MF_ROWS + cc;
+      float out = v[0];
+      if constexpr (NR == 2) out = silu_f32(v[0]) * v[1];
+      if (n < sg.N) sg.y[size_t(m) * size_t(sg.N) + size_t(n)] = out;
+    }
+  };
+
+  // Tiles blockIdx.x, + gridDim.x, ...: while a tile is decoded its
+  // registers are refilled with the tile PD steps ahead, so PD tiles of loads
+  // stay in flight.  Inside the loops every load is unconditional (the
+  // compiler's waits stay exact); the last PD tiles are peeled off.
+  if constexpr (PD == 1) {
+    int t = t0;
+    for (int i = 0; i + 1 < nmine; ++i, t += step) {
+      next_of(nx, t + step);
+      process(w, t, std::true_type{}, nx);
+    }
+    process(w, t, std::false_type{}, nx);
+  } else {
+    int i = 0;
+    for (; i + 3 < nmine; i += 2) {
+      next_of(nx, t0 + (i + 2) * step);
+      process(w, t0 + i * step, std::true_type{}, nx);
+      next_of(nx, t0 + (i + 3) * step);
+      process(w2, t0 + (i + 1) * step, std::true_type{}, nx);
+    }
+    const int left = nmine - i;
+    if (left == 3) {
+      next_of(nx, t0 + (i + 2) * step);
+      process(w, t0 + i * step, std::true_type{}, nx);
+      process(w2, t0 + (i + 1) * step, std::false_type{}, nx);
+      process(w, t0 + (i + 2) * step, std::false_type{}, nx);
+    } else if (left == 2) {
+      process(w, t0 + i * step, std::false_type{}, nx);
+      process(w2, t0 + (i + 1) * step, std::false_type{}, nx);
+    } else {
+      process(w, t0 + i * step, std::false_type{}, nx);
+    }
+  }
+}
+
+// Registry entry: ro = output rows per tile, j = fp16 activation terms,
+// x_lds = 2 (matrix cores), waves = most waves per workgroup, kw = blocks per
+// wave.  The prefetch depth is not part of the key (one depth per instance).
+template <int FMT, int M, int WAVES, int BPW, int XT, int EPI, int PD>
+inline GemvEntry gemv_mfma_entry() {
+  constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
+  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, M, WAVES, BPW, XT, EPI, PD>),
+              FMT, M, EPI, MF_ROWS, XT, 2, WAVES, BPW};
+  e.lds = MfLds<M, WAVES, BPW, XT, NR>::BYTES;
+  e.max_nb = WAVES * BPW;
+  return e;
+}
+
+}  // namespace skg

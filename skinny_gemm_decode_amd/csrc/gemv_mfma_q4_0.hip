@@ -1,0 +1,27 @@
+// q4_0 weights x fp32 activations on the matrix cores, M = 1..8.
+#include "gemv_instances.h"
+#include "gemv_mfma.h"
+
+// MF(M, fp16 activation terms, prefetch depth)
+#define SKG_MF(M, XT, PD) out.push_back(skg::gemv_mfma_entry<SKG_Q4_0_F32, M, 8, 16, XT, SKG_EPI_NONE, PD>());
+
+namespace skg {
+// Registered before the vector-ALU instances: the defaults for M = 2..8,
+// measured on MI355X under cold-cache rotation (K = 4096, N = 14336).
+void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
+  SKG_MF(2, 2, 1)
+  SKG_MF(3, 2, 1)
+  SKG_MF(4, 2, 1)
+  SKG_MF(5, 2, 1)
+  SKG_MF(6, 2, 1)
+  SKG_MF(7, 2, 1)
+  SKG_MF(8, 2, 1)
+}
+// Registered after them: measurement variants (at M = 1 the vector kernel
+// is faster).
+void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
+  SKG_MF(1, 2, 1)
+  SKG_MF(1, 1, 2)
+  SKG_MF(8, 1, 2)
+}
+}  // namespace skg

@@ -1,0 +1,28 @@
+// q8_0 weights x fp32 activations on the matrix cores, M = 1..8.
+#include "gemv_instances.h"
+#include "gemv_mfma.h"
+
+// MF(M, fp16 activation terms, prefetch depth)
+#define SKG_MF(M, XT, PD) out.push_back(skg::gemv_mfma_entry<SKG_Q8_0_F32, M, 8, 16, XT, SKG_EPI_NONE, PD>());
+
+namespace skg {
+// Registered before the vector-ALU instances: the defaults for M = 4..8,
+// measured on MI355X under cold-cache rotation (K = 4096, N = 14336).  With
+// two planes per block the two-term activation does not fit the register
+// file beyond M = 2, so these carry the activation as one fp16 term.
+void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
+  SKG_MF(4, 1, 1)
+  SKG_MF(5, 1, 1)
+  SKG_MF(6, 1, 1)
+  SKG_MF(7, 1, 1)
+  SKG_MF(8, 1, 1)
+}
+// Registered after them: measurement variants.
+void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
+  SKG_MF(1, 2, 1)
+  SKG_MF(2, 2, 1)
+  SKG_MF(3, 2, 1)
+  SKG_MF(4, 2, 1)
+  SKG_MF(8, 2, 1)
+}
+}  // namespace skg

@@ -6,6 +6,7 @@ void register_gemv_q8_0_f32(std::vector<GemvEntry>& out) {
   // The first instance of each (format, M, epilogue) is its default, chosen
   // by measurement on MI355X under cold-cache rotation.
   SKG_I(SKG_Q8_0_F32, 1, 4, 2, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q8_0_F32, 2, 4, 1, true, 4, SKG_EPI_NONE)
   SKG_M12(SKG_Q8_0_F32, 4, 2, 4, 1, 2, 2)
   SKG_IK(SKG_Q8_0_F32, 1, 4, 1, 4, SKG_EPI_NONE, 2)
   SKG_IK(SKG_Q8_0_F32, 1, 8, 1, 4, SKG_EPI_NONE, 2)
@@ -15,6 +16,5 @@ void register_gemv_q8_0_f32(std::vector<GemvEntry>& out) {
   SKG_I(SKG_Q8_0_F32, 1, 4, 1, false, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q8_0_F32, 1, 8, 1, false, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q8_0_F32, 1, 8, 2, true, 4, SKG_EPI_NONE)
-  SKG_I(SKG_Q8_0_F32, 2, 4, 1, true, 4, SKG_EPI_NONE)
 }
 }  // namespace skg

@@ -153,3 +153,11 @@ def test_valid_call_without_gpu_reports_device_error(skg):
     # Arguments are valid, so only the device check can reject the call.
     assert skg.lib.skg_gemv(2, 1, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_DEVICE
     assert "device" in skg.last_error().lower()
+
+
+def test_single_hip_runtime(skg):
+    """The library shares PyTorch's HIP runtime: exactly one libamdhip64 is
+    mapped into the process after import."""
+    with open("/proc/self/maps") as f:
+        libs = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(libs) == 1, libs

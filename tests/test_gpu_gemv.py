@@ -100,8 +100,9 @@ def test_every_compiled_variant(skg):
         for v in variants:
             fmt, M, epi = v["fmt"], v["M"], v["epi"]
             N = 300
-            K = 4104 if fmt == skg.BF16_BF16 else 4128
-            key = (fmt, M, epi)
+            # the matrix-core variants (x_lds == 2) take K % 256 == 0, K <= 4096
+            K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] == 2 else 4128)
+            key = (fmt, M, epi, K)
             if key not in cache:
                 W0, x = make_inputs(skg, fmt, M, N, K, seed=5000 + 10 * fmt + M)
                 W1, _ = make_inputs(skg, fmt, 1, N, K, seed=6000 + 10 * fmt + M)
@@ -229,3 +230,83 @@ def test_bf16_scale_boundaries(skg):
     y, _ = run_gemv(skg, skg.BF16_BF16, 1, N, K, W, x)
     y_ref, bound = oracle.gemv_ref_fmt("bf16", W, x, x_kind="bf16")
     assert_close(y, y_ref, bound, "bf16 boundaries")
+
+
+# Shapes the matrix-core kernel takes (K % 512 == 0, K <= 4096): one wave
+# (K = 512), a partial workgroup (K = 1536: 3 waves), ragged row tiles, and
+# N large enough that workgroups walk 2, 3 and 5+ tiles.  The default-path
+# part also runs K = 1280, which the matrix-core kernel does not take.
+MFMA_SHAPES = [(1, 512), (19, 512), (300, 4096), (1000, 1536), (37, 1280), (9000, 4096), (20000, 4096)]
+
+
+def mfma_variants(skg, fmt, M):
+    return [v for v in skg.gemv_variants()
+            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] == 2]
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_gemv_mfma_shapes(skg, fmt, M):
+    """Default path at the shapes the matrix-core kernel takes, then every
+    matrix-core variant against its own precision: with two fp16 activation
+    terms (~22 bits) the error stays under 2e-5 of sum|w x|, which fails if the
+    low term were lost; with one term it stays under 2^-11 (its rounding) plus
+    fp32 accumulation, 8e-4 of sum|w x|."""
+    cases = []
+    for i, (N, K) in enumerate(MFMA_SHAPES):
+        if N * K * M > 20000 * 4096 * 2:
+            continue
+        W, x = make_inputs(skg, fmt, M, N, K, seed=8000 + 100 * fmt + 10 * M + i)
+        y_ref, bound = reference(skg, fmt, W, x, None)
+        cases.append((N, K, W, x, y_ref, bound))
+        y, _ = run_gemv(skg, fmt, M, N, K, W, x)
+        assert_close(y, y_ref, bound, f"default fmt={fmt} M={M} N={N} K={K}")
+    try:
+        for v in mfma_variants(skg, fmt, M):
+            skg.gemv_set_variant(fmt, M, 0, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+            rel = 2e-5 if v["j"] == 2 else 8e-4
+            for N, K, W, x, y_ref, bound in cases:
+                nb = K // 32
+                if nb % v["kw"] or nb > v["waves"] * v["kw"]:
+                    continue
+                note(f"variant {v} N={N} K={K}")
+                y, _ = run_gemv(skg, fmt, M, N, K, W, x)
+                assert_close(y, y_ref, bound, f"variant {v} N={N} K={K}", rel=rel)
+    finally:
+        skg.gemv_set_variant(fmt, M, 0, 0)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_gemv_mfma_activation_range(skg, fmt):
+    """Activations far outside fp16 range, far below it, an all-zero row and
+    a single huge outlier: the per-wave power-of-two scaling keeps the two
+    fp16 terms exact enough everywhere."""
+    M, N, K = 5, 300, 4096
+    rng = si.rng_for(0, 99, 8900 + fmt)
+    W = si.weights(wkind(skg, fmt), rng, N, K)
+    x = si.activations_f32(rng, M, K)
+    x[0] *= np.float32(1e6)          # |x| up to ~5e6 (fp16 max is 65504)
+    x[1] = 0.0
+    x[2] *= np.float32(1e-30)        # far below fp16's smallest subnormal
+    x[3, 1234] = np.float32(3e9)     # one outlier dominating its wave's range
+    x[4, : K // 2] *= np.float32(1e20)
+    y, _ = run_gemv(skg, fmt, M, N, K, W, x)
+    y_ref, bound = reference(skg, fmt, W, x, None)
+    assert_close(y, y_ref, bound, f"fmt={fmt} range")
+    assert np.all(y[1] == 0.0), "all-zero activation row must give exact zeros"
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_gemv_multi_mfma(skg, fmt):
+    """Several matrices in one matrix-core launch (fused QKV shape)."""
+    K, M = 4096, 3
+    Ns = [96, 33, 130]
+    Ws = [make_inputs(skg, fmt, 1, n, K, seed=8800 + 10 * fmt + i)[0] for i, n in enumerate(Ns)]
+    _, x = make_inputs(skg, fmt, M, 1, K, seed=8850 + fmt)
+    note(f"gemv_multi mfma fmt={fmt}")
+    Wp = skg.pack_weights_multi(fmt, Ns, K, [dev(w) for w in Ws])
+    ys = [poisoned((M, n)) for n in Ns]
+    skg.gemv_multi(fmt, M, K, Ns, Wp, dev(x), ys)
+    for W, y in zip(Ws, ys):
+        y_ref, bound = reference(skg, fmt, W, x, None)
+        assert_close(host(y), y_ref, bound, f"multi mfma fmt={fmt}")
