@@ -228,6 +228,11 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
  *   fp16, relative error 2^-11), waves = most waves per workgroup, kw =
  *   quantisation blocks per wave; it takes K with (K / 32) % kw == 0 and
  *   K / 32 <= waves * kw.
+ *   x_lds = 3 names the same matrix-core computation with the weight tiles
+ *   copied by direct global-to-LDS transfers into a ring of two or three
+ *   16-row slots (the activation as for x_lds = 2); compiled for K = 4096 only
+ *   (waves * kw = 128 blocks), so a call with any other K returns
+ *   SKG_E_UNSUPPORTED while it is selected.
  * skg_gemv_variants: writes up to max_entries records of 8 ints
  *   {fmt, M, epi, ro, j, x_lds, waves, kw} to out (host) and returns the
  *   number of compiled variants.  For each (fmt, M, epi) and K the default is

@@ -110,10 +110,12 @@ void init_registry() {
   });
 }
 
-// The matrix-core kernel runs nb / kw waves of kw blocks each.
+// The matrix-core kernels run nb / kw waves of kw blocks each; the LDS-ring
+// variant (x_lds = 3) is compiled for one K.
 bool variant_supports(const GemvEntry& e, int64_t K) {
-  if (e.xlds != 2) return true;
   const int64_t nb = K / 32;
+  if (e.xlds == 3) return nb == e.max_nb;
+  if (e.xlds != 2) return true;
   return nb % e.kw == 0 && nb >= e.kw && nb <= e.max_nb;
 }
 
@@ -185,13 +187,18 @@ skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64
   skg_status st = check_device(&cus);
   if (st != SKG_OK) return st;
   const int threads = int(a.nb / uint32_t(v.kw)) * 64;
-  const size_t lds = size_t(v.lds);
+  const size_t lds = size_t(v.lds);  // dynamic LDS (the LDS-ring variant's is static)
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   }
   const int64_t resident = int64_t(cus) * blocks_per_cu(v.fn, threads, lds);
-  const int grid = int(tiles < resident ? tiles : resident);
+  int64_t grid = tiles < resident ? tiles : resident;
+  if (v.xlds == 3) {
+    // the LDS-ring kernel processes at most MF_DMA_TILES tiles per workgroup
+    const int64_t need = (tiles + MF_DMA_TILES - 1) / MF_DMA_TILES;
+    if (grid < need) grid = need;
+  }
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(v.fn, dim3(unsigned(grid)), dim3(unsigned(threads)), args, lds, stream);
   if (e != hipSuccess) return fail(SKG_E_HIP, "gemv launch: %s", hipGetErrorString(e));
@@ -210,7 +217,7 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
   if (!v)
     return fail(SKG_E_UNSUPPORTED, "no compiled kernel (or the selected variant does not take K=%lld) for fmt=%d "
                 "M=%lld epi=%d", (long long)K, fmt, (long long)M, epi);
-  if (v->xlds == 2) return launch_gemv_mfma(*v, K, nseg, Ns, W, x, ys, epi, stream);
+  if (v->xlds == 2 || v->xlds == 3) return launch_gemv_mfma(*v, K, nseg, Ns, W, x, ys, epi, stream);
   const int wk = wkind_of(fmt);
   GemvArgs a;
   std::memset(&a, 0, sizeof a);
@@ -218,6 +225,7 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
   a.nu = uint32_t(wk == WK_BF16 ? K / 8 : K / 32);
   a.x = static_cast<const uint8_t*>(x);
   const int rows_per_block = (v->waves / v->kw) * v->ro;
+  if (rows_per_block <= 0) return fail(SKG_E_UNSUPPORTED, "variant with x_lds=%d has no VALU row layout", v->xlds);
   int64_t blocks = 0;
   const uint8_t* base = static_cast<const uint8_t*>(W);
   if (epi == SKG_EPI_SWIGLU) {

@@ -227,6 +227,88 @@ struct MfLds {
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
 };
 
+// Activation staging of one wave: loads the wave's span of K of every
+// activation row once, calls between() (which may issue weight loads into
+// registers, so they are in flight during the arithmetic), picks a
+// power-of-two scale per row, calls after_x() once the activation registers
+// have been consumed (weight transfers straight into LDS go there: the
+// compiler drains those before any later use of a register load), and leaves
+// the fp16 A operands of the wave's BPW blocks in ah / al.  Passes of 8
+// blocks go through the wave-private LDS area `area`.
+template <int M, int BPW, int XT, class Between, class AfterX>
+__device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ah)[BPW],
+                                f16x8 (&al)[BPW], float (&unscale)[4], Between between, AfterX after_x) {
+  const int g = lane >> 4, c = lane & 15;
+  uint8_t* hi_base = area;
+  uint8_t* lo_base = hi_base + 8 * 4 * M * 16;
+  const int mr = (c < M) ? c : c % M;
+  f32x4 xv[M][BPW / 8];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int e = 0; e < BPW / 8; ++e)
+      xv[m][e] = *reinterpret_cast<const f32x4*>(a.x + size_t(m) * size_t(a.K) + size_t(blk0) * 32 + 256 * e + 4 * lane);
+  __builtin_amdgcn_sched_barrier(0);
+  between();
+  __builtin_amdgcn_sched_barrier(0);
+  // per activation row: the largest |x| in this wave's span of K
+  float sc[M], us[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < BPW / 8; ++e)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][e].x), fabsf(xv[m][e].y)), fmaxf(fabsf(xv[m][e].z), fabsf(xv[m][e].w))));
+    mx = wave_max(mx);
+    // mx = f 2^e with f in [0.5, 1): |x| 2^(15-e) < 2^15; both factors stay
+    // normal floats
+    int se = 15 - __builtin_amdgcn_frexp_expf(mx);
+    se = se > 126 ? 126 : (se < -126 ? -126 : se);
+    sc[m] = __builtin_ldexpf(1.0f, se);
+    us[m] = __builtin_ldexpf(1.0f, -se);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m0 = i, m1 = 4 + i;
+    unscale[i] = (m0 < M) ? us[m0 < M ? m0 : 0] : 1.f;
+    if (m1 < M && g == 1) unscale[i] = us[m1 < M ? m1 : 0];
+  }
+  after_x();
+  // A wave's LDS accesses complete in order, so its own writes are visible
+  // to its reads without a barrier, and a pass's reads finish before the
+  // next pass overwrites.
+#pragma unroll
+  for (int e = 0; e < BPW / 8; ++e) {
+    // element 256 e + 4 lane + i of the wave lies in block 8 e + bl, quarter
+    // gq, half h; slots 4h .. 4h+3 of A entry (bl, gq, m) hold elements
+    // 0, 2, 1, 3.
+    const int bl = lane >> 3, h = (lane >> 2) & 1, gq = lane & 3;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const f32x4 v = xv[m][e] * sc[m];
+      const f16x2 h02 = __builtin_convertvector((f32x2{v.x, v.z}), f16x2);
+      const f16x2 h13 = __builtin_convertvector((f32x2{v.y, v.w}), f16x2);
+      const size_t off = size_t(((bl * 4 + gq) * M + m) * 16 + 8 * h);
+      *reinterpret_cast<u32x2*>(hi_base + off) = u32x2{bits(h02), bits(h13)};
+      if constexpr (XT == 2) {
+        const f32x2 r02 = f32x2{v.x, v.z} - __builtin_convertvector(h02, f32x2);
+        const f32x2 r13 = f32x2{v.y, v.w} - __builtin_convertvector(h13, f32x2);
+        *reinterpret_cast<u32x2*>(lo_base + off) =
+            u32x2{bits(__builtin_convertvector(r02, f16x2)), bits(__builtin_convertvector(r13, f16x2))};
+      }
+    }
+#pragma unroll
+    for (int jl = 0; jl < 8; ++jl) {
+      const size_t off = size_t(((jl * 4 + g) * M + mr) * 16);
+      ah[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hi_base + off));
+      if constexpr (XT == 2)
+        al[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lo_base + off));
+      else
+        al[8 * e + jl] = ah[8 * e + jl];
+    }
+  }
+}
+
 // Launched with nb / BPW waves (at most WAVES), so every wave owns BPW
 // blocks; requires nb % BPW == 0.
 template <int FMT, int M, int WAVES, int BPW, int XT, int EPI, int PD>
@@ -278,102 +360,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
       nx[r].nb = P.nb;
     }
   };
-  // ---- activation staging: A operands of this wave's BPW blocks ----
-  // The activation is loaded once into registers, the first tile's weight
-  // loads are issued right behind it, and the staging arithmetic runs while
-  // the weights are in flight.
+  // ---- activation staging: A operands of this wave's BPW blocks, with the
+  // first tiles' weight loads issued between the activation loads and the
+  // staging arithmetic ----
   MfW<NP, BPW> w[NR], w2[NR];
   MfNext nx[NR];
   f16x8 ah[BPW], al[BPW];
   float unscale[4];  // 2^e of the activation rows this lane's outputs belong to
-  {
-    using L = MfLds<M, WAVES, BPW, XT, 1>;
-    uint8_t* hi_base = lds + size_t(wave) * L::WAVE_STAGE;
-    uint8_t* lo_base = hi_base + 8 * 4 * M * 16;
-    const int mr = (c < M) ? c : c % M;
-    f32x4 xv[M][BPW / 8];
+  mf_stage<M, BPW, XT>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al, unscale,
+                       [&] {
+                         next_of(nx, t0);
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+                         for (int r = 0; r < NR; ++r) {
 #pragma unroll
-      for (int e = 0; e < BPW / 8; ++e)
-        xv[m][e] =
-            *reinterpret_cast<const f32x4*>(a.x + size_t(m) * size_t(a.K) + size_t(blk0) * 32 + 256 * e + 4 * lane);
-    __builtin_amdgcn_sched_barrier(0);
-    next_of(nx, t0);
+                           for (int q = 0; q < BPW / 4; ++q)
+                             mf_load_quad<NP, BPW>(w[r], q, nx[r].rowp, nx[r].nb, blk0, g);
+                           mf_load_scales<NP, BPW>(w[r], nx[r].srow, blk0);
+                         }
+                         if constexpr (PD == 2) {
+                           // second tile (the first again when there is none:
+                           // unconditional loads keep the compiler's waits exact)
+                           next_of(nx, nmine > 1 ? t0 + step : t0);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
+                           for (int r = 0; r < NR; ++r) {
 #pragma unroll
-      for (int q = 0; q < BPW / 4; ++q) mf_load_quad<NP, BPW>(w[r], q, nx[r].rowp, nx[r].nb, blk0, g);
-      mf_load_scales<NP, BPW>(w[r], nx[r].srow, blk0);
-    }
-    if constexpr (PD == 2) {
-      // second tile (the first again when there is none: unconditional
-      // loads keep the compiler's waits exact)
-      next_of(nx, nmine > 1 ? t0 + step : t0);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-#pragma unroll
-        for (int q = 0; q < BPW / 4; ++q) mf_load_quad<NP, BPW>(w2[r], q, nx[r].rowp, nx[r].nb, blk0, g);
-        mf_load_scales<NP, BPW>(w2[r], nx[r].srow, blk0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // per activation row: the largest |x| in this wave's span of K
-    float sc[M], us[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < BPW / 8; ++e)
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][e].x), fabsf(xv[m][e].y)), fmaxf(fabsf(xv[m][e].z), fabsf(xv[m][e].w))));
-      mx = wave_max(mx);
-      // mx = f 2^e with f in [0.5, 1): |x| 2^(15-e) < 2^15; both factors stay
-      // normal floats
-      int se = 15 - __builtin_amdgcn_frexp_expf(mx);
-      se = se > 126 ? 126 : (se < -126 ? -126 : se);
-      sc[m] = __builtin_ldexpf(1.0f, se);
-      us[m] = __builtin_ldexpf(1.0f, -se);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m0 = i, m1 = 4 + i;
-      unscale[i] = (m0 < M) ? us[m0 < M ? m0 : 0] : 1.f;
-      if (m1 < M && g == 1) unscale[i] = us[m1 < M ? m1 : 0];
-    }
-    // Passes of 8 blocks through one wave-private area: a wave's LDS accesses
-    // complete in order, so its own writes are visible to its reads without
-    // a barrier, and a pass's reads finish before the next pass overwrites.
-#pragma unroll
-    for (int e = 0; e < BPW / 8; ++e) {
-      // element 256 e + 4 lane + i of the wave lies in block 8 e + bl,
-      // quarter gq, half h; slots 4h .. 4h+3 of A entry (bl, gq, m) hold
-      // elements 0, 2, 1, 3.
-      const int bl = lane >> 3, h = (lane >> 2) & 1, gq = lane & 3;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const f32x4 v = xv[m][e] * sc[m];
-        const f16x2 h02 = __builtin_convertvector((f32x2{v.x, v.z}), f16x2);
-        const f16x2 h13 = __builtin_convertvector((f32x2{v.y, v.w}), f16x2);
-        const size_t off = size_t(((bl * 4 + gq) * M + m) * 16 + 8 * h);
-        *reinterpret_cast<u32x2*>(hi_base + off) = u32x2{bits(h02), bits(h13)};
-        if constexpr (XT == 2) {
-          const f32x2 r02 = f32x2{v.x, v.z} - __builtin_convertvector(h02, f32x2);
-          const f32x2 r13 = f32x2{v.y, v.w} - __builtin_convertvector(h13, f32x2);
-          *reinterpret_cast<u32x2*>(lo_base + off) =
-              u32x2{bits(__builtin_convertvector(r02, f16x2)), bits(__builtin_convertvector(r13, f16x2))};
-        }
-      }
-#pragma unroll
-      for (int jl = 0; jl < 8; ++jl) {
-        const size_t off = size_t(((jl * 4 + g) * M + mr) * 16);
-        ah[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hi_base + off));
-        if constexpr (XT == 2)
-          al[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lo_base + off));
-        else
-          al[8 * e + jl] = ah[8 * e + jl];
-      }
-    }
-  }
+                             for (int q = 0; q < BPW / 4; ++q)
+                               mf_load_quad<NP, BPW>(w2[r], q, nx[r].rowp, nx[r].nb, blk0, g);
+                             mf_load_scales<NP, BPW>(w2[r], nx[r].srow, blk0);
+                           }
+                         }
+                       },
+                       [] {});
   __syncthreads();  // the staging area becomes the reduction buffers
 
   float* red = reinterpret_cast<float*>(lds);
@@ -452,6 +469,231 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
       process(w, t0 + i * step, std::false_type{}, nx);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// K = 4096 variant with the weights streamed into LDS.  The loads of the
+// register-fed kernel above touch 16 rows x 64 bytes per wave instruction;
+// here each wave instruction moves 1 KB of one row straight from HBM into LDS
+// (global_load_lds_dwordx4), so every request is whole cache lines and no
+// weight registers are held.  Rows sit 16 bytes apart from a multiple of the
+// LDS bank period, so the B operand reads (16 rows per 16-lane group) are
+// conflict-free.  A ring of R tile slots (16 rows x all of K, plus scales)
+// keeps R - 1 tiles in flight while one is decoded; one barrier per tile.
+
+constexpr int MF_DMA_TILES = 4;  // most tiles one workgroup processes
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((const lds_u8*)p));
+}
+
+// Lane i copies 16 bytes from src (its own address) to LDS byte address
+// dst + 16 i (dst uniform across the wave).  Written as asm on purpose: the
+// compiler tracks these transfers only coarsely and would drain every
+// transfer in flight at each LDS read behind a branch, so the kernel keeps
+// the vmcnt bookkeeping itself (wait_vmcnt before each barrier) and issues
+// no register loads while transfers are in flight.  The asm writes no VGPR.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
+__device__ inline void dma16(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) (N <= 63), other counters untouched.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int FMT>
+struct MfDmaGeom {
+  static constexpr int NP = (FMT == SKG_Q8_0_F32) ? 2 : 1;
+  static constexpr int NB = 128;                     // blocks per row (K = 4096)
+  static constexpr int RB = NB * 16 * NP;            // payload bytes per row
+  static constexpr int PRS = RB + 16;                // padded LDS row stride
+  static constexpr int SRS = NB * 2;                 // LDS scale-row stride (4 rows per transfer)
+  static constexpr int SLOT = 16 * PRS + 16 * SRS;   // one tile
+  static constexpr int CH = RB / 1024;               // 1 KB transfers per row
+  static constexpr int P = 2 * CH + 1;               // transfers per wave per tile (2 rows + 4 scale rows)
+};
+
+// R: ring slots; ALIAS: the activation staging area shares the last slot
+// (its first load is issued after staging).
+template <int FMT, int M, int XT, int R, bool ALIAS>
+__global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32, "fp32-activation quantised formats only");
+  static_assert(R == 2 || R == 3, "ring slots");
+  using G = MfDmaGeom<FMT>;
+  constexpr int NP = G::NP, BPW = 16, WAVES = 8, P = G::P;
+  constexpr int RR = M < 4 ? M : 4;
+  constexpr int WAVE_STAGE = MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE;
+  static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
+  __shared__ __attribute__((aligned(16))) uint8_t slot0[G::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t slot1[G::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t slot2[R == 3 ? G::SLOT : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_own[ALIAS ? 16 : WAVES * WAVE_STAGE];
+  __shared__ __attribute__((aligned(16))) float red[2 * WAVES * MF_ROWS * M];
+
+  uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+  asm volatile("" : "+s"(mlo));
+  asm volatile("" : "+s"(mhi));
+  asm volatile("" : "+v"(magic));
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const uint32_t blk0 = uint32_t(wave) * BPW;
+  const int t0 = blockIdx.x;
+  const int step = int(gridDim.x);
+  if (t0 >= a.ntiles) return;  // uniform per workgroup
+  const int nmine = (a.ntiles - t0 + step - 1) / step;
+
+  auto seg_of = [&](int t) {
+    MfSeg sg = a.seg[0];
+#pragma unroll
+    for (int i = 1; i < MAX_SEGS; ++i)
+      if (i < a.nseg && t >= a.seg[i].tile_begin) sg = a.seg[i];
+    return sg;
+  };
+  // This wave's share of tile i: rows 2 wave and 2 wave + 1, payload and scales.
+  auto dma_tile = [&](uint8_t* slot, int i) {
+    const int t = t0 + i * step;
+    const MfSeg sg = seg_of(t);
+    const int64_t rbase = int64_t(t - sg.tile_begin) * MF_ROWS;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 2 * wave + k;
+      const int64_t n = (rbase + r < sg.N) ? rbase + r : sg.N - 1;
+      const uint8_t* rowp = sg.w0.payload + size_t(n) * sg.w0.row_bytes;
+#pragma unroll
+      for (int ch = 0; ch < G::CH; ++ch)
+        dma16(rowp + ch * 1024 + lane * 16, lds_addr(slot) + uint32_t(r * G::PRS + ch * 1024));
+    }
+    // Scales of rows 4 (wave % 4) .. +3, all 64 lanes (waves 4..7 repeat the
+    // identical copies of waves 0..3, so every wave issues the same number of
+    // transfers per tile).
+    {
+      const int r = 4 * (wave & 3) + (lane >> 4);
+      const int64_t n = (rbase + r < sg.N) ? rbase + r : sg.N - 1;
+      const uint16_t* srow = sg.w0.scales + size_t(n) * sg.w0.nb;
+      dma16(srow + (lane & 15) * 8, lds_addr(slot) + uint32_t(16 * G::PRS + 4 * (wave & 3) * G::SRS));
+    }
+  };
+
+  uint8_t* stage_area = ALIAS ? (R == 3 ? slot2 : slot1) : stage_own;
+  f16x8 ah[BPW], al[BPW];
+  float unscale[4];
+  // The first R tiles' transfers are unconditional (a workgroup with fewer
+  // tiles copies its last one again): conditional transfers here would make
+  // the compiler drain them all before the staging arithmetic.
+  auto clamp = [&](int i) { return i < nmine ? i : nmine - 1; };
+  mf_stage<M, BPW, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {}, [&] {
+    dma_tile(slot0, 0);
+    if constexpr (!(R == 2 && ALIAS)) dma_tile(slot1, clamp(1));
+    if constexpr (R == 3 && !ALIAS) dma_tile(slot2, clamp(2));
+  });
+  if constexpr (ALIAS) {
+    // every wave has read its staged operands before the shared slot refills
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (R == 2) dma_tile(slot1, clamp(1));
+    if constexpr (R == 3) dma_tile(slot2, clamp(2));
+  }
+
+  // Waits until this wave's transfers of tile i have landed: tiles
+  // i+1 .. min(issued, nmine) - 1 may stay in flight.
+  // `issued`: tiles 0 .. issued - 1 have been requested (the first R always).
+  auto wait_tile = [&](int i, int issued) {
+    const int last = (issued > R ? (issued < nmine ? issued : nmine) : R) - 1;
+    const int after = last - i;
+    if (after >= 2)
+      wait_vmcnt<2 * P>();
+    else if (after == 1)
+      wait_vmcnt<P>();
+    else
+      wait_vmcnt<0>();
+  };
+  auto sync = [] {
+    asm volatile("" ::: "memory");       // no LDS access moves past the barrier
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  wait_tile(0, R);
+  sync();
+
+  int parity = 0;
+  auto run = [&](uint8_t* slot, int i) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+      MfW<NP, BPW> w;
+#pragma unroll
+      for (int q = 0; q < BPW / 4; ++q)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          w.u[q][p] =
+              *reinterpret_cast<const u32x4*>(slot + c * G::PRS + (p * G::NB + int(blk0) + 4 * q + g) * 16);
+#pragma unroll
+      for (int k = 0; k < BPW / 8; ++k)
+        w.sc[k] = *reinterpret_cast<const u32x4*>(slot + 16 * G::PRS + c * G::SRS + int(blk0) * 2 + k * 16);
+      const MfNext none{};
+      mf_tile<NP, BPW, RR, XT, false>(w, ah, al, acc, mlo, mhi, magic, none, blk0, g);
+    }
+    float* rb = red + parity * (WAVES * MF_ROWS * M);
+    parity ^= 1;
+#pragma unroll
+    for (int k = 0; k < RR; ++k) {
+      const int m = 4 * g + k;
+      if (m < M) rb[(wave * MF_ROWS + c) * M + m] = acc[k] * unscale[k];
+    }
+    // next tile's transfers landed (this wave's), partial sums written;
+    // after the barrier every wave is past this slot and the next is full
+    if (i + 1 < nmine) wait_tile(i + 1, i + R);
+    sync();
+    if (i + R < nmine) dma_tile(slot, i + R);
+    const int t = t0 + i * step;
+    for (int o = int(threadIdx.x); o < MF_ROWS * M; o += 512) {
+      const int cc = o / M, m = o % M;
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WAVES; ++ww) v += rb[(ww * MF_ROWS + cc) * M + m];
+      const MfSeg sg = seg_of(t);
+      const int64_t n = int64_t(t - sg.tile_begin) * MF_ROWS + cc;
+      if (n < sg.N) sg.y[size_t(m) * size_t(sg.N) + size_t(n)] = v;
+    }
+  };
+  // Straight-line over at most MF_DMA_TILES tiles (the launch sizes the grid
+  // so no workgroup gets more): inside a loop the compiler could not tell
+  // which slot's transfers had landed and would drain them all per tile.
+  static_assert(MF_DMA_TILES == 4, "unrolled for four tiles");
+  run(slot0, 0);
+  if (1 < nmine) run(slot1, 1);
+  if constexpr (R == 3) {
+    if (2 < nmine) run(slot2, 2);
+    if (3 < nmine) run(slot0, 3);
+  } else {
+    if (2 < nmine) run(slot0, 2);
+    if (3 < nmine) run(slot1, 3);
+  }
+  // a workgroup with fewer tiles than slots still has its repeated first
+  // transfers in flight: none may outlive the workgroup's LDS
+  wait_vmcnt<0>();
+}
+
+template <int FMT, int M, int XT, int R, bool ALIAS>
+inline GemvEntry gemv_mfma_dma_entry() {
+  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<FMT, M, XT, R, ALIAS>),
+              FMT, M, SKG_EPI_NONE, MF_ROWS, XT, 3, 8, 16};
+  e.lds = 0;
+  e.max_nb = MfDmaGeom<FMT>::NB;
+  return e;
 }
 
 // Registry entry: ro = output rows per tile, j = fp16 activation terms,

@@ -11,14 +11,20 @@ namespace skg {
 // two planes per block the two-term activation does not fit the register
 // file beyond M = 2, so these carry the activation as one fp16 term.
 void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
+  // M = 4: the LDS-ring kernel (weights copied straight into LDS, two-term
+  // activation) edges out the register-fed one
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 4, 2, 2, true>());
   SKG_MF(4, 1, 1)
   SKG_MF(5, 1, 1)
   SKG_MF(6, 1, 1)
   SKG_MF(7, 1, 1)
   SKG_MF(8, 1, 1)
 }
-// Registered after them: measurement variants.
+// Registered after the vector-ALU instances: measurement variants.
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 1, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 2, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 8, 2, 2, true>());
   SKG_MF(1, 2, 1)
   SKG_MF(2, 2, 1)
   SKG_MF(3, 2, 1)

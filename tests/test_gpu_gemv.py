@@ -101,7 +101,7 @@ def test_every_compiled_variant(skg):
             fmt, M, epi = v["fmt"], v["M"], v["epi"]
             N = 300
             # the matrix-core variants (x_lds == 2) take K % 256 == 0, K <= 4096
-            K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] == 2 else 4128)
+            K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] in (2, 3) else 4128)
             key = (fmt, M, epi, K)
             if key not in cache:
                 W0, x = make_inputs(skg, fmt, M, N, K, seed=5000 + 10 * fmt + M)
@@ -241,7 +241,7 @@ MFMA_SHAPES = [(1, 512), (19, 512), (300, 4096), (1000, 1536), (37, 1280), (9000
 
 def mfma_variants(skg, fmt, M):
     return [v for v in skg.gemv_variants()
-            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] == 2]
+            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3)]
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
@@ -269,6 +269,8 @@ def test_gemv_mfma_shapes(skg, fmt, M):
                 nb = K // 32
                 if nb % v["kw"] or nb > v["waves"] * v["kw"]:
                     continue
+                if v["x_lds"] == 3 and nb != v["waves"] * v["kw"]:
+                    continue  # the LDS-ring variant is compiled for K = 4096 only
                 note(f"variant {v} N={N} K={K}")
                 y, _ = run_gemv(skg, fmt, M, N, K, W, x)
                 assert_close(y, y_ref, bound, f"variant {v} N={N} K={K}", rel=rel)
