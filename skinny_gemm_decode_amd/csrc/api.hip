@@ -11,7 +11,7 @@
 #include <tuple>
 #include <vector>
 
-#include "gemv_instances.h"
+#include "gemv_registry.h"
 #include "gemv_mfma.h"
 #include "kernels.h"
 

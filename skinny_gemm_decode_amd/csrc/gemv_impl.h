@@ -41,7 +41,7 @@ struct Fmt<SKG_Q8_0_F32> {
 template <>
 struct Fmt<SKG_Q4_0_F32> {
   static constexpr int E = 32, WV = 4, XB = 128, XF = 32;
-  static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q4_0_Q8_1> {
@@ -112,6 +112,9 @@ __device__ inline void load_w(WUnit<FMT>& u, const uint8_t* rowp, const uint16_t
   }
 }
 
+typedef _Float16 q4h __attribute__((ext_vector_type(2)));
+__device__ inline q4h q4h_of(uint32_t v) { return __builtin_bit_cast(q4h, v); }
+
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ inline float ubyte(uint32_t w, int i) { return float((w >> (8 * i)) & 0xFFu); }
@@ -153,18 +156,10 @@ __device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
       x.v[4 * p + 3] = __uint_as_float(v.w);
     }
     // The block sum is accumulated in the same element order as the code x
-    // activation chain of unit_acc, so that a block whose codes are all equal
-    // (all 8 for q4_0, all 0 for q8_0) cancels to exactly zero: scaling every
-    // term by a power of two commutes with each rounding.
-    if constexpr (FMT == SKG_Q4_0_F32) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += x.v[4 * k + i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += x.v[16 + 4 * k + i];
-      }
-    } else {
+    // activation chain of unit_acc, so that a block whose codes are all 0
+    // (q8_0) cancels to exactly zero: scaling every term by a power of two
+    // commutes with each rounding.
+    if constexpr (Fmt<FMT>::XSUM) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) s += x.v[i];
     }
@@ -246,9 +241,23 @@ __device__ inline int unit_idot(const WUnit<FMT>& w, const XUnit<FMT, true>& x) 
   return si;
 }
 
+// Decode constants of the q4_0 fp16 path, made opaque once per kernel
+// (SGPR masks, fp16 1024.0 pair in a VGPR) so each code pair decodes in one
+// v_and_or_b32: an instruction of that encoding takes at most one literal.
+struct DecodeK {
+  uint32_t mlo, mhi, magic;
+};
+__device__ inline DecodeK decode_consts() {
+  DecodeK k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  asm volatile("" : "+s"(k.mlo));
+  asm volatile("" : "+s"(k.mhi));
+  asm volatile("" : "+v"(k.magic));
+  return k;
+}
+
 // acc + (contribution of one weight unit against one activation unit).
 template <int FMT>
-__device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float acc) {
+__device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float acc, const DecodeK& dk) {
   if constexpr (FMT == SKG_BF16_BF16) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -257,18 +266,37 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
     }
     return acc;
   } else if constexpr (FMT == SKG_Q4_0_F32) {
-    // sum_i (c_i - 8) x_i = sum_i c_i x_i - 8 sum_i x_i
-    float s = 0.f;
+    // Codes decode exactly to fp16 pairs c - 8 (two per v_and_or_b32 and one
+    // packed add or fma), and each product takes the fp16 weight and the fp32
+    // activation in one mixed-precision fma: exact products, one rounding per
+    // element, and a code of 8 contributes exactly zero.
+    // two chains (low and high nibbles) halve the dependent-fma depth
+    float s = 0.f, t = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = w.w[k] & 0x0F0F0F0Fu;
-      const uint32_t hi = (w.w[k] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(ubyte(lo, i), x.v[4 * k + i], s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(ubyte(hi, i), x.v[16 + 4 * k + i], s);
+      const uint32_t v = w.w[k], v8 = v >> 8;
+      // elements 4k, 4k+2 | 4k+1, 4k+3 (low nibbles) as 1024 + c
+      const q4h lo02 = q4h_of((v & dk.mlo) | dk.magic);
+      const q4h lo13 = q4h_of((v8 & dk.mlo) | dk.magic);
+      // elements 16+4k, 16+4k+2 | 16+4k+1, 16+4k+3 (high nibbles) as 1024 + 16 c
+      const q4h hi02 = q4h_of((v & dk.mhi) | dk.magic);
+      const q4h hi13 = q4h_of((v8 & dk.mhi) | dk.magic);
+      const q4h off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+      const q4h sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      const q4h off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+      const q4h a = lo02 + off, b = lo13 + off;
+      const q4h c = __builtin_elementwise_fma(hi02, sixteenth, off16);
+      const q4h e = __builtin_elementwise_fma(hi13, sixteenth, off16);
+      s = fmaf(float(a[0]), x.v[4 * k + 0], s);
+      s = fmaf(float(b[0]), x.v[4 * k + 1], s);
+      s = fmaf(float(a[1]), x.v[4 * k + 2], s);
+      s = fmaf(float(b[1]), x.v[4 * k + 3], s);
+      t = fmaf(float(c[0]), x.v[16 + 4 * k + 0], t);
+      t = fmaf(float(e[0]), x.v[16 + 4 * k + 1], t);
+      t = fmaf(float(c[1]), x.v[16 + 4 * k + 2], t);
+      t = fmaf(float(e[1]), x.v[16 + 4 * k + 3], t);
     }
-    return fmaf(w.d, fmaf(-8.f, x.sum, s), acc);
+    return fmaf(w.d, s + t, acc);
   } else if constexpr (FMT == SKG_Q8_0_F32) {
     // int8 q + 128 is the unsigned byte of q ^ 0x80: sum_i q_i x_i =
     // sum_i (q_i + 128) x_i - 128 sum_i x_i
@@ -354,6 +382,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
+  DecodeK dk{};
+  if constexpr (FMT == SKG_Q4_0_F32) dk = decode_consts();
   const int nchunks = int((nu + UC - 1) / UC);
   for (int c = kw; c < nchunks; c += KW) {
     const uint32_t ub = uint32_t(c) * UC;
@@ -436,7 +466,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
           x_from_raw<FMT>(xu, xr[j][m], uok);
         }
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r][m] = unit_acc<FMT>(w[r][j], xu, acc[r][m]);
+        for (int r = 0; r < RT; ++r) acc[r][m] = unit_acc<FMT>(w[r][j], xu, acc[r][m], dk);
       }
     }
   }

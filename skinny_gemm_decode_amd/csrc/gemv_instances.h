@@ -32,17 +32,3 @@
   SKG_M(F, 6, ROL, JL, XL, SROL)       \
   SKG_M(F, 7, ROL, JL, XL, SROL)       \
   SKG_M(F, 8, ROL, JL, XL, SROL)
-
-namespace skg {
-void register_gemv_bf16(std::vector<GemvEntry>& out);
-void register_gemv_q8_0_f32(std::vector<GemvEntry>& out);
-void register_gemv_q8_0_f32_m38(std::vector<GemvEntry>& out);
-void register_gemv_q4_0_f32(std::vector<GemvEntry>& out);
-void register_gemv_q4_0_f32_m35(std::vector<GemvEntry>& out);
-void register_gemv_q4_0_f32_m68(std::vector<GemvEntry>& out);
-void register_gemv_q8_1(std::vector<GemvEntry>& out);
-void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out);
-void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out);
-void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out);
-void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out);
-}  // namespace skg

@@ -27,5 +27,9 @@ void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
   SKG_MF(1, 2, 1)
   SKG_MF(1, 1, 2)
   SKG_MF(8, 2, 1)
+  // 16 waves of 8 blocks: twice the waves per SIMD to hide latency
+  out.push_back(skg::gemv_mfma_entry<SKG_Q4_0_F32, 1, 16, 8, 2, SKG_EPI_NONE, 1>());
+  out.push_back(skg::gemv_mfma_entry<SKG_Q4_0_F32, 1, 16, 8, 1, SKG_EPI_NONE, 1>());
+  out.push_back(skg::gemv_mfma_entry<SKG_Q4_0_F32, 2, 16, 8, 2, SKG_EPI_NONE, 1>());
 }
 }  // namespace skg

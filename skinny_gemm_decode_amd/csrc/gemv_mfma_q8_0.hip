@@ -30,5 +30,6 @@ void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
   SKG_MF(3, 2, 1)
   SKG_MF(4, 2, 1)
   SKG_MF(8, 2, 1)
+  out.push_back(skg::gemv_mfma_entry<SKG_Q8_0_F32, 1, 16, 8, 2, SKG_EPI_NONE, 1>());
 }
 }  // namespace skg
