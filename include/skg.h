@@ -76,7 +76,11 @@ typedef enum skg_fmt {
   SKG_Q4_0_F32 = 2,  /* q4_0 W  x float32 x       (gemv)                    */
   SKG_Q4_0_Q8_1 = 3, /* q4_0 W  x Q8_1 x, integer dot (gemv)                */
   SKG_Q8_0_Q8_1 = 4, /* q8_0 W  x Q8_1 x, integer dot (gemv)                */
-  SKG_Q4_0_BF16 = 5  /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
+  SKG_Q4_0_BF16 = 5, /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
+  SKG_Q4_0_Q8_1F = 6, /* q4_0 W x float32 x quantised to Q8_1 inside the
+                         kernel, integer dot (gemv)                        */
+  SKG_Q8_0_Q8_1F = 7  /* q8_0 W x float32 x quantised to Q8_1 inside the
+                         kernel, integer dot (gemv)                        */
 } skg_fmt;
 
 typedef enum skg_epi {

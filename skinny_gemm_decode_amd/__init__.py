@@ -26,8 +26,11 @@ Q4_0_F32 = 2
 Q4_0_Q8_1 = 3
 Q8_0_Q8_1 = 4
 Q4_0_BF16 = 5
+Q4_0_Q8_1F = 6  # fp32 activation, quantised to Q8_1 inside the kernel
+Q8_0_Q8_1F = 7
 FMT_NAMES = {BF16_BF16: "bf16_bf16", Q8_0_F32: "q8_0_f32", Q4_0_F32: "q4_0_f32",
-             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16"}
+             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16",
+             Q4_0_Q8_1F: "q4_0_q8_1f", Q8_0_Q8_1F: "q8_0_q8_1f"}
 # skg_epi
 EPI_NONE = 0
 EPI_SWIGLU = 1

@@ -59,8 +59,10 @@ skg_status check_device(int* cus = nullptr) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool is_gemv_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1; }
-bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q4_0_BF16; }
+bool is_gemv_fmt(int fmt) {
+  return (fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1) || fmt == SKG_Q4_0_Q8_1F || fmt == SKG_Q8_0_Q8_1F;
+}
+bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1F; }
 
 // K and N rules shared by packing and products.
 skg_status check_nk(int fmt, int64_t N, int64_t K) {
@@ -83,7 +85,7 @@ std::once_flag g_reg_once;
 std::vector<GemvEntry>* g_reg = nullptr;
 std::mutex g_sel_mu;
 // selected registry index per (fmt, M, epi); -1 = default (first registered)
-int g_sel[5][9][2];
+int g_sel[SKG_Q8_0_Q8_1F + 1][9][2];
 std::atomic<int64_t> g_lds_pad{0};
 
 void init_registry() {
@@ -100,6 +102,7 @@ void init_registry() {
     register_gemv_q4_0_f32_m35(*v);
     register_gemv_q4_0_f32_m68(*v);
     register_gemv_q8_1(*v);
+    register_gemv_q8_1f(*v);
     register_gemv_mfma_q4_0_alt(*v);
     register_gemv_mfma_q8_0_alt(*v);
     for (auto& a : g_sel)

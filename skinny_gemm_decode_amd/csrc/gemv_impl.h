@@ -31,27 +31,39 @@ struct Fmt;
 template <>
 struct Fmt<SKG_BF16_BF16> {
   static constexpr int E = 8, WV = 4, XB = 16, XF = 8;
-  static constexpr bool SCALE = false, XQ8 = false, XSUM = false;
+  static constexpr bool SCALE = false, XQ8 = false, XSUM = false, XIN32 = false;
 };
 template <>
 struct Fmt<SKG_Q8_0_F32> {
   static constexpr int E = 32, WV = 8, XB = 128, XF = 32;
-  static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = true, XIN32 = false;
 };
 template <>
 struct Fmt<SKG_Q4_0_F32> {
   static constexpr int E = 32, WV = 4, XB = 128, XF = 32;
-  static constexpr bool SCALE = true, XQ8 = false, XSUM = false;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = false, XIN32 = false;
 };
 template <>
 struct Fmt<SKG_Q4_0_Q8_1> {
   static constexpr int E = 32, WV = 4, XB = 36, XF = 0;
-  static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = false;
 };
 template <>
 struct Fmt<SKG_Q8_0_Q8_1> {
   static constexpr int E = 32, WV = 8, XB = 36, XF = 0;
-  static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = false;
+};
+// Q8_1 arithmetic on a binary32 activation: each lane quantises the 32-element
+// blocks it consumes in registers (XB = 128 raw bytes per unit).
+template <>
+struct Fmt<SKG_Q4_0_Q8_1F> {
+  static constexpr int E = 32, WV = 4, XB = 128, XF = 0;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = true;
+};
+template <>
+struct Fmt<SKG_Q8_0_Q8_1F> {
+  static constexpr int E = 32, WV = 8, XB = 128, XF = 0;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = true;
 };
 
 // One 16-byte (bf16, q4_0) or 2x16-byte (q8_0) weight unit and its scale.
@@ -169,7 +181,7 @@ __device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
 
 // Raw activation unit as loaded from global memory: 16-byte pieces (bf16,
 // fp32) or the nine dwords of a Q8_1 block.
-template <int FMT, bool Q8 = Fmt<FMT>::XQ8>
+template <int FMT, bool Q8 = Fmt<FMT>::XQ8 && !Fmt<FMT>::XIN32>
 struct XRaw;
 template <int FMT>
 struct XRaw<FMT, false> {
@@ -183,7 +195,7 @@ struct XRaw<FMT, true> {
 // Loads activation unit u of row m (u must be in range).
 template <int FMT>
 __device__ inline void load_x_raw(XRaw<FMT>& r, const uint8_t* xb, int64_t K, uint32_t nb, int m, uint32_t u) {
-  if constexpr (Fmt<FMT>::XQ8) {
+  if constexpr (Fmt<FMT>::XQ8 && !Fmt<FMT>::XIN32) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(xb + (size_t(m) * nb + u) * 36);
 #pragma unroll
     for (int k = 0; k < 9; ++k) r.w[k] = p[k];
@@ -200,7 +212,24 @@ __device__ inline void load_x_raw(XRaw<FMT>& r, const uint8_t* xb, int64_t K, ui
 // no branch).
 template <int FMT>
 __device__ inline void x_from_raw(XUnit<FMT>& x, const XRaw<FMT>& r, bool ok) {
-  if constexpr (Fmt<FMT>::XQ8) {
+  if constexpr (Fmt<FMT>::XIN32) {
+    // the block's Q8_1 form, as the standalone quantiser would store it (an
+    // out-of-range unit quantises all-zero input: q = 0, d = 0, s = 0)
+    float v[QK];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const u32x4 t = ok ? r.pc[p] : u32x4{0u, 0u, 0u, 0u};
+      v[4 * p + 0] = __uint_as_float(t.x);
+      v[4 * p + 1] = __uint_as_float(t.y);
+      v[4 * p + 2] = __uint_as_float(t.z);
+      v[4 * p + 3] = __uint_as_float(t.w);
+    }
+    const Q8_1Block b = quantize_block_q8_1(v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.q[k] = b.q[k];
+    x.d = h2f(b.d16);
+    x.s = h2f(b.s16);
+  } else if constexpr (Fmt<FMT>::XQ8) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) x.q[k] = ok ? r.w[1 + k] : 0u;
     const uint32_t ds = ok ? r.w[0] : 0u;
@@ -228,7 +257,7 @@ __device__ inline void fetch_x_global(XUnit<FMT>& x, const uint8_t* xb, int64_t 
 template <int FMT>
 __device__ inline int unit_idot(const WUnit<FMT>& w, const XUnit<FMT, true>& x) {
   int si = 0;
-  if constexpr (FMT == SKG_Q4_0_Q8_1) {
+  if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q4_0_Q8_1F) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       si = __builtin_amdgcn_sdot4(int(w.w[k] & 0x0F0F0F0Fu), int(x.q[k]), si, false);
@@ -308,7 +337,7 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
       for (int i = 0; i < 4; ++i) s = fmaf(ubyte(b, i), x.v[4 * k + i], s);
     }
     return fmaf(w.d, fmaf(-128.f, x.sum, s), acc);
-  } else if constexpr (FMT == SKG_Q4_0_Q8_1) {
+  } else if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q4_0_Q8_1F) {
     const int si = unit_idot<FMT>(w, x);
     return fmaf(w.d, fmaf(x.d, float(si), -8.f * x.s), acc);
   } else {
@@ -347,6 +376,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   constexpr int GROUPS = WAVES / KW;  // row groups per workgroup
   static_assert(WAVES % KW == 0, "KW must divide WAVES");
   static_assert(KW == 1 || !XLDS, "K split across waves keeps the activation in registers");
+  static_assert(!(XLDS && F::XIN32), "in-kernel quantisation keeps the activation in registers");
   extern __shared__ u32x4 xlds[];
   __shared__ float red[KW > 1 ? WAVES : 1][KW > 1 ? RT * M : 1];
 

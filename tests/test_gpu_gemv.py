@@ -24,11 +24,18 @@ def skg():
 
 def wkind(skg, fmt):
     return {skg.BF16_BF16: "bf16", skg.Q8_0_F32: "q8_0", skg.Q4_0_F32: "q4_0",
-            skg.Q4_0_Q8_1: "q4_0", skg.Q8_0_Q8_1: "q8_0"}[fmt]
+            skg.Q4_0_Q8_1: "q4_0", skg.Q8_0_Q8_1: "q8_0",
+            skg.Q4_0_Q8_1F: "q4_0", skg.Q8_0_Q8_1F: "q8_0"}[fmt]
 
 
 def is_q8_1(skg, fmt):
+    """The kernel reads Q8_1 blocks (quantised beforehand)."""
     return fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+
+
+def is_q8_1f(skg, fmt):
+    """The kernel reads fp32 and quantises to Q8_1 itself."""
+    return fmt in (skg.Q4_0_Q8_1F, skg.Q8_0_Q8_1F)
 
 
 def make_inputs(skg, fmt, M, N, K, seed):
@@ -42,6 +49,8 @@ def gpu_activation(skg, fmt, x):
     """Device activation in the format the kernel reads (Q8_1 quantised on the
     GPU and checked bit-exactly against the oracle's quantiser first)."""
     xd = dev(x)
+    if is_q8_1f(skg, fmt):
+        return xd, oracle.quantize_q8_1(x)
     if not is_q8_1(skg, fmt):
         return xd, None
     import torch
@@ -54,10 +63,10 @@ def gpu_activation(skg, fmt, x):
 
 def reference(skg, fmt, W, x, xq_ref):
     kind = wkind(skg, fmt)
-    if fmt == skg.Q4_0_Q8_1:
+    if fmt in (skg.Q4_0_Q8_1, skg.Q4_0_Q8_1F):
         y, _, bound = oracle.gemv_q4_0_q8_1_ref(W, xq_ref)
         return y, bound
-    if fmt == skg.Q8_0_Q8_1:
+    if fmt in (skg.Q8_0_Q8_1, skg.Q8_0_Q8_1F):
         return oracle.gemv_q8_0_q8_1_ref(W, xq_ref)
     return oracle.gemv_ref_fmt(kind, W, x, x_kind="bf16" if fmt == skg.BF16_BF16 else "f32")
 
@@ -71,7 +80,7 @@ def run_gemv(skg, fmt, M, N, K, W, x):
     return host(y), xq_ref
 
 
-GEMV_FMTS = [0, 1, 2, 3, 4]
+GEMV_FMTS = [0, 1, 2, 3, 4, 6, 7]
 
 
 def shapes_for(fmt):
@@ -312,3 +321,32 @@ def test_gemv_multi_mfma(skg, fmt):
     for W, y in zip(Ws, ys):
         y_ref, bound = reference(skg, fmt, W, x, None)
         assert_close(host(y), y_ref, bound, f"multi mfma fmt={fmt}")
+
+
+@pytest.mark.parametrize("pair", [(6, 3), (7, 4)])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+def test_in_kernel_quantisation_matches_two_step_path(skg, pair, M):
+    """fp32 activation quantised inside the GEMV == standalone quantiser then
+    the Q8_1 GEMV, bit for bit (same block quantiser, same default variant
+    and accumulation order), for plain, multi-output and SwiGLU launches,
+    with a K tail and ragged rows."""
+    fused, twostep = pair
+    K, N = 4128, 131
+    W, x = make_inputs(skg, fused, M, N, K, seed=9300 + 10 * fused + M)
+    W2, _ = make_inputs(skg, fused, M, N, K, seed=9400 + 10 * fused + M)
+    note(f"in-kernel quantisation fmt={fused} M={M}")
+    xd = dev(x)
+    xq, _ = gpu_activation(skg, twostep, x)
+    Wp = skg.pack_weights(fused, N, K, dev(W))
+    ya, yb = poisoned((M, N)), poisoned((M, N))
+    skg.gemv(fused, M, K, N, Wp, xd, ya)
+    skg.gemv(twostep, M, K, N, Wp, xq, yb)
+    assert np.array_equal(host(ya), host(yb)), "plain"
+    Wpm = skg.pack_weights_multi(fused, [N, N], K, [dev(W), dev(W2)])
+    for epi, nout in ((skg.EPI_NONE, 2), (skg.EPI_SWIGLU, 1)):
+        ya = [poisoned((M, N)) for _ in range(nout)]
+        yb = [poisoned((M, N)) for _ in range(nout)]
+        skg.gemv_multi(fused, M, K, [N, N], Wpm, xd, ya, epi=epi)
+        skg.gemv_multi(twostep, M, K, [N, N], Wpm, xq, yb, epi=epi)
+        for a, b in zip(ya, yb):
+            assert np.array_equal(host(a), host(b)), f"epi={epi}"
