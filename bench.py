@@ -273,10 +273,12 @@ def bench_ceiling(skg, torch, timer, steps, warm_s):
     return res
 
 
-def bench_layer(skg, si, torch, timer, steps, warm_s):
-    """Llama-2-7B-shaped q4_0 x Q8_1 decode layer, M=1, 32 distinct layers:
-    quantize(x) -> QKV (one launch) -> gate/up + SwiGLU (one launch) ->
-    quantize(h) -> down (K=11008).  One step = one layer."""
+def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
+    """Llama-2-7B-shaped q4_0 x Q8_1 decode layer, M=1, 32 distinct layers.
+    One step = one layer.  Plain form (5 launches): quantize(x) -> QKV (one
+    launch) -> gate/up + SwiGLU (one launch) -> quantize(h) -> down (K=11008).
+    Fused form (4 launches): the gate/up launch also writes the Q8_1 blocks of
+    h (the bits quantize(h) would write), so down reads them directly."""
     D, F = 4096, 11008
     fmt = skg.Q4_0_Q8_1
     layers = []
@@ -302,16 +304,25 @@ def bench_layer(skg, si, torch, timer, steps, warm_s):
     N2 = (ctypes.c_int64 * 2)(F, F)
     Y3 = (ctypes.c_void_p * 3)(yq.data_ptr(), yk.data_ptr(), yv.data_ptr())
     Y1 = (ctypes.c_void_p * 1)(h.data_ptr())
+    Y2 = (ctypes.c_void_p * 2)(h.data_ptr(), hq.data_ptr())
     ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in layers]
     xp, xqp, hp, hqp, yop = x.data_ptr(), xq.data_ptr(), h.data_ptr(), hq.data_ptr(), yo.data_ptr()
 
-    def launch(i, sh):
-        pq, pg, pd = ptrs[i]
-        lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
-        lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
-        lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, 1, sh)
-        lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
-        lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+    if fused:
+        def launch(i, sh):
+            pq, pg, pd = ptrs[i]
+            lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y2, skg.EPI_SWIGLU_Q8_1, sh)
+            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+    else:
+        def launch(i, sh):
+            pq, pg, pd = ptrs[i]
+            lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, skg.EPI_SWIGLU, sh)
+            lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
+            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
 
     launch(0, sh)
     torch.cuda.synchronize()
@@ -320,9 +331,14 @@ def bench_layer(skg, si, torch, timer, steps, warm_s):
     res = timer.run(launch, 32, steps, 0, per_repeat=32, warm_s=warm_s)
     wbytes = (skg.packed_size_multi(fmt, [D, D, D], D) + skg.packed_size_multi(fmt, [F, F], D)
               + skg.packed_size(fmt, D, F))
-    alg = wbytes + 2 * (D // 32 * 36) + 2 * (F // 32 * 36) + 4 * (3 * D + F + D) + 4 * (D + F)
-    res.update(name="llama2_7b_q4_0_q8_1_layer", layers=32, working_set_bytes=32 * wbytes,
-               algorithmic_bytes=alg, launches_per_layer=5)
+    if fused:
+        # quantize: x in, xq out; QKV and gate/up read xq; gate/up writes h and hq; down reads hq
+        alg = wbytes + 4 * D + 3 * (D // 32 * 36) + 4 * F + 2 * (F // 32 * 36) + 4 * (3 * D + D)
+    else:
+        # quantisers read x and h (fp32) and write their Q8_1 blocks; products read the blocks
+        alg = wbytes + 2 * (D // 32 * 36) + 2 * (F // 32 * 36) + 4 * (3 * D + F + D) + 4 * (D + F)
+    res.update(name="llama2_7b_q4_0_q8_1_layer" + ("_q8_1_epilogue" if fused else ""), layers=32,
+               working_set_bytes=32 * wbytes, algorithmic_bytes=alg, launches_per_layer=4 if fused else 5)
     res["us_per_layer"] = res.pop("us_per_launch")
     res["gbs"] = alg / (res["us_per_layer"] * 1e-6) / 1e9
     res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
@@ -469,7 +485,7 @@ def main():
                            ("q4_0", skg.Q4_0_Q8_1, "q8_1")):
         if key not in arms:
             continue
-        Ms = (1, 2, 4, 8) if ("multi_m" in arms and key != "q8_1") else (1,)
+        Ms = (1, 2, 4, 8) if ("multi_m" in arms and key in ("q8_0", "q4_0")) else (1,)
         for M in Ms:
             xh = si.activations_f32(si.rng_for(0, 4, M), M, 4096)
             r, _ = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
@@ -485,10 +501,11 @@ def main():
         details["arms"][r["name"]] = r
         log(f"[{r['name']}] {r['us_per_launch']:.2f} us (graph {r['graph']['us_per_launch']:.2f} us)")
     if "layer" in arms:
-        r = bench_layer(skg, si, torch, timer, 640, 0.3)
-        details["arms"]["layer"] = r
-        log(f"[layer] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
-            f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
+        for fused in (False, True):
+            r = bench_layer(skg, si, torch, timer, 640, 0.3, fused=fused)
+            details["arms"][r["name"]] = r
+            log(f"[{r['name']}] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
+                f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
     if "prefill" in arms:
         r = bench_prefill(skg, si, torch, timer, 500, 0.3)
         details["arms"]["prefill"] = r

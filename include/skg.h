@@ -76,16 +76,13 @@ typedef enum skg_fmt {
   SKG_Q4_0_F32 = 2,  /* q4_0 W  x float32 x       (gemv)                    */
   SKG_Q4_0_Q8_1 = 3, /* q4_0 W  x Q8_1 x, integer dot (gemv)                */
   SKG_Q8_0_Q8_1 = 4, /* q8_0 W  x Q8_1 x, integer dot (gemv)                */
-  SKG_Q4_0_BF16 = 5, /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
-  SKG_Q4_0_Q8_1F = 6, /* q4_0 W x float32 x quantised to Q8_1 inside the
-                         kernel, integer dot (gemv)                        */
-  SKG_Q8_0_Q8_1F = 7  /* q8_0 W x float32 x quantised to Q8_1 inside the
-                         kernel, integer dot (gemv)                        */
+  SKG_Q4_0_BF16 = 5  /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
 } skg_fmt;
 
 typedef enum skg_epi {
-  SKG_EPI_NONE = 0,  /* each matrix writes its own output                   */
-  SKG_EPI_SWIGLU = 1 /* two matrices (gate, up) -> h = silu(g) * u          */
+  SKG_EPI_NONE = 0,       /* each matrix writes its own output              */
+  SKG_EPI_SWIGLU = 1,     /* two matrices (gate, up) -> h = silu(g) * u     */
+  SKG_EPI_SWIGLU_Q8_1 = 2 /* as SWIGLU, and h also as Q8_1 blocks           */
 } skg_epi;
 
 /* ABI version of the loaded library (SKG_ABI_VERSION it was built with). */
@@ -171,6 +168,16 @@ skg_status skg_gemv(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W,
  * epi == SKG_EPI_SWIGLU : n == 2 (gate first, then up), Ns[0] == Ns[1],
  *                         ys[0] = float32 [M][Ns[0]] receives
  *                         h = silu(g) * u, silu(z) = z / (1 + e^-z) in fp32.
+ * epi == SKG_EPI_SWIGLU_Q8_1 : as SKG_EPI_SWIGLU, and ys[1] (4-byte aligned)
+ *                         receives h as [M][Ns[0] / 32] Q8_1 blocks, the bits
+ *                         skg_quantize_act_q8_1(M, Ns[0], ys[0]) would write.
+ *                         The workgroup that computes 32 consecutive outputs
+ *                         quantises them, so the down projection reads Q8_1
+ *                         without a separate quantisation launch (the RX 6700
+ *                         XT write-up, Approach & Methodology, has the
+ *                         producer of an activation emit its Q8_1 form).
+ *                         fmt must be SKG_Q4_0_Q8_1 or SKG_Q8_0_Q8_1 and
+ *                         Ns[0] % 32 == 0 (else SKG_E_UNSUPPORTED / SKG_E_SHAPE).
  * Other arguments and errors as skg_gemv.
  */
 skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_t* Ns, const void* W,
@@ -252,7 +259,9 @@ int skg_gemv_variants(int* out, int max_entries);
 skg_status skg_set_lds_pad(int64_t bytes);
 /* skg_gemm_tiled_set_variant: prefill kernel organisation, 0 = every wave
  * decodes weights and runs MFMAs, 1 = producer waves decode, consumer waves
- * run MFMAs (default).  Process-wide. */
+ * run MFMAs, 4 consumer waves of 64 rows, 2 = as 1 with 8 consumer waves of
+ * 32 rows, 3 = as 1 with a triple-buffered weight tile so fragment reads
+ * overlap the MFMAs (default); -1 restores the default.  Process-wide. */
 skg_status skg_gemm_tiled_set_variant(int variant);
 
 #ifdef __cplusplus

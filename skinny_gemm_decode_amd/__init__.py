@@ -26,14 +26,12 @@ Q4_0_F32 = 2
 Q4_0_Q8_1 = 3
 Q8_0_Q8_1 = 4
 Q4_0_BF16 = 5
-Q4_0_Q8_1F = 6  # fp32 activation, quantised to Q8_1 inside the kernel
-Q8_0_Q8_1F = 7
 FMT_NAMES = {BF16_BF16: "bf16_bf16", Q8_0_F32: "q8_0_f32", Q4_0_F32: "q4_0_f32",
-             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16",
-             Q4_0_Q8_1F: "q4_0_q8_1f", Q8_0_Q8_1F: "q8_0_q8_1f"}
+             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16"}
 # skg_epi
 EPI_NONE = 0
 EPI_SWIGLU = 1
+EPI_SWIGLU_Q8_1 = 2  # SwiGLU, and h also written as Q8_1 blocks (ys[1])
 # skg_status
 OK, E_INVALID_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_DEVICE, E_HIP = range(7)
 
@@ -192,13 +190,18 @@ def gemv(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
 
 
 def gemv_multi(fmt: int, M: int, K: int, Ns: Sequence[int], W, x, ys=None, epi: int = EPI_NONE, stream=None):
-    """Several packed matrices sharing x in one launch; SwiGLU writes one output."""
+    """Several packed matrices sharing x in one launch.  SwiGLU writes one
+    output h; SwiGLU_Q8_1 writes h and its Q8_1 blocks (uint8 [M, N/32, 36])."""
     import torch
 
     n = len(Ns)
-    nout = 1 if epi == EPI_SWIGLU else n
+    nout = {EPI_SWIGLU: 1, EPI_SWIGLU_Q8_1: 2}.get(epi, n)
     if ys is None:
-        ys = [torch.empty((M, Ns[i]), dtype=torch.float32, device=W.device) for i in range(nout)]
+        if epi == EPI_SWIGLU_Q8_1:
+            ys = [torch.empty((M, Ns[0]), dtype=torch.float32, device=W.device),
+                  torch.empty((M, Ns[0] // 32, 36), dtype=torch.uint8, device=W.device)]
+        else:
+            ys = [torch.empty((M, Ns[i]), dtype=torch.float32, device=W.device) for i in range(nout)]
     arr = (ctypes.c_int64 * n)(*Ns)
     yp = (ctypes.c_void_p * nout)(*[_dev_ptr(t) for t in ys])
     check(lib.skg_gemv_multi(fmt, M, K, n, arr, _dev_ptr(W), _dev_ptr(x), yp, epi, _stream(stream)))

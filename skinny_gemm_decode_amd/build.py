@@ -36,7 +36,6 @@ SOURCES = [
     "gemv_q8_0_f32.hip",
     "gemv_q4_0_f32.hip",
     "gemv_q8_1.hip",
-    "gemv_q8_1f.hip",
 ]
 
 # Packed fp32 arithmetic is disabled for every HIP translation unit; the host

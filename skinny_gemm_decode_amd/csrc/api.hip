@@ -59,10 +59,8 @@ skg_status check_device(int* cus = nullptr) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool is_gemv_fmt(int fmt) {
-  return (fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1) || fmt == SKG_Q4_0_Q8_1F || fmt == SKG_Q8_0_Q8_1F;
-}
-bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1F; }
+bool is_gemv_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1; }
+bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q4_0_BF16; }
 
 // K and N rules shared by packing and products.
 skg_status check_nk(int fmt, int64_t N, int64_t K) {
@@ -85,7 +83,7 @@ std::once_flag g_reg_once;
 std::vector<GemvEntry>* g_reg = nullptr;
 std::mutex g_sel_mu;
 // selected registry index per (fmt, M, epi); -1 = default (first registered)
-int g_sel[SKG_Q8_0_Q8_1F + 1][9][2];
+int g_sel[5][9][3];
 std::atomic<int64_t> g_lds_pad{0};
 
 void init_registry() {
@@ -102,7 +100,6 @@ void init_registry() {
     register_gemv_q4_0_f32_m35(*v);
     register_gemv_q4_0_f32_m68(*v);
     register_gemv_q8_1(*v);
-    register_gemv_q8_1f(*v);
     register_gemv_mfma_q4_0_alt(*v);
     register_gemv_mfma_q8_0_alt(*v);
     for (auto& a : g_sel)
@@ -231,12 +228,16 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
   if (rows_per_block <= 0) return fail(SKG_E_UNSUPPORTED, "variant with x_lds=%d has no VALU row layout", v->xlds);
   int64_t blocks = 0;
   const uint8_t* base = static_cast<const uint8_t*>(W);
-  if (epi == SKG_EPI_SWIGLU) {
+  if (epi == SKG_EPI_SWIGLU_Q8_1 && rows_per_block % 32 != 0)
+    return fail(SKG_E_UNSUPPORTED, "selected variant covers %d rows per workgroup; the Q8_1 epilogue needs whole "
+                "32-row blocks", rows_per_block);
+  if (epi != SKG_EPI_NONE) {
     const Layout L = layout_of(wk, Ns[0], K);
     a.nseg = 1;
     a.seg[0].w0 = packed_view(base, L);
     a.seg[0].w1 = packed_view(base + L.total, L);
     a.seg[0].y = ys[0];
+    a.seg[0].yq = (epi == SKG_EPI_SWIGLU_Q8_1) ? reinterpret_cast<uint8_t*>(ys[1]) : nullptr;
     a.seg[0].N = Ns[0];
     a.seg[0].blk_begin = 0;
     blocks = (Ns[0] + rows_per_block - 1) / rows_per_block;
@@ -380,15 +381,20 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
   if (!Ns || !ys) return fail(SKG_E_INVALID_ARG, "null Ns or ys");
   if (epi == SKG_EPI_NONE) {
     if (n < 1 || n > MAX_SEGS) return fail(SKG_E_INVALID_ARG, "n must be 1..%d (got %d)", MAX_SEGS, n);
-  } else if (epi == SKG_EPI_SWIGLU) {
+  } else if (epi == SKG_EPI_SWIGLU || epi == SKG_EPI_SWIGLU_Q8_1) {
     if (n != 2) return fail(SKG_E_INVALID_ARG, "SwiGLU needs n == 2 (gate, up), got %d", n);
     if (Ns[0] != Ns[1]) return fail(SKG_E_SHAPE, "SwiGLU needs Ns[0] == Ns[1]");
+    if (epi == SKG_EPI_SWIGLU_Q8_1) {
+      if (fmt != SKG_Q4_0_Q8_1 && fmt != SKG_Q8_0_Q8_1)
+        return fail(SKG_E_UNSUPPORTED, "the Q8_1 SwiGLU epilogue exists for SKG_Q4_0_Q8_1 and SKG_Q8_0_Q8_1");
+      if (Ns[0] % 32) return fail(SKG_E_SHAPE, "the Q8_1 SwiGLU epilogue needs Ns[0] %% 32 == 0");
+    }
   } else {
     return fail(SKG_E_INVALID_ARG, "unknown epilogue %d", int(epi));
   }
   for (int i = 0; i < n; ++i)
     if ((st = check_nk(fmt, Ns[i], K)) != SKG_OK) return st;
-  const int nout = (epi == SKG_EPI_SWIGLU) ? 1 : n;
+  const int nout = (epi == SKG_EPI_SWIGLU) ? 1 : (epi == SKG_EPI_SWIGLU_Q8_1) ? 2 : n;
   for (int i = 0; i < nout; ++i) {
     if (!ys[i]) return fail(SKG_E_INVALID_ARG, "null ys[%d]", i);
     if (!aligned(ys[i], 4)) return fail(SKG_E_ALIGN, "ys[%d] must be 4-byte aligned", i);
@@ -446,7 +452,8 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
 skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw) {
   if (!is_gemv_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown gemv fmt %d", int(fmt));
   if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "M must be 1..8");
-  if (epi != SKG_EPI_NONE && epi != SKG_EPI_SWIGLU) return fail(SKG_E_INVALID_ARG, "unknown epilogue");
+  if (epi != SKG_EPI_NONE && epi != SKG_EPI_SWIGLU && epi != SKG_EPI_SWIGLU_Q8_1)
+    return fail(SKG_E_INVALID_ARG, "unknown epilogue");
   init_registry();
   int idx = -1;
   if (ro != 0) {
@@ -488,8 +495,8 @@ int skg_gemv_variants(int* out, int max_entries) {
 }
 
 skg_status skg_gemm_tiled_set_variant(int variant) {
-  if (variant < 0 || variant > 1) return fail(SKG_E_INVALID_ARG, "prefill variant must be 0 or 1");
-  g_gemm_variant = variant;
+  if (variant < -1 || variant > 3) return fail(SKG_E_INVALID_ARG, "prefill variant must be -1..3");
+  g_gemm_variant = variant < 0 ? kGemmDefaultVariant : variant;
   return ok();
 }
 

@@ -20,11 +20,9 @@ __host__ __device__ inline int wkind_of(int fmt) {
   switch (fmt) {
     case SKG_BF16_BF16: return WK_BF16;
     case SKG_Q8_0_F32:
-    case SKG_Q8_0_Q8_1:
-    case SKG_Q8_0_Q8_1F: return WK_Q8_0;
+    case SKG_Q8_0_Q8_1: return WK_Q8_0;
     case SKG_Q4_0_F32:
     case SKG_Q4_0_Q8_1:
-    case SKG_Q4_0_Q8_1F:
     case SKG_Q4_0_BF16: return WK_Q4_0;
     default: return WK_INVALID;
   }
@@ -101,31 +99,54 @@ __device__ inline float h2f(uint32_t bits16) {
   return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }
 
-// One Q8_1 block {fp16 d, fp16 s, int8 q[32]} from 32 binary32 values, as the
-// RX 6700 XT Llama 2 7B decode write-up (austxu.dev, Approach & Methodology)
-// feeds the Q4_0 integer-dot matvec.  Every step is one IEEE binary32
-// operation (the library is built without fast-math, so '/' is correctly
-// rounded, and contraction is off here):
+// Q8_1 quantisation of one 32-element block {fp16 d, fp16 s, int8 q[32]}, as
+// the RX 6700 XT Llama 2 7B decode write-up (austxu.dev, Approach &
+// Methodology) feeds the Q4_0 integer-dot matvec.  Every step is one IEEE
+// binary32 operation (the library is built without fast-math, so '/' is
+// correctly rounded, and contraction is off in these helpers):
 //   amax = max|x_i|, d = amax / 127, id = d != 0 ? 1 / d : 0,
 //   q_i = round-half-away(x_i * id), stored d = fp16_rne(d),
 //   stored s = fp16_rne(binary32(d * sum_i q_i)).
-// The standalone quantiser and the GEMVs that quantise their fp32 activation
-// in registers share this function, so their codes agree bit for bit.
+// The steps are shared by the standalone quantiser (one thread per block) and
+// the SwiGLU epilogue that quantises its output (one lane per element); max
+// and the integer sum do not depend on the order of reduction, so both
+// produce the same bits.
+__device__ inline float q8_1_d(float amax) {
+#pragma clang fp contract(off)
+  return amax / 127.0f;
+}
+__device__ inline float q8_1_id(float d) {
+#pragma clang fp contract(off)
+  return (d != 0.0f) ? 1.0f / d : 0.0f;
+}
+__device__ inline int q8_1_code(float v, float id) {
+#pragma clang fp contract(off)
+  const int q = int(roundf(v * id));
+  return q > 127 ? 127 : (q < -127 ? -127 : q);
+}
+// fp16 bits of d and of the block sum s = d * sum.
+__device__ inline uint32_t q8_1_d16(float d) { return __half_as_ushort(__float2half_rn(d)); }
+__device__ inline uint32_t q8_1_s16(float d, int sum) {
+#pragma clang fp contract(off)
+  // The empty asm pins the binary32 product in a register: without it the
+  // backend folds multiply and conversion into one v_fma_mix (one rounding,
+  // which differs on rare double-rounding ties).
+  float sp = d * float(sum);
+  asm volatile("" : "+v"(sp));
+  return __half_as_ushort(__float2half_rn(sp));
+}
+
 struct Q8_1Block {
   uint32_t q[8];  // codes 4k .. 4k+3 in word k, low byte first
   uint32_t d16, s16;
 };
 
 __device__ inline Q8_1Block quantize_block_q8_1(const float (&v)[QK]) {
-  // No contraction, so that fp16(d * sum) rounds the binary32 product, never
-  // the exact one (a fused multiply-convert rounds once and differs on rare
-  // double-rounding ties).
-#pragma clang fp contract(off)
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < QK; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const float d = amax / 127.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const float d = q8_1_d(amax);
+  const float id = q8_1_id(d);
   int sum = 0;
   Q8_1Block b;
 #pragma unroll
@@ -133,19 +154,14 @@ __device__ inline Q8_1Block quantize_block_q8_1(const float (&v)[QK]) {
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int q = int(roundf(v[4 * k + i] * id));
-      q = q > 127 ? 127 : (q < -127 ? -127 : q);
+      const int q = q8_1_code(v[4 * k + i], id);
       sum += q;
       word |= (uint32_t(q) & 0xFFu) << (8 * i);
     }
     b.q[k] = word;
   }
-  b.d16 = __half_as_ushort(__float2half_rn(d));
-  // The empty asm pins the binary32 product in a register: without it the
-  // backend folds multiply and conversion into one v_fma_mix (one rounding).
-  float sp = d * float(sum);
-  asm volatile("" : "+v"(sp));
-  b.s16 = __half_as_ushort(__float2half_rn(sp));
+  b.d16 = q8_1_d16(d);
+  b.s16 = q8_1_s16(d, sum);
   return b;
 }
 

@@ -31,39 +31,27 @@ struct Fmt;
 template <>
 struct Fmt<SKG_BF16_BF16> {
   static constexpr int E = 8, WV = 4, XB = 16, XF = 8;
-  static constexpr bool SCALE = false, XQ8 = false, XSUM = false, XIN32 = false;
+  static constexpr bool SCALE = false, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q8_0_F32> {
   static constexpr int E = 32, WV = 8, XB = 128, XF = 32;
-  static constexpr bool SCALE = true, XQ8 = false, XSUM = true, XIN32 = false;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
 };
 template <>
 struct Fmt<SKG_Q4_0_F32> {
   static constexpr int E = 32, WV = 4, XB = 128, XF = 32;
-  static constexpr bool SCALE = true, XQ8 = false, XSUM = false, XIN32 = false;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q4_0_Q8_1> {
   static constexpr int E = 32, WV = 4, XB = 36, XF = 0;
-  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = false;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q8_0_Q8_1> {
   static constexpr int E = 32, WV = 8, XB = 36, XF = 0;
-  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = false;
-};
-// Q8_1 arithmetic on a binary32 activation: each lane quantises the 32-element
-// blocks it consumes in registers (XB = 128 raw bytes per unit).
-template <>
-struct Fmt<SKG_Q4_0_Q8_1F> {
-  static constexpr int E = 32, WV = 4, XB = 128, XF = 0;
-  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = true;
-};
-template <>
-struct Fmt<SKG_Q8_0_Q8_1F> {
-  static constexpr int E = 32, WV = 8, XB = 128, XF = 0;
-  static constexpr bool SCALE = true, XQ8 = true, XSUM = false, XIN32 = true;
+  static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
 };
 
 // One 16-byte (bf16, q4_0) or 2x16-byte (q8_0) weight unit and its scale.
@@ -181,7 +169,7 @@ __device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
 
 // Raw activation unit as loaded from global memory: 16-byte pieces (bf16,
 // fp32) or the nine dwords of a Q8_1 block.
-template <int FMT, bool Q8 = Fmt<FMT>::XQ8 && !Fmt<FMT>::XIN32>
+template <int FMT, bool Q8 = Fmt<FMT>::XQ8>
 struct XRaw;
 template <int FMT>
 struct XRaw<FMT, false> {
@@ -195,7 +183,7 @@ struct XRaw<FMT, true> {
 // Loads activation unit u of row m (u must be in range).
 template <int FMT>
 __device__ inline void load_x_raw(XRaw<FMT>& r, const uint8_t* xb, int64_t K, uint32_t nb, int m, uint32_t u) {
-  if constexpr (Fmt<FMT>::XQ8 && !Fmt<FMT>::XIN32) {
+  if constexpr (Fmt<FMT>::XQ8) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(xb + (size_t(m) * nb + u) * 36);
 #pragma unroll
     for (int k = 0; k < 9; ++k) r.w[k] = p[k];
@@ -212,24 +200,7 @@ __device__ inline void load_x_raw(XRaw<FMT>& r, const uint8_t* xb, int64_t K, ui
 // no branch).
 template <int FMT>
 __device__ inline void x_from_raw(XUnit<FMT>& x, const XRaw<FMT>& r, bool ok) {
-  if constexpr (Fmt<FMT>::XIN32) {
-    // the block's Q8_1 form, as the standalone quantiser would store it (an
-    // out-of-range unit quantises all-zero input: q = 0, d = 0, s = 0)
-    float v[QK];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const u32x4 t = ok ? r.pc[p] : u32x4{0u, 0u, 0u, 0u};
-      v[4 * p + 0] = __uint_as_float(t.x);
-      v[4 * p + 1] = __uint_as_float(t.y);
-      v[4 * p + 2] = __uint_as_float(t.z);
-      v[4 * p + 3] = __uint_as_float(t.w);
-    }
-    const Q8_1Block b = quantize_block_q8_1(v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x.q[k] = b.q[k];
-    x.d = h2f(b.d16);
-    x.s = h2f(b.s16);
-  } else if constexpr (Fmt<FMT>::XQ8) {
+  if constexpr (Fmt<FMT>::XQ8) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) x.q[k] = ok ? r.w[1 + k] : 0u;
     const uint32_t ds = ok ? r.w[0] : 0u;
@@ -257,7 +228,7 @@ __device__ inline void fetch_x_global(XUnit<FMT>& x, const uint8_t* xb, int64_t 
 template <int FMT>
 __device__ inline int unit_idot(const WUnit<FMT>& w, const XUnit<FMT, true>& x) {
   int si = 0;
-  if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q4_0_Q8_1F) {
+  if constexpr (FMT == SKG_Q4_0_Q8_1) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       si = __builtin_amdgcn_sdot4(int(w.w[k] & 0x0F0F0F0Fu), int(x.q[k]), si, false);
@@ -337,7 +308,7 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
       for (int i = 0; i < 4; ++i) s = fmaf(ubyte(b, i), x.v[4 * k + i], s);
     }
     return fmaf(w.d, fmaf(-128.f, x.sum, s), acc);
-  } else if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q4_0_Q8_1F) {
+  } else if constexpr (FMT == SKG_Q4_0_Q8_1) {
     const int si = unit_idot<FMT>(w, x);
     return fmaf(w.d, fmaf(x.d, float(si), -8.f * x.s), acc);
   } else {
@@ -348,10 +319,12 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
 
 __device__ inline float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
-// One output segment of a launch: a matrix (two for SwiGLU) and its output.
+// One output segment of a launch: a matrix (two for SwiGLU) and its output
+// (plus the Q8_1 form of the SwiGLU output for SKG_EPI_SWIGLU_Q8_1).
 struct Seg {
   PackedW w0, w1;
   float* y;
+  uint8_t* yq;
   int64_t N;
   int blk_begin;
 };
@@ -366,19 +339,68 @@ struct GemvArgs {
   const uint8_t* x;
 };
 
+// Reductions over each 32-lane half of a wave, every lane receiving its
+// half's result: DPP within 16-lane rows (pairs, quads, mirrored eights, the
+// two mirrored halves of a row), then one swizzle that swaps the two rows of
+// each half (bit-mask mode, lane ^ 16).
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int SKG_SWZ_XOR16 = 0x1F | (0x10 << 10);
+
+__device__ inline float half_max(float v) {
+  v = fmaxf(v, dpp_f<SKG_DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<SKG_DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f<SKG_DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<SKG_DPP_ROW_MIRROR>(v));
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), SKG_SWZ_XOR16)));
+}
+__device__ inline int half_sum(int v) {
+  v += dpp_i<SKG_DPP_QUAD_XOR1>(v);
+  v += dpp_i<SKG_DPP_QUAD_XOR2>(v);
+  v += dpp_i<SKG_DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_i<SKG_DPP_ROW_MIRROR>(v);
+  return v + __builtin_amdgcn_ds_swizzle(v, SKG_SWZ_XOR16);
+}
+
+// One Q8_1 block from 32 values held one per lane by a 32-lane half-wave
+// (lane e holds element e), written to dst (36 bytes, 4-byte aligned) when
+// `store`.  The per-block steps are those of the standalone quantiser, and
+// the cross-lane max and integer sum are exact, so the bits are its bits.
+__device__ inline void quantise_half_q8_1(float v, uint8_t* dst, bool store) {
+  const uint32_t e = threadIdx.x & 31;
+  const float d = q8_1_d(half_max(fabsf(v)));
+  const int q = q8_1_code(v, q8_1_id(d));
+  const int sum = half_sum(q);
+  // codes of lanes 4k .. 4k+3 into one word (quad_perm broadcasts of lanes 1, 2, 3 of each quad)
+  const uint32_t b = uint32_t(q) & 0xFFu;
+  const uint32_t word = b | (uint32_t(dpp_i<0x55>(int(b))) << 8) | (uint32_t(dpp_i<0xAA>(int(b))) << 16) |
+                        (uint32_t(dpp_i<0xFF>(int(b))) << 24);
+  const uint32_t ds = q8_1_d16(d) | (q8_1_s16(d, sum) << 16);
+  if (store) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(dst);
+    if ((e & 3) == 0) w[1 + (e >> 2)] = word;
+    if (e == 0) w[0] = ds;
+  }
+}
+
 template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI, int KW>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   using F = Fmt<FMT>;
-  constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
+  constexpr int NR = (EPI == SKG_EPI_NONE) ? 1 : 2;
   constexpr int RT = RO * NR;
   constexpr int UC = 64 * J;
   constexpr int PP = F::XB / 16;
   constexpr int GROUPS = WAVES / KW;  // row groups per workgroup
   static_assert(WAVES % KW == 0, "KW must divide WAVES");
   static_assert(KW == 1 || !XLDS, "K split across waves keeps the activation in registers");
-  static_assert(!(XLDS && F::XIN32), "in-kernel quantisation keeps the activation in registers");
   extern __shared__ u32x4 xlds[];
   __shared__ float red[KW > 1 ? WAVES : 1][KW > 1 ? RT * M : 1];
+  // SwiGLU outputs of the workgroup's rows, gathered for their Q8_1 blocks
+  constexpr int RWG = GROUPS * RO;
+  static_assert(EPI != SKG_EPI_SWIGLU_Q8_1 || RWG % QK == 0, "Q8_1 output needs whole 32-row blocks per workgroup");
+  __shared__ float hq[EPI == SKG_EPI_SWIGLU_Q8_1 ? M * RWG : 1];
 
   const int blk = blockIdx.x;
   // Segment of this workgroup; selected with compile-time indices so the
@@ -516,16 +538,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
         for (int m = 0; m < M; ++m) red[wave][r * M + m] = acc[r][m];
     }
     __syncthreads();
-    if (kw != 0) return;
+    // (with the Q8_1 epilogue every wave stays for the block barrier below)
+    if (EPI != SKG_EPI_SWIGLU_Q8_1 && kw != 0) return;
+    if (kw == 0) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float t = red[wave][r * M + m];
+        for (int m = 0; m < M; ++m) {
+          float t = red[wave][r * M + m];
 #pragma unroll
-        for (int k = 1; k < KW; ++k) t += red[wave + k][r * M + m];
-        acc[r][m] = t;
-      }
+          for (int k = 1; k < KW; ++k) t += red[wave + k][r * M + m];
+          acc[r][m] = t;
+        }
+    }
   }
 
   float out = 0.f;
@@ -534,16 +559,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
       if (lane == ro * M + m) {
-        if constexpr (EPI == SKG_EPI_SWIGLU)
+        if constexpr (EPI != SKG_EPI_NONE)
           out = silu_f32(acc[ro][m]) * acc[RO + ro][m];
         else
           out = acc[ro][m];
       }
-  if (lane < RO * M) {
+  if (kw == 0 && lane < RO * M) {
     const int ro = lane / M;
     const int m = lane % M;
     const int64_t n = n0 + ro;
     if (n < sg.N) sg.y[size_t(m) * size_t(sg.N) + size_t(n)] = out;
+    if constexpr (EPI == SKG_EPI_SWIGLU_Q8_1) hq[m * RWG + (wave / KW) * RO + ro] = out;
+  }
+  if constexpr (EPI == SKG_EPI_SWIGLU_Q8_1) {
+    // Every wave reaches this barrier (none returned above).  Then each
+    // 32-lane half-wave quantises one block of 32 consecutive outputs of one
+    // activation row; blocks past N (N is a multiple of 32) are skipped.
+    __syncthreads();
+    constexpr int NBLK = M * (RWG / QK);
+    const int64_t row0 = int64_t(blk - sg.blk_begin) * RWG;
+    const int64_t nbh = sg.N / QK;
+    for (int bi = int(threadIdx.x >> 5); bi < NBLK; bi += WAVES * 2) {
+      const int m = bi / (RWG / QK), b = bi % (RWG / QK);
+      const int64_t hb = row0 / QK + b;  // block index along N
+      const float v = hq[m * RWG + b * QK + int(threadIdx.x & 31)];
+      quantise_half_q8_1(v, sg.yq + (size_t(m) * size_t(nbh) + size_t(hb < nbh ? hb : 0)) * 36, hb < nbh);
+    }
   }
 }
 

@@ -15,7 +15,6 @@ void register_gemv_q4_0_f32(std::vector<GemvEntry>& out);
 void register_gemv_q4_0_f32_m35(std::vector<GemvEntry>& out);
 void register_gemv_q4_0_f32_m68(std::vector<GemvEntry>& out);
 void register_gemv_q8_1(std::vector<GemvEntry>& out);
-void register_gemv_q8_1f(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out);

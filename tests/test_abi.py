@@ -115,6 +115,14 @@ def test_gemv_multi_errors(skg):
     assert g(2, 1, 64, 2, Ns, FAKE, FAKE, ys, 7, None) == skg.E_INVALID_ARG        # unknown epilogue
     ysn = (ctypes.c_void_p * 2)(FAKE, None)
     assert g(2, 1, 64, 2, Ns, FAKE, FAKE, ysn, 0, None) == skg.E_INVALID_ARG       # null output
+    # SwiGLU with Q8_1 output: integer-dot formats, whole 32-row blocks, two outputs
+    assert g(2, 1, 64, 2, Ns, FAKE, FAKE, ys, 2, None) == skg.E_UNSUPPORTED        # fp32-activation format
+    Ns48 = (ctypes.c_int64 * 2)(48, 48)
+    assert g(3, 1, 64, 2, Ns48, FAKE, FAKE, ys, 2, None) == skg.E_SHAPE            # N % 32 != 0
+    assert g(3, 1, 64, 2, Ns, FAKE, FAKE, ysn, 2, None) == skg.E_INVALID_ARG       # null Q8_1 output
+    ysm = (ctypes.c_void_p * 2)(FAKE, MISALIGNED)
+    assert g(3, 1, 64, 2, Ns, FAKE, FAKE, ysm, 2, None) == skg.E_ALIGN             # Q8_1 output alignment
+    assert g(3, 1, 64, 3, Ns, FAKE, FAKE, ys, 2, None) == skg.E_INVALID_ARG        # n must be 2
 
 
 @no_gpu
@@ -144,6 +152,9 @@ def test_variant_registry(skg):
         for M in range(1, 9):
             for epi in (0, 1):
                 assert (fmt, M, epi) in seen, (fmt, M, epi)
+    for fmt in (3, 4):
+        for M in range(1, 9):
+            assert (fmt, M, 2) in seen, (fmt, M, 2)
     skg.gemv_set_variant(2, 1, 0, 16, 2, 0, 4, 1)
     skg.gemv_set_variant(2, 1, 0, 0)
 

@@ -133,12 +133,22 @@ def test_llama2_7b_q4_0_q8_1_layer_chain(skg):
     del torch
 
 
-def test_prefill_tile_m512_k4096_n14336(skg):
+PREFILL_VARIANTS = [0, 1, 2, 3]
+
+
+@pytest.fixture(params=PREFILL_VARIANTS)
+def prefill_variant(skg, request):
+    skg.gemm_tiled_set_variant(request.param)
+    yield request.param
+    skg.gemm_tiled_set_variant(-1)
+
+
+def test_prefill_tile_m512_k4096_n14336(skg, prefill_variant):
     M, N, K = 512, 14336, 4096
     rng = si.rng_for(0, 5, 0)
     W = si.q4_0_weights(rng, N, K)
     A = si.activations_bf16(rng, M, K)
-    note("gemm_tiled M=512 K=4096 N=14336")
+    note(f"gemm_tiled M=512 K=4096 N=14336 variant {prefill_variant}")
     Wp = skg.pack_weights(skg.Q4_0_BF16, N, K, dev(W))
     y = poisoned((M, N))
     skg.gemm_tiled(skg.Q4_0_BF16, M, K, N, Wp, dev(A), y)
@@ -153,14 +163,14 @@ def test_prefill_tile_m512_k4096_n14336(skg):
 
 
 @pytest.mark.parametrize("M,N,K", [(2048, 256, 2048), (300, 250, 2080), (1, 1, 32), (17, 129, 96), (257, 113, 4096)])
-def test_prefill_tile_ragged_shapes(skg, M, N, K):
+def test_prefill_tile_ragged_shapes(skg, prefill_variant, M, N, K):
     """Ragged tiles, odd block counts (K tail inside a 64-wide step), and the
     m=2048, n=256, k=2048 attention-projection shape on which the pages'
     Metal tile returned -inf."""
     rng = si.rng_for(0, 5, M + N + K)
     W = si.q4_0_weights(rng, N, K)
     A = si.activations_bf16(rng, M, K)
-    note(f"gemm_tiled M={M} N={N} K={K}")
+    note(f"gemm_tiled M={M} N={N} K={K} variant {prefill_variant}")
     Wp = skg.pack_weights(skg.Q4_0_BF16, N, K, dev(W))
     y = poisoned((M, N))
     skg.gemm_tiled(skg.Q4_0_BF16, M, K, N, Wp, dev(A), y)

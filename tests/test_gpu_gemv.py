@@ -24,18 +24,11 @@ def skg():
 
 def wkind(skg, fmt):
     return {skg.BF16_BF16: "bf16", skg.Q8_0_F32: "q8_0", skg.Q4_0_F32: "q4_0",
-            skg.Q4_0_Q8_1: "q4_0", skg.Q8_0_Q8_1: "q8_0",
-            skg.Q4_0_Q8_1F: "q4_0", skg.Q8_0_Q8_1F: "q8_0"}[fmt]
+            skg.Q4_0_Q8_1: "q4_0", skg.Q8_0_Q8_1: "q8_0"}[fmt]
 
 
 def is_q8_1(skg, fmt):
-    """The kernel reads Q8_1 blocks (quantised beforehand)."""
     return fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
-
-
-def is_q8_1f(skg, fmt):
-    """The kernel reads fp32 and quantises to Q8_1 itself."""
-    return fmt in (skg.Q4_0_Q8_1F, skg.Q8_0_Q8_1F)
 
 
 def make_inputs(skg, fmt, M, N, K, seed):
@@ -49,8 +42,6 @@ def gpu_activation(skg, fmt, x):
     """Device activation in the format the kernel reads (Q8_1 quantised on the
     GPU and checked bit-exactly against the oracle's quantiser first)."""
     xd = dev(x)
-    if is_q8_1f(skg, fmt):
-        return xd, oracle.quantize_q8_1(x)
     if not is_q8_1(skg, fmt):
         return xd, None
     import torch
@@ -63,10 +54,10 @@ def gpu_activation(skg, fmt, x):
 
 def reference(skg, fmt, W, x, xq_ref):
     kind = wkind(skg, fmt)
-    if fmt in (skg.Q4_0_Q8_1, skg.Q4_0_Q8_1F):
+    if fmt == skg.Q4_0_Q8_1:
         y, _, bound = oracle.gemv_q4_0_q8_1_ref(W, xq_ref)
         return y, bound
-    if fmt in (skg.Q8_0_Q8_1, skg.Q8_0_Q8_1F):
+    if fmt == skg.Q8_0_Q8_1:
         return oracle.gemv_q8_0_q8_1_ref(W, xq_ref)
     return oracle.gemv_ref_fmt(kind, W, x, x_kind="bf16" if fmt == skg.BF16_BF16 else "f32")
 
@@ -80,7 +71,7 @@ def run_gemv(skg, fmt, M, N, K, W, x):
     return host(y), xq_ref
 
 
-GEMV_FMTS = [0, 1, 2, 3, 4, 6, 7]
+GEMV_FMTS = [0, 1, 2, 3, 4]
 
 
 def shapes_for(fmt):
@@ -108,7 +99,7 @@ def test_every_compiled_variant(skg):
     try:
         for v in variants:
             fmt, M, epi = v["fmt"], v["M"], v["epi"]
-            N = 300
+            N = 320 if epi == skg.EPI_SWIGLU_Q8_1 else 300
             # the matrix-core variants (x_lds == 2) take K % 256 == 0, K <= 4096
             K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] in (2, 3) else 4128)
             key = (fmt, M, epi, K)
@@ -129,12 +120,17 @@ def test_every_compiled_variant(skg):
             else:
                 Wp = skg.pack_weights_multi(fmt, [N, N], K, [dev(W0), dev(W1)])
                 h = poisoned((M, N))
-                skg.gemv_multi(fmt, M, K, [N, N], Wp, xin, [h], epi=skg.EPI_SWIGLU)
+                outs = [h]
+                if epi == skg.EPI_SWIGLU_Q8_1:
+                    outs.append(poisoned_q8_1(M, N))
+                skg.gemv_multi(fmt, M, K, [N, N], Wp, xin, outs, epi=epi)
                 g_ref, bg = reference(skg, fmt, W0, x, xq_ref)
                 u_ref, bu = reference(skg, fmt, W1, x, xq_ref)
                 tol = oracle.swiglu_tolerance(g_ref, u_ref, oracle.tolerance(bg), oracle.tolerance(bu))
                 ok, worst = oracle.check_close(host(h), oracle.swiglu_ref(g_ref, u_ref), tol)
                 assert ok, f"variant {v}: worst {worst}"
+                if epi == skg.EPI_SWIGLU_Q8_1:
+                    assert_q8_1_of(host(outs[1]), host(h), f"variant {v}")
             skg.gemv_set_variant(fmt, M, epi, 0)
     finally:
         for v in variants:
@@ -155,6 +151,49 @@ def test_gemv_multi_qkv_three_outputs(skg, fmt):
     for i, (w, y) in enumerate(zip(Ws, ys)):
         y_ref, bound = reference(skg, fmt, w, x, xq_ref)
         assert_close(host(y), y_ref, bound, f"qkv output {i}")
+
+
+def poisoned_q8_1(M, N):
+    """Q8_1 output buffer [M, N/32, 36] filled with 0xA5 bytes."""
+    import torch
+    return torch.full((M, N // 32, 36), 0xA5, dtype=torch.uint8, device="cuda")
+
+
+def assert_q8_1_of(hq, h, what):
+    """hq (bytes [M, N/32, 36]) holds exactly the oracle's Q8_1 blocks of h."""
+    M, N = h.shape
+    ref = oracle.quantize_q8_1(h.astype(np.float32))
+    assert np.array_equal(hq.reshape(M, N // 32, 36), np.asarray(ref).reshape(M, N // 32, 36)), \
+        f"{what}: Q8_1 blocks of h differ from the oracle's quantisation of h"
+
+
+@pytest.mark.parametrize("fmt", [3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+def test_swiglu_q8_1_epilogue(skg, fmt, M):
+    """SwiGLU whose workgroups also write the Q8_1 blocks of h: h within the
+    SwiGLU tolerance of the oracle, its blocks bit-identical to the oracle's
+    quantisation of the h the GPU wrote, and the down projection fed from
+    them equal (bit for bit) to the one fed from a standalone quantisation."""
+    K, N = 4128, 32 * 13
+    Wg, x = make_inputs(skg, fmt, M, N, K, seed=9700 + 10 * fmt + M)
+    Wu, _ = make_inputs(skg, fmt, M, N, K, seed=9800 + 10 * fmt + M)
+    Wd, _ = make_inputs(skg, fmt, 1, 96, N, seed=9900 + 10 * fmt + M)
+    note(f"swiglu q8_1 epilogue fmt={fmt} M={M}")
+    Wp = skg.pack_weights_multi(fmt, [N, N], K, [dev(Wg), dev(Wu)])
+    xin, xq_ref = gpu_activation(skg, fmt, x)
+    h, hq = poisoned((M, N)), poisoned_q8_1(M, N)
+    skg.gemv_multi(fmt, M, K, [N, N], Wp, xin, [h, hq], epi=skg.EPI_SWIGLU_Q8_1)
+    g_ref, bg = reference(skg, fmt, Wg, x, xq_ref)
+    u_ref, bu = reference(skg, fmt, Wu, x, xq_ref)
+    tol = oracle.swiglu_tolerance(g_ref, u_ref, oracle.tolerance(bg), oracle.tolerance(bu))
+    ok, worst = oracle.check_close(host(h), oracle.swiglu_ref(g_ref, u_ref), tol)
+    assert ok, f"swiglu worst {worst}"
+    assert_q8_1_of(host(hq), host(h), "epilogue")
+    Wdp = skg.pack_weights(fmt, 96, N, dev(Wd))
+    ya, yb = poisoned((M, 96)), poisoned((M, 96))
+    skg.gemv(fmt, M, N, 96, Wdp, hq, ya)
+    skg.gemv(fmt, M, N, 96, Wdp, skg.quantize_act_q8_1(h), yb)
+    assert np.array_equal(host(ya), host(yb))
 
 
 @pytest.mark.parametrize("fmt", GEMV_FMTS)
@@ -321,32 +360,3 @@ def test_gemv_multi_mfma(skg, fmt):
     for W, y in zip(Ws, ys):
         y_ref, bound = reference(skg, fmt, W, x, None)
         assert_close(host(y), y_ref, bound, f"multi mfma fmt={fmt}")
-
-
-@pytest.mark.parametrize("pair", [(6, 3), (7, 4)])
-@pytest.mark.parametrize("M", [1, 2, 3, 8])
-def test_in_kernel_quantisation_matches_two_step_path(skg, pair, M):
-    """fp32 activation quantised inside the GEMV == standalone quantiser then
-    the Q8_1 GEMV, bit for bit (same block quantiser, same default variant
-    and accumulation order), for plain, multi-output and SwiGLU launches,
-    with a K tail and ragged rows."""
-    fused, twostep = pair
-    K, N = 4128, 131
-    W, x = make_inputs(skg, fused, M, N, K, seed=9300 + 10 * fused + M)
-    W2, _ = make_inputs(skg, fused, M, N, K, seed=9400 + 10 * fused + M)
-    note(f"in-kernel quantisation fmt={fused} M={M}")
-    xd = dev(x)
-    xq, _ = gpu_activation(skg, twostep, x)
-    Wp = skg.pack_weights(fused, N, K, dev(W))
-    ya, yb = poisoned((M, N)), poisoned((M, N))
-    skg.gemv(fused, M, K, N, Wp, xd, ya)
-    skg.gemv(twostep, M, K, N, Wp, xq, yb)
-    assert np.array_equal(host(ya), host(yb)), "plain"
-    Wpm = skg.pack_weights_multi(fused, [N, N], K, [dev(W), dev(W2)])
-    for epi, nout in ((skg.EPI_NONE, 2), (skg.EPI_SWIGLU, 1)):
-        ya = [poisoned((M, N)) for _ in range(nout)]
-        yb = [poisoned((M, N)) for _ in range(nout)]
-        skg.gemv_multi(fused, M, K, [N, N], Wpm, xd, ya, epi=epi)
-        skg.gemv_multi(twostep, M, K, [N, N], Wpm, xq, yb, epi=epi)
-        for a, b in zip(ya, yb):
-            assert np.array_equal(host(a), host(b)), f"epi={epi}"
