@@ -7,6 +7,12 @@
     python -m skinny_gemm_decode_amd.rocprof_summary source-hash
         sha256 of the sources that define the bf16 M=1 GEMV kernel (a traffic
         figure measured with hardware counters is valid only for these sources)
+    python -m skinny_gemm_decode_amd.rocprof_summary traffic-md FETCH_DIR WRITE_DIR
+        markdown summary of the headline GEMV's HBM traffic from one FETCH_SIZE
+        and one WRITE_SIZE pass of `bench.py --arms none --calibrate-copy`,
+        scaled by what the counters read for a 256 MiB device copy
+    python -m skinny_gemm_decode_amd.rocprof_summary trace-md DIR TITLE COMMAND
+        markdown table of DIR/**/*kernel_stats.csv
 """
 
 from __future__ import annotations
@@ -58,6 +64,86 @@ def stats(d):
     return "\n".join(out)
 
 
+def _counter_means(d, counter):
+    """{kernel: (dispatches, mean, max)} of one counter over DIR/**/*counter_collection.csv."""
+    acc = collections.defaultdict(list)
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"].split("(")[0]].append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v), max(v)) for k, v in acc.items()}
+
+
+COPY_BYTES = 1 << 28            # bench.py --calibrate-copy: 256 MiB device-to-device copies
+HEADLINE_BYTES = 12288 * 4096 * 2 + 4096 * 2 + 12288 * 4   # weights + x + y of the headline GEMV
+
+
+def traffic_md(fetch_dir, write_dir):
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    gemv = max((k for k in fetch if k.startswith("void skg::gemv_kernel<0, 1,")), key=lambda k: fetch[k][0])
+    read = next(k for k in fetch if "stream_read_kernel" in k)
+    copy = next(k for k in fetch if "copyBuffer" in k)
+    # the copy's largest dispatch is the 256 MiB one (read and write COPY_BYTES)
+    f_copy, w_copy = fetch[copy][2], write[copy][2]
+    f_scale = COPY_BYTES / 1024.0 / f_copy
+    w_scale = COPY_BYTES / 1024.0 / w_copy
+    fg, wg = fetch[gemv][1], write.get(gemv, (0, 0.0, 0.0))[1]
+    traffic = int(round((fg * f_scale + wg * w_scale) * 1024))
+    lines = [
+        "# HBM traffic of the bf16 GEMV M=1 K=4096 N=12288 (hardware counters)",
+        "",
+        "Two counter runs of the same command, one counter each (run from the repository root on one MI355X):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_FETCH_SIZE -o run -- python -u bench.py --arms none "
+        "--no-cpu-baseline --steps 200 --warmup 200 --calibrate-copy",
+        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_WRITE_SIZE -o run -- python -u bench.py --arms none "
+        "--no-cpu-baseline --steps 200 --warmup 200 --calibrate-copy",
+        "    python -m skinny_gemm_decode_amd.rocprof_summary traffic-md gpurun_out/pmc_FETCH_SIZE gpurun_out/pmc_WRITE_SIZE",
+        "",
+        "Per-dispatch means (KiB):",
+        "",
+        "| kernel | dispatches | FETCH_SIZE | WRITE_SIZE |",
+        "|---|---|---|---|",
+        f"| `{gemv}` (bf16 M=1 default) | {fetch[gemv][0]} | {fg:.1f} | {wg:.1f} |",
+        f"| `{read}` over the same 100,663,296-byte buffers | {fetch[read][0]} | {fetch[read][1]:.1f} | "
+        f"{write.get(read, (0, 0.0, 0.0))[1]:.1f} |",
+        f"| `{copy}`, 256 MiB device-to-device copy (largest dispatch) | {fetch[copy][0]} | {f_copy:.1f} | {w_copy:.1f} |",
+        "",
+        f"Calibration against the plain copy of known size ({COPY_BYTES:,} bytes read and written): FETCH_SIZE is "
+        f"scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f} (counter KiB to bytes read / written).",
+        "",
+        f"Scaled traffic per GEMV launch: {fg:.1f} x {f_scale:.4f} + {wg:.1f} x {w_scale:.4f} KiB = {traffic:,} bytes, "
+        f"against {HEADLINE_BYTES:,} algorithmic bytes (weights 100,663,296 + x 8,192 + y 49,152): "
+        f"{traffic / HEADLINE_BYTES:.4f}x.",
+        "",
+        "Machine-readable (bench.py reports this traffic only while the GEMV sources hash to this value):",
+        "",
+        f"    traffic_bytes_per_launch: {traffic}",
+        f"    gemv_source_sha256: {gemv_source_hash()}",
+    ]
+    return "\n".join(lines)
+
+
+def trace_md(d, title, command):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Name"].split("(")[0]
+                if "skg::" not in name:
+                    continue
+                rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                             float(r["MaxNs"]) / 1e3))
+    lines = [f"# Kernel-trace summary: {title}", "", "Command (run from the repository root on one MI355X):", "",
+             f"    {command}", "", "Source: `run_kernel_stats.csv` (this library's kernels only).", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx in sorted(rows, key=lambda r: -r[1] * r[2]):
+        lines.append(f"| `{name}` | {calls} | {avg:.3f} | {mn:.3f} | {mx:.3f} |")
+    return "\n".join(lines)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "counters":
         print(counters(argv[1:]))
@@ -65,6 +151,10 @@ def main(argv):
         print(stats(argv[1]))
     elif argv == ["source-hash"]:
         print(gemv_source_hash())
+    elif len(argv) == 3 and argv[0] == "traffic-md":
+        print(traffic_md(argv[1], argv[2]))
+    elif len(argv) == 4 and argv[0] == "trace-md":
+        print(trace_md(argv[1], argv[2], argv[3]))
     else:
         print(__doc__, file=sys.stderr)
         return 2
