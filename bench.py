@@ -15,7 +15,7 @@ HBM GB/s = algorithmic bytes (weights + x + y) per launch / time per launch.
 Times come from HIP events recorded on the stream the kernels run on.
 
 Further arms (same protocol, shorter): the streaming-read ceiling, q8_0 / q4_0
-x fp32 and q4_0 x Q8_1 at M=1..8 (K=4096, N=14336), the Llama-2-7B-shaped
+x fp32 and q4_0 / q8_0 x Q8_1 at M=1..8 (K=4096, N=14336), the Llama-2-7B-shaped
 q4_0 x Q8_1 decode layer over 32 distinct layers, the q8_0 M=1 K=256 N=512
 launch-bound case, and the M=512 MFMA prefill tile.  The CPU oracle is timed
 on a bounded sample of the headline workload on this host's cores.
@@ -482,10 +482,10 @@ def main():
         details["arms"]["ceiling"] = bench_ceiling(skg, torch, timer, short["steps"], short["warm_s"])
         log(f"[ceiling] {details['arms']['ceiling']['gbs']:.0f} GB/s")
     for kind, fmt, key in (("q8_0", skg.Q8_0_F32, "q8_0"), ("q4_0", skg.Q4_0_F32, "q4_0"),
-                           ("q4_0", skg.Q4_0_Q8_1, "q8_1")):
+                           ("q4_0", skg.Q4_0_Q8_1, "q8_1"), ("q8_0", skg.Q8_0_Q8_1, "q8_1")):
         if key not in arms:
             continue
-        Ms = (1, 2, 4, 8) if ("multi_m" in arms and key in ("q8_0", "q4_0")) else (1,)
+        Ms = (1, 2, 4, 8) if "multi_m" in arms else (1,)
         for M in Ms:
             xh = si.activations_f32(si.rng_for(0, 4, M), M, 4096)
             r, _ = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
