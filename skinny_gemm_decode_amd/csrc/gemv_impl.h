@@ -444,8 +444,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     // weight stream second; the first wait then covers only the activation
     // and every weight load stays in flight until it is consumed.
     XRaw<FMT> xr[XLDS ? 1 : J][XLDS ? 1 : M];
-    u32x4 stage[XLDS ? (M * UC * PP + WAVES * 64 - 1) / (WAVES * 64) : 1];
-    if constexpr (!XLDS) {
+    u32x4 stage[XLDS && !F::XQ8 ? (M * UC * PP + WAVES * 64 - 1) / (WAVES * 64) : 1];
+    // Q8_1 activation staged whole blocks per thread (nine dwords each)
+    constexpr int NQ = (XLDS && F::XQ8) ? (M * UC + WAVES * 64 - 1) / (WAVES * 64) : 1;
+    uint32_t qstage[NQ][9];
+    if constexpr (XLDS && F::XQ8) {
+      // Cooperative staging of this chunk's Q8_1 activation, all M rows: thread
+      // t copies block t (36 contiguous bytes; a wave reads 2304 contiguous
+      // bytes) into nine LDS planes [m][dword][unit], so both the writes here
+      // and the lane-per-unit reads later hit consecutive banks.
+      if (c > 0) __syncthreads();
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        const int i = int(threadIdx.x) + t * WAVES * 64;
+        const int m = i / UC, uu = i % UC;
+        const uint32_t gu = ub + uint32_t(uu);
+        const bool ok = (m < M) && (gu < nu);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.x + (size_t(ok ? m : 0) * nb + (ok ? gu : 0u)) * 36);
+#pragma unroll
+        for (int k = 0; k < 9; ++k) qstage[t][k] = ok ? src[k] : 0u;
+      }
+    } else if constexpr (!XLDS) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const uint32_t u = ub + uint32_t(j * 64 + lane);
@@ -488,7 +507,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     }
     // Every load of the chunk is issued before any result is used.
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XLDS) {
+    if constexpr (XLDS && F::XQ8) {
+      uint32_t* ql = reinterpret_cast<uint32_t*>(xlds);
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        const int i = int(threadIdx.x) + t * WAVES * 64;
+        if (i < M * UC) {
+          const int m = i / UC, uu = i % UC;
+#pragma unroll
+          for (int k = 0; k < 9; ++k) ql[(m * 9 + k) * UC + uu] = qstage[t][k];
+        }
+      }
+      __syncthreads();
+    } else if constexpr (XLDS) {
       constexpr int NS = sizeof(stage) / sizeof(stage[0]);
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
@@ -509,7 +540,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         XUnit<FMT> xu;
-        if constexpr (XLDS) {
+        if constexpr (XLDS && F::XQ8) {
+          const uint32_t* ql = reinterpret_cast<const uint32_t*>(xlds);
+          XRaw<FMT> r;
+#pragma unroll
+          for (int k = 0; k < 9; ++k) r.w[k] = ql[(m * 9 + k) * UC + j * 64 + lane];
+          x_from_raw<FMT>(xu, r, uok);
+        } else if constexpr (XLDS) {
           u32x4 pc[PP];
 #pragma unroll
           for (int p = 0; p < PP; ++p) pc[p] = xlds[(m * PP + p) * UC + j * 64 + lane];
@@ -609,7 +646,7 @@ inline GemvEntry gemv_entry() {
 // LDS bytes an instance needs (0 when the activation lives in registers).
 inline size_t gemv_lds_bytes(int fmt, int M, int J, int xlds) {
   if (!xlds) return 0;
-  const int xb = (fmt == SKG_BF16_BF16) ? 16 : 128;
+  const int xb = (fmt == SKG_BF16_BF16) ? 16 : (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1) ? 36 : 128;
   return size_t(M) * size_t(64 * J) * size_t(xb);
 }
 
