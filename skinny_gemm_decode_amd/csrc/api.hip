@@ -193,7 +193,11 @@ skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64
     if (e != hipSuccess) return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   }
   const int64_t resident = int64_t(cus) * blocks_per_cu(v.fn, threads, lds);
-  int64_t grid = tiles < resident ? tiles : resident;
+  // As many passes over the resident workgroups as the tiles need, with the
+  // tiles spread evenly over them (896 tiles on 512 resident workgroups:
+  // 448 workgroups of two tiles, rather than 384 of two and 128 of one).
+  const int64_t passes = (tiles + resident - 1) / resident;
+  int64_t grid = (tiles + passes - 1) / passes;
   if (v.xlds == 3) {
     // the LDS-ring kernel processes at most MF_DMA_TILES tiles per workgroup
     const int64_t need = (tiles + MF_DMA_TILES - 1) / MF_DMA_TILES;

@@ -5,7 +5,10 @@ namespace skg {
 void register_gemv_q4_0_f32(std::vector<GemvEntry>& out) {
   // The first instance of each (format, M, epilogue) is its default, chosen
   // by measurement on MI355X under cold-cache rotation.
-  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 4, SKG_EPI_NONE)
+  // M = 1 at K = 4096, N = 14336: 9.06 us (4 rows per wave, 16-row
+  // workgroups) against 9.7 us with 8 rows per wave and 9.0-15.4 us for the
+  // other measured organisations
+  SKG_I(SKG_Q4_0_F32, 1, 4, 2, true, 4, SKG_EPI_NONE)
   SKG_M12(SKG_Q4_0_F32, 8, 2, 8, 1, 4, 4)
   SKG_IK(SKG_Q4_0_F32, 1, 8, 1, 4, SKG_EPI_NONE, 2)
   SKG_IK(SKG_Q4_0_F32, 1, 4, 1, 4, SKG_EPI_NONE, 2)
@@ -16,5 +19,13 @@ void register_gemv_q4_0_f32(std::vector<GemvEntry>& out) {
   SKG_I(SKG_Q4_0_F32, 1, 16, 1, false, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 16, 2, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 2, 8, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 2, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 1, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 4, 2, true, 2, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 8, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 4, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 8, SKG_EPI_NONE)
+  SKG_I(SKG_Q4_0_F32, 1, 2, 2, true, 4, SKG_EPI_NONE)
 }
 }  // namespace skg
