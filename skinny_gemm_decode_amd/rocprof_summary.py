@@ -13,6 +13,9 @@
         scaled by what the counters read for a 256 MiB device copy
     python -m skinny_gemm_decode_amd.rocprof_summary trace-md DIR TITLE COMMAND
         markdown table of DIR/**/*kernel_stats.csv
+    python -m skinny_gemm_decode_amd.rocprof_summary counters-md TITLE COMMAND DIR [DIR ...]
+        markdown table of the per-dispatch mean of every counter, per kernel of
+        this library, over the counter runs in the DIRs
 """
 
 from __future__ import annotations
@@ -144,6 +147,31 @@ def trace_md(d, title, command):
     return "\n".join(lines)
 
 
+def counters_md(title, command, dirs):
+    means = collections.defaultdict(dict)
+    calls = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            acc = collections.defaultdict(list)
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = r["Kernel_Name"].split("(")[0]
+                    if "skg::" in k:
+                        acc[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+            for (k, c), v in acc.items():
+                means[k][c] = sum(v) / len(v)
+                calls[k] = max(calls.get(k, 0), len(v))
+    names = sorted({c for m in means.values() for c in m})
+    lines = [f"# Hardware counters: {title}", "", "Commands (run from the repository root on one MI355X, one counter",
+             "set per run):", ""] + [f"    {c}" for c in command.split(" ;; ")] + [
+             "", "Per-dispatch means over every dispatch of each kernel:", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for k in sorted(means, key=lambda k: -calls[k]):
+        lines.append(f"| `{k}` | {calls[k]} | " + " | ".join(
+            f"{means[k][c]:.4g}" if c in means[k] else "" for c in names) + " |")
+    return "\n".join(lines)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "counters":
         print(counters(argv[1:]))
@@ -155,6 +183,8 @@ def main(argv):
         print(traffic_md(argv[1], argv[2]))
     elif len(argv) == 4 and argv[0] == "trace-md":
         print(trace_md(argv[1], argv[2], argv[3]))
+    elif len(argv) >= 4 and argv[0] == "counters-md":
+        print(counters_md(argv[1], argv[2], argv[3:]))
     else:
         print(__doc__, file=sys.stderr)
         return 2
