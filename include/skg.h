@@ -261,7 +261,9 @@ skg_status skg_set_lds_pad(int64_t bytes);
  * decodes weights and runs MFMAs, 1 = producer waves decode, consumer waves
  * run MFMAs, 4 consumer waves of 64 rows, 2 = as 1 with 8 consumer waves of
  * 32 rows, 3 = as 1 with a triple-buffered weight tile so fragment reads
- * overlap the MFMAs (default); -1 restores the default.  Process-wide. */
+ * overlap the MFMAs, 4 = as 3 with the activation slices copied straight
+ * from global memory into LDS (default); -1 restores the default.
+ * Process-wide. */
 skg_status skg_gemm_tiled_set_variant(int variant);
 
 #ifdef __cplusplus

@@ -499,7 +499,7 @@ int skg_gemv_variants(int* out, int max_entries) {
 }
 
 skg_status skg_gemm_tiled_set_variant(int variant) {
-  if (variant < -1 || variant > 3) return fail(SKG_E_INVALID_ARG, "prefill variant must be -1..3");
+  if (variant < -1 || variant > 4) return fail(SKG_E_INVALID_ARG, "prefill variant must be -1..4");
   g_gemm_variant = variant < 0 ? kGemmDefaultVariant : variant;
   return ok();
 }

@@ -165,6 +165,34 @@ __device__ inline Q8_1Block quantize_block_q8_1(const float (&v)[QK]) {
   return b;
 }
 
+// Direct global -> LDS copies (global_load_lds_dwordx4) and their waits.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((const lds_u8*)p));
+}
+
+// Lane i copies 16 bytes from src (its own address) to LDS byte address
+// dst + 16 i (dst uniform across the wave).  Written as asm on purpose: the
+// compiler tracks these transfers only coarsely and would drain every
+// transfer in flight at each LDS read behind a branch, so the kernel keeps
+// the vmcnt bookkeeping itself (wait_vmcnt before each barrier) and issues
+// no register loads while transfers are in flight.  The asm writes no VGPR.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
+__device__ inline void dma16(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) (N <= 63), other counters untouched.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // DPP row operations (gfx9 encodings).
 #define SKG_DPP_QUAD_XOR1 0xB1   // quad_perm [1,0,3,2]
 #define SKG_DPP_QUAD_XOR2 0x4E   // quad_perm [2,3,0,1]

@@ -390,12 +390,21 @@ __global__ __launch_bounds__((CW + 4) * 64) void gemm_q4_0_bf16_pc_kernel(Packed
 // slice of step s+1, request that of step s+2, and run
 //   read (s, second half) | MFMA (s, first half) | read (s+1, first half) |
 //   MFMA (s, second half) | barrier.
-template <int NB16, int PW>
+//
+// With ADMA the activation slices are copied straight from global memory into
+// LDS (global_load_lds_dwordx4: no registers, no LDS store instructions) into a
+// ring of three slots per consumer wave; the copy of step s+2 is issued at the
+// start of step s and waited for (vector-memory counter, in order) just before
+// the fragments of step s+1 are read.  Each lane fetches the chunk whose
+// swizzled slot is its own destination, so the slots keep the swizzled
+// layout the fragment reads expect.
+template <int NB16, int PW, bool ADMA>
 __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, const uint16_t* __restrict__ A,
                                                                   float* __restrict__ y, int M, int N, int K) {
   constexpr int BN = 16 * NB16;
+  constexpr int ASLOTS = ADMA ? 3 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t Bs[3][128 * GT_LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t As_raw[4 * 2 * 64 * 8 * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t As_raw[4 * ASLOTS * 64 * 8 * 16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -474,8 +483,11 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   }
 
   // ---------------- consumer: activation slice + fragments + MFMA ----------------
-  // Activation slices as in the kernel above (wave-private, swizzled, two slots).
-  u32x4* As = reinterpret_cast<u32x4*>(As_raw) + wave * (2 * 64 * 8);
+  // Activation slices as in the kernel above (wave-private, swizzled).
+  u32x4* As = reinterpret_cast<u32x4*>(As_raw) + wave * (ASLOTS * 64 * 8);
+  // wave-uniform (the copy destination is a scalar register)
+  const uint32_t as_lds =
+      __builtin_amdgcn_readfirstlane(lds_addr(As_raw) + uint32_t(wave) * (ASLOTS * 64 * 8 * 16));
   const int mw = m0 + wave * 64;
   u32x4 araw[8];
   auto load_a = [&](int s) {
@@ -525,12 +537,44 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
                                                               acc[mi][nj], 0, 0, 0);
     }
   };
+  // slice of step s into slot `slot` by direct copies: instruction i fills
+  // slots 64 i .. 64 i + 63 (row 8 i + l / 8, physical chunk l % 8 for lane l),
+  // so lane l fetches logical chunk (l % 8) ^ (row & 7) of its row
+  auto dma_a = [&](int slot, int s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      const int cl = (lane & 7) ^ (r & 7);
+      const int m = min(mw + r, M - 1);
+      const int k = min(s * GT_BK + cl * 8, K - 8);
+      dma16(A + size_t(m) * size_t(K) + size_t(k), as_lds + uint32_t(slot) * 8192u + uint32_t(i) * 1024u);
+    }
+  };
   using std::integral_constant;
-  load_a(0);
-  park_a(0);
-  load_a(1);
+  if constexpr (ADMA) {
+    dma_a(0, 0);
+    dma_a(1, 1);
+    wait_vmcnt<8>();  // slice 0 has landed; slice 1 may be in flight
+    asm volatile("" ::: "memory");
+  } else {
+    load_a(0);
+    park_a(0);
+    load_a(1);
+  }
   lds_barrier();  // weight buffers 0 and 1 decoded
   read_frags(integral_constant<int, 0>{}, 0, 0, 0);
+  auto dstep = [&](auto ca_c, auto cb_c, int s) {
+    constexpr int CA = decltype(ca_c)::value;  // activation slot of step s (mod 3)
+    constexpr int CB = decltype(cb_c)::value;  // weight buffer of step s
+    dma_a((CA + 2) % 3, s + 2);  // that slot was last read during step s-1
+    read_frags(integral_constant<int, 1>{}, CA, CB, 1);
+    mfmas(integral_constant<int, 0>{});
+    wait_vmcnt<8>();  // slice s+1 (requested one step ago) has landed
+    asm volatile("" ::: "memory");
+    read_frags(integral_constant<int, 0>{}, (CA + 1) % 3, (CB + 1) % 3, 0);
+    mfmas(integral_constant<int, 1>{});
+    lds_barrier();
+  };
   auto cstep = [&](auto ca_c, auto cb_c, int s) {
     constexpr int CA = decltype(ca_c)::value;  // activation slot of step s
     constexpr int CB = decltype(cb_c)::value;  // weight buffer of step s
@@ -543,11 +587,19 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     lds_barrier();
   };
   for (int s0 = 0; s0 < steps; s0 += U) {
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((s0 + I < steps ? cstep(integral_constant<int, I % 2>{}, integral_constant<int, I % 3>{}, s0 + I) : void()),
-       ...);
-    }(std::make_integer_sequence<int, U>{});
+    if constexpr (ADMA) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((s0 + I < steps ? dstep(integral_constant<int, I % 3>{}, integral_constant<int, I % 3>{}, s0 + I) : void()),
+         ...);
+      }(std::make_integer_sequence<int, U>{});
+    } else {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((s0 + I < steps ? cstep(integral_constant<int, I % 2>{}, integral_constant<int, I % 3>{}, s0 + I) : void()),
+         ...);
+      }(std::make_integer_sequence<int, U>{});
+    }
   }
+  if constexpr (ADMA) wait_vmcnt<0>();  // no copy into LDS outlives the workgroup
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -565,9 +617,10 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
 
 // 0: one role per wave; 1: producer/consumer waves, 4 consumer waves of 64
 // rows; 2: producer/consumer waves, 8 consumer waves of 32 rows; 3: pipelined
-// producer/consumer waves (triple-buffered weight tile)
-// measured on MI355X at M=512, K=4096, N=14336: 80.8 / 71.3 / 71.4 / 68.4 us
-extern const int kGemmDefaultVariant = 3;
+// producer/consumer waves (triple-buffered weight tile); 4: as 3 with the
+// activation slices copied straight into LDS
+// measured on MI355X at M=512, K=4096, N=14336: 80.8 / 71.3 / 71.4 / 67.6 / 64.8 us
+extern const int kGemmDefaultVariant = 4;
 int g_gemm_variant = kGemmDefaultVariant;
 
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,
@@ -602,12 +655,19 @@ hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, con
     else
       hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<8, GT_PW, 8>), dim3(grid), dim3(768), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
-  } else {
+  } else if (g_gemm_variant == 3) {
     if (seven)
-      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, false>), dim3(grid), dim3(512), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
     else
-      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, false>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+                         int(M), int(N), int(K));
+  } else {
+    if (seven)
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, true>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+                         int(M), int(N), int(K));
+    else
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, true>), dim3(grid), dim3(512), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
   }
   return hipGetLastError();

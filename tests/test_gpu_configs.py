@@ -133,7 +133,7 @@ def test_llama2_7b_q4_0_q8_1_layer_chain(skg):
     del torch
 
 
-PREFILL_VARIANTS = [0, 1, 2, 3]
+PREFILL_VARIANTS = [0, 1, 2, 3, 4]
 
 
 @pytest.fixture(params=PREFILL_VARIANTS)
