@@ -177,18 +177,24 @@ def swiglu_tolerance(g_ref, u_ref, tol_g, tol_u) -> np.ndarray:
 # read the weights once per 64x64 tile instead of once per row).
 # --------------------------------------------------------------------------
 
-def gemm_tiled_ref(Wq4, A_bf16):
-    """q4_0 [N, nb, 18] x bf16 bit patterns [M, K] -> (y, bound, y_bf16w) [M, N].
+def gemm_tiled_ref(Wq, A_bf16, kind: str = "q4_0"):
+    """Quantised weights [N, nb, block] ("q4_0" 18-byte or "q8_0" 34-byte
+    blocks) x bf16 bit patterns [M, K] -> (y, bound, y_bf16w) [M, N].
 
+    "Chapter 2.2 - speed - 64-lane Metal" (the tile) decodes each weight tile
+    once and multiplies it against every activation row; the product itself
+    is the plain definition, y[m][n] = sum_k w[n][k] x[m][k] in fp64.
     y_bf16w rounds every decoded weight to bf16 (nearest-even) before the
     float64 product: the value a kernel that stages bf16 weights computes
     exactly up to summation order.  It is a second reference for classifying
     deviations, not the gate.
     """
-    Wd = decode_q4_0(Wq4)
+    if kind not in ("q4_0", "q8_0"):
+        raise ValueError(f"tile weights are q4_0 or q8_0, not {kind!r}")
+    Wd = dequantize(kind, Wq)
     A = decode_bf16(A_bf16)
     y, bound = gemv_ref(Wd, A)
-    w32 = Wd.astype(np.float32)                            # exact: 11+4 bits
+    w32 = Wd.astype(np.float32)                            # exact: 11 + 4 (q4_0) or 11 + 8 (q8_0) bits
     u = w32.view(np.uint32).astype(np.uint64)
     wb = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     y_bf16w, _ = gemv_ref(decode_bf16(wb), A)

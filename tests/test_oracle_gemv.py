@@ -198,13 +198,14 @@ def test_swiglu_tolerance_covers_perturbed_inputs():
     assert np.all(err <= oracle.swiglu_tolerance(g, u, tg, tu))
 
 
-def test_gemm_tiled_reference_brute_force_tile():
+@pytest.mark.parametrize("kind", ["q4_0", "q8_0"])
+def test_gemm_tiled_reference_brute_force_tile(kind):
     rng = si.rng_for(0, 99, 14)
     M, N, K = 64, 64, 64
-    W = si.q4_0_weights(rng, N, K)
+    W = si.weights(kind, rng, N, K)
     A = si.activations_bf16(rng, M, K)
-    y, bound, y_b = oracle.gemm_tiled_ref(W, A)
-    Wd = [[float(v) for v in ex.row_values("q4_0", W[n].tobytes(), K)] for n in range(N)]
+    y, bound, y_b = oracle.gemm_tiled_ref(W, A, kind)
+    Wd = [[float(v) for v in ex.row_values(kind, W[n].tobytes(), K)] for n in range(N)]
     Ad = [[float(ex.bf16_value(int(v))) for v in A[m]] for m in range(M)]
     for m in range(0, M, 7):
         for n in range(N):
