@@ -349,12 +349,12 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
     return res
 
 
-def bench_prefill(skg, si, torch, timer, steps, warm_s):
+def bench_prefill(skg, si, torch, timer, steps, warm_s, kind="q4_0"):
     M, N, K = 512, 14336, 4096
-    fmt = skg.Q4_0_BF16
+    fmt = skg.Q4_0_BF16 if kind == "q4_0" else skg.Q8_0_BF16
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
-    bufs, _ = make_packed_rotation(skg, si, torch, "q4_0", fmt, N, K, n_rot, seed0=70_000)
+    bufs, _ = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=70_000)
     A = torch.from_numpy(si.activations_bf16(si.rng_for(0, 5, 9), M, K).view("int16")).cuda()
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     lib = skg.lib
@@ -371,7 +371,7 @@ def bench_prefill(skg, si, torch, timer, steps, warm_s):
         raise RuntimeError("prefill tile produced non-finite output")
     res = timer.run(launch, n_rot, steps, 0, per_repeat=50, warm_s=warm_s)
     flops = 2.0 * M * N * K
-    res.update(name="prefill_q4_0_bf16_m512", M=M, N=N, K=K, rotation_buffers=n_rot, flop=flops,
+    res.update(name=f"prefill_{kind}_bf16_m512", M=M, N=N, K=K, rotation_buffers=n_rot, flop=flops,
                tflops=flops / (res["us_per_launch"] * 1e-6) / 1e12)
     res["frac_peak_mfma_bf16"] = res["tflops"] / PEAK_BF16_TFLOPS
     del bufs
@@ -507,10 +507,11 @@ def main():
             log(f"[{r['name']}] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
                 f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
     if "prefill" in arms:
-        r = bench_prefill(skg, si, torch, timer, 500, 0.3)
-        details["arms"]["prefill"] = r
-        log(f"[prefill] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "
-            f"({100 * r['frac_peak_mfma_bf16']:.1f}% of bf16 peak)")
+        for kind in ("q4_0", "q8_0"):
+            r = bench_prefill(skg, si, torch, timer, 500, 0.3, kind=kind)
+            details["arms"][r["name"]] = r
+            log(f"[{r['name']}] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "
+                f"({100 * r['frac_peak_mfma_bf16']:.1f}% of bf16 peak)")
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda").random_(0, 255)

@@ -76,7 +76,8 @@ typedef enum skg_fmt {
   SKG_Q4_0_F32 = 2,  /* q4_0 W  x float32 x       (gemv)                    */
   SKG_Q4_0_Q8_1 = 3, /* q4_0 W  x Q8_1 x, integer dot (gemv)                */
   SKG_Q8_0_Q8_1 = 4, /* q8_0 W  x Q8_1 x, integer dot (gemv)                */
-  SKG_Q4_0_BF16 = 5  /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
+  SKG_Q4_0_BF16 = 5, /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
+  SKG_Q8_0_BF16 = 6  /* q8_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
 } skg_fmt;
 
 typedef enum skg_epi {
@@ -190,10 +191,14 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
  * the weights once per activation row: each 64x64 weight tile is decoded once
  * into padded on-chip memory and serves every row of its output tile.
  *
- * fmt : SKG_Q4_0_BF16.  W : skg_pack_weights(SKG_Q4_0_BF16, N, K) output.
+ * fmt : SKG_Q4_0_BF16 or SKG_Q8_0_BF16 (the q8_0 tile of the same page's
+ *       q8_0 measurements).  W : skg_pack_weights(fmt, N, K) output.
  * x   : bf16 [M][K] device, 16-byte aligned.  y : float32 [M][N], overwritten.
- * Weights are decoded to bf16 (w = bf16_rne(d * (c - 8))) and multiplied on
- * bf16 MFMA with fp32 accumulation.  M >= 1, N >= 1, K % 32 == 0.
+ * Weights are decoded to bf16 (w = bf16_rne(d * (c - 8)) for q4_0,
+ * bf16_rne(d * q) for q8_0) and multiplied on bf16 MFMA with fp32
+ * accumulation.  M >= 1, N >= 1, K % 32 == 0.  q8_0 weights run on the
+ * pipelined organisations (skg_gemm_tiled_set_variant 3 or 4); with another
+ * organisation selected a q8_0 call returns SKG_E_UNSUPPORTED.
  */
 skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x,
                           float* y, hipStream_t stream);

@@ -26,8 +26,9 @@ Q4_0_F32 = 2
 Q4_0_Q8_1 = 3
 Q8_0_Q8_1 = 4
 Q4_0_BF16 = 5
+Q8_0_BF16 = 6
 FMT_NAMES = {BF16_BF16: "bf16_bf16", Q8_0_F32: "q8_0_f32", Q4_0_F32: "q4_0_f32",
-             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16"}
+             Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16", Q8_0_BF16: "q8_0_bf16"}
 # skg_epi
 EPI_NONE = 0
 EPI_SWIGLU = 1

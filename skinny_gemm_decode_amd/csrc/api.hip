@@ -60,7 +60,7 @@ skg_status check_device(int* cus = nullptr) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool is_gemv_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1; }
-bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q4_0_BF16; }
+bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_BF16; }
 
 // K and N rules shared by packing and products.
 skg_status check_nk(int fmt, int64_t N, int64_t K) {
@@ -410,7 +410,10 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
 skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x, float* y,
                           hipStream_t stream) {
   if (!is_any_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown fmt %d", int(fmt));
-  if (fmt != SKG_Q4_0_BF16) return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16 only");
+  if (fmt != SKG_Q4_0_BF16 && fmt != SKG_Q8_0_BF16)
+    return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16 and SKG_Q8_0_BF16");
+  if (fmt == SKG_Q8_0_BF16 && g_gemm_variant != 3 && g_gemm_variant != 4)
+    return fail(SKG_E_UNSUPPORTED, "q8_0 tiles run on prefill organisations 3 and 4 (selected: %d)", g_gemm_variant);
   skg_status st = check_nk(fmt, N, K);
   if (st != SKG_OK) return st;
   if (M < 1 || M > (int64_t(1) << 31)) return fail(SKG_E_SHAPE, "M must be >= 1 (got %lld)", (long long)M);
@@ -418,7 +421,7 @@ skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const vo
   if (!aligned(W, 16) || !aligned(x, 16)) return fail(SKG_E_ALIGN, "W and x must be 16-byte aligned");
   if (!aligned(y, 4)) return fail(SKG_E_ALIGN, "y must be 4-byte aligned");
   if ((st = check_device()) != SKG_OK) return st;
-  const Layout L = layout_of(WK_Q4_0, N, K);
+  const Layout L = layout_of(wkind_of(fmt), N, K);
   hipError_t e = launch_gemm_tiled(M, K, N, W, L, x, y, stream);
   if (e != hipSuccess) return fail(SKG_E_HIP, "gemm_tiled: %s", hipGetErrorString(e));
   return ok();

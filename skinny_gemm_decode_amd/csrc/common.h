@@ -20,7 +20,8 @@ __host__ __device__ inline int wkind_of(int fmt) {
   switch (fmt) {
     case SKG_BF16_BF16: return WK_BF16;
     case SKG_Q8_0_F32:
-    case SKG_Q8_0_Q8_1: return WK_Q8_0;
+    case SKG_Q8_0_Q8_1:
+    case SKG_Q8_0_BF16: return WK_Q8_0;
     case SKG_Q4_0_F32:
     case SKG_Q4_0_Q8_1:
     case SKG_Q4_0_BF16: return WK_Q4_0;
@@ -182,7 +183,11 @@ __device__ inline uint32_t lds_addr(const void* p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else in these kernels uses it
 __device__ inline void dma16(const void* src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+  // dst is wave-uniform; readfirstlane keeps it in a scalar register whatever
+  // the surrounding code lets the compiler prove
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(dst)),
+               "v"(src)
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

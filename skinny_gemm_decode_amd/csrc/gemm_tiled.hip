@@ -398,9 +398,13 @@ __global__ __launch_bounds__((CW + 4) * 64) void gemm_q4_0_bf16_pc_kernel(Packed
 // the fragments of step s+1 are read.  Each lane fetches the chunk whose
 // swizzled slot is its own destination, so the slots keep the swizzled
 // layout the fragment reads expect.
-template <int NB16, int PW, bool ADMA>
+// WK selects the weight format: q4_0 (one 16-byte unit per block) or q8_0
+// (two planes of 16 bytes per block: codes 0-15 and 16-31).
+template <int NB16, int PW, bool ADMA, int WK = WK_Q4_0>
 __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, const uint16_t* __restrict__ A,
                                                                   float* __restrict__ y, int M, int N, int K) {
+  static_assert(WK == WK_Q4_0 || WK == WK_Q8_0, "q4_0 or q8_0 weights");
+  constexpr int NPL = (WK == WK_Q8_0) ? 2 : 1;  // 16-byte planes per block
   constexpr int BN = 16 * NB16;
   constexpr int ASLOTS = ADMA ? 3 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t Bs[3][128 * GT_LDS_ROW];
@@ -426,32 +430,51 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     const int dn = min(n0 + drow, N - 1);
     const uint8_t* dpay = P.payload + size_t(dn) * P.row_bytes;
     const uint16_t* dsc = P.scales + size_t(dn) * P.nb;
-    u32x4 wraw[PW];
+    u32x4 wraw[PW][NPL];
     uint32_t wsc[PW];
     bool wok[PW];
     auto load_w = [&](auto slot_c, int s) {
       constexpr int SL = decltype(slot_c)::value;
       const int kb = s * 2 + dblk;
       const int kc = min(kb, nbk - 1);
-      wraw[SL] = ld_u32x4(dpay + size_t(kc) * 16);
+#pragma unroll
+      for (int p = 0; p < NPL; ++p) wraw[SL][p] = ld_u32x4(dpay + (size_t(p) * size_t(nbk) + size_t(kc)) * 16);
       wsc[SL] = dsc[kc];
       wok[SL] = kb < nbk;
     };
+    // o[j] = bf16 pair (element 2j, element 2j+1) of the block, each
+    // bf16_rne(d * code) with the product exact in fp32 (fma: one rounding).
     auto store_w = [&](auto slot_c, auto buf_c) {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int BUF = decltype(buf_c)::value;
       const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
-      const float nd8 = -8.0f * d;
-      const uint32_t pw[4] = {wraw[SL].x, wraw[SL].y, wraw[SL].z, wraw[SL].w};
       uint32_t o[16];
+      if constexpr (WK == WK_Q4_0) {
+        // w = d (c - 8); element i < 16 is the low nibble of byte i, i + 16 its high nibble
+        const float nd8 = -8.0f * d;
+        const uint32_t pw[4] = {wraw[SL][0].x, wraw[SL][0].y, wraw[SL][0].z, wraw[SL][0].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = pw[k] & 0x0F0F0F0Fu;
-        const uint32_t hi = (pw[k] >> 4) & 0x0F0F0F0Fu;
-        o[2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(lo), d, nd8), fmaf(cvt_ubyte<1>(lo), d, nd8));
-        o[2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(lo), d, nd8), fmaf(cvt_ubyte<3>(lo), d, nd8));
-        o[8 + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(hi), d, nd8), fmaf(cvt_ubyte<1>(hi), d, nd8));
-        o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(hi), d, nd8), fmaf(cvt_ubyte<3>(hi), d, nd8));
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = pw[k] & 0x0F0F0F0Fu;
+          const uint32_t hi = (pw[k] >> 4) & 0x0F0F0F0Fu;
+          o[2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(lo), d, nd8), fmaf(cvt_ubyte<1>(lo), d, nd8));
+          o[2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(lo), d, nd8), fmaf(cvt_ubyte<3>(lo), d, nd8));
+          o[8 + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(hi), d, nd8), fmaf(cvt_ubyte<1>(hi), d, nd8));
+          o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(hi), d, nd8), fmaf(cvt_ubyte<3>(hi), d, nd8));
+        }
+      } else {
+        // w = d q; q + 128 is the unsigned byte of q ^ 0x80, so w = d (u - 128)
+        const float nd128 = -128.0f * d;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t pw[4] = {wraw[SL][p].x ^ 0x80808080u, wraw[SL][p].y ^ 0x80808080u,
+                                  wraw[SL][p].z ^ 0x80808080u, wraw[SL][p].w ^ 0x80808080u};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            o[8 * p + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(pw[k]), d, nd128), fmaf(cvt_ubyte<1>(pw[k]), d, nd128));
+            o[8 * p + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(pw[k]), d, nd128), fmaf(cvt_ubyte<3>(pw[k]), d, nd128));
+          }
+        }
       }
       u32x4* dst = reinterpret_cast<u32x4*>(&Bs[BUF][drow * GT_LDS_ROW + dblk * 32]);
 #pragma unroll
@@ -625,6 +648,34 @@ int g_gemm_variant = kGemmDefaultVariant;
 
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,
                              float* y, hipStream_t stream) {
+  if (L.wk == WK_Q8_0) {
+    // q8_0 weights: the pipelined organisations only
+    const PackedW P = packed_view(W, L);
+    const int64_t mtiles = (M + GT_BM - 1) / GT_BM;
+    const int64_t t7 = mtiles * ((N + 111) / 112), t8 = mtiles * ((N + 127) / 128);
+    const int cus = 256;
+    const double e7 = double(t7) / double(((t7 + cus - 1) / cus) * cus);
+    const double e8 = double(t8) / double(((t8 + cus - 1) / cus) * cus);
+    const bool seven = e7 > e8;
+    const unsigned grid = unsigned(seven ? t7 : t8);
+    const uint16_t* xa = static_cast<const uint16_t*>(x);
+    if (g_gemm_variant == 3) {
+      if (seven)
+        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, false, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
+                           xa, y, int(M), int(N), int(K));
+      else
+        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, false, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
+                           xa, y, int(M), int(N), int(K));
+    } else {
+      if (seven)
+        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, true, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
+                           xa, y, int(M), int(N), int(K));
+      else
+        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, true, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
+                           xa, y, int(M), int(N), int(K));
+    }
+    return hipGetLastError();
+  }
   const PackedW P = packed_view(W, L);
   const int64_t mtiles = (M + GT_BM - 1) / GT_BM;
   // Tile width: 7 or 8 16-column groups, whichever leaves the fewest idle

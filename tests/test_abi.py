@@ -135,6 +135,10 @@ def test_other_entry_point_errors(skg):
     assert L.skg_gemm_tiled(2, 512, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED
     assert L.skg_gemm_tiled(5, 0, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_gemm_tiled(5, 512, 4100, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_gemm_tiled_set_variant(1) == skg.OK
+    assert L.skg_gemm_tiled(6, 512, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED  # q8_0: 3, 4 only
+    assert L.skg_gemm_tiled_set_variant(-1) == skg.OK
+    assert L.skg_gemm_tiled(6, 512, 4100, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_pack_weights(2, 4, 64, FAKE, MISALIGNED, None) == skg.E_ALIGN
     assert L.skg_pack_weights(2, 4, 64, ctypes.c_void_p((1 << 20) + 1), FAKE, None) == skg.E_ALIGN
     assert L.skg_pack_weights(2, 4, 60, FAKE, FAKE, None) == skg.E_SHAPE

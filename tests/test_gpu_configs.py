@@ -179,3 +179,28 @@ def test_prefill_tile_ragged_shapes(skg, prefill_variant, M, N, K):
     mrows = sample_rows(M, n=64, seed=7)
     y_ref, bound, _ = oracle.gemm_tiled_ref(W, A[mrows])
     assert_close(yh[mrows], y_ref, bound, f"tile M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("variant", [3, 4])
+@pytest.mark.parametrize("M,N,K", [(512, 14336, 4096), (300, 250, 2080), (17, 129, 96), (2048, 256, 2048)])
+def test_prefill_tile_q8_0(skg, variant, M, N, K):
+    """The q8_0 weight tile (pipelined organisations), sampled at the
+    M=512 workload size, with ragged tiles and a K tail."""
+    rng = si.rng_for(0, 6, M + N + K)
+    W = si.q8_0_weights(rng, N, K)
+    A = si.activations_bf16(rng, M, K)
+    note(f"gemm_tiled q8_0 M={M} N={N} K={K} variant {variant}")
+    skg.gemm_tiled_set_variant(variant)
+    try:
+        Wp = skg.pack_weights(skg.Q8_0_BF16, N, K, dev(W))
+        y = poisoned((M, N))
+        skg.gemm_tiled(skg.Q8_0_BF16, M, K, N, Wp, dev(A), y)
+        yh = host(y)
+    finally:
+        skg.gemm_tiled_set_variant(-1)
+    assert np.all(np.isfinite(yh))
+    mrows = sample_rows(M, n=32, seed=8)
+    ncols = sample_rows(N, n=1024, seed=9) if N > 1024 else np.arange(N)
+    y_ref, bound, y_b = oracle.gemm_tiled_ref(W[ncols], A[mrows], "q8_0")
+    assert_close(yh[np.ix_(mrows, ncols)], y_ref, bound, "q8_0 tile vs exact weights")
+    assert_close(yh[np.ix_(mrows, ncols)], y_b, bound, "q8_0 tile vs bf16 weights", rel=1e-4)
