@@ -22,7 +22,8 @@ Sources (the four web pages this method is described on):
 * "Chapter 2.2 - speed - 64-lane Metal" (llama-3x-prompt-speed): the 64x64
   tiled prefill GEMM at M=512.
 * the RX 6700 XT Llama 2 7B decode write-up (austxu.dev):
-  Q4_0 x Q8_1 integer-dot matvec, fused QKV and gate/up + SwiGLU.
+  Q4_0 x Q8_1 integer-dot matvec, fused QKV and gate/up + SwiGLU, and the
+  RMSNorm-plus-scale that writes the Q8_1 activation directly.
 
 Pins: every function here is checked by the ``-m "not gpu"`` tests against
 hand-worked blocks (``tests/golden/``), closed forms, round-trip invariants and
@@ -51,6 +52,12 @@ from .quant import (  # noqa: F401
     quantize_q8_0,
     quantize_q4_0,
     round_half_away_f32,
+)
+from .norm import (  # noqa: F401
+    RMS_REL_TOL,
+    RMS_ABS_TOL,
+    rmsnorm,
+    rmsnorm_tolerance,
 )
 from .gemv import (  # noqa: F401
     REL_TOL,
