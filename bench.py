@@ -16,7 +16,9 @@ Times come from HIP events recorded on the stream the kernels run on.
 
 Further arms (same protocol, shorter): the streaming-read ceiling, q8_0 / q4_0
 x fp32 and q4_0 / q8_0 x Q8_1 at M=1..8 (K=4096, N=14336), the Llama-2-7B-shaped
-q4_0 x Q8_1 decode layer over 32 distinct layers, the q8_0 M=1 K=256 N=512
+q4_0 x Q8_1 decode layer over 32 distinct layers (plain, with the SwiGLU launch
+writing Q8_1, and with the layer's RMSNorm as its own launch or writing Q8_1
+itself), the fused RMSNorm -> Q8_1 launch alone, the q8_0 M=1 K=256 N=512
 launch-bound case, and the M=512 MFMA prefill tile.  The CPU oracle is timed
 on a bounded sample of the headline workload on this host's cores.
 
@@ -273,12 +275,28 @@ def bench_ceiling(skg, torch, timer, steps, warm_s):
     return res
 
 
-def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
+LAYER_MODES = {
+    # name suffix, launches per layer
+    "plain": ("", 5),
+    "q8_1_epilogue": ("_q8_1_epilogue", 4),
+    "norm_unfused": ("_rmsnorm_unfused", 6),
+    "norm_fused": ("_rmsnorm_fused", 4),
+}
+
+
+def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
     """Llama-2-7B-shaped q4_0 x Q8_1 decode layer, M=1, 32 distinct layers.
-    One step = one layer.  Plain form (5 launches): quantize(x) -> QKV (one
-    launch) -> gate/up + SwiGLU (one launch) -> quantize(h) -> down (K=11008).
-    Fused form (4 launches): the gate/up launch also writes the Q8_1 blocks of
-    h (the bits quantize(h) would write), so down reads them directly."""
+    One step = one layer.
+      plain (5 launches): quantize(x) -> QKV (one launch) -> gate/up + SwiGLU
+        (one launch) -> quantize(h) -> down (K=11008).
+      q8_1_epilogue (4): the gate/up launch also writes the Q8_1 blocks of h
+        (the bits quantize(h) would write), so down reads them directly.
+      norm_unfused (6): the layer's RMSNorm (per-layer gain) as its own launch
+        writing fp32, then quantize -> QKV -> gate/up + SwiGLU -> quantize(h)
+        -> down.
+      norm_fused (4): RMSNorm writes the Q8_1 blocks of its output itself,
+        then QKV -> gate/up + SwiGLU with Q8_1 output -> down."""
+    suffix, launches = LAYER_MODES[mode]
     D, F = 4096, 11008
     fmt = skg.Q4_0_Q8_1
     layers = []
@@ -286,12 +304,14 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
         q, k, v = (si.torch_weights("q4_0", D, D, 50_000 + 10 * l + j, "cuda") for j in range(3))
         g, u = (si.torch_weights("q4_0", F, D, 50_005 + 10 * l + j, "cuda") for j in range(2))
         d = si.torch_weights("q4_0", D, F, 50_009 + 10 * l, "cuda")
+        gain = torch.from_numpy(si.norm_gain_f32(si.rng_for(l, 3, 8), D)).cuda()
         layers.append((skg.pack_weights_multi(fmt, [D, D, D], D, [q, k, v]),
                        skg.pack_weights_multi(fmt, [F, F], D, [g, u]),
-                       skg.pack_weights(fmt, D, F, d)))
+                       skg.pack_weights(fmt, D, F, d), gain))
         del q, k, v, g, u, d
     torch.cuda.synchronize()
     x = torch.from_numpy(si.activations_f32(si.rng_for(0, 3, 7), 1, D)).cuda()
+    xn = torch.empty((1, D), dtype=torch.float32, device="cuda")
     xq = torch.empty((1, D // 32, 36), dtype=torch.uint8, device="cuda")
     yq, yk, yv = (torch.empty((1, D), dtype=torch.float32, device="cuda") for _ in range(3))
     h = torch.empty((1, F), dtype=torch.float32, device="cuda")
@@ -305,23 +325,40 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
     Y3 = (ctypes.c_void_p * 3)(yq.data_ptr(), yk.data_ptr(), yv.data_ptr())
     Y1 = (ctypes.c_void_p * 1)(h.data_ptr())
     Y2 = (ctypes.c_void_p * 2)(h.data_ptr(), hq.data_ptr())
-    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in layers]
-    xp, xqp, hp, hqp, yop = x.data_ptr(), xq.data_ptr(), h.data_ptr(), hq.data_ptr(), yo.data_ptr()
+    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), gn.data_ptr()) for a, b, c, gn in layers]
+    xp, xnp, xqp, hp, hqp, yop = x.data_ptr(), xn.data_ptr(), xq.data_ptr(), h.data_ptr(), hq.data_ptr(), yo.data_ptr()
+    eps = 1e-5
 
-    if fused:
+    if mode == "plain":
         def launch(i, sh):
-            pq, pg, pd = ptrs[i]
-            lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y2, skg.EPI_SWIGLU_Q8_1, sh)
-            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
-    else:
-        def launch(i, sh):
-            pq, pg, pd = ptrs[i]
+            pq, pg, pd, _ = ptrs[i]
             lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
             lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
             lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, skg.EPI_SWIGLU, sh)
             lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
+            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+    elif mode == "q8_1_epilogue":
+        def launch(i, sh):
+            pq, pg, pd, _ = ptrs[i]
+            lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y2, skg.EPI_SWIGLU_Q8_1, sh)
+            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+    elif mode == "norm_unfused":
+        def launch(i, sh):
+            pq, pg, pd, gp = ptrs[i]
+            lib.skg_rmsnorm_q8_1(1, D, xp, gp, eps, xnp, None, sh)
+            lib.skg_quantize_act_q8_1(1, D, xnp, xqp, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, skg.EPI_SWIGLU, sh)
+            lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
+            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+    else:
+        def launch(i, sh):
+            pq, pg, pd, gp = ptrs[i]
+            lib.skg_rmsnorm_q8_1(1, D, xp, gp, eps, None, xqp, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
+            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y2, skg.EPI_SWIGLU_Q8_1, sh)
             lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
 
     launch(0, sh)
@@ -331,14 +368,22 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
     res = timer.run(launch, 32, steps, 0, per_repeat=32, warm_s=warm_s)
     wbytes = (skg.packed_size_multi(fmt, [D, D, D], D) + skg.packed_size_multi(fmt, [F, F], D)
               + skg.packed_size(fmt, D, F))
-    if fused:
-        # quantize: x in, xq out; QKV and gate/up read xq; gate/up writes h and hq; down reads hq
-        alg = wbytes + 4 * D + 3 * (D // 32 * 36) + 4 * F + 2 * (F // 32 * 36) + 4 * (3 * D + D)
-    else:
+    xqb, hqb = D // 32 * 36, F // 32 * 36
+    outs = 4 * (3 * D + D)                       # q, k, v and the down projection's output
+    if mode == "plain":
         # quantisers read x and h (fp32) and write their Q8_1 blocks; products read the blocks
-        alg = wbytes + 2 * (D // 32 * 36) + 2 * (F // 32 * 36) + 4 * (3 * D + F + D) + 4 * (D + F)
-    res.update(name="llama2_7b_q4_0_q8_1_layer" + ("_q8_1_epilogue" if fused else ""), layers=32,
-               working_set_bytes=32 * wbytes, algorithmic_bytes=alg, launches_per_layer=4 if fused else 5)
+        alg = wbytes + 2 * xqb + 2 * hqb + 4 * F + outs + 4 * (D + F)
+    elif mode == "q8_1_epilogue":
+        # quantize: x in, xq out; QKV and gate/up read xq; gate/up writes h and hq; down reads hq
+        alg = wbytes + 4 * D + 3 * xqb + 4 * F + 2 * hqb + outs
+    elif mode == "norm_unfused":
+        # norm reads x and its gain and writes xn; quantize reads xn; then as plain
+        alg = wbytes + 4 * D * 4 + 3 * xqb + 4 * F * 2 + 2 * hqb + outs
+    else:
+        # norm reads x and its gain and writes xq; then as the Q8_1 epilogue form
+        alg = wbytes + 8 * D + 3 * xqb + 4 * F + 2 * hqb + outs
+    res.update(name="llama2_7b_q4_0_q8_1_layer" + suffix, layers=32,
+               working_set_bytes=32 * (wbytes + 4 * D), algorithmic_bytes=alg, launches_per_layer=launches)
     res["us_per_layer"] = res.pop("us_per_launch")
     res["gbs"] = alg / (res["us_per_layer"] * 1e-6) / 1e9
     res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
@@ -346,6 +391,30 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, fused=False):
     res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
     del layers
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_norm(skg, si, torch, timer, steps, warm_s, M=1, K=4096):
+    """The fused RMSNorm -> Q8_1 launch alone (M x K fp32 in, Q8_1 out), over
+    32 distinct inputs and gains.  Launch-bound: 2 x 16 KB in, 4.6 KB out."""
+    n = 32
+    xs = [torch.from_numpy(si.activations_f32(si.rng_for(i, 6, 10), M, K)).cuda() for i in range(n)]
+    gs = [torch.from_numpy(si.norm_gain_f32(si.rng_for(i, 6, 11), K)).cuda() for i in range(n)]
+    xq = torch.empty((M, K // 32, 36), dtype=torch.uint8, device="cuda")
+    lib = skg.lib
+    sh = torch.cuda.current_stream().cuda_stream
+    ptrs = [(a.data_ptr(), b.data_ptr()) for a, b in zip(xs, gs)]
+    qp = xq.data_ptr()
+
+    def launch(i, sh):
+        xp, gp = ptrs[i]
+        lib.skg_rmsnorm_q8_1(M, K, xp, gp, 1e-5, None, qp, sh)
+
+    skg.check(lib.skg_rmsnorm_q8_1(M, K, ptrs[0][0], ptrs[0][1], 1e-5, None, qp, sh))
+    torch.cuda.synchronize()
+    res = timer.run(launch, n, steps, 0, per_repeat=200, warm_s=warm_s)
+    res.update(name=f"rmsnorm_q8_1_m{M}_k{K}", algorithmic_bytes=4 * M * K + 4 * K + M * (K // 32) * 36)
+    res["graph"] = bench_graph(torch, launch, n, per_graph=200)
     return res
 
 
@@ -436,7 +505,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000, help="timed launches (repeats of 200)")
     ap.add_argument("--warmup", type=int, default=60000, help="untimed warm-up launches (~1 s)")
     ap.add_argument("--arms", default="all", help="all, none, or a comma list of: ceiling,q8_0,q4_0,q8_1,"
-                                                  "multi_m,layer,small,prefill")
+                                                  "multi_m,layer,small,norm,prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -462,7 +531,7 @@ def main():
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     timer = Timer(torch)
     arms = set() if args.arms == "none" else (
-        {"ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "prefill"} if args.arms == "all"
+        {"ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill"} if args.arms == "all"
         else set(args.arms.split(",")))
 
     # ---- headline: bf16 M=1 K=4096 N=12288 ----
@@ -500,9 +569,14 @@ def main():
                               short["steps"], 0, short["warm_s"], xh, graph=True)
         details["arms"][r["name"]] = r
         log(f"[{r['name']}] {r['us_per_launch']:.2f} us (graph {r['graph']['us_per_launch']:.2f} us)")
+    if "norm" in arms:
+        for M in (1, 8):
+            r = bench_norm(skg, si, torch, timer, short["steps"], short["warm_s"], M=M)
+            details["arms"][r["name"]] = r
+            log(f"[{r['name']}] {r['us_per_launch']:.2f} us (graph {r['graph']['us_per_launch']:.2f} us)")
     if "layer" in arms:
-        for fused in (False, True):
-            r = bench_layer(skg, si, torch, timer, 640, 0.3, fused=fused)
+        for mode in LAYER_MODES:
+            r = bench_layer(skg, si, torch, timer, 640, 0.3, mode=mode)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
                 f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")

@@ -139,6 +139,35 @@ skg_status skg_pack_weights_multi(skg_fmt fmt, int n, const int64_t* Ns, int64_t
 skg_status skg_quantize_act_q8_1(int64_t M, int64_t K, const float* x, void* xq, hipStream_t stream);
 
 /*
+ * RMSNorm with a per-channel gain, optionally writing its Q8_1 encoding in
+ * the same launch.
+ *
+ * The RX 6700 XT Llama 2 7B decode write-up (austxu.dev, Approach &
+ * Methodology) has the RMSNorm-plus-scale dispatch before a Q4_0 matvec write
+ * the Q8_1 activation that matvec reads, so no standalone quantisation
+ * dispatch runs; "Six hypotheses, four refutations" (Hypothesis ledger:
+ * fewer, longer kernels) counts the same fusion among its launch savings.
+ * Per row m, in IEEE binary32: ss = sum_k x[m][k]^2 (a fixed reduction order,
+ * so repeated calls give identical bits); r = 1 / sqrt(ss / K + eps);
+ * xn[m][k] = (x[m][k] * r) * g[k].  xq receives exactly
+ * skg_quantize_act_q8_1 of those xn values.
+ *
+ * x  : float32 [M][K] device, 16-byte aligned.
+ * g  : float32 [K] device, 16-byte aligned, or NULL for a gain of 1.
+ * eps: finite, >= 0.  With eps == 0 an all-zero row has no normalisation
+ *      (its outputs are NaN); a row whose sum of squares overflows binary32
+ *      is outside the domain.
+ * xn : float32 [M][K] device, 16-byte aligned, or NULL (not written).
+ * xq : [M][K/32] 36-byte Q8_1 blocks, device, 4-byte aligned, or NULL.
+ * At least one of xn and xq is given.  1 <= M <= 2^24; 32 <= K <= 16384,
+ * K % 32 == 0.  x must not overlap xn or xq.
+ * Errors: SKG_E_SHAPE (M, K), SKG_E_INVALID_ARG (null x, both outputs null,
+ * eps negative or not finite), SKG_E_ALIGN.
+ */
+skg_status skg_rmsnorm_q8_1(int64_t M, int64_t K, const float* x, const float* g, float eps, float* xn, void* xq,
+                            hipStream_t stream);
+
+/*
  * Skinny GEMM / GEMV: y[m][n] = sum_k W[n][k] x[m][k], 1 <= M <= 8.
  *
  * fmt   : SKG_BF16_BF16, SKG_Q8_0_F32, SKG_Q4_0_F32, SKG_Q4_0_Q8_1, SKG_Q8_0_Q8_1.

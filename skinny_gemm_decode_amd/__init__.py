@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "skg_packed_size_multi": (sz, [i32, i32, ctypes.POINTER(i64), i64]),
         "skg_pack_weights_multi": (i32, [i32, i32, ctypes.POINTER(i64), i64, ctypes.POINTER(vp), vp, vp]),
         "skg_quantize_act_q8_1": (i32, [i64, i64, vp, vp, vp]),
+        "skg_rmsnorm_q8_1": (i32, [i64, i64, vp, vp, ctypes.c_float, vp, vp, vp]),
         "skg_gemv": (i32, [i32, i64, i64, i64, vp, vp, vp, vp]),
         "skg_gemv_multi": (i32, [i32, i64, i64, i32, ctypes.POINTER(i64), vp, vp, ctypes.POINTER(vp), i32, vp]),
         "skg_gemm_tiled": (i32, [i32, i64, i64, i64, vp, vp, vp, vp]),
@@ -176,6 +177,36 @@ def quantize_act_q8_1(x, xq=None, stream=None):
         xq = torch.empty((M, K // 32, Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
     check(lib.skg_quantize_act_q8_1(M, K, _dev_ptr(x), _dev_ptr(xq), _stream(stream)))
     return xq
+
+
+def rmsnorm_q8_1(x, g=None, eps: float = 1e-5, xn=True, xq=True, stream=None):
+    """RMSNorm of float32 [M, K] rows with per-channel gain g (None: 1).
+
+    xn / xq: True to allocate the output, a tensor to write into, or
+    None / False to skip it (at least one is produced).  Returns (xn, xq):
+    float32 [M, K] and uint8 [M, K/32, 36] Q8_1 blocks of exactly xn.
+    """
+    import torch
+
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    M, K = x.shape
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 tensor")
+    if g is not None and (g.dtype != torch.float32 or not g.is_contiguous() or g.numel() != K):
+        raise ValueError("g must be a contiguous float32 tensor of K elements")
+    if xn is True:
+        xn = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    elif xn is False:
+        xn = None
+    if xq is True:
+        xq = torch.empty((M, K // 32, Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    elif xq is False:
+        xq = None
+    check(lib.skg_rmsnorm_q8_1(M, K, _dev_ptr(x), _dev_ptr(g) if g is not None else None, float(eps),
+                               _dev_ptr(xn) if xn is not None else None,
+                               _dev_ptr(xq) if xq is not None else None, _stream(stream)))
+    return xn, xq
 
 
 # ---- products -------------------------------------------------------------

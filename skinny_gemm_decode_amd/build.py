@@ -30,6 +30,7 @@ SOURCES = [
     "api.hip",
     "pack.hip",
     "quant.hip",
+    "norm.hip",
     "misc.hip",
     "gemm_tiled.hip",
     "gemv_bf16.hip",

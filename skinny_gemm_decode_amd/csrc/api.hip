@@ -3,6 +3,7 @@
 // the host before any HIP call, so every error path can be exercised without
 // a GPU; nothing falls back to another code path when validation fails.
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -364,6 +365,24 @@ skg_status skg_quantize_act_q8_1(int64_t M, int64_t K, const float* x, void* xq,
   if (st != SKG_OK) return st;
   hipError_t e = launch_quantize_q8_1(M, K, x, xq, stream);
   if (e != hipSuccess) return fail(SKG_E_HIP, "quantize: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_rmsnorm_q8_1(int64_t M, int64_t K, const float* x, const float* g, float eps, float* xn, void* xq,
+                            hipStream_t stream) {
+  if (M < 1 || M > kNormMaxM) return fail(SKG_E_SHAPE, "M must be in [1, %lld] (got %lld)", (long long)kNormMaxM, (long long)M);
+  if (K < 32 || K % 32 || K > kNormMaxK)
+    return fail(SKG_E_SHAPE, "K must be a multiple of 32 in [32, %lld] (got %lld)", (long long)kNormMaxK, (long long)K);
+  if (!x) return fail(SKG_E_INVALID_ARG, "null x");
+  if (!xn && !xq) return fail(SKG_E_INVALID_ARG, "at least one of xn and xq must be given");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(SKG_E_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(x, 16) || (g && !aligned(g, 16)) || (xn && !aligned(xn, 16)))
+    return fail(SKG_E_ALIGN, "x, g and xn must be 16-byte aligned");
+  if (xq && !aligned(xq, 4)) return fail(SKG_E_ALIGN, "xq must be 4-byte aligned");
+  skg_status st = check_device();
+  if (st != SKG_OK) return st;
+  hipError_t e = launch_rmsnorm_q8_1(M, K, x, g, eps, xn, xq, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "rmsnorm: %s", hipGetErrorString(e));
   return ok();
 }
 

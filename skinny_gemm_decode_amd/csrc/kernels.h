@@ -9,6 +9,11 @@ namespace skg {
 
 hipError_t launch_pack(int wk, int64_t N, int64_t K, const void* src, void* dst, hipStream_t stream);
 hipError_t launch_quantize_q8_1(int64_t M, int64_t K, const float* x, void* xq, hipStream_t stream);
+// RMSNorm (+ Q8_1 of its output): K <= kNormMaxK, K % 32 == 0, M <= kNormMaxM.
+constexpr int64_t kNormMaxK = 16384;
+constexpr int64_t kNormMaxM = int64_t(1) << 24;
+hipError_t launch_rmsnorm_q8_1(int64_t M, int64_t K, const float* x, const float* g, float eps, float* xn,
+                               void* xq, hipStream_t stream);
 hipError_t launch_block_dots(int fmt, const void* W, const Layout& L, int64_t n0, int64_t nr, const void* xq,
                              int32_t* out, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int grid, hipStream_t stream);

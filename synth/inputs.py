@@ -95,6 +95,22 @@ def activations_f32(rng: np.random.Generator, M: int, K: int) -> np.ndarray:
     return rng.normal(0.0, 1.0, size=(M, K)).astype(np.float32)
 
 
+def activations_f32_outliers(rng: np.random.Generator, M: int, K: int, channels: int = 8,
+                             scale: float = 40.0) -> np.ndarray:
+    """float32 [M, K] N(0, 1) with `channels` randomly chosen channels scaled by
+    `scale`: a residual stream with a few large channels, which RMSNorm inputs
+    have and the pages do not characterise further."""
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    cols = rng.choice(K, size=min(channels, K), replace=False)
+    x[:, cols] *= np.float32(scale)
+    return x
+
+
+def norm_gain_f32(rng: np.random.Generator, K: int) -> np.ndarray:
+    """float32 [K] per-channel RMSNorm gain drawn from N(1, 0.25)."""
+    return (1.0 + 0.25 * rng.standard_normal(K)).astype(np.float32)
+
+
 def activations_bf16(rng: np.random.Generator, M: int, K: int) -> np.ndarray:
     """uint16 [M, K] bf16 bit patterns of N(0, 1) values."""
     return _f32_to_bf16_bits(activations_f32(rng, M, K))

@@ -55,3 +55,12 @@ def assert_close(y, y_ref, bound, what: str, rel=oracle.REL_TOL, abs_=oracle.ABS
         raise AssertionError(f"{what}: worst err/tol = {worst:.3g} at {i}: y={np.asarray(y)[i]!r} "
                              f"ref={y_ref[i]!r} bound={bound[i]!r}")
     return worst
+
+
+def sample_rows(N, n=256, seed=0):
+    """Sorted output rows to check at full size: a seeded sample plus both ends
+    and the last 40 rows (the ragged tail of any row tiling)."""
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    rows |= {0, 1, N - 2, N - 1} | set(range(max(0, N - 40), N))
+    return np.array(sorted(r for r in rows if 0 <= r < N))

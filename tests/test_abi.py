@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["skg_pack_weights", "skg_pack_weights_multi", "skg_packed_size", "skg_packed_size_multi",
-                     "skg_quantize_act_q8_1", "skg_gemv", "skg_gemv_multi", "skg_gemm_tiled",
+                     "skg_quantize_act_q8_1", "skg_rmsnorm_q8_1", "skg_gemv", "skg_gemv_multi", "skg_gemm_tiled",
                      "skg_status_str", "skg_last_error", "skg_debug_block_dots", "skg_stream_read"]:
         assert required in names
 
@@ -132,6 +132,24 @@ def test_other_entry_point_errors(skg):
     assert L.skg_quantize_act_q8_1(1, 48, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_quantize_act_q8_1(1, 64, MISALIGNED, FAKE, None) == skg.E_ALIGN
     assert L.skg_quantize_act_q8_1(1, 64, FAKE, None, None) == skg.E_INVALID_ARG
+    nrm = L.skg_rmsnorm_q8_1
+    assert nrm(0, 4096, FAKE, FAKE, 1e-5, FAKE, FAKE, None) == skg.E_SHAPE            # M = 0
+    assert nrm((1 << 24) + 1, 4096, FAKE, FAKE, 1e-5, FAKE, FAKE, None) == skg.E_SHAPE
+    assert nrm(1, 48, FAKE, FAKE, 1e-5, FAKE, FAKE, None) == skg.E_SHAPE              # K % 32
+    assert nrm(1, 16416, FAKE, FAKE, 1e-5, FAKE, FAKE, None) == skg.E_SHAPE           # K > 16384
+    assert nrm(1, 0, FAKE, FAKE, 1e-5, FAKE, FAKE, None) == skg.E_SHAPE
+    assert nrm(1, 4096, None, FAKE, 1e-5, FAKE, FAKE, None) == skg.E_INVALID_ARG      # null x
+    assert nrm(1, 4096, FAKE, FAKE, 1e-5, None, None, None) == skg.E_INVALID_ARG      # no output
+    for eps in (-1e-5, float("nan"), float("inf")):
+        assert nrm(1, 4096, FAKE, FAKE, eps, FAKE, FAKE, None) == skg.E_INVALID_ARG
+    for args in ((MISALIGNED, FAKE, FAKE, FAKE), (FAKE, MISALIGNED, FAKE, FAKE),
+                 (FAKE, FAKE, MISALIGNED, FAKE), (FAKE, FAKE, FAKE, MISALIGNED)):
+        x, g, xn, xq = args
+        assert nrm(1, 4096, x, g, 1e-5, xn, xq, None) == skg.E_ALIGN
+    four = ctypes.c_void_p((1 << 20) + 4)                                          # 4- but not 16-byte aligned
+    for args in ((four, FAKE, FAKE, FAKE), (FAKE, four, FAKE, FAKE), (FAKE, FAKE, four, FAKE)):
+        x, g, xn, xq = args
+        assert nrm(1, 4096, x, g, 1e-5, xn, xq, None) == skg.E_ALIGN
     assert L.skg_gemm_tiled(2, 512, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED
     assert L.skg_gemm_tiled(5, 0, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_gemm_tiled(5, 512, 4100, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE

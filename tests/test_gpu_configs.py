@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from synth import inputs as si
-from tests._gpu import assert_close, dev, host, note, poisoned
+from tests._gpu import assert_close, dev, host, note, poisoned, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -17,13 +17,6 @@ pytestmark = pytest.mark.gpu
 def skg():
     import skinny_gemm_decode_amd as m
     return m
-
-
-def sample_rows(N, n=256, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(N, size=min(n, N), replace=False).tolist())
-    rows |= {0, 1, N - 2, N - 1} | set(range(max(0, N - 40), N))
-    return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
 def test_q8_0_m1_k256_n512(skg):

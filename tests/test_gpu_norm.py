@@ -1,0 +1,161 @@
+"""Parity of the fused RMSNorm -> Q8_1 dispatch with the oracle (GPU).
+
+xn is compared element by element with the float64 RMSNorm, within the
+binary32 bound the oracle states.  xq must be bit-identical to the oracle's
+Q8_1 quantiser applied to the xn the GPU stored: the integer decision is taken
+from the same binary32 values on both sides.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import inputs as si
+from tests._gpu import assert_close, dev, host, note, poisoned, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def skg():
+    import skinny_gemm_decode_amd as m
+    return m
+
+NORM_WORKLOAD = 6
+
+# Several 1024-element chunks per thread and ragged tails (K not a multiple of
+# 1024), one block (K = 32), the largest K, and a prefill-sized M.
+SHAPES = [(1, 4096), (2, 4096), (8, 4096), (1, 11008), (3, 32), (1, 1056), (5, 2080), (2, 16384), (512, 4096)]
+
+
+def _inputs(M, K, seed, outliers=False):
+    rng = si.rng_for(seed, NORM_WORKLOAD, 0)
+    x = si.activations_f32_outliers(rng, M, K) if outliers else si.activations_f32(rng, M, K)
+    g = si.norm_gain_f32(si.rng_for(seed, NORM_WORKLOAD, 1), K)
+    return x, g
+
+
+def _check_xn(xn, x, g, eps, what):
+    ref = oracle.rmsnorm(x, g, eps)
+    tol = oracle.rmsnorm_tolerance(ref)
+    err = np.abs(xn.astype(np.float64) - ref)
+    bad = ~(err <= tol)
+    if np.any(bad):
+        i = np.unravel_index(np.argmax(np.where(bad, err / tol, 0)), err.shape)
+        raise AssertionError(f"{what}: xn[{i}] = {xn[i]!r}, ref {ref[i]!r}, err/tol {err[i] / tol[i]:.3g}")
+
+
+def _check_xq(xq, xn, what):
+    expect = oracle.quantize_q8_1(xn)
+    if not np.array_equal(xq, expect):
+        m, b = np.argwhere(np.any(xq != expect, axis=2))[0]
+        raise AssertionError(f"{what}: Q8_1 block ({m}, {b}) differs from the quantiser of the stored xn")
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+@pytest.mark.parametrize("eps", [1e-5, 1e-6])
+def test_rmsnorm_q8_1_parity(skg, M, K, eps):
+    import torch
+    x, g = _inputs(M, K, seed=M * 7 + K)
+    note(f"rmsnorm_q8_1 M={M} K={K} eps={eps}")
+    # One extra row in each output stays poisoned: nothing past M is written.
+    xn_buf = poisoned((M + 1, K))
+    xq_buf = poisoned((M + 1, K // 32, 36), dtype=torch.uint8)
+    skg.rmsnorm_q8_1(dev(x), dev(g), eps, xn=xn_buf[:M], xq=xq_buf[:M])
+    xn_all, xq_all = host(xn_buf), host(xq_buf)
+    assert np.all(np.isnan(xn_all[M])) and np.all(xq_all[M] == 0xFF)
+    xn, xq = xn_all[:M], xq_all[:M]
+    _check_xn(xn, x, g, eps, f"M={M} K={K}")
+    _check_xq(xq, xn, f"M={M} K={K}")
+
+
+def test_outlier_channels(skg):
+    M, K = 4, 4096
+    x, g = _inputs(M, K, seed=5, outliers=True)
+    note("rmsnorm_q8_1 outlier channels")
+    xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g), 1e-5)
+    xn, xq = host(xn), host(xq)
+    _check_xn(xn, x, g, 1e-5, "outliers")
+    _check_xq(xq, xn, "outliers")
+
+
+def test_modes_and_repeats_give_identical_bits(skg):
+    """xn-only, xq-only and both-output calls, a gain of None and of ones, and
+    repeated calls all produce the same bits (one fixed reduction order)."""
+    import torch
+    M, K = 3, 11008
+    x, g = _inputs(M, K, seed=9)
+    xd, gd = dev(x), dev(g)
+    note("rmsnorm_q8_1 output modes")
+    xn_b, xq_b = skg.rmsnorm_q8_1(xd, gd, 1e-5)
+    xn_o, none_q = skg.rmsnorm_q8_1(xd, gd, 1e-5, xq=None)
+    none_n, xq_o = skg.rmsnorm_q8_1(xd, gd, 1e-5, xn=None)
+    assert none_q is None and none_n is None
+    xn_r, xq_r = skg.rmsnorm_q8_1(xd, gd, 1e-5)
+    for a, b in ((xn_b, xn_o), (xn_b, xn_r)):
+        assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+    for a, b in ((xq_b, xq_o), (xq_b, xq_r)):
+        assert np.array_equal(host(a), host(b))
+    xn_1, xq_1 = skg.rmsnorm_q8_1(xd, None, 1e-5)
+    xn_ones, xq_ones = skg.rmsnorm_q8_1(xd, torch.ones(K, dtype=torch.float32, device="cuda"), 1e-5)
+    assert np.array_equal(host(xn_1).view(np.uint32), host(xn_ones).view(np.uint32))
+    assert np.array_equal(host(xq_1), host(xq_ones))
+    _check_xn(host(xn_1), x, None, 1e-5, "no gain")
+    _check_xq(host(xq_1), host(xn_1), "no gain")
+
+
+def test_degenerate_rows(skg):
+    """An all-zero row (eps > 0) normalises to zeros and Q8_1 blocks with
+    d = s = 0; a constant row gives g * c / sqrt(c^2 + eps)."""
+    K = 1024
+    x = np.zeros((3, K), dtype=np.float32)
+    x[1] = np.float32(-2.0)
+    x[2] = si.activations_f32(si.rng_for(1, NORM_WORKLOAD, 2), 1, K)[0]
+    g = si.norm_gain_f32(si.rng_for(1, NORM_WORKLOAD, 3), K)
+    note("rmsnorm_q8_1 degenerate rows")
+    xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g), 5.0)
+    xn, xq = host(xn), host(xq)
+    assert not np.any(xn[0]) and not np.any(xq[0])
+    assert np.allclose(xn[1], g.astype(np.float64) * (-2.0 / 3.0), rtol=4e-6, atol=0)
+    _check_xn(xn, x, g, 5.0, "degenerate rows")
+    _check_xq(xq, xn, "degenerate rows")
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -60, 2.0 ** 40])
+def test_extreme_magnitudes_without_eps(skg, scale):
+    """With eps = 0 the result does not depend on the scale of the row, down
+    to squares near the binary32 normal range and up to sums near 2^100."""
+    M, K = 2, 4096
+    x, g = _inputs(M, K, seed=13)
+    xs = (x * np.float32(scale)).astype(np.float32)
+    note(f"rmsnorm_q8_1 scale {scale}")
+    xn, xq = skg.rmsnorm_q8_1(dev(xs), dev(g), 0.0)
+    xn, xq = host(xn), host(xq)
+    _check_xn(xn, xs, g, 0.0, f"scale {scale}")
+    _check_xq(xq, xn, f"scale {scale}")
+
+
+def test_fused_norm_feeds_q4_0_qkv(skg):
+    """The Llama-2-7B layer head with the norm fused: RMSNorm -> Q8_1 in one
+    launch, then the fused QKV product on those blocks.  Each stage is checked
+    on its own input: xq against the quantiser of the GPU's xn, QKV against the
+    oracle's integer-dot reference on the GPU's xq."""
+    D = 4096
+    rng = si.rng_for(0, 3, 0)
+    Wq, Wk, Wv = (si.q4_0_weights(rng, D, D) for _ in range(3))
+    x, g = _inputs(1, D, seed=17, outliers=True)
+    fmt = skg.Q4_0_Q8_1
+    note("fused norm -> qkv: pack")
+    Pqkv = skg.pack_weights_multi(fmt, [D, D, D], D, [dev(Wq), dev(Wk), dev(Wv)])
+    note("fused norm -> qkv: norm")
+    xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g), 1e-5)
+    xn_h, xq_h = host(xn), host(xq)
+    _check_xn(xn_h, x, g, 1e-5, "layer norm")
+    _check_xq(xq_h, xn_h, "layer norm")
+    note("fused norm -> qkv: products")
+    ys = [poisoned((1, D)) for _ in range(3)]
+    skg.gemv_multi(fmt, 1, D, [D, D, D], Pqkv, xq, ys)
+    rows = sample_rows(D, seed=21)
+    for name, W, y in zip("qkv", (Wq, Wk, Wv), ys):
+        y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(W[rows], xq_h)
+        assert_close(host(y)[:, rows], y_ref, bound, f"{name} after fused norm")
