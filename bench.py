@@ -281,6 +281,8 @@ LAYER_MODES = {
     "q8_1_epilogue": ("_q8_1_epilogue", 4),
     "norm_unfused": ("_rmsnorm_unfused", 6),
     "norm_fused": ("_rmsnorm_fused", 4),
+    "full_unfused": ("_full_rmsnorm_unfused", 10),
+    "full_fused": ("_full_rmsnorm_fused", 7),
 }
 
 
@@ -295,8 +297,15 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
         writing fp32, then quantize -> QKV -> gate/up + SwiGLU -> quantize(h)
         -> down.
       norm_fused (4): RMSNorm writes the Q8_1 blocks of its output itself,
-        then QKV -> gate/up + SwiGLU with Q8_1 output -> down."""
+        then QKV -> gate/up + SwiGLU with Q8_1 output -> down.
+      full_unfused (10) / full_fused (7): every weight product of the layer,
+        with the 4096 x 4096 attention-output projection O and both RMSNorms
+        (attention, then feed-forward).  Attention and the residual adds are
+        not part of the path: O reads the Q8_1 blocks of a fixed stand-in for
+        the attention output, quantised each layer, and the second norm reads
+        a fixed stand-in for the residual stream."""
     suffix, launches = LAYER_MODES[mode]
+    full = mode.startswith("full")
     D, F = 4096, 11008
     fmt = skg.Q4_0_Q8_1
     layers = []
@@ -304,16 +313,21 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
         q, k, v = (si.torch_weights("q4_0", D, D, 50_000 + 10 * l + j, "cuda") for j in range(3))
         g, u = (si.torch_weights("q4_0", F, D, 50_005 + 10 * l + j, "cuda") for j in range(2))
         d = si.torch_weights("q4_0", D, F, 50_009 + 10 * l, "cuda")
-        gain = torch.from_numpy(si.norm_gain_f32(si.rng_for(l, 3, 8), D)).cuda()
+        o = si.torch_weights("q4_0", D, D, 60_000 + l, "cuda") if full else None
+        gains = [torch.from_numpy(si.norm_gain_f32(si.rng_for(l, 3, 8 + j), D)).cuda() for j in range(2)]
         layers.append((skg.pack_weights_multi(fmt, [D, D, D], D, [q, k, v]),
                        skg.pack_weights_multi(fmt, [F, F], D, [g, u]),
-                       skg.pack_weights(fmt, D, F, d), gain))
-        del q, k, v, g, u, d
+                       skg.pack_weights(fmt, D, F, d),
+                       skg.pack_weights(fmt, D, D, o) if full else None, gains))
+        del q, k, v, g, u, d, o
     torch.cuda.synchronize()
     x = torch.from_numpy(si.activations_f32(si.rng_for(0, 3, 7), 1, D)).cuda()
+    x2 = torch.from_numpy(si.activations_f32(si.rng_for(0, 3, 10), 1, D)).cuda()
+    att = torch.from_numpy(si.activations_f32(si.rng_for(0, 3, 11), 1, D)).cuda()
     xn = torch.empty((1, D), dtype=torch.float32, device="cuda")
     xq = torch.empty((1, D // 32, 36), dtype=torch.uint8, device="cuda")
-    yq, yk, yv = (torch.empty((1, D), dtype=torch.float32, device="cuda") for _ in range(3))
+    aq = torch.empty((1, D // 32, 36), dtype=torch.uint8, device="cuda")
+    yq, yk, yv, ya = (torch.empty((1, D), dtype=torch.float32, device="cuda") for _ in range(4))
     h = torch.empty((1, F), dtype=torch.float32, device="cuda")
     hq = torch.empty((1, F // 32, 36), dtype=torch.uint8, device="cuda")
     yo = torch.empty((1, D), dtype=torch.float32, device="cuda")
@@ -325,65 +339,60 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
     Y3 = (ctypes.c_void_p * 3)(yq.data_ptr(), yk.data_ptr(), yv.data_ptr())
     Y1 = (ctypes.c_void_p * 1)(h.data_ptr())
     Y2 = (ctypes.c_void_p * 2)(h.data_ptr(), hq.data_ptr())
-    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), gn.data_ptr()) for a, b, c, gn in layers]
-    xp, xnp, xqp, hp, hqp, yop = x.data_ptr(), xn.data_ptr(), xq.data_ptr(), h.data_ptr(), hq.data_ptr(), yo.data_ptr()
+    ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr(), o.data_ptr() if o is not None else None,
+             [gn.data_ptr() for gn in gs]) for a, b, c, o, gs in layers]
+    xp, x2p, attp, xnp, xqp, aqp = (t.data_ptr() for t in (x, x2, att, xn, xq, aq))
+    hp, hqp, yop, yap = h.data_ptr(), hq.data_ptr(), yo.data_ptr(), ya.data_ptr()
     eps = 1e-5
+    xqb, hqb = D // 32 * 36, F // 32 * 36
 
-    if mode == "plain":
-        def launch(i, sh):
-            pq, pg, pd, _ = ptrs[i]
-            lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, skg.EPI_SWIGLU, sh)
-            lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
-            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
-    elif mode == "q8_1_epilogue":
-        def launch(i, sh):
-            pq, pg, pd, _ = ptrs[i]
-            lib.skg_quantize_act_q8_1(1, D, xp, xqp, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y2, skg.EPI_SWIGLU_Q8_1, sh)
-            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
-    elif mode == "norm_unfused":
-        def launch(i, sh):
-            pq, pg, pd, gp = ptrs[i]
-            lib.skg_rmsnorm_q8_1(1, D, xp, gp, eps, xnp, None, sh)
-            lib.skg_quantize_act_q8_1(1, D, xnp, xqp, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y1, skg.EPI_SWIGLU, sh)
-            lib.skg_quantize_act_q8_1(1, F, hp, hqp, sh)
-            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
-    else:
-        def launch(i, sh):
-            pq, pg, pd, gp = ptrs[i]
-            lib.skg_rmsnorm_q8_1(1, D, xp, gp, eps, None, xqp, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 3, N3, pq, xqp, Y3, 0, sh)
-            lib.skg_gemv_multi(fmt, 1, D, 2, N2, pg, xqp, Y2, skg.EPI_SWIGLU_Q8_1, sh)
-            lib.skg_gemv(fmt, 1, F, D, pd, hqp, yop, sh)
+    # Each step: (function of (layer, stream), algorithmic bytes read + written).
+    def quantize(src, dst, K, qb):
+        return (lambda i, s: lib.skg_quantize_act_q8_1(1, K, src, dst, s), 4 * K + qb)
+
+    def norm_fp32(src, j):
+        return (lambda i, s: lib.skg_rmsnorm_q8_1(1, D, src, ptrs[i][4][j], eps, xnp, None, s), 3 * 4 * D)
+
+    def norm_q8_1(src, j):
+        return (lambda i, s: lib.skg_rmsnorm_q8_1(1, D, src, ptrs[i][4][j], eps, None, xqp, s), 2 * 4 * D + xqb)
+
+    qkv = (lambda i, s: lib.skg_gemv_multi(fmt, 1, D, 3, N3, ptrs[i][0], xqp, Y3, 0, s), xqb + 3 * 4 * D)
+    swiglu = (lambda i, s: lib.skg_gemv_multi(fmt, 1, D, 2, N2, ptrs[i][1], xqp, Y1, skg.EPI_SWIGLU, s),
+              xqb + 4 * F)
+    swiglu_q = (lambda i, s: lib.skg_gemv_multi(fmt, 1, D, 2, N2, ptrs[i][1], xqp, Y2, skg.EPI_SWIGLU_Q8_1, s),
+                xqb + 4 * F + hqb)
+    down = (lambda i, s: lib.skg_gemv(fmt, 1, F, D, ptrs[i][2], hqp, yop, s), hqb + 4 * D)
+    oproj = (lambda i, s: lib.skg_gemv(fmt, 1, D, D, ptrs[i][3], aqp, yap, s), xqb + 4 * D)
+
+    chains = {
+        "plain": [quantize(xp, xqp, D, xqb), qkv, swiglu, quantize(hp, hqp, F, hqb), down],
+        "q8_1_epilogue": [quantize(xp, xqp, D, xqb), qkv, swiglu_q, down],
+        "norm_unfused": [norm_fp32(xp, 0), quantize(xnp, xqp, D, xqb), qkv, swiglu, quantize(hp, hqp, F, hqb), down],
+        "norm_fused": [norm_q8_1(xp, 0), qkv, swiglu_q, down],
+        "full_unfused": [norm_fp32(xp, 0), quantize(xnp, xqp, D, xqb), qkv, quantize(attp, aqp, D, xqb), oproj,
+                         norm_fp32(x2p, 1), quantize(xnp, xqp, D, xqb), swiglu, quantize(hp, hqp, F, hqb), down],
+        "full_fused": [norm_q8_1(xp, 0), qkv, quantize(attp, aqp, D, xqb), oproj, norm_q8_1(x2p, 1), swiglu_q,
+                       down],
+    }
+    chain = chains[mode]
+    assert len(chain) == launches
+    fns = [f for f, _ in chain]
+
+    def launch(i, sh):
+        for f in fns:
+            f(i, sh)
 
     launch(0, sh)
     torch.cuda.synchronize()
-    if not bool(torch.isfinite(yo).all()):
+    if not bool(torch.isfinite(yo).all()) or (full and not bool(torch.isfinite(ya).all())):
         raise RuntimeError("layer chain produced non-finite output")
     res = timer.run(launch, 32, steps, 0, per_repeat=32, warm_s=warm_s)
     wbytes = (skg.packed_size_multi(fmt, [D, D, D], D) + skg.packed_size_multi(fmt, [F, F], D)
-              + skg.packed_size(fmt, D, F))
-    xqb, hqb = D // 32 * 36, F // 32 * 36
-    outs = 4 * (3 * D + D)                       # q, k, v and the down projection's output
-    if mode == "plain":
-        # quantisers read x and h (fp32) and write their Q8_1 blocks; products read the blocks
-        alg = wbytes + 2 * xqb + 2 * hqb + 4 * F + outs + 4 * (D + F)
-    elif mode == "q8_1_epilogue":
-        # quantize: x in, xq out; QKV and gate/up read xq; gate/up writes h and hq; down reads hq
-        alg = wbytes + 4 * D + 3 * xqb + 4 * F + 2 * hqb + outs
-    elif mode == "norm_unfused":
-        # norm reads x and its gain and writes xn; quantize reads xn; then as plain
-        alg = wbytes + 4 * D * 4 + 3 * xqb + 4 * F * 2 + 2 * hqb + outs
-    else:
-        # norm reads x and its gain and writes xq; then as the Q8_1 epilogue form
-        alg = wbytes + 8 * D + 3 * xqb + 4 * F + 2 * hqb + outs
+              + skg.packed_size(fmt, D, F) + (skg.packed_size(fmt, D, D) if full else 0))
+    alg = wbytes + sum(b for _, b in chain)
     res.update(name="llama2_7b_q4_0_q8_1_layer" + suffix, layers=32,
-               working_set_bytes=32 * (wbytes + 4 * D), algorithmic_bytes=alg, launches_per_layer=launches)
+               working_set_bytes=32 * (wbytes + 2 * 4 * D), weight_bytes_per_layer=wbytes,
+               algorithmic_bytes=alg, launches_per_layer=launches)
     res["us_per_layer"] = res.pop("us_per_launch")
     res["gbs"] = alg / (res["us_per_layer"] * 1e-6) / 1e9
     res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS

@@ -135,27 +135,67 @@ def test_extreme_magnitudes_without_eps(skg, scale):
     _check_xq(xq, xn, f"scale {scale}")
 
 
-def test_fused_norm_feeds_q4_0_qkv(skg):
-    """The Llama-2-7B layer head with the norm fused: RMSNorm -> Q8_1 in one
-    launch, then the fused QKV product on those blocks.  Each stage is checked
-    on its own input: xq against the quantiser of the GPU's xn, QKV against the
-    oracle's integer-dot reference on the GPU's xq."""
-    D = 4096
+def test_full_layer_with_fused_norms(skg):
+    """Every weight product of a Llama-2-7B-shaped layer with both norms fused
+    into Q8_1 producers: norm -> QKV; quantize(attention output) -> O;
+    norm -> gate/up + SwiGLU with Q8_1 output -> down.  Each stage is checked
+    on its own input: Q8_1 blocks bit-exactly against the quantiser of the
+    values the GPU stored, products against the oracle's integer-dot reference
+    on the GPU's blocks.  Attention and the residual adds are not part of the
+    path; seeded stand-ins take their place."""
+    D, F = 4096, 11008
     rng = si.rng_for(0, 3, 0)
-    Wq, Wk, Wv = (si.q4_0_weights(rng, D, D) for _ in range(3))
-    x, g = _inputs(1, D, seed=17, outliers=True)
+    Wq, Wk, Wv, Wo = (si.q4_0_weights(rng, D, D) for _ in range(4))
+    Wg, Wu = si.q4_0_weights(rng, F, D), si.q4_0_weights(rng, F, D)
+    Wd = si.q4_0_weights(rng, D, F)
+    x, g1 = _inputs(1, D, seed=17, outliers=True)
+    x2, g2 = _inputs(1, D, seed=18)
+    att = si.activations_f32(si.rng_for(19, NORM_WORKLOAD, 4), 1, D)
     fmt = skg.Q4_0_Q8_1
-    note("fused norm -> qkv: pack")
+    note("full layer: pack")
     Pqkv = skg.pack_weights_multi(fmt, [D, D, D], D, [dev(Wq), dev(Wk), dev(Wv)])
-    note("fused norm -> qkv: norm")
-    xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g), 1e-5)
+    Po = skg.pack_weights(fmt, D, D, dev(Wo))
+    Pgu = skg.pack_weights_multi(fmt, [F, F], D, [dev(Wg), dev(Wu)])
+    Pd = skg.pack_weights(fmt, D, F, dev(Wd))
+    rows = sample_rows(D, seed=21)
+    frows = sample_rows(F, seed=22)
+
+    note("full layer: attention norm -> qkv")
+    xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g1), 1e-5)
     xn_h, xq_h = host(xn), host(xq)
-    _check_xn(xn_h, x, g, 1e-5, "layer norm")
-    _check_xq(xq_h, xn_h, "layer norm")
-    note("fused norm -> qkv: products")
+    _check_xn(xn_h, x, g1, 1e-5, "attention norm")
+    _check_xq(xq_h, xn_h, "attention norm")
     ys = [poisoned((1, D)) for _ in range(3)]
     skg.gemv_multi(fmt, 1, D, [D, D, D], Pqkv, xq, ys)
-    rows = sample_rows(D, seed=21)
     for name, W, y in zip("qkv", (Wq, Wk, Wv), ys):
         y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(W[rows], xq_h)
         assert_close(host(y)[:, rows], y_ref, bound, f"{name} after fused norm")
+
+    note("full layer: attention output projection")
+    aq = skg.quantize_act_q8_1(dev(att))
+    aq_ref = oracle.quantize_q8_1(att)
+    assert np.array_equal(host(aq), aq_ref)
+    yo = poisoned((1, D))
+    skg.gemv(fmt, 1, D, D, Po, aq, yo)
+    y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(Wo[rows], aq_ref)
+    assert_close(host(yo)[:, rows], y_ref, bound, "O projection")
+
+    note("full layer: feed-forward norm -> gate/up + SwiGLU (Q8_1 out)")
+    xn2, xq2 = skg.rmsnorm_q8_1(dev(x2), dev(g2), 1e-5)
+    xn2_h, xq2_h = host(xn2), host(xq2)
+    _check_xn(xn2_h, x2, g2, 1e-5, "feed-forward norm")
+    _check_xq(xq2_h, xn2_h, "feed-forward norm")
+    h, hq = skg.gemv_multi(fmt, 1, D, [F, F], Pgu, xq2, epi=skg.EPI_SWIGLU_Q8_1)
+    h_h, hq_h = host(h), host(hq)
+    g_ref, _, bg = oracle.gemv_q4_0_q8_1_ref(Wg[frows], xq2_h)
+    u_ref, _, bu = oracle.gemv_q4_0_q8_1_ref(Wu[frows], xq2_h)
+    tol = oracle.swiglu_tolerance(g_ref, u_ref, oracle.tolerance(bg), oracle.tolerance(bu))
+    ok, worst = oracle.check_close(h_h[:, frows], oracle.swiglu_ref(g_ref, u_ref), tol)
+    assert ok, f"swiglu worst {worst}"
+    assert np.array_equal(hq_h.reshape(1, F // 32, 36), oracle.quantize_q8_1(h_h))
+
+    note("full layer: down projection")
+    yd = poisoned((1, D))
+    skg.gemv(fmt, 1, F, D, Pd, hq, yd)
+    y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(Wd[rows], hq_h.reshape(1, F // 32, 36))
+    assert_close(host(yd)[:, rows], y_ref, bound, "down projection")
