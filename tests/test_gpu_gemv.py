@@ -12,6 +12,7 @@ import pytest
 import oracle
 from synth import inputs as si
 from tests._gpu import assert_close, dev, host, note, poisoned
+from tests._q8_1_check import q8_1_violations
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +190,10 @@ def test_swiglu_q8_1_epilogue(skg, fmt, M):
     ok, worst = oracle.check_close(host(h), oracle.swiglu_ref(g_ref, u_ref), tol)
     assert ok, f"swiglu worst {worst}"
     assert_q8_1_of(host(hq), host(h), "epilogue")
+    # and, with no GPU value as oracle input: valid Q8_1 of values within the
+    # SwiGLU tolerance of the oracle's h
+    bad = q8_1_violations(host(hq).reshape(M, N // 32, 36), oracle.swiglu_ref(g_ref, u_ref), tol)
+    assert not bad, "; ".join(bad[:3])
     Wdp = skg.pack_weights(fmt, 96, N, dev(Wd))
     ya, yb = poisoned((M, 96)), poisoned((M, 96))
     skg.gemv(fmt, M, N, 96, Wdp, hq, ya)

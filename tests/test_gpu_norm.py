@@ -12,6 +12,7 @@ import pytest
 import oracle
 from synth import inputs as si
 from tests._gpu import assert_close, dev, host, note, poisoned, sample_rows
+from tests._q8_1_check import q8_1_violations
 
 pytestmark = pytest.mark.gpu
 
@@ -45,11 +46,19 @@ def _check_xn(xn, x, g, eps, what):
         raise AssertionError(f"{what}: xn[{i}] = {xn[i]!r}, ref {ref[i]!r}, err/tol {err[i] / tol[i]:.3g}")
 
 
-def _check_xq(xq, xn, what):
+def _check_xq(xq, xn, what, x=None, g=None, eps=None):
+    """Bit-exact against the quantiser of the stored xn (the stage check) and,
+    when the inputs are given, valid Q8_1 of values within the norm's
+    tolerance of the float64 reference (a check with no GPU value as oracle
+    input)."""
     expect = oracle.quantize_q8_1(xn)
     if not np.array_equal(xq, expect):
         m, b = np.argwhere(np.any(xq != expect, axis=2))[0]
         raise AssertionError(f"{what}: Q8_1 block ({m}, {b}) differs from the quantiser of the stored xn")
+    if x is not None:
+        ref = oracle.rmsnorm(x, g, eps)
+        bad = q8_1_violations(xq, ref, oracle.rmsnorm_tolerance(ref))
+        assert not bad, f"{what}: " + "; ".join(bad[:3])
 
 
 @pytest.mark.parametrize("M,K", SHAPES)
@@ -66,7 +75,7 @@ def test_rmsnorm_q8_1_parity(skg, M, K, eps):
     assert np.all(np.isnan(xn_all[M])) and np.all(xq_all[M] == 0xFF)
     xn, xq = xn_all[:M], xq_all[:M]
     _check_xn(xn, x, g, eps, f"M={M} K={K}")
-    _check_xq(xq, xn, f"M={M} K={K}")
+    _check_xq(xq, xn, f"M={M} K={K}", x, g, eps)
 
 
 def test_outlier_channels(skg):
@@ -76,7 +85,7 @@ def test_outlier_channels(skg):
     xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g), 1e-5)
     xn, xq = host(xn), host(xq)
     _check_xn(xn, x, g, 1e-5, "outliers")
-    _check_xq(xq, xn, "outliers")
+    _check_xq(xq, xn, "outliers", x, g, 1e-5)
 
 
 def test_modes_and_repeats_give_identical_bits(skg):
@@ -101,7 +110,7 @@ def test_modes_and_repeats_give_identical_bits(skg):
     assert np.array_equal(host(xn_1).view(np.uint32), host(xn_ones).view(np.uint32))
     assert np.array_equal(host(xq_1), host(xq_ones))
     _check_xn(host(xn_1), x, None, 1e-5, "no gain")
-    _check_xq(host(xq_1), host(xn_1), "no gain")
+    _check_xq(host(xq_1), host(xn_1), "no gain", x, None, 1e-5)
 
 
 def test_degenerate_rows(skg):
@@ -118,7 +127,7 @@ def test_degenerate_rows(skg):
     assert not np.any(xn[0]) and not np.any(xq[0])
     assert np.allclose(xn[1], g.astype(np.float64) * (-2.0 / 3.0), rtol=4e-6, atol=0)
     _check_xn(xn, x, g, 5.0, "degenerate rows")
-    _check_xq(xq, xn, "degenerate rows")
+    _check_xq(xq, xn, "degenerate rows", x, g, 5.0)
 
 
 @pytest.mark.parametrize("scale", [2.0 ** -60, 2.0 ** 40])
@@ -132,7 +141,7 @@ def test_extreme_magnitudes_without_eps(skg, scale):
     xn, xq = skg.rmsnorm_q8_1(dev(xs), dev(g), 0.0)
     xn, xq = host(xn), host(xq)
     _check_xn(xn, xs, g, 0.0, f"scale {scale}")
-    _check_xq(xq, xn, f"scale {scale}")
+    _check_xq(xq, xn, f"scale {scale}", xs, g, 0.0)
 
 
 def test_full_layer_with_fused_norms(skg):
@@ -164,7 +173,7 @@ def test_full_layer_with_fused_norms(skg):
     xn, xq = skg.rmsnorm_q8_1(dev(x), dev(g1), 1e-5)
     xn_h, xq_h = host(xn), host(xq)
     _check_xn(xn_h, x, g1, 1e-5, "attention norm")
-    _check_xq(xq_h, xn_h, "attention norm")
+    _check_xq(xq_h, xn_h, "attention norm", x, g1, 1e-5)
     ys = [poisoned((1, D)) for _ in range(3)]
     skg.gemv_multi(fmt, 1, D, [D, D, D], Pqkv, xq, ys)
     for name, W, y in zip("qkv", (Wq, Wk, Wv), ys):
@@ -184,7 +193,7 @@ def test_full_layer_with_fused_norms(skg):
     xn2, xq2 = skg.rmsnorm_q8_1(dev(x2), dev(g2), 1e-5)
     xn2_h, xq2_h = host(xn2), host(xq2)
     _check_xn(xn2_h, x2, g2, 1e-5, "feed-forward norm")
-    _check_xq(xq2_h, xn2_h, "feed-forward norm")
+    _check_xq(xq2_h, xn2_h, "feed-forward norm", x2, g2, 1e-5)
     h, hq = skg.gemv_multi(fmt, 1, D, [F, F], Pgu, xq2, epi=skg.EPI_SWIGLU_Q8_1)
     h_h, hq_h = host(h), host(hq)
     g_ref, _, bg = oracle.gemv_q4_0_q8_1_ref(Wg[frows], xq2_h)

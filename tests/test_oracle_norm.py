@@ -128,3 +128,35 @@ def test_rejects_bad_inputs():
     x[3] = np.inf
     with pytest.raises(ValueError):
         oracle.rmsnorm(x)
+
+
+def test_q8_1_validity_check_accepts_the_quantiser_and_rejects_slips():
+    """The no-GPU-input Q8_1 check used on the fused norm: it accepts the
+    oracle's quantisation of the binary32-rounded reference and rejects a code
+    moved by one, a wrong block sum and a block that misses the full range."""
+    from tests._q8_1_check import q8_1_violations
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 1024)).astype(np.float32)
+    g = (1 + 0.25 * rng.standard_normal(1024)).astype(np.float32)
+    ref = oracle.rmsnorm(x, g, 1e-5)
+    tol = oracle.rmsnorm_tolerance(ref)
+    xq = oracle.quantize_q8_1(ref.astype(np.float32))
+    assert q8_1_violations(xq, ref, tol) == []
+    # one code moved by one: pick the element with the smallest residual
+    d, _, q = oracle.q8_1_fields(xq)
+    resid = np.abs(d[..., None] * q - ref.reshape(3, 32, 32))
+    m, b, i = np.unravel_index(np.argmin(np.where(np.abs(q) < 120, resid, np.inf)), resid.shape)
+    bad = xq.copy()
+    bad[m, b, 4 + i] = np.uint8((int(q[m, b, i]) + 1) & 0xFF)
+    assert q8_1_violations(bad, ref, tol)
+    # block sum off by a few fp16 ulps
+    bad = xq.copy()
+    s = int(bad[1, 5, 2]) | (int(bad[1, 5, 3]) << 8)
+    s += 8
+    bad[1, 5, 2], bad[1, 5, 3] = s & 0xFF, s >> 8
+    assert q8_1_violations(bad, ref, tol)
+    # a block whose codes were all halved (scale doubled) misses the full range
+    bad = xq.copy()
+    qq = bad[2, 7, 4:].view(np.int8).astype(int) // 2
+    bad[2, 7, 4:] = (qq & 0xFF).astype(np.uint8)
+    assert q8_1_violations(bad, ref, tol)
