@@ -1,0 +1,99 @@
+"""Host-side tooling of the measurement (CPU only): the bench's contract
+checks, its rotation sizing and repeat statistics, the gating of the counter
+traffic by the GEMV sources, and the rocprofv3 summaries on synthetic CSVs."""
+
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from skinny_gemm_decode_amd import rocprof_summary as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("nbytes", [139_264, 33_030_144, 62_390_272, 100_663_296, 3 * 10**9])
+def test_rotation_covers_two_gigabytes(nbytes):
+    n = bench.rotation_count(nbytes)
+    assert n >= 1
+    assert n * nbytes >= 2 * 1000**3 or n == 1
+    assert (n - 1) * nbytes < 2 * 1000**3
+
+
+def test_summarize_spread_and_gate():
+    r = bench.summarize([10.0, 10.2, 9.8, 10.0], total_ms=8.0, steps=800)
+    assert r["us_per_launch"] == pytest.approx(10.0)
+    assert r["spread"] == pytest.approx(0.4 / 10.0)
+    assert r["spread_ok"]
+    assert not bench.summarize([10.0, 11.0], 2.1, 200)["spread_ok"]
+
+
+def test_counter_traffic_is_gated_by_the_gemv_sources(tmp_path, monkeypatch):
+    good = tmp_path / "good.md"
+    good.write_text(f"x\n    traffic_bytes_per_launch: 123456\n    gemv_source_sha256: {rs.gemv_source_hash()}\n")
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(good))
+    assert bench.counter_traffic() == 123456
+    stale = tmp_path / "stale.md"
+    stale.write_text("    traffic_bytes_per_launch: 123456\n    gemv_source_sha256: " + "0" * 64 + "\n")
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(stale))
+    assert bench.counter_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "missing.md"))
+    assert bench.counter_traffic() is None
+
+
+def _counter_csv(path, rows):
+    path.mkdir(parents=True, exist_ok=True)
+    with open(path / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow([i, k, c, v])
+
+
+def test_traffic_md_scales_by_the_copy(tmp_path):
+    gemv = "void skg::gemv_kernel<0, 1, 2, 1, false, 8, 0, 8>(skg::GemvArgs)"
+    read = "skg::stream_read_kernel(uint4 const*, long, unsigned int, unsigned int*)"
+    copy = "__amd_rocclr_copyBuffer"
+    mib256 = (1 << 28) / 1024.0
+    # FETCH reads half the bytes (x2 scale), WRITE exact; a smaller copy must not set the scale
+    _counter_csv(tmp_path / "f", [(gemv, "FETCH_SIZE", 49000.0), (gemv, "FETCH_SIZE", 49400.0),
+                                  (read, "FETCH_SIZE", 49100.0), (copy, "FETCH_SIZE", 10.0),
+                                  (copy, "FETCH_SIZE", mib256 / 2)])
+    _counter_csv(tmp_path / "w", [(gemv, "WRITE_SIZE", 192.0), (copy, "WRITE_SIZE", 5.0),
+                                  (copy, "WRITE_SIZE", mib256)])
+    md = rs.traffic_md(str(tmp_path / "f"), str(tmp_path / "w"))
+    expect = int(round((49200.0 * 2.0 + 192.0) * 1024))
+    assert f"traffic_bytes_per_launch: {expect}" in md
+    assert "FETCH_SIZE is scaled by 2.0000 and WRITE_SIZE by 1.0000" in md
+    assert f"gemv_source_sha256: {rs.gemv_source_hash()}" in md
+
+
+def test_trace_and_counter_tables_keep_only_library_kernels(tmp_path):
+    d = tmp_path / "t"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"])
+        w.writerow(["void skg::gemv_kernel<0, 1>(skg::GemvArgs)", 10, 157000, 15700, 90, 15000, 16500, 1])
+        w.writerow(["at::native::elementwise_kernel<...>(...)", 5, 5000, 1000, 10, 900, 1100, 1])
+    md = rs.trace_md(str(d), "T", "cmd --x")
+    assert "| `void skg::gemv_kernel<0, 1>` | 10 | 15.700 | 15.000 | 16.500 |" in md
+    assert "elementwise" not in md and "    cmd --x" in md
+    _counter_csv(tmp_path / "c1", [("skg::quantize_q8_1_kernel(float const*)", "SQ_WAVES", 4.0),
+                                   ("skg::quantize_q8_1_kernel(float const*)", "SQ_WAVES", 6.0),
+                                   ("at::native::foo", "SQ_WAVES", 1.0)])
+    _counter_csv(tmp_path / "c2", [("skg::quantize_q8_1_kernel(float const*)", "SQ_BUSY_CYCLES", 100.0)])
+    md = rs.counters_md("C", "a ;; b", [str(tmp_path / "c1"), str(tmp_path / "c2")])
+    assert "| kernel | dispatches | SQ_BUSY_CYCLES | SQ_WAVES |" in md
+    assert "| `skg::quantize_q8_1_kernel` | 2 | 100 | 5 |" in md
+    assert "    a\n    b" in md and "foo" not in md
