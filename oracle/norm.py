@@ -26,10 +26,10 @@ import numpy as np
 
 # Tolerance of a binary32 evaluation against the float64 definition, per
 # element: xn = (x * r) * g with r = 1 / sqrt(ss / K + eps).  A binary32 sum of
-# squares whose longest chain of dependent additions has depth D is off by at
-# most about D * u relatively (u = 2^-24); r inherits half of that plus one
+# (positive) squares whose longest chain of dependent additions has depth D is
+# off by at most D * u relatively (u = 2^-24); r inherits half of that plus one
 # rounding each for / K, + eps, sqrt and 1 / (4 u), and the two products add
-# 2 u.  For D <= 64 that is 32 u + 6 u = 38 u ~ 2.3e-6; the gate is 4e-6 of
+# 2 u.  For D <= 80 that is 40 u + 6 u = 46 u ~ 2.7e-6; the gate is 4e-6 of
 # |xn| plus an absolute floor for zero and underflowing outputs.
 RMS_REL_TOL = 4e-6
 RMS_ABS_TOL = 1e-30
