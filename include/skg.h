@@ -107,8 +107,9 @@ const char* skg_last_error(void);
  * loads.  The packed layout is opaque and versioned by skg_packed_size.
  *
  * skg_packed_size: bytes of the packed buffer for an N x K matrix of the
- *   weight format of `fmt`, or 0 if (fmt, N, K) is invalid.  N >= 1; K >= 32
- *   and K % 32 == 0 for q8_0/q4_0, K >= 8 and K % 8 == 0 for bf16.
+ *   weight format of `fmt`, or 0 if (fmt, N, K) is invalid.  1 <= N <=
+ *   2^31 - 1; K <= 2^30 and K >= 32, K % 32 == 0 for q8_0/q4_0, K >= 8 and
+ *   K % 8 == 0 for bf16.
  * skg_pack_weights: src = canonical N x K weights (device, 2-byte aligned),
  *   dst = packed buffer of skg_packed_size bytes (device, 256-byte aligned).
  *   src and dst must not overlap.
@@ -225,7 +226,9 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
  * x   : bf16 [M][K] device, 16-byte aligned.  y : float32 [M][N], overwritten.
  * Weights are decoded to bf16 (w = bf16_rne(d * (c - 8)) for q4_0,
  * bf16_rne(d * q) for q8_0) and multiplied on bf16 MFMA with fp32
- * accumulation.  M >= 1, N >= 1, K % 32 == 0.  q8_0 weights run on the
+ * accumulation.  1 <= M <= 2^31 - 1, N >= 1, K % 32 == 0, and the output
+ * must fit one launch: ceil(M / 256) * ceil(N / 112) <= 2^31 - 1 (else
+ * SKG_E_SHAPE).  q8_0 weights run on the
  * pipelined organisations (skg_gemm_tiled_set_variant 3 or 4); with another
  * organisation selected a q8_0 call returns SKG_E_UNSUPPORTED.
  */

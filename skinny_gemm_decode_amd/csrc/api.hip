@@ -3,6 +3,7 @@
 // the host before any HIP call, so every error path can be exercised without
 // a GPU; nothing falls back to another code path when validation fails.
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -73,7 +74,7 @@ skg_status check_nk(int fmt, int64_t N, int64_t K) {
   } else {
     if (K < 32 || K % 32) return fail(SKG_E_SHAPE, "q8_0/q4_0 need K >= 32 and K %% 32 == 0 (got %lld)", (long long)K);
   }
-  if (K > (int64_t(1) << 30) || N > (int64_t(1) << 31))
+  if (K > (int64_t(1) << 30) || N > INT32_MAX)
     return fail(SKG_E_SHAPE, "N=%lld K=%lld exceed the supported range", (long long)N, (long long)K);
   return SKG_OK;
 }
@@ -150,6 +151,23 @@ int blocks_per_cu(const void* fn, int threads, size_t lds) {
   return n;
 }
 
+// Raises a kernel's dynamic LDS limit once per (device, kernel) instead of on
+// every launch.
+hipError_t ensure_dynamic_lds(const void* fn, size_t lds) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<std::tuple<int, const void*, size_t>> done;
+  std::lock_guard<std::mutex> lk(mu);
+  for (auto& d : done)
+    if (std::get<0>(d) == dev && std::get<1>(d) == fn && std::get<2>(d) >= lds) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e == hipSuccess) done.emplace_back(dev, fn, lds);
+  return e;
+}
+
 skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64_t* Ns, const void* W,
                             const void* x, float* const* ys, int epi, hipStream_t stream) {
   const int wk = wkind_of(v.fmt);
@@ -189,10 +207,8 @@ skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64
   if (st != SKG_OK) return st;
   const int threads = int(a.nb / uint32_t(v.kw)) * 64;
   const size_t lds = size_t(v.lds);  // dynamic LDS (the LDS-ring variant's is static)
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-  }
+  if (hipError_t e = ensure_dynamic_lds(v.fn, lds); e != hipSuccess)
+    return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   const int64_t resident = int64_t(cus) * blocks_per_cu(v.fn, threads, lds);
   // As many passes over the resident workgroups as the tiles need, with the
   // tiles spread evenly over them (896 tiles on 512 resident workgroups:
@@ -263,10 +279,8 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
   if (blocks > 0x7FFFFFFF) return fail(SKG_E_SHAPE, "too many rows");
   size_t lds = gemv_lds_bytes(fmt, int(M), v->j, v->xlds) + size_t(g_lds_pad.load());
   if (lds > 160 * 1024) return fail(SKG_E_UNSUPPORTED, "variant needs %zu bytes of LDS", lds);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
-  }
+  if (hipError_t e = ensure_dynamic_lds(v->fn, lds); e != hipSuccess)
+    return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(v->fn, dim3(unsigned(blocks)), dim3(unsigned(v->waves * 64)), args, lds, stream);
   if (e != hipSuccess) return fail(SKG_E_HIP, "gemv launch: %s", hipGetErrorString(e));
@@ -431,11 +445,16 @@ skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const vo
   if (!is_any_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown fmt %d", int(fmt));
   if (fmt != SKG_Q4_0_BF16 && fmt != SKG_Q8_0_BF16)
     return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16 and SKG_Q8_0_BF16");
-  if (fmt == SKG_Q8_0_BF16 && g_gemm_variant != 3 && g_gemm_variant != 4)
-    return fail(SKG_E_UNSUPPORTED, "q8_0 tiles run on prefill organisations 3 and 4 (selected: %d)", g_gemm_variant);
+  const int variant = g_gemm_variant.load(std::memory_order_relaxed);
+  if (fmt == SKG_Q8_0_BF16 && variant != 3 && variant != 4)
+    return fail(SKG_E_UNSUPPORTED, "q8_0 tiles run on prefill organisations 3 and 4 (selected: %d)", variant);
   skg_status st = check_nk(fmt, N, K);
   if (st != SKG_OK) return st;
-  if (M < 1 || M > (int64_t(1) << 31)) return fail(SKG_E_SHAPE, "M must be >= 1 (got %lld)", (long long)M);
+  if (M < 1 || M > INT32_MAX) return fail(SKG_E_SHAPE, "M must be in [1, 2^31 - 1] (got %lld)", (long long)M);
+  // one workgroup per 256 x 112 (or 256 x 128) output tile, in a 1-D grid
+  if (((M + 255) / 256) * ((N + 111) / 112) > INT32_MAX)
+    return fail(SKG_E_SHAPE, "M=%lld x N=%lld needs more output tiles than one launch takes", (long long)M,
+                (long long)N);
   if (!W || !x || !y) return fail(SKG_E_INVALID_ARG, "null W, x or y");
   if (!aligned(W, 16) || !aligned(x, 16)) return fail(SKG_E_ALIGN, "W and x must be 16-byte aligned");
   if (!aligned(y, 4)) return fail(SKG_E_ALIGN, "y must be 4-byte aligned");
@@ -522,7 +541,7 @@ int skg_gemv_variants(int* out, int max_entries) {
 
 skg_status skg_gemm_tiled_set_variant(int variant) {
   if (variant < -1 || variant > 4) return fail(SKG_E_INVALID_ARG, "prefill variant must be -1..4");
-  g_gemm_variant = variant < 0 ? kGemmDefaultVariant : variant;
+  g_gemm_variant.store(variant < 0 ? kGemmDefaultVariant : variant, std::memory_order_relaxed);
   return ok();
 }
 

@@ -644,10 +644,11 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
 // activation slices copied straight into LDS
 // measured on MI355X at M=512, K=4096, N=14336: 80.8 / 71.3 / 71.4 / 67.6 / 64.8 us
 extern const int kGemmDefaultVariant = 4;
-int g_gemm_variant = kGemmDefaultVariant;
+std::atomic<int> g_gemm_variant{kGemmDefaultVariant};
 
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,
                              float* y, hipStream_t stream) {
+  const int variant = g_gemm_variant.load(std::memory_order_relaxed);
   if (L.wk == WK_Q8_0) {
     // q8_0 weights: the pipelined organisations only
     const PackedW P = packed_view(W, L);
@@ -659,7 +660,7 @@ hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, con
     const bool seven = e7 > e8;
     const unsigned grid = unsigned(seven ? t7 : t8);
     const uint16_t* xa = static_cast<const uint16_t*>(x);
-    if (g_gemm_variant == 3) {
+    if (variant == 3) {
       if (seven)
         hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, false, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
                            xa, y, int(M), int(N), int(K));
@@ -687,26 +688,26 @@ hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, con
   const bool seven = e7 > e8;
   const unsigned grid = unsigned(seven ? t7 : t8);
   const uint16_t* xa = static_cast<const uint16_t*>(x);
-  if (g_gemm_variant == 0) {
+  if (variant == 0) {
     if (seven)
       hipLaunchKernelGGL((gemm_q4_0_bf16_kernel<7, GT_PW>), dim3(grid), dim3(256), 0, stream, P, xa, y, int(M), int(N), int(K));
     else
       hipLaunchKernelGGL((gemm_q4_0_bf16_kernel<8, GT_PW>), dim3(grid), dim3(256), 0, stream, P, xa, y, int(M), int(N), int(K));
-  } else if (g_gemm_variant == 1) {
+  } else if (variant == 1) {
     if (seven)
       hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<7, GT_PW, 4>), dim3(grid), dim3(512), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
     else
       hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<8, GT_PW, 4>), dim3(grid), dim3(512), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
-  } else if (g_gemm_variant == 2) {
+  } else if (variant == 2) {
     if (seven)
       hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<7, GT_PW, 8>), dim3(grid), dim3(768), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
     else
       hipLaunchKernelGGL((gemm_q4_0_bf16_pc_kernel<8, GT_PW, 8>), dim3(grid), dim3(768), 0, stream, P, xa, y,
                          int(M), int(N), int(K));
-  } else if (g_gemm_variant == 3) {
+  } else if (variant == 3) {
     if (seven)
       hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, false>), dim3(grid), dim3(512), 0, stream, P, xa, y,
                          int(M), int(N), int(K));

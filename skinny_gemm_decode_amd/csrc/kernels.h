@@ -1,6 +1,7 @@
 // Host-side launchers of the library's kernels (internal).
 #pragma once
 
+#include <atomic>
 #include <vector>
 
 #include "common.h"
@@ -18,7 +19,7 @@ hipError_t launch_block_dots(int fmt, const void* W, const Layout& L, int64_t n0
                              int32_t* out, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int grid, hipStream_t stream);
 // Prefill kernel in use: 0 = one role per wave, 1 = producer/consumer waves.
-extern int g_gemm_variant;
+extern std::atomic<int> g_gemm_variant;
 extern const int kGemmDefaultVariant;
 
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,

@@ -157,6 +157,11 @@ def test_other_entry_point_errors(skg):
     assert L.skg_gemm_tiled(6, 512, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED  # q8_0: 3, 4 only
     assert L.skg_gemm_tiled_set_variant(-1) == skg.OK
     assert L.skg_gemm_tiled(6, 512, 4100, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    # more output tiles than one launch takes, and M or N beyond 32-bit indices
+    assert L.skg_gemm_tiled(5, 1 << 30, 4096, 1 << 20, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_gemm_tiled(5, 1 << 31, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_gemm_tiled(5, 512, 4096, 1 << 31, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
+    assert L.skg_packed_size(2, 1 << 31, 4096) == 0
     assert L.skg_pack_weights(2, 4, 64, FAKE, MISALIGNED, None) == skg.E_ALIGN
     assert L.skg_pack_weights(2, 4, 64, ctypes.c_void_p((1 << 20) + 1), FAKE, None) == skg.E_ALIGN
     assert L.skg_pack_weights(2, 4, 60, FAKE, FAKE, None) == skg.E_SHAPE
