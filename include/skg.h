@@ -111,6 +111,7 @@ const char* skg_last_error(void);
  *   2^31 - 1; K <= 2^30 and K >= 32, K % 32 == 0 for q8_0/q4_0, K >= 8 and
  *   K % 8 == 0 for bf16.
  * skg_pack_weights: src = canonical N x K weights (device, 2-byte aligned),
+ *   N * K / 32 / 256 < 2^31 - 1 for q8_0/q4_0 (one launch; else SKG_E_SHAPE),
  *   dst = packed buffer of skg_packed_size bytes (device, 256-byte aligned).
  *   src and dst must not overlap.
  * skg_packed_size_multi / skg_pack_weights_multi: n (1..4) matrices of

@@ -79,6 +79,14 @@ skg_status check_nk(int fmt, int64_t N, int64_t K) {
   return SKG_OK;
 }
 
+// Packing and the block-dot hook launch one thread per block in a 1-D grid of
+// 256-thread workgroups: at most 2^31 - 1 workgroups.
+skg_status check_block_grid(int64_t rows, int64_t K, const char* what) {
+  if (rows * (K / 32) / 256 >= INT32_MAX)
+    return fail(SKG_E_SHAPE, "%s: %lld rows x K=%lld exceed one launch", what, (long long)rows, (long long)K);
+  return SKG_OK;
+}
+
 // ---- GEMV variant registry ------------------------------------------------
 
 std::once_flag g_reg_once;
@@ -337,6 +345,7 @@ size_t skg_packed_size_multi(skg_fmt fmt, int n, const int64_t* Ns, int64_t K) {
 skg_status skg_pack_weights(skg_fmt fmt, int64_t N, int64_t K, const void* src, void* dst, hipStream_t stream) {
   skg_status st = check_nk(fmt, N, K);
   if (st != SKG_OK) return st;
+  if ((st = check_block_grid(N, K, "pack")) != SKG_OK) return st;
   if (!src || !dst) return fail(SKG_E_INVALID_ARG, "null src or dst");
   if (!aligned(src, 2)) return fail(SKG_E_ALIGN, "src must be 2-byte aligned");
   if (!aligned(dst, 16)) return fail(SKG_E_ALIGN, "dst must be 16-byte aligned");
@@ -353,6 +362,7 @@ skg_status skg_pack_weights_multi(skg_fmt fmt, int n, const int64_t* Ns, int64_t
   for (int i = 0; i < n; ++i) {
     skg_status st = check_nk(fmt, Ns[i], K);
     if (st != SKG_OK) return st;
+    if ((st = check_block_grid(Ns[i], K, "pack")) != SKG_OK) return st;
     if (!srcs[i]) return fail(SKG_E_INVALID_ARG, "null srcs[%d]", i);
     if (!aligned(srcs[i], 2)) return fail(SKG_E_ALIGN, "srcs[%d] must be 2-byte aligned", i);
   }
@@ -474,6 +484,7 @@ skg_status skg_debug_block_dots(skg_fmt fmt, int64_t N, int64_t K, int64_t n0, i
   skg_status st = check_nk(fmt, N, K);
   if (st != SKG_OK) return st;
   if (n0 < 0 || nr < 1 || n0 + nr > N) return fail(SKG_E_SHAPE, "rows [n0, n0+nr) must lie in [0, N)");
+  if ((st = check_block_grid(nr, K, "block dots")) != SKG_OK) return st;
   if (!W || !xq || !out) return fail(SKG_E_INVALID_ARG, "null W, xq or out");
   if (!aligned(W, 16) || !aligned(xq, 4) || !aligned(out, 4)) return fail(SKG_E_ALIGN, "misaligned pointer");
   if ((st = check_device()) != SKG_OK) return st;
@@ -485,6 +496,7 @@ skg_status skg_debug_block_dots(skg_fmt fmt, int64_t N, int64_t K, int64_t n0, i
 skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream) {
   if (!buf || !out) return fail(SKG_E_INVALID_ARG, "null buf or out");
   if (bytes == 0 || bytes % 16) return fail(SKG_E_SHAPE, "bytes must be a positive multiple of 16");
+  if (bytes / 4096 >= INT32_MAX) return fail(SKG_E_SHAPE, "bytes exceed one launch (4 KB per workgroup)");
   if (!aligned(buf, 16) || !aligned(out, 4)) return fail(SKG_E_ALIGN, "buf must be 16-byte aligned");
   int cus = 0;
   skg_status st = check_device(&cus);

@@ -162,6 +162,7 @@ def test_other_entry_point_errors(skg):
     assert L.skg_gemm_tiled(5, 1 << 31, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_gemm_tiled(5, 512, 4096, 1 << 31, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_packed_size(2, 1 << 31, 4096) == 0
+    assert L.skg_pack_weights(2, (1 << 31) - 1, 1 << 30, FAKE, FAKE, None) == skg.E_SHAPE  # grid too large
     assert L.skg_pack_weights(2, 4, 64, FAKE, MISALIGNED, None) == skg.E_ALIGN
     assert L.skg_pack_weights(2, 4, 64, ctypes.c_void_p((1 << 20) + 1), FAKE, None) == skg.E_ALIGN
     assert L.skg_pack_weights(2, 4, 60, FAKE, FAKE, None) == skg.E_SHAPE
