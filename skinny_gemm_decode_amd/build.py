@@ -24,6 +24,7 @@ ARCH = "gfx950"
 SOURCES = [
     "gemv_mfma_q4_0.hip",
     "gemv_mfma_q8_0.hip",
+    "gemv_mfma_q8_1.hip",
     "gemv_q4_0_f32_m68.hip",
     "gemv_q4_0_f32_m35.hip",
     "gemv_q8_0_f32_m38.hip",

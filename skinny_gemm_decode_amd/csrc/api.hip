@@ -99,8 +99,9 @@ std::atomic<int64_t> g_lds_pad{0};
 void init_registry() {
   std::call_once(g_reg_once, [] {
     auto* v = new std::vector<GemvEntry>();
-    // Matrix-core defaults first (M >= 2 for q4_0, M >= 4 for q8_0, where
-    // they measure faster); their measurement variants last.
+    // Matrix-core defaults first (fp32 activations: M >= 2 for q4_0, M >= 4
+    // for q8_0; Q8_1 activations: M = 7, 8), where they measure faster; their
+    // measurement variants last.
     register_gemv_mfma_q4_0(*v);
     register_gemv_mfma_q8_0(*v);
     register_gemv_bf16(*v);
@@ -109,7 +110,9 @@ void init_registry() {
     register_gemv_q4_0_f32(*v);
     register_gemv_q4_0_f32_m35(*v);
     register_gemv_q4_0_f32_m68(*v);
+    register_gemv_mfma_q8_1(*v);
     register_gemv_q8_1(*v);
+    register_gemv_mfma_q8_1_alt(*v);
     register_gemv_mfma_q4_0_alt(*v);
     register_gemv_mfma_q8_0_alt(*v);
     for (auto& a : g_sel)

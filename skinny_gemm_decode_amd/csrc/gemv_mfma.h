@@ -216,6 +216,119 @@ __device__ inline void mf_tile(MfW<NP, BPW>& r, const f16x8 (&ah)[BPW], const f1
   }
 }
 
+// ---------------------------------------------------------------------------
+// Q8_1 activations on the integer matrix cores (v_mfma_i32_16x16x32_i8).  The
+// activation is already int8 with one scale per block, so the A operand of a
+// block is read straight from its 36-byte Q8_1 block: lane (g, c) takes the
+// codes of elements 4g..4g+3 and 16+4g..16+4g+3 of activation row c (dwords
+// 1 + g and 5 + g; rows c >= M repeat row c % M and their outputs are never
+// stored).  The B operand holds the same elements of weight row c as int8:
+// 16 (code - 8) for q4_0 (a nibble shifted into the high half of a byte, sign
+// bit flipped), the codes themselves for q8_0.  The block's int32 result is
+// exact, and is scaled in fp32 by the weight scale (over 16 for q4_0) and the
+// activation scale of each output row: y += dW dA S.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// A operands of the wave's BPW blocks and the activation scales of the four
+// output rows 4g..4g+3 this lane accumulates (zero for rows >= M).  The wave's
+// M x BPW blocks (BPW * 36 contiguous bytes per activation row) are copied
+// with coalesced dword loads into the wave-private LDS area and picked apart
+// there; between() runs once those loads are issued (the first tiles' weight
+// loads go there).
+template <int M, int BPW, class Between>
+__device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, uint64_t (&aq)[BPW],
+                                   f32x4 (&da)[BPW], Between between) {
+  constexpr int RW = BPW * 9;                 // dwords per activation row of the wave's span
+  constexpr int NL = (M * RW + 63) / 64;      // dword loads per lane
+  const int g = lane >> 4, c = lane & 15;
+  const int mr = (c < M) ? c : c % M;
+  const uint32_t* xw = reinterpret_cast<const uint32_t*>(a.x);
+  uint32_t v[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int f = i * 64 + lane;              // flat dword of [m][RW]
+    const int m = f / RW, o = f % RW;
+    v[i] = (f < M * RW) ? xw[(size_t(m) * a.nb + blk0) * 9 + size_t(o)] : 0u;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  between();
+  __builtin_amdgcn_sched_barrier(0);
+  // A wave's LDS accesses complete in order: its own writes are visible to
+  // its later reads without a barrier.
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int f = i * 64 + lane;
+    if (f < M * RW) area[f] = v[i];
+  }
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const uint32_t* blk = area + mr * RW + j * 9;
+    aq[j] = uint64_t(blk[1 + g]) | (uint64_t(blk[5 + g]) << 32);
+    float d4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      d4[i] = (m < M) ? h2f(area[(m < M ? m : 0) * RW + j * 9] & 0xFFFFu) : 0.f;
+    }
+    da[j] = f32x4{d4[0], d4[1], d4[2], d4[3]};
+  }
+}
+
+// One tile of one matrix against Q8_1 activations; loads and reloads as in
+// mf_tile.
+template <int NP, int BPW, int RR, bool RELOAD>
+__device__ inline void mf_tile_q8(MfW<NP, BPW>& r, const uint64_t (&aq)[BPW], const f32x4 (&da)[BPW],
+                                  float (&acc)[4], const MfNext& nx, uint32_t blk0, int g) {
+  uint32_t scw[BPW / 2];
+#pragma unroll
+  for (int i = 0; i < BPW / 8; ++i) {
+    scw[4 * i + 0] = r.sc[i].x;
+    scw[4 * i + 1] = r.sc[i].y;
+    scw[4 * i + 2] = r.sc[i].z;
+    scw[4 * i + 3] = r.sc[i].w;
+  }
+  if constexpr (RELOAD) {
+    mf_load_scales<NP, BPW>(r, nx.srow, blk0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // q4_0 codes enter the product as 16 (c - 8)
+  constexpr float WSCALE = (NP == 1) ? 0.0625f : 1.0f;
+#pragma unroll
+  for (int q = 0; q < BPW / 4; ++q) {
+    uint32_t t[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      t[p][0] = r.u[q][p].x;
+      t[p][1] = r.u[q][p].y;
+      t[p][2] = r.u[q][p].z;
+      t[p][3] = r.u[q][p].w;
+      transpose_rows4(t[p]);
+    }
+    if constexpr (RELOAD) {
+      mf_load_quad<NP, BPW>(r, q, nx.rowp, nx.nb, blk0, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * q + jj;
+      uint64_t bv;
+      if constexpr (NP == 1) {
+        const uint32_t w = t[0][jj];
+        const uint32_t wl = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u;  // elements 4g..4g+3
+        const uint32_t wh = (w & 0xF0F0F0F0u) ^ 0x80808080u;         // elements 16+4g..16+4g+3
+        bv = uint64_t(wl) | (uint64_t(wh) << 32);
+      } else {
+        bv = uint64_t(t[0][jj]) | (uint64_t(t[1][jj]) << 32);
+      }
+      const i32x4 sdot = __builtin_amdgcn_mfma_i32_16x16x32_i8(long(aq[j]), long(bv), i32x4{0, 0, 0, 0}, 0, 0, 0);
+      const uint32_t sw = scw[j >> 1];
+      const float s = h2f((j & 1) ? (sw >> 16) : (sw & 0xFFFFu)) * WSCALE;
+#pragma unroll
+      for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, da[j][i] * float(sdot[i]), acc[i]);
+    }
+  }
+}
+
 // LDS bytes of one launch with up to WAVES waves: per-wave activation
 // staging, reused afterwards for the two reduction buffers.
 template <int M, int WAVES, int BPW, int XT, int NR>
@@ -315,8 +428,10 @@ template <int FMT, int M, int WAVES, int BPW, int XT, int EPI, int PD>
 __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
   static_assert(PD == 1 || PD == 2, "prefetch depth: tiles in flight per wave");
   static_assert(BPW % 8 == 0, "whole 16-byte scale loads");
-  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32, "fp32-activation quantised formats only");
-  constexpr int NP = (FMT == SKG_Q8_0_F32) ? 2 : 1;
+  constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
+  static_assert(!Q8 || (XT == 1 && EPI == SKG_EPI_NONE), "Q8_1 activations: one integer term, plain output");
+  constexpr int NP = (FMT == SKG_Q8_0_F32 || FMT == SKG_Q8_0_Q8_1) ? 2 : 1;
   constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
   constexpr int RR = M < 4 ? M : 4;  // accumulator rows a lane can own
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -365,32 +480,38 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
   // staging arithmetic ----
   MfW<NP, BPW> w[NR], w2[NR];
   MfNext nx[NR];
-  f16x8 ah[BPW], al[BPW];
-  float unscale[4];  // 2^e of the activation rows this lane's outputs belong to
-  mf_stage<M, BPW, XT>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al, unscale,
-                       [&] {
-                         next_of(nx, t0);
+  f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
+  uint64_t aq[Q8 ? BPW : 1];
+  f32x4 da[Q8 ? BPW : 1];
+  float unscale[4] = {1.f, 1.f, 1.f, 1.f};  // 2^e of the activation rows this lane's outputs belong to
+  auto first_loads = [&] {
+    next_of(nx, t0);
 #pragma unroll
-                         for (int r = 0; r < NR; ++r) {
+    for (int r = 0; r < NR; ++r) {
 #pragma unroll
-                           for (int q = 0; q < BPW / 4; ++q)
-                             mf_load_quad<NP, BPW>(w[r], q, nx[r].rowp, nx[r].nb, blk0, g);
-                           mf_load_scales<NP, BPW>(w[r], nx[r].srow, blk0);
-                         }
-                         if constexpr (PD == 2) {
-                           // second tile (the first again when there is none:
-                           // unconditional loads keep the compiler's waits exact)
-                           next_of(nx, nmine > 1 ? t0 + step : t0);
+      for (int q = 0; q < BPW / 4; ++q)
+        mf_load_quad<NP, BPW>(w[r], q, nx[r].rowp, nx[r].nb, blk0, g);
+      mf_load_scales<NP, BPW>(w[r], nx[r].srow, blk0);
+    }
+    if constexpr (PD == 2) {
+      // second tile (the first again when there is none:
+      // unconditional loads keep the compiler's waits exact)
+      next_of(nx, nmine > 1 ? t0 + step : t0);
 #pragma unroll
-                           for (int r = 0; r < NR; ++r) {
+      for (int r = 0; r < NR; ++r) {
 #pragma unroll
-                             for (int q = 0; q < BPW / 4; ++q)
-                               mf_load_quad<NP, BPW>(w2[r], q, nx[r].rowp, nx[r].nb, blk0, g);
-                             mf_load_scales<NP, BPW>(w2[r], nx[r].srow, blk0);
-                           }
-                         }
-                       },
-                       [] {});
+        for (int q = 0; q < BPW / 4; ++q)
+          mf_load_quad<NP, BPW>(w2[r], q, nx[r].rowp, nx[r].nb, blk0, g);
+        mf_load_scales<NP, BPW>(w2[r], nx[r].srow, blk0);
+      }
+    }
+  };
+  if constexpr (Q8)
+    mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(lds) + size_t(wave) * (M * BPW * 9), blk0, lane, aq, da,
+                        first_loads);
+  else
+    mf_stage<M, BPW, XT>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al, unscale,
+                         first_loads, [] {});
   __syncthreads();  // the staging area becomes the reduction buffers
 
   float* red = reinterpret_cast<float*>(lds);
@@ -403,7 +524,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
     for (int r = 0; r < NR; ++r) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
-      mf_tile<NP, BPW, RR, XT, RELOAD>(w[r], ah, al, acc[r], mlo, mhi, magic, nx[r], blk0, g);
+      if constexpr (Q8)
+        mf_tile_q8<NP, BPW, RR, RELOAD>(w[r], aq, da, acc[r], nx[r], blk0, g);
+      else
+        mf_tile<NP, BPW, RR, XT, RELOAD>(w[r], ah, al, acc[r], mlo, mhi, magic, nx[r], blk0, g);
     }
     // partial sums: lane (g, c) holds rows m = 4g + i of output row c
     float* rb = red + size_t(parity) * (WAVES * NR * MF_ROWS * M);
@@ -678,6 +802,10 @@ inline GemvEntry gemv_mfma_entry() {
   GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_kernel<FMT, M, WAVES, BPW, XT, EPI, PD>),
               FMT, M, EPI, MF_ROWS, XT, 2, WAVES, BPW};
   e.lds = MfLds<M, WAVES, BPW, XT, NR>::BYTES;
+  if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1) {
+    constexpr int q8_stage = WAVES * M * BPW * 36;  // each wave's Q8_1 blocks
+    if (e.lds < q8_stage) e.lds = q8_stage;
+  }
   e.max_nb = WAVES * BPW;
   return e;
 }

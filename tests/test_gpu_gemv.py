@@ -297,27 +297,29 @@ def mfma_variants(skg, fmt, M):
             if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3)]
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemv_mfma_shapes(skg, fmt, M):
     """Default path at the shapes the matrix-core kernel takes, then every
     matrix-core variant against its own precision: with two fp16 activation
     terms (~22 bits) the error stays under 2e-5 of sum|w x|, which fails if the
     low term were lost; with one term it stays under 2^-11 (its rounding) plus
-    fp32 accumulation, 8e-4 of sum|w x|."""
+    fp32 accumulation, 8e-4 of sum|w x|; on Q8_1 activations the block dots
+    are exact int32 and only the fp32 scaling rounds, 2e-5 of sum|w a|."""
     cases = []
     for i, (N, K) in enumerate(MFMA_SHAPES):
         if N * K * M > 20000 * 4096 * 2:
             continue
         W, x = make_inputs(skg, fmt, M, N, K, seed=8000 + 100 * fmt + 10 * M + i)
-        y_ref, bound = reference(skg, fmt, W, x, None)
+        xq_ref = oracle.quantize_q8_1(x) if is_q8_1(skg, fmt) else None
+        y_ref, bound = reference(skg, fmt, W, x, xq_ref)
         cases.append((N, K, W, x, y_ref, bound))
         y, _ = run_gemv(skg, fmt, M, N, K, W, x)
         assert_close(y, y_ref, bound, f"default fmt={fmt} M={M} N={N} K={K}")
     try:
         for v in mfma_variants(skg, fmt, M):
             skg.gemv_set_variant(fmt, M, 0, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
-            rel = 2e-5 if v["j"] == 2 else 8e-4
+            rel = 2e-5 if (v["j"] == 2 or is_q8_1(skg, fmt)) else 8e-4
             for N, K, W, x, y_ref, bound in cases:
                 nb = K // 32
                 if nb % v["kw"] or nb > v["waves"] * v["kw"]:
