@@ -23,8 +23,8 @@ launch-bound case, and the M=512 MFMA prefill tile.  The CPU oracle is timed
 on a bounded sample of the headline workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 60000] [--arms all|none|a,b]
-Prints one JSON line on stdout; details go to --details (default
-gpurun_out/bench_details.json when that directory exists).
+Prints one JSON line on stdout; per-arm details go to the --details file when
+one is given.
 """
 
 from __future__ import annotations
@@ -651,8 +651,7 @@ def main():
     }
     details["line"] = line
     details["cpu_baseline"] = cpu
-    path = args.details or (os.path.join(ROOT, "gpurun_out", "bench_details.json")
-                            if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else None)
+    path = args.details
     if path:
         with open(path, "w") as f:
             json.dump(details, f, indent=1, default=lambda o: o.tolist() if hasattr(o, "tolist") else str(o))
