@@ -72,13 +72,77 @@ def counter_traffic():
 # timing helpers
 # --------------------------------------------------------------------------
 
+class Telemetry:
+    """Clock levels, temperatures and power of the GPU torch uses, read from
+    sysfs (the amdgpu driver's pp_dpm_* levels and hwmon sensors of the PCI
+    device whose bus number torch reports).  Reading is host-side file I/O and
+    puts nothing on the GPU's queues."""
+
+    def __init__(self, torch, root: str = "/sys/class/drm"):
+        import glob
+        self.dev = None
+        try:
+            bus = int(torch.cuda.get_device_properties(0).pci_bus_id)
+        except Exception:
+            return
+        for d in sorted(glob.glob(os.path.join(root, "card*", "device"))):
+            try:
+                slot = [l.split("=", 1)[1].strip() for l in open(os.path.join(d, "uevent")) if
+                        l.startswith("PCI_SLOT_NAME=")][0]
+            except (OSError, IndexError):
+                continue
+            if int(slot.split(":")[1], 16) == bus and os.path.exists(os.path.join(d, "pp_dpm_sclk")):
+                self.dev, self.slot = d, slot
+                self.hwmon = sorted(glob.glob(os.path.join(d, "hwmon", "hwmon*")))
+                break
+
+    @staticmethod
+    def _level(path):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            pass
+        return None
+
+    def read(self):
+        if self.dev is None:
+            return None
+        out = {"sclk_mhz": self._level(os.path.join(self.dev, "pp_dpm_sclk")),
+               "mclk_mhz": self._level(os.path.join(self.dev, "pp_dpm_mclk"))}
+        for h in self.hwmon:
+            for name, key, scale in (("temp2", "t_junction_c", 1e-3), ("temp3", "t_mem_c", 1e-3),
+                                     ("power1", "power_w", 1e-6)):
+                f = os.path.join(h, name + "_input")
+                if key not in out and os.path.exists(f):
+                    try:
+                        out[key] = float(open(f).read()) * scale
+                    except (OSError, ValueError):
+                        pass
+        return out
+
+    @staticmethod
+    def summary(samples):
+        samples = [s for s in samples if s]
+        if not samples:
+            return None
+        res = {"samples": len(samples)}
+        for k in ("sclk_mhz", "mclk_mhz", "t_junction_c", "t_mem_c", "power_w"):
+            v = [s[k] for s in samples if s.get(k) is not None]
+            if v:
+                res[k] = [round(min(v), 1), round(max(v), 1)]
+        return res
+
+
 class Timer:
     """Times `launch(i)` calls on torch's current stream with HIP events."""
 
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, launch, n_rot: int, steps: int, warmup: int, per_repeat: int = 200, warm_s: float | None = None):
+    def run(self, launch, n_rot: int, steps: int, warmup: int, per_repeat: int = 200, warm_s: float | None = None,
+            telemetry: Telemetry | None = None):
         torch = self.torch
         stream = torch.cuda.current_stream()
         sh = stream.cuda_stream
@@ -102,16 +166,25 @@ class Timer:
             left -= n
         events = [torch.cuda.Event(enable_timing=True) for _ in range(len(reps) + 1)]
         torch.cuda.synchronize()
+        samples = []
         events[0].record(stream)
         for r, n in enumerate(reps):
             for _ in range(n):
                 launch(i % n_rot, sh)
                 i += 1
             events[r + 1].record(stream)
+            # the host runs ahead of the queue: this sample falls while earlier
+            # timed launches execute, and adds no gap between them
+            if telemetry is not None:
+                samples.append(telemetry.read())
         torch.cuda.synchronize()
         rep_us = [events[r].elapsed_time(events[r + 1]) * 1000.0 / reps[r] for r in range(len(reps))]
         total_ms = events[0].elapsed_time(events[-1])
-        return summarize(rep_us, total_ms, steps)
+        res = summarize(rep_us, total_ms, steps)
+        if telemetry is not None:
+            res["telemetry_per_repeat"] = samples
+            res["telemetry"] = Telemetry.summary(samples)
+        return res
 
 
 def summarize(rep_us, total_ms, steps):
@@ -162,7 +235,7 @@ def check_outputs_sane(torch, ys):
 
 
 def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmup, warm_s, x_host, keep_rows=None,
-                   graph=False):
+                   graph=False, telemetry=None):
     import ctypes
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
@@ -195,7 +268,7 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
             raise RuntimeError(f"[{name}] GEMV not deterministic on buffer {i}")
         outs.append(a)
     check_outputs_sane(torch, outs)
-    res = timer.run(launch, n_rot, steps, warmup, warm_s=warm_s)
+    res = timer.run(launch, n_rot, steps, warmup, warm_s=warm_s, telemetry=telemetry)
     alg = wbytes + xbytes + M * N * 4
     res.update(name=name, fmt=skg.FMT_NAMES[fmt], M=M, N=N, K=K, rotation_buffers=n_rot,
                working_set_bytes=n_rot * wbytes, algorithmic_bytes=alg,
@@ -548,8 +621,11 @@ def main():
     x_host = si.activations_bf16(si.rng_for(0, 2, 0), 1, K)
     keep = np.array(sorted({0, 1, N - 1, N - 2} | set(np.random.default_rng(0).choice(N, 60, replace=False).tolist())))
     head, sample = bench_gemv_arm(skg, si, torch, timer, "bf16_m1_k4096_n12288", "bf16", skg.BF16_BF16, 1, N, K,
-                                  args.steps, args.warmup, None, x_host.view(np.int16), keep_rows=keep, graph=True)
+                                  args.steps, args.warmup, None, x_host.view(np.int16), keep_rows=keep, graph=True,
+                                  telemetry=Telemetry(torch))
     sample["x"] = x_host
+    if head.get("telemetry"):
+        log(f"[headline] telemetry over the timed repeats: {head['telemetry']}")
     log(f"[headline] {head['us_per_launch']:.2f} us/launch  {head['gbs']:.0f} GB/s  "
         f"({100 * head['frac_peak']:.1f}% of 8 TB/s)  spread {100 * head['spread']:.2f}%  "
         f"graph {head['graph']['us_per_launch']:.2f} us  read-ceiling {head['ceiling_us']:.2f} us")
@@ -637,6 +713,7 @@ def main():
             "frac_of_stream_read_ceiling": round(head["frac_ceiling"], 4),
             "timer": "HIP events on the launch stream, eager launches, 200 per repeat",
         },
+        "telemetry": head.get("telemetry"),
         "roofline": {
             "bound": "hbm",
             "achieved": round(head["gbs"], 2),

@@ -97,3 +97,29 @@ def test_trace_and_counter_tables_keep_only_library_kernels(tmp_path):
     assert "| kernel | dispatches | SQ_BUSY_CYCLES | SQ_WAVES |" in md
     assert "| `skg::quantize_q8_1_kernel` | 2 | 100 | 5 |" in md
     assert "    a\n    b" in md and "foo" not in md
+
+
+def test_telemetry_reads_the_device_torch_uses(tmp_path):
+    """Clock levels (the starred pp_dpm line), hwmon temperatures and power of
+    the card whose PCI bus torch reports; other cards are ignored."""
+    for card, slot, sclk in (("card0", "0000:11:00.0", "2100"), ("card1", "0000:75:00.0", "2400")):
+        d = tmp_path / card / "device"
+        (d / "hwmon" / "hwmon3").mkdir(parents=True)
+        (d / "uevent").write_text(f"DRIVER=amdgpu\nPCI_SLOT_NAME={slot}\n")
+        (d / "pp_dpm_sclk").write_text(f"0: 500Mhz\n1: {sclk}Mhz *\n")
+        (d / "pp_dpm_mclk").write_text("0: 2000Mhz *\n")
+        (d / "hwmon" / "hwmon3" / "temp2_input").write_text("61000\n")
+        (d / "hwmon" / "hwmon3" / "temp3_input").write_text("48000\n")
+        (d / "hwmon" / "hwmon3" / "power1_input").write_text("812000000\n")
+
+    class FakeTorch:
+        class cuda:
+            @staticmethod
+            def get_device_properties(i):
+                return type("P", (), {"pci_bus_id": 0x75})()
+
+    t = bench.Telemetry(FakeTorch, root=str(tmp_path))
+    r = t.read()
+    assert r == {"sclk_mhz": 2400.0, "mclk_mhz": 2000.0, "t_junction_c": 61.0, "t_mem_c": 48.0, "power_w": 812.0}
+    assert bench.Telemetry.summary([r, None, dict(r, sclk_mhz=2300.0)])["sclk_mhz"] == [2300.0, 2400.0]
+    assert bench.Telemetry(FakeTorch, root=str(tmp_path / "none")).read() is None
