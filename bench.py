@@ -234,8 +234,24 @@ def check_outputs_sane(torch, ys):
             raise RuntimeError("non-finite GEMV output; refusing to time")
 
 
+def compare_abba(timer, launch_a, launch_b, n_rot, steps, cycles=3):
+    """Interleaved comparison of two launch functions: `cycles` independent
+    cycles in the fixed order A1 B1 B2 A2, and the ratio B / A as the mean of
+    the per-cycle ratios (the RX 6700 XT write-up, Approach & Methodology;
+    "Six hypotheses, four refutations", How the agents searched: A/B/A rather
+    than A/B).  Clock or temperature drift within a cycle cancels."""
+    out = []
+    for _ in range(cycles):
+        legs = [timer.run(f, n_rot, steps, 0)["us_per_launch"] for f in (launch_a, launch_b, launch_b, launch_a)]
+        a, b = (legs[0] + legs[3]) / 2, (legs[1] + legs[2]) / 2
+        out.append({"a_us": [round(legs[0], 4), round(legs[3], 4)], "b_us": [round(legs[1], 4), round(legs[2], 4)],
+                    "b_over_a": b / a})
+    return {"order": "A1 B1 B2 A2", "cycles": out, "steps_per_leg": steps,
+            "b_over_a": statistics.fmean(c["b_over_a"] for c in out)}
+
+
 def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmup, warm_s, x_host, keep_rows=None,
-                   graph=False, telemetry=None):
+                   graph=False, telemetry=None, abba=0):
     import ctypes
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
@@ -285,6 +301,8 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
     res["ceiling_us"] = ceil["us_per_launch"]
     res["ceiling_gbs"] = wbytes / (ceil["us_per_launch"] * 1e-6) / 1e9
     res["frac_ceiling"] = ceil["us_per_launch"] / res["us_per_launch"]
+    if abba:
+        res["abba_vs_read"] = compare_abba(timer, launch, read, n_rot, abba)
     if graph:
         res["graph"] = bench_graph(torch, launch, n_rot)
         res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
@@ -622,10 +640,11 @@ def main():
     keep = np.array(sorted({0, 1, N - 1, N - 2} | set(np.random.default_rng(0).choice(N, 60, replace=False).tolist())))
     head, sample = bench_gemv_arm(skg, si, torch, timer, "bf16_m1_k4096_n12288", "bf16", skg.BF16_BF16, 1, N, K,
                                   args.steps, args.warmup, None, x_host.view(np.int16), keep_rows=keep, graph=True,
-                                  telemetry=Telemetry(torch))
+                                  telemetry=Telemetry(torch), abba=1000)
     sample["x"] = x_host
     if head.get("telemetry"):
         log(f"[headline] telemetry over the timed repeats: {head['telemetry']}")
+    log(f"[headline] ABBA against the streaming read of the same buffers: {head['abba_vs_read']}")
     log(f"[headline] {head['us_per_launch']:.2f} us/launch  {head['gbs']:.0f} GB/s  "
         f"({100 * head['frac_peak']:.1f}% of 8 TB/s)  spread {100 * head['spread']:.2f}%  "
         f"graph {head['graph']['us_per_launch']:.2f} us  read-ceiling {head['ceiling_us']:.2f} us")
@@ -711,6 +730,7 @@ def main():
             "spread_ok": head["spread_ok"],
             "stream_read_ceiling_us": round(head["ceiling_us"], 3),
             "frac_of_stream_read_ceiling": round(head["frac_ceiling"], 4),
+            "stream_read_over_gemv_abba": round(head["abba_vs_read"]["b_over_a"], 4),
             "timer": "HIP events on the launch stream, eager launches, 200 per repeat",
         },
         "telemetry": head.get("telemetry"),

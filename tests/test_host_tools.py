@@ -123,3 +123,30 @@ def test_telemetry_reads_the_device_torch_uses(tmp_path):
     assert r == {"sclk_mhz": 2400.0, "mclk_mhz": 2000.0, "t_junction_c": 61.0, "t_mem_c": 48.0, "power_w": 812.0}
     assert bench.Telemetry.summary([r, None, dict(r, sclk_mhz=2300.0)])["sclk_mhz"] == [2300.0, 2400.0]
     assert bench.Telemetry(FakeTorch, root=str(tmp_path / "none")).read() is None
+
+
+def test_abba_order_and_ratio():
+    """Legs run A1 B1 B2 A2 per cycle and the ratio is the mean of the cycle
+    ratios; a linear drift across a cycle cancels."""
+    calls = []
+
+    class FakeTimer:
+        t = 0.0
+
+        def run(self, f, n_rot, steps, warmup):
+            calls.append(f.__name__)
+            FakeTimer.t += 1.0                       # drift: every leg 1 us slower than the last
+            base = 10.0 if f.__name__ == "a" else 12.0
+            return {"us_per_launch": base + FakeTimer.t}
+
+    def a(i, sh):
+        pass
+
+    def b(i, sh):
+        pass
+
+    r = bench.compare_abba(FakeTimer(), a, b, 4, 100, cycles=2)
+    assert calls == ["a", "b", "b", "a"] * 2
+    # cycle 1: A legs 11, 14 -> 12.5; B legs 14, 15 -> 14.5 (drift cancels in the means' centres)
+    assert r["cycles"][0]["b_over_a"] == pytest.approx(14.5 / 12.5)
+    assert r["b_over_a"] == pytest.approx((14.5 / 12.5 + 18.5 / 16.5) / 2)
