@@ -1,8 +1,9 @@
 """Python binding of libskg, the MI355X (gfx950) skinny decode GEMM / GEMV library.
 
-Argument marshalling only: every function here checks that its tensors live on
-the GPU, passes raw device pointers and the current HIP stream to the C ABI
-declared in ``include/skg.h``, and raises ``SkgError`` on a nonzero status.
+Argument marshalling only: every function here checks that its tensors are
+contiguous GPU tensors large enough for the call (the C ABI sees raw pointers
+and cannot), passes raw device pointers and the current HIP stream to the C
+ABI declared in ``include/skg.h``, and raises ``SkgError`` on a nonzero status.
 All arithmetic happens in the library's HIP kernels; there is no CPU fallback.
 Importing this module fails with ImportError when ``libskg.so`` has not been
 built (``python skinny_gemm_decode_amd/build.py``).
@@ -102,12 +103,6 @@ def check(status: int) -> None:
         raise SkgError(status, last_error())
 
 
-def _dev_ptr(t) -> int:
-    if not t.is_cuda:
-        raise ValueError("tensor must be on the GPU")
-    return t.data_ptr()
-
-
 def _stream(stream) -> int:
     import torch
 
@@ -118,6 +113,37 @@ def _stream(stream) -> int:
 
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
+
+
+# Bytes per K element of an activation row, by product format (Q8_1: 36-byte
+# blocks of 32 elements), and of a canonical weight row element.
+_X_BYTES_PER_32 = {BF16_BF16: 64, Q8_0_F32: 128, Q4_0_F32: 128, Q4_0_Q8_1: 36, Q8_0_Q8_1: 36,
+                   Q4_0_BF16: 64, Q8_0_BF16: 64}
+_W_BYTES_PER_32 = {BF16_BF16: 64, Q8_0_F32: 34, Q4_0_F32: 18, Q4_0_Q8_1: 18, Q8_0_Q8_1: 34,
+                   Q4_0_BF16: 18, Q8_0_BF16: 34}
+
+
+def _need(t, nbytes: int, what: str) -> int:
+    """Device pointer of t after checking that it is a contiguous GPU tensor
+    holding at least nbytes: the library sees raw pointers only, so a short or
+    strided tensor would otherwise be read or written out of bounds."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what} holds {_nbytes(t)} bytes, the call needs {nbytes}")
+    return t.data_ptr()
+
+
+def _x_bytes(fmt: int, M: int, K: int) -> int:
+    return M * (K // 32) * _X_BYTES_PER_32.get(fmt, 0) + (M * (K % 32) * 2 if fmt == BF16_BF16 else 0)
+
+
+def _w_bytes(fmt: int, N: int, K: int) -> int:
+    return N * K * 2 if fmt == BF16_BF16 else N * (K // 32) * _W_BYTES_PER_32.get(fmt, 0)
 
 
 # ---- packing -----------------------------------------------------------
@@ -140,9 +166,8 @@ def pack_weights(fmt: int, N: int, K: int, src, dst=None, stream=None):
         check(lib.skg_pack_weights(fmt, N, K, None, None, None))
     if dst is None:
         dst = torch.empty(size, dtype=torch.uint8, device=src.device)
-    elif _nbytes(dst) < size:
-        raise ValueError(f"dst holds {_nbytes(dst)} bytes, packing needs {size}")
-    check(lib.skg_pack_weights(fmt, N, K, _dev_ptr(src), _dev_ptr(dst), _stream(stream)))
+    check(lib.skg_pack_weights(fmt, N, K, _need(src, _w_bytes(fmt, N, K), "src"), _need(dst, size, "dst"),
+                               _stream(stream)))
     return dst
 
 
@@ -155,12 +180,12 @@ def pack_weights_multi(fmt: int, Ns: Sequence[int], K: int, srcs, dst=None, stre
     arr = (ctypes.c_int64 * n)(*Ns)
     if size == 0:
         check(lib.skg_pack_weights_multi(fmt, n, arr, K, None, None, None))
+    if len(srcs) != n:
+        raise ValueError(f"{n} sizes but {len(srcs)} source matrices")
     if dst is None:
         dst = torch.empty(size, dtype=torch.uint8, device=srcs[0].device)
-    elif _nbytes(dst) < size:
-        raise ValueError(f"dst holds {_nbytes(dst)} bytes, packing needs {size}")
-    ptrs = (ctypes.c_void_p * n)(*[_dev_ptr(s) for s in srcs])
-    check(lib.skg_pack_weights_multi(fmt, n, arr, K, ptrs, _dev_ptr(dst), _stream(stream)))
+    ptrs = (ctypes.c_void_p * n)(*[_need(s, _w_bytes(fmt, N, K), f"srcs[{i}]") for i, (s, N) in enumerate(zip(srcs, Ns))])
+    check(lib.skg_pack_weights_multi(fmt, n, arr, K, ptrs, _need(dst, size, "dst"), _stream(stream)))
     return dst
 
 
@@ -175,7 +200,8 @@ def quantize_act_q8_1(x, xq=None, stream=None):
     M, K = x.shape
     if xq is None:
         xq = torch.empty((M, K // 32, Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
-    check(lib.skg_quantize_act_q8_1(M, K, _dev_ptr(x), _dev_ptr(xq), _stream(stream)))
+    check(lib.skg_quantize_act_q8_1(M, K, _need(x, M * K * 4, "x"), _need(xq, M * (K // 32) * Q8_1_BLOCK_BYTES, "xq"),
+                                    _stream(stream)))
     return xq
 
 
@@ -203,9 +229,10 @@ def rmsnorm_q8_1(x, g=None, eps: float = 1e-5, xn=True, xq=True, stream=None):
         xq = torch.empty((M, K // 32, Q8_1_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
     elif xq is False:
         xq = None
-    check(lib.skg_rmsnorm_q8_1(M, K, _dev_ptr(x), _dev_ptr(g) if g is not None else None, float(eps),
-                               _dev_ptr(xn) if xn is not None else None,
-                               _dev_ptr(xq) if xq is not None else None, _stream(stream)))
+    check(lib.skg_rmsnorm_q8_1(M, K, _need(x, M * K * 4, "x"), _need(g, K * 4, "g") if g is not None else None,
+                               float(eps), _need(xn, M * K * 4, "xn") if xn is not None else None,
+                               _need(xq, M * (K // 32) * Q8_1_BLOCK_BYTES, "xq") if xq is not None else None,
+                               _stream(stream)))
     return xn, xq
 
 
@@ -217,7 +244,8 @@ def gemv(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
 
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=W.device)
-    check(lib.skg_gemv(fmt, M, K, N, _dev_ptr(W), _dev_ptr(x), _dev_ptr(y), _stream(stream)))
+    check(lib.skg_gemv(fmt, M, K, N, _need(W, packed_size(fmt, N, K), "W"), _need(x, _x_bytes(fmt, M, K), "x"),
+                       _need(y, M * N * 4, "y"), _stream(stream)))
     return y
 
 
@@ -235,8 +263,15 @@ def gemv_multi(fmt: int, M: int, K: int, Ns: Sequence[int], W, x, ys=None, epi: 
         else:
             ys = [torch.empty((M, Ns[i]), dtype=torch.float32, device=W.device) for i in range(nout)]
     arr = (ctypes.c_int64 * n)(*Ns)
-    yp = (ctypes.c_void_p * nout)(*[_dev_ptr(t) for t in ys])
-    check(lib.skg_gemv_multi(fmt, M, K, n, arr, _dev_ptr(W), _dev_ptr(x), yp, epi, _stream(stream)))
+    if len(ys) < nout:
+        raise ValueError(f"{nout} outputs needed, {len(ys)} given")
+    if epi in (EPI_SWIGLU, EPI_SWIGLU_Q8_1):
+        need = [M * Ns[0] * 4, M * (Ns[0] // 32) * Q8_1_BLOCK_BYTES][:nout]
+    else:
+        need = [M * Ns[i] * 4 for i in range(nout)]
+    yp = (ctypes.c_void_p * nout)(*[_need(t, b, f"ys[{i}]") for i, (t, b) in enumerate(zip(ys, need))])
+    check(lib.skg_gemv_multi(fmt, M, K, n, arr, _need(W, packed_size_multi(fmt, Ns, K), "W"),
+                             _need(x, _x_bytes(fmt, M, K), "x"), yp, epi, _stream(stream)))
     return ys
 
 
@@ -246,7 +281,8 @@ def gemm_tiled(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
 
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=W.device)
-    check(lib.skg_gemm_tiled(fmt, M, K, N, _dev_ptr(W), _dev_ptr(x), _dev_ptr(y), _stream(stream)))
+    check(lib.skg_gemm_tiled(fmt, M, K, N, _need(W, packed_size(fmt, N, K), "W"), _need(x, M * K * 2, "x"),
+                             _need(y, M * N * 4, "y"), _stream(stream)))
     return y
 
 
@@ -256,7 +292,9 @@ def debug_block_dots(fmt: int, N: int, K: int, n0: int, nr: int, W, xq, out=None
 
     if out is None:
         out = torch.empty((nr, K // 32), dtype=torch.int32, device=W.device)
-    check(lib.skg_debug_block_dots(fmt, N, K, n0, nr, _dev_ptr(W), _dev_ptr(xq), _dev_ptr(out), _stream(stream)))
+    check(lib.skg_debug_block_dots(fmt, N, K, n0, nr, _need(W, packed_size(fmt, N, K), "W"),
+                                   _need(xq, (K // 32) * Q8_1_BLOCK_BYTES, "xq"),
+                                   _need(out, max(nr, 0) * (K // 32) * 4, "out"), _stream(stream)))
     return out
 
 
@@ -267,7 +305,7 @@ def stream_read(buf, nbytes: int | None = None, out=None, stream=None):
     if out is None:
         out = torch.zeros(1, dtype=torch.int32, device=buf.device)
     nbytes = _nbytes(buf) if nbytes is None else nbytes
-    check(lib.skg_stream_read(_dev_ptr(buf), nbytes, _dev_ptr(out), _stream(stream)))
+    check(lib.skg_stream_read(_need(buf, nbytes, "buf"), nbytes, _need(out, 4, "out"), _stream(stream)))
     return out
 
 

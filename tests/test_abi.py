@@ -200,3 +200,47 @@ def test_single_hip_runtime(skg):
     with open("/proc/self/maps") as f:
         libs = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+class _FakeTensor:
+    """Duck-typed stand-in for a device tensor (no GPU here)."""
+
+    def __init__(self, nbytes, cuda=True, contiguous=True):
+        self.nbytes_, self.cuda, self.contig = nbytes, cuda, contiguous
+
+    is_cuda = property(lambda self: self.cuda)
+
+    def is_contiguous(self):
+        return self.contig
+
+    def numel(self):
+        return self.nbytes_
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return 0x10000
+
+
+def test_binding_checks_buffer_sizes(skg):
+    """The binding refuses host, strided and short tensors before any call:
+    the library sees raw pointers and would read or write past them."""
+    assert skg._need(_FakeTensor(64), 64, "y") == 0x10000
+    for t, msg in ((_FakeTensor(64, cuda=False), "on the GPU"), (_FakeTensor(64, contiguous=False), "contiguous"),
+                   (_FakeTensor(63), "63 bytes")):
+        with pytest.raises(ValueError, match=msg):
+            skg._need(t, 64, "y")
+    with pytest.raises(ValueError, match="required"):
+        skg._need(None, 4, "x")
+    # activation and canonical weight bytes by format
+    assert skg._x_bytes(skg.BF16_BF16, 2, 4104) == 2 * 4104 * 2
+    assert skg._x_bytes(skg.Q4_0_F32, 3, 4096) == 3 * 4096 * 4
+    assert skg._x_bytes(skg.Q8_0_Q8_1, 2, 4096) == 2 * 128 * 36
+    assert skg._w_bytes(skg.Q4_0_Q8_1, 5, 4096) == 5 * 128 * 18
+    assert skg._w_bytes(skg.Q8_0_F32, 5, 4096) == 5 * 128 * 34
+    assert skg._w_bytes(skg.BF16_BF16, 5, 4104) == 5 * 4104 * 2
+    # a short output is refused before the library is called
+    W, x, y = _FakeTensor(skg.packed_size(skg.Q4_0_F32, 64, 256)), _FakeTensor(4 * 256), _FakeTensor(4 * 64 - 4)
+    with pytest.raises(ValueError, match="y holds"):
+        skg.gemv(skg.Q4_0_F32, 1, 256, 64, W, x, y)

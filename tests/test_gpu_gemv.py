@@ -367,3 +367,26 @@ def test_gemv_multi_mfma(skg, fmt):
     for W, y in zip(Ws, ys):
         y_ref, bound = reference(skg, fmt, W, x, None)
         assert_close(host(y), y_ref, bound, f"multi mfma fmt={fmt}")
+
+
+def test_binding_refuses_short_and_strided_buffers(skg):
+    """Real device tensors that are too short or not contiguous are refused by
+    the binding before anything is launched; the output stays untouched."""
+    import torch
+
+    M, N, K = 2, 64, 256
+    W, x = make_inputs(skg, 2, M, N, K, seed=9100)
+    Wp = skg.pack_weights(2, N, K, dev(W))
+    xd = dev(x)
+    y = poisoned((M, N))
+    before = host(y).copy()
+    with pytest.raises(ValueError, match="y holds"):
+        skg.gemv(2, M, K, N, Wp, xd, y[:1])
+    with pytest.raises(ValueError, match="x holds"):
+        skg.gemv(2, M, K, N, Wp, xd[:1], y)
+    with pytest.raises(ValueError, match="W holds"):
+        skg.gemv(2, M, K, N, Wp[:-16], xd, y)
+    with pytest.raises(ValueError, match="contiguous"):
+        skg.gemv(2, M, K, N, Wp, torch.cat([xd, xd], dim=1)[:, ::2], y)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), before, equal_nan=True)
