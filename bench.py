@@ -576,6 +576,17 @@ def cpu_baseline(si, gpu_sample, budget_s=12.0):
         times.append(time.perf_counter() - t1)
     per = sum(times) / len(times)
     alg = N * K * 2 + K * 2 + N * 4
+    # the same GEMVs with the BLAS pool held to one thread (a few, for scale)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            for r in range(3):
+                oracle.gemv_ref_fmt("bf16", Ws[r % 2], x, x_kind="bf16")
+            one = (time.perf_counter() - t1) / 3
+    except ImportError:
+        pass
     # parity of the GPU's sampled rows on the timed rotation buffers
     worst = 0.0
     for rows_w, y_gpu in zip(gpu_sample["kept_rows"], gpu_sample["outputs"]):
@@ -593,6 +604,7 @@ def cpu_baseline(si, gpu_sample, budget_s=12.0):
                    f"({sum(times):.1f} s of oracle time: exact decode to fp64, single-threaded, then numpy "
                    f"fp64 matvec on the BLAS threads given in cores); host has {os.cpu_count()} logical CPUs"),
         "us_per_gemv": per * 1e6,
+        "one_blas_thread": None if one is None else {"us_per_gemv": one * 1e6, "value": alg / one / 1e9},
         "gpu_parity_worst_err_over_tol": worst,
     }
 
@@ -704,6 +716,9 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(si, sample)
     if cpu:
         log(f"[cpu oracle] {cpu['value']:.2f} GB/s ({cpu['us_per_gemv']:.0f} us per GEMV, {cpu['cores']} threads)")
+        if cpu["one_blas_thread"]:
+            o = cpu["one_blas_thread"]
+            log(f"[cpu oracle] {o['value']:.2f} GB/s ({o['us_per_gemv']:.0f} us per GEMV) with one BLAS thread")
 
     traffic = counter_traffic()
     line = {
