@@ -390,3 +390,18 @@ def test_binding_refuses_short_and_strided_buffers(skg):
         skg.gemv(2, M, K, N, Wp, torch.cat([xd, xd], dim=1)[:, ::2], y)
     torch.cuda.synchronize()
     assert np.array_equal(host(y), before, equal_nan=True)
+
+
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_gemv_long_k(skg, fmt, M):
+    """K far beyond the model widths (16384, 32768): rows walk many K chunks,
+    and at M >= 2 the matrix-core defaults (K <= 4096) hand the call to the
+    vector kernels; ragged N."""
+    for i, K in enumerate((16384, 32768)):
+        N = 67
+        W, x = make_inputs(skg, fmt, M, N, K, seed=9300 + 100 * fmt + 10 * M + i)
+        note(f"long K fmt={fmt} M={M} K={K}")
+        y, xq_ref = run_gemv(skg, fmt, M, N, K, W, x)
+        y_ref, bound = reference(skg, fmt, W, x, xq_ref)
+        assert_close(y, y_ref, bound, f"fmt={fmt} M={M} N={N} K={K}")
