@@ -14,6 +14,10 @@ void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
   SKG_MF(4, 2, 1)
   SKG_MF(5, 2, 1)
   SKG_MF(6, 2, 1)
+  // M = 7: the LDS-ring kernel, 13.00 against 13.24 us (three A1 B1 B2 A2
+  // cycles; K = 4096 only, other K take the register-fed kernel below); it
+  // loses at M = 3 (13.10 against 11.96), 5 and 8 and ties at 6
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 2, 2, false>());
   SKG_MF(7, 2, 1)
   SKG_MF(8, 1, 2)  // one fp16 term: within the accuracy bound, 8% faster at M = 8
 }

@@ -6,14 +6,24 @@
 #define SKG_MF(M, XT, PD) out.push_back(skg::gemv_mfma_entry<SKG_Q8_0_F32, M, 8, 16, XT, SKG_EPI_NONE, PD>());
 
 namespace skg {
-// Registered before the vector-ALU instances: the defaults for M = 4..8,
+// Registered before the vector-ALU instances: the defaults for M = 2..8,
 // measured on MI355X under cold-cache rotation (K = 4096, N = 14336).  With
 // two planes per block the two-term activation does not fit the register
 // file beyond M = 2, so these carry the activation as one fp16 term.
 void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
-  // M = 4: the LDS-ring kernel (weights copied straight into LDS, two-term
-  // activation) edges out the register-fed one
+  // M = 2..7: the LDS-ring kernel (weights copied straight into LDS,
+  // two-term activation) beats the register-fed and the vector kernels
+  // (three A1 B1 B2 A2 cycles each, us: M = 2 15.65 against 15.98, M = 3
+  // 16.43 against 18.07, M = 5 16.83 against 17.66, M = 6 17.06 against
+  // 17.85, M = 7 17.06 against 18.21; at M = 8 it loses, 19.73 against
+  // 18.84).  It is compiled for K = 4096 only; other K fall through to the
+  // register-fed kernel (M >= 4) or the vector kernel (M = 2, 3).
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 2, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 3, 2, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 4, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 5, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 6, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 7, 2, 2, true>());
   SKG_MF(4, 1, 1)
   SKG_MF(5, 1, 1)
   SKG_MF(6, 1, 1)
@@ -23,7 +33,6 @@ void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
 // Registered after the vector-ALU instances: measurement variants.
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 1, 2, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 2, 2, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 8, 2, 2, true>());
   SKG_MF(1, 2, 1)
   SKG_MF(2, 2, 1)
