@@ -234,10 +234,12 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // M x BPW blocks (BPW * 36 contiguous bytes per activation row) are copied
 // with coalesced dword loads into the wave-private LDS area and picked apart
 // there; between() runs once those loads are issued (the first tiles' weight
-// loads go there).
-template <int M, int BPW, class Between>
+// loads go there), after_x() once they have been written to LDS (direct
+// global-to-LDS weight transfers go there: the compiler would drain them
+// before any later use of a register load).
+template <int M, int BPW, class Between, class AfterX>
 __device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, uint64_t (&aq)[BPW],
-                                   f32x4 (&da)[BPW], Between between) {
+                                   f32x4 (&da)[BPW], Between between, AfterX after_x) {
   constexpr int RW = BPW * 9;                 // dwords per activation row of the wave's span
   constexpr int NL = (M * RW + 63) / 64;      // dword loads per lane
   const int g = lane >> 4, c = lane & 15;
@@ -260,6 +262,7 @@ __device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk
     const int f = i * 64 + lane;
     if (f < M * RW) area[f] = v[i];
   }
+  after_x();
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
     const uint32_t* blk = area + mr * RW + j * 9;
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
   };
   if constexpr (Q8)
     mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(lds) + size_t(wave) * (M * BPW * 9), blk0, lane, aq, da,
-                        first_loads);
+                        first_loads, [] {});
   else
     mf_stage<M, BPW, XT>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al, unscale,
                          first_loads, [] {});
@@ -609,7 +612,7 @@ constexpr int MF_DMA_TILES = 4;  // most tiles one workgroup processes
 
 template <int FMT>
 struct MfDmaGeom {
-  static constexpr int NP = (FMT == SKG_Q8_0_F32) ? 2 : 1;
+  static constexpr int NP = (FMT == SKG_Q8_0_F32 || FMT == SKG_Q8_0_Q8_1) ? 2 : 1;
   static constexpr int NB = 128;                     // blocks per row (K = 4096)
   static constexpr int RB = NB * 16 * NP;            // payload bytes per row
   static constexpr int PRS = RB + 16;                // padded LDS row stride
@@ -623,12 +626,15 @@ struct MfDmaGeom {
 // (its first load is issued after staging).
 template <int FMT, int M, int XT, int R, bool ALIAS>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
-  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32, "fp32-activation quantised formats only");
+  constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
+  static_assert(!Q8 || XT == 1, "Q8_1 activations: one integer term");
   static_assert(R == 2 || R == 3, "ring slots");
   using G = MfDmaGeom<FMT>;
   constexpr int NP = G::NP, BPW = 16, WAVES = 8, P = G::P;
   constexpr int RR = M < 4 ? M : 4;
-  constexpr int WAVE_STAGE = MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE;
+  // per-wave activation staging: fp16 A operands, or the raw Q8_1 blocks
+  constexpr int WAVE_STAGE = Q8 ? M * BPW * 36 : MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   __shared__ __attribute__((aligned(16))) uint8_t slot0[G::SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[G::SLOT];
@@ -683,17 +689,24 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   };
 
   uint8_t* stage_area = ALIAS ? (R == 3 ? slot2 : slot1) : stage_own;
-  f16x8 ah[BPW], al[BPW];
-  float unscale[4];
+  f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
+  uint64_t aq[Q8 ? BPW : 1];
+  f32x4 da[Q8 ? BPW : 1];
+  float unscale[4] = {1.f, 1.f, 1.f, 1.f};
   // The first R tiles' transfers are unconditional (a workgroup with fewer
   // tiles copies its last one again): conditional transfers here would make
   // the compiler drain them all before the staging arithmetic.
   auto clamp = [&](int i) { return i < nmine ? i : nmine - 1; };
-  mf_stage<M, BPW, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {}, [&] {
+  auto first_dma = [&] {
     dma_tile(slot0, 0);
     if constexpr (!(R == 2 && ALIAS)) dma_tile(slot1, clamp(1));
     if constexpr (R == 3 && !ALIAS) dma_tile(slot2, clamp(2));
-  });
+  };
+  if constexpr (Q8)
+    mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da,
+                        [] {}, first_dma);
+  else
+    mf_stage<M, BPW, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {}, first_dma);
   if constexpr (ALIAS) {
     // every wave has read its staged operands before the shared slot refills
     asm volatile("" ::: "memory");
@@ -741,7 +754,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       for (int k = 0; k < BPW / 8; ++k)
         w.sc[k] = *reinterpret_cast<const u32x4*>(slot + 16 * G::PRS + c * G::SRS + int(blk0) * 2 + k * 16);
       const MfNext none{};
-      mf_tile<NP, BPW, RR, XT, false>(w, ah, al, acc, mlo, mhi, magic, none, blk0, g);
+      if constexpr (Q8)
+        mf_tile_q8<NP, BPW, RR, false>(w, aq, da, acc, none, blk0, g);
+      else
+        mf_tile<NP, BPW, RR, XT, false>(w, ah, al, acc, mlo, mhi, magic, none, blk0, g);
     }
     float* rb = red + parity * (WAVES * MF_ROWS * M);
     parity ^= 1;
