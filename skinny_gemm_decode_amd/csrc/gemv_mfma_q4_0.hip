@@ -11,13 +11,19 @@ namespace skg {
 void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
   SKG_MF(2, 2, 1)
   SKG_MF(3, 2, 1)
+  // M = 4, 6: the LDS-ring kernel with one fp16 activation term, 12.00 /
+  // 12.79 us against 12.58 / 12.94 (it loses at M = 2, 3, 5 by 1-2%)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 4, 1, 3, false>());
   SKG_MF(4, 2, 1)
   SKG_MF(5, 2, 1)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 6, 1, 3, false>());
   SKG_MF(6, 2, 1)
-  // M = 7: the LDS-ring kernel, 13.00 against 13.24 us (three A1 B1 B2 A2
-  // cycles; K = 4096 only, other K take the register-fed kernel below); it
-  // loses at M = 3 (13.10 against 11.96), 5 and 8 and ties at 6
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 2, 2, false>());
+  // M = 7, 8: the LDS-ring kernel with one fp16 activation term (one
+  // rounding, 2^-11, inside the accuracy bound), 12.24 / 12.82 us against
+  // 12.99 (the ring with two terms) / 14.18 (register-fed, one term), three
+  // A1 B1 B2 A2 cycles; K = 4096 only, other K take the register-fed kernels
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 1, 2, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 1, 2, false>());
   SKG_MF(7, 2, 1)
   SKG_MF(8, 1, 2)  // one fp16 term: within the accuracy bound, 8% faster at M = 8
 }
@@ -27,6 +33,7 @@ void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 1, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 2, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 4, 2, 3, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 2, 2, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 2, 2, false>());
   SKG_MF(1, 2, 1)
   SKG_MF(1, 1, 2)

@@ -11,19 +11,22 @@ namespace skg {
 // two planes per block the two-term activation does not fit the register
 // file beyond M = 2, so these carry the activation as one fp16 term.
 void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
-  // M = 2..7: the LDS-ring kernel (weights copied straight into LDS,
-  // two-term activation) beats the register-fed and the vector kernels
-  // (three A1 B1 B2 A2 cycles each, us: M = 2 15.65 against 15.98, M = 3
-  // 16.43 against 18.07, M = 5 16.83 against 17.66, M = 6 17.06 against
-  // 17.85, M = 7 17.06 against 18.21; at M = 8 it loses, 19.73 against
-  // 18.84).  It is compiled for K = 4096 only; other K fall through to the
-  // register-fed kernel (M >= 4) or the vector kernel (M = 2, 3).
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 2, 2, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 3, 2, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 4, 2, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 5, 2, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 6, 2, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 7, 2, 2, true>());
+  // M = 2..8: the LDS-ring kernel (weights copied straight into LDS) with
+  // one fp16 activation term (one rounding, 2^-11, inside the accuracy
+  // bound) beats the ring with two terms, the register-fed and the vector
+  // kernels; three A1 B1 B2 A2 cycles each, us (one term / two terms /
+  // previous default): M = 2 15.46 / 15.70 / 15.98 vector, M = 3 15.73 /
+  // 16.47 / 18.07 vector, M = 4 15.65 / 16.52, M = 5 16.10 / 16.79 / 17.66,
+  // M = 6 16.36 / 17.03 / 17.85, M = 7 16.54 / 17.05 / 18.21, M = 8 17.06 /
+  // 19.73 / 18.81 register-fed.  It is compiled for K = 4096 only; other K
+  // fall through to the register-fed kernel (M >= 4) or the vector kernel.
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 2, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 3, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 4, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 5, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 6, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 7, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 8, 1, 2, true>());
   SKG_MF(4, 1, 1)
   SKG_MF(5, 1, 1)
   SKG_MF(6, 1, 1)
@@ -33,7 +36,13 @@ void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
 // Registered after the vector-ALU instances: measurement variants.
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 1, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 5, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 6, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 7, 2, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 8, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 2, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 3, 2, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 4, 2, 2, true>());
   SKG_MF(1, 2, 1)
   SKG_MF(2, 2, 1)
   SKG_MF(3, 2, 1)
