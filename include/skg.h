@@ -256,6 +256,16 @@ skg_status skg_debug_block_dots(skg_fmt fmt, int64_t N, int64_t K, int64_t n0, i
  */
 skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
 
+/*
+ * Launch-floor reference: enqueues one kernel of `grid` workgroups of `block`
+ * threads that does nothing, so back-to-back launches of it measure the fixed
+ * cost every launch pays ("Six hypotheses, four refutations", Hypothesis
+ * ledger: the per-kernel floor that the dispatch count multiplies).
+ * grid : 1 .. 2^31 - 1.  block : a multiple of 64 in 64 .. 1024.  Touches no
+ * memory.  SKG_E_SHAPE for any other grid or block.
+ */
+skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream);
+
 
 /*
  * Tuning hooks (measurement only).  The GEMV kernels are compiled in several
@@ -289,11 +299,21 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
  * skg_set_lds_pad: extra dynamic LDS bytes (0..65536) requested by every gemv
  *   launch, which lowers occupancy without changing the code (the MI50 case
  *   study's diagnostic control).  Initial value: $SKG_LDS_PAD_BYTES or 0.
+ *   The environment value must be a base-10 integer in 0..65536 (blanks
+ *   around it allowed); any other value makes every skg_gemv and
+ *   skg_gemv_multi call return SKG_E_INVALID_ARG, before any HIP call, until
+ *   skg_set_lds_pad sets a valid pad.
  * These settings are process-wide and must not change while another thread
  * is launching gemv work.
  */
 skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw);
 int skg_gemv_variants(int* out, int max_entries);
+/* skg_gemv_default_variant: the record (8 ints, as skg_gemv_variants) of the
+ * variant a skg_gemv / skg_gemv_multi call with this (fmt, M, epi, K) runs
+ * now, honouring skg_gemv_set_variant; out is host memory.  SKG_E_UNSUPPORTED
+ * when no compiled variant takes K; SKG_E_INVALID_ARG / SKG_E_SHAPE for an
+ * unknown fmt or epilogue or M outside 1..8.  Host only, no HIP call. */
+skg_status skg_gemv_default_variant(skg_fmt fmt, int M, skg_epi epi, int64_t K, int* out);
 skg_status skg_set_lds_pad(int64_t bytes);
 /* skg_gemm_tiled_set_variant: prefill kernel organisation, 0 = every wave
  * decodes weights and runs MFMAs, 1 = producer waves decode, consumer waves

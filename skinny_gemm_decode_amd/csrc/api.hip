@@ -4,6 +4,7 @@
 // a GPU; nothing falls back to another code path when validation fails.
 #include <atomic>
 #include <climits>
+#include <cerrno>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -95,6 +96,25 @@ std::mutex g_sel_mu;
 // selected registry index per (fmt, M, epi); -1 = default (first registered)
 int g_sel[5][9][3];
 std::atomic<int64_t> g_lds_pad{0};
+// Set when SKG_LDS_PAD_BYTES holds something other than an integer in
+// 0..kMaxLdsPad: every GEMV call is then refused until skg_set_lds_pad
+// replaces the value.
+constexpr int64_t kMaxLdsPad = 64 * 1024;
+std::atomic<bool> g_lds_pad_env_bad{false};
+char g_lds_pad_env[64] = "";
+
+// Whole-string base-10 integer in [0, kMaxLdsPad] (leading/trailing blanks allowed).
+bool parse_lds_pad(const char* s, int64_t* out) {
+  if (!s) return false;
+  errno = 0;
+  char* end = nullptr;
+  const long long v = std::strtoll(s, &end, 10);
+  if (end == s || errno == ERANGE) return false;
+  while (*end == ' ' || *end == '\t') ++end;
+  if (*end != '\0' || v < 0 || v > kMaxLdsPad) return false;
+  *out = int64_t(v);
+  return true;
+}
 
 void init_registry() {
   std::call_once(g_reg_once, [] {
@@ -118,7 +138,15 @@ void init_registry() {
     for (auto& a : g_sel)
       for (auto& b : a)
         for (int& c : b) c = -1;
-    if (const char* e = std::getenv("SKG_LDS_PAD_BYTES")) g_lds_pad.store(std::atoll(e));
+    if (const char* e = std::getenv("SKG_LDS_PAD_BYTES")) {
+      int64_t pad = 0;
+      if (parse_lds_pad(e, &pad)) {
+        g_lds_pad.store(pad);
+      } else {
+        std::snprintf(g_lds_pad_env, sizeof g_lds_pad_env, "%s", e);
+        g_lds_pad_env_bad.store(true);
+      }
+    }
     g_reg = v;
   });
 }
@@ -304,6 +332,10 @@ skg_status check_gemv_common(int fmt, int64_t M, int64_t K, const void* W, const
     return fail(SKG_E_INVALID_ARG, "unknown fmt %d", fmt);
   }
   if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "gemv needs 1 <= M <= 8 (got %lld)", (long long)M);
+  init_registry();
+  if (g_lds_pad_env_bad.load())
+    return fail(SKG_E_INVALID_ARG, "SKG_LDS_PAD_BYTES='%s' is not an integer in 0..%lld", g_lds_pad_env,
+                (long long)kMaxLdsPad);
   if (!W || !x) return fail(SKG_E_INVALID_ARG, "null W or x");
   if (!aligned(W, 16)) return fail(SKG_E_ALIGN, "W must be 16-byte aligned");
   const bool q8 = (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1);
@@ -509,6 +541,30 @@ skg_status skg_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStre
   return ok();
 }
 
+skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream) {
+  if (grid < 1 || grid > INT32_MAX) return fail(SKG_E_SHAPE, "grid must be 1..2^31-1 (got %lld)", (long long)grid);
+  if (block < 64 || block > 1024 || block % 64)
+    return fail(SKG_E_SHAPE, "block must be a multiple of 64 in 64..1024 (got %d)", block);
+  skg_status st = check_device();
+  if (st != SKG_OK) return st;
+  hipError_t e = launch_empty(grid, block, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "empty launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+skg_status skg_gemv_default_variant(skg_fmt fmt, int M, skg_epi epi, int64_t K, int* out) {
+  if (!is_gemv_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown gemv fmt %d", int(fmt));
+  if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "M must be 1..8");
+  if (epi != SKG_EPI_NONE && epi != SKG_EPI_SWIGLU && epi != SKG_EPI_SWIGLU_Q8_1)
+    return fail(SKG_E_INVALID_ARG, "unknown epilogue");
+  if (!out) return fail(SKG_E_INVALID_ARG, "null out");
+  const GemvEntry* e = find_variant(fmt, M, epi, K);
+  if (!e) return fail(SKG_E_UNSUPPORTED, "no compiled variant takes K=%lld", (long long)K);
+  const int rec[8] = {e->fmt, e->M, e->epi, e->ro, e->j, e->xlds, e->waves, e->kw};
+  for (int i = 0; i < 8; ++i) out[i] = rec[i];
+  return ok();
+}
+
 skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw) {
   if (!is_gemv_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown gemv fmt %d", int(fmt));
   if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "M must be 1..8");
@@ -561,9 +617,10 @@ skg_status skg_gemm_tiled_set_variant(int variant) {
 }
 
 skg_status skg_set_lds_pad(int64_t bytes) {
-  if (bytes < 0 || bytes > 64 * 1024) return fail(SKG_E_INVALID_ARG, "LDS pad must be 0..65536 bytes");
+  if (bytes < 0 || bytes > kMaxLdsPad) return fail(SKG_E_INVALID_ARG, "LDS pad must be 0..65536 bytes");
   init_registry();
   g_lds_pad.store(bytes);
+  g_lds_pad_env_bad.store(false);
   return ok();
 }
 

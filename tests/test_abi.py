@@ -244,3 +244,42 @@ def test_binding_checks_buffer_sizes(skg):
     W, x, y = _FakeTensor(skg.packed_size(skg.Q4_0_F32, 64, 256)), _FakeTensor(4 * 256), _FakeTensor(4 * 64 - 4)
     with pytest.raises(ValueError, match="y holds"):
         skg.gemv(skg.Q4_0_F32, 1, 256, 64, W, x, y)
+
+
+_PAD_PROBE = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r})
+import skinny_gemm_decode_amd as skg
+lib = skg.lib
+# W = NULL: rejected on the host by every path, so nothing is ever launched;
+# the message tells which check refused the call
+st = lib.skg_gemv(2, 1, 4096, 64, None, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None)
+print(st, lib.skg_last_error().decode())
+st2 = lib.skg_set_lds_pad(ctypes.c_int64(128))
+st3 = lib.skg_gemv(2, 1, 4096, 64, None, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), None)
+print(st2, st3, lib.skg_last_error().decode())
+"""
+
+
+@pytest.mark.parametrize("value,bad", [("-5", True), ("70000", True), ("12abc", True), ("", True),
+                                       ("99999999999999999999999", True), ("0", False), ("1024", False),
+                                       (" 4096 ", False), ("65536", False)])
+def test_lds_pad_environment_value_is_validated(skg, value, bad):
+    """SKG_LDS_PAD_BYTES outside 0..65536 (or not an integer) refuses every
+    GEMV call with SKG_E_INVALID_ARG until skg_set_lds_pad sets a valid pad;
+    a valid value is accepted (the call then fails only on its null W)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, SKG_LDS_PAD_BYTES=value)
+    r = subprocess.run([sys.executable, "-c", _PAD_PROBE.format(root=ROOT)], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    first, second = r.stdout.strip().splitlines()[-2:]
+    st, msg = first.split(" ", 1)
+    assert int(st) == 1   # SKG_E_INVALID_ARG either way
+    if bad:
+        assert "SKG_LDS_PAD_BYTES" in msg, msg
+    else:
+        assert "null W" in msg, msg
+    st2, st3, msg3 = second.split(" ", 2)
+    assert int(st2) == 0 and int(st3) == 1 and "null W" in msg3, second

@@ -222,3 +222,84 @@ def test_tolerance_helpers():
     assert not ok
     ok, _ = oracle.check_close([np.nan], [0.0], oracle.tolerance(np.array([1.0])))
     assert not ok
+
+
+BF16 = (8, -126)   # significand bits incl. the hidden bit, minimum normal exponent
+
+
+@pytest.mark.parametrize("N,K,M", [(3, 96, 2), (2, 64, 1)])
+def test_q8_0_q8_1_reference_exact_rational(N, K, M):
+    """gemv_q8_0_q8_1_ref against exact rational sums of the decoded
+    operands: q8_0 values d*q from the block bytes, Q8_1 values dA*qa from the
+    activation block bytes, multiplied and summed as Fractions."""
+    rng = si.rng_for(0, 99, 15 + N + K)
+    W = si.q8_0_weights(rng, N, K)
+    xq = oracle.quantize_q8_1(si.activations_f32(rng, M, K))
+    y, bound = oracle.gemv_q8_0_q8_1_ref(W, xq)
+    assert y.shape == (M, N) and bound.shape == (M, N)
+    for m in range(M):
+        acts = []
+        for b in range(K // 32):
+            dA, _, qa = ex.q8_1_block_fields(xq[m, b].tobytes())
+            acts += [dA * v for v in qa]
+        for n in range(N):
+            row = ex.row_values("q8_0", W[n].tobytes(), K)
+            ye = sum(r * a for r, a in zip(row, acts))
+            be = sum(abs(r * a) for r, a in zip(row, acts))
+            assert abs(float(ye) - y[m, n]) <= 1e-13 * float(be) + 1e-300
+            assert abs(float(be) - bound[m, n]) <= 1e-13 * float(be) + 1e-300
+
+
+def test_q8_0_q8_1_reference_hand_block():
+    """One hand-worked block pair: weights d=0.5 with codes 1..32, activation
+    d=0.25 with codes all 2 (block sum irrelevant to the decoded dot):
+    y = 0.5 * 0.25 * 2 * (1 + ... + 32) = 0.25 * 528 = 132."""
+    W = np.zeros((1, 1, 34), np.uint8)
+    W[0, 0, 0:2] = [0x00, 0x38]                      # fp16 0.5
+    W[0, 0, 2:] = np.arange(1, 33, dtype=np.uint8)
+    xq = np.zeros((1, 1, 36), np.uint8)
+    xq[0, 0, 0:2] = [0x00, 0x34]                     # fp16 0.25
+    xq[0, 0, 4:] = 2
+    y, bound = oracle.gemv_q8_0_q8_1_ref(W, xq)
+    assert y[0, 0] == 132.0 and bound[0, 0] == 132.0
+    xq[0, 0, 4:] = np.uint8(0xFE)                    # codes -2: the sign flips
+    y, bound = oracle.gemv_q8_0_q8_1_ref(W, xq)
+    assert y[0, 0] == -132.0 and bound[0, 0] == 132.0
+
+
+@pytest.mark.parametrize("kind", ["q4_0", "q8_0"])
+def test_gemm_tiled_bf16_weight_reference_exact(kind):
+    """y_bf16w of gemm_tiled_ref: every decoded weight rounded to bf16 by
+    exact integer arithmetic (nearest, ties to even), then the exact rational
+    product; a truncating or ties-away rounding fails the tie rows below."""
+    rng = si.rng_for(0, 99, 16)
+    M, N, K = 3, 6, 64
+    W = si.weights(kind, rng, N, K)
+    # rows whose decoded weights sit exactly halfway between two bf16 values
+    # (both tie directions), one that rounds up into the next binade and one
+    # that rounds down; the other rows keep their random blocks
+    half = {"q4_0": (18, 9), "q8_0": (34, 1)}[kind]
+    blk, code = half
+    for n, dbits in ((0, 0x3C04), (1, 0x3C0C), (2, 0x3FFF), (3, 0x3C01)):
+        W[n, :, 0] = dbits & 0xFF
+        W[n, :, 1] = dbits >> 8
+        if kind == "q4_0":
+            W[n, :, 2:] = 0x99 if n < 3 else W[n, :, 2:]   # codes 9: w = d
+        else:
+            W[n, :, 2:] = code if n < 3 else W[n, :, 2:]   # codes 1: w = d
+    assert W.shape[-1] == blk
+    A = si.activations_bf16(rng, M, K)
+    _, _, y_b = oracle.gemm_tiled_ref(W, A, kind)
+    for n in range(N):
+        wr = [ex.round_binary(v, BF16) for v in ex.row_values(kind, W[n].tobytes(), K)]
+        if n == 0:   # d = 1 + 2^-8: halfway between 1 and 1 + 2^-7; the even one is 1
+            assert wr[0] == 1
+        if n == 1:   # d = 1 + 3*2^-8: halfway between 1 + 2^-7 and 1 + 2^-6; the even one is 1 + 2^-6
+            assert wr[0] == 1 + Fraction(1, 64)
+        if n == 2:   # d = 2 - 2^-10 rounds up into the next binade
+            assert wr[0] == 2
+        for m in range(M):
+            av = [ex.bf16_value(int(v)) for v in A[m]]
+            ye = sum(w * a for w, a in zip(wr, av))
+            be = sum(abs(w * a) for w, a in zip(wr, av))
+            assert abs(float(ye) - y_b[m, n]) <= 1e-13 * float(be) + 1e-300, (m, n)
