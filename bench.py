@@ -6,23 +6,31 @@ weights per launch), the decode shape of "The Shape That Actually Matters"
 (The shape a decode step actually runs).  Following its instrument (The
 instrument came first): enough distinct weight buffers rotate per launch that
 the working set (>= 2 GB) is far past the 256 MB Infinity Cache, so every
-launch streams its weights from HBM; warm-up on the same rotation; then the
-timed launches in repeats of 200, and no ratio is claimed unless the
-run-to-run spread of the repeats is under 5%.
+launch streams its weights from HBM; at least 1 s of warm-up on the same
+rotation; then repeats of 200 timed launches, and no ratio is claimed unless
+there are at least 10 repeats and their run-to-run spread is under 5%
+(`config.protocol_ok`).
 
-One step = one GEMV launch on the next rotation buffer.  `value` is achieved
-HBM GB/s = algorithmic bytes (weights + x + y) per launch / time per launch.
-Times come from HIP events recorded on the stream the kernels run on.
+One step = one repeat of 200 GEMV launches, each on the next rotation buffer;
+--steps repeats are timed after --warmup untimed ones (plus whatever tops the
+warm-up up to 1 s).  `value` is achieved HBM GB/s = algorithmic bytes (weights
++ x + y) per launch / time per launch.  Times come from HIP events recorded on
+the stream the kernels run on.  Before any workload is timed, sampled outputs
+of five of its rotation buffers are checked against the CPU oracle; a failure
+stops the run (no number is reported for a wrong kernel).
 
-Further arms (same protocol, shorter): the streaming-read ceiling, q8_0 / q4_0
-x fp32 and q4_0 / q8_0 x Q8_1 at M=1..8 (K=4096, N=14336), the Llama-2-7B-shaped
-q4_0 x Q8_1 decode layer over 32 distinct layers (plain, with the SwiGLU launch
+Further arms (same protocol): the launch floor (an empty kernel back to back,
+eager and from a graph, and the streaming read at 33 MB .. 1 GiB), the
+streaming-read ceiling, q8_0 / q4_0 x fp32 and q4_0 / q8_0 x Q8_1 at M=1..8
+(K=4096, N=14336; fp32-activation defaults that carry the activation as one
+fp16 term are timed beside the two-term kernel), the Llama-2-7B-shaped q4_0 x
+Q8_1 decode layer over 32 distinct layers (plain, with the SwiGLU launch
 writing Q8_1, and with the layer's RMSNorm as its own launch or writing Q8_1
 itself), the fused RMSNorm -> Q8_1 launch alone, the q8_0 M=1 K=256 N=512
 launch-bound case, and the M=512 MFMA prefill tile.  The CPU oracle is timed
 on a bounded sample of the headline workload on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 2000] [--warmup 60000] [--arms all|none|a,b]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 5] [--arms all|none|a,b] [--ms 1,2,4,8]
 Prints one JSON line on stdout; per-arm details go to the --details file when
 one is given.
 """
@@ -136,40 +144,36 @@ class Telemetry:
 
 
 class Timer:
-    """Times `launch(i)` calls on torch's current stream with HIP events."""
+    """Times `launch(i, stream)` calls on torch's current stream with HIP events."""
 
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, launch, n_rot: int, steps: int, warmup: int, per_repeat: int = 200, warm_s: float | None = None,
-            telemetry: Telemetry | None = None):
+    def run(self, launch, n_rot: int, repeats: int = 10, per_repeat: int = 200, warm_repeats: int = 0,
+            warm_s: float | None = None, telemetry: Telemetry | None = None):
+        """`warm_repeats` untimed repeats, topped up to at least `warm_s`
+        seconds of untimed launches, then `repeats` timed repeats of
+        `per_repeat` launches, each bracketed by events; launch i uses
+        rotation slot i % n_rot."""
         torch = self.torch
         stream = torch.cuda.current_stream()
         sh = stream.cuda_stream
         i = 0
-        if warm_s is not None:
-            t_end = time.time() + warm_s
-            while time.time() < t_end:
-                for _ in range(per_repeat):
-                    launch(i % n_rot, sh)
-                    i += 1
-                torch.cuda.synchronize()
-        for _ in range(warmup):
-            launch(i % n_rot, sh)
-            i += 1
-        torch.cuda.synchronize()
-        reps = []
-        left = steps
-        while left > 0:
-            n = min(per_repeat, left)
-            reps.append(n)
-            left -= n
-        events = [torch.cuda.Event(enable_timing=True) for _ in range(len(reps) + 1)]
+        t0 = time.time()
+        done = 0
+        while done < warm_repeats or (warm_s is not None and time.time() - t0 < warm_s):
+            for _ in range(per_repeat):
+                launch(i % n_rot, sh)
+                i += 1
+            done += 1
+            torch.cuda.synchronize()
+        warm_time = time.time() - t0
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(repeats + 1)]
         torch.cuda.synchronize()
         samples = []
         events[0].record(stream)
-        for r, n in enumerate(reps):
-            for _ in range(n):
+        for r in range(repeats):
+            for _ in range(per_repeat):
                 launch(i % n_rot, sh)
                 i += 1
             events[r + 1].record(stream)
@@ -178,28 +182,45 @@ class Timer:
             if telemetry is not None:
                 samples.append(telemetry.read())
         torch.cuda.synchronize()
-        rep_us = [events[r].elapsed_time(events[r + 1]) * 1000.0 / reps[r] for r in range(len(reps))]
+        rep_us = [events[r].elapsed_time(events[r + 1]) * 1000.0 / per_repeat for r in range(repeats)]
         total_ms = events[0].elapsed_time(events[-1])
-        res = summarize(rep_us, total_ms, steps)
+        res = summarize(rep_us, total_ms, repeats * per_repeat)
+        res.update(repeats=repeats, launches_per_repeat=per_repeat, warm_repeats=done,
+                   warm_s=round(warm_time, 3))
         if telemetry is not None:
             res["telemetry_per_repeat"] = samples
             res["telemetry"] = Telemetry.summary(samples)
         return res
 
 
-def summarize(rep_us, total_ms, steps):
+#: the instrument of "The Shape That Actually Matters" (The instrument came
+#: first): at least 1 s of warm-up, 200 launches per repeat, 10 repeats, and no
+#: ratio claimed unless the spread of the repeats is under 5%
+PROTOCOL = {"min_warm_s": 1.0, "per_repeat": 200, "min_repeats": 10, "max_spread": 0.05}
+
+
+def summarize(rep_us, total_ms, launches):
+    """Per-launch time of a run of repeats.  spread = (max - min) / mean of
+    the repeats, None with fewer than two (no spread can be claimed then)."""
     mean = statistics.fmean(rep_us)
-    spread = (max(rep_us) - min(rep_us)) / mean if mean > 0 else 0.0
+    spread = (max(rep_us) - min(rep_us)) / mean if (len(rep_us) >= 2 and mean > 0) else None
     return {
-        "us_per_launch": total_ms * 1000.0 / steps,
+        "us_per_launch": total_ms * 1000.0 / launches,
         "us_median": statistics.median(rep_us),
         "us_min": min(rep_us),
         "us_max": max(rep_us),
         "spread": spread,
-        "spread_ok": spread < 0.05,
+        "spread_ok": spread is not None and spread < PROTOCOL["max_spread"],
         "repeats_us": [round(v, 4) for v in rep_us],
         "total_ms": total_ms,
     }
+
+
+def protocol_ok(res) -> bool:
+    """The run followed the instrument: enough warm-up, enough repeats of
+    enough launches, and a spread under 5%."""
+    return (res["warm_s"] >= PROTOCOL["min_warm_s"] and res["repeats"] >= PROTOCOL["min_repeats"]
+            and res["launches_per_repeat"] >= PROTOCOL["per_repeat"] and res["spread_ok"])
 
 
 # --------------------------------------------------------------------------
@@ -210,31 +231,33 @@ def rotation_count(bytes_per_buffer: int, minimum: int = 1) -> int:
     return max(minimum, -(-ROTATION_BYTES // bytes_per_buffer))
 
 
-def make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0, keep_rows=None):
-    """n_rot packed weight buffers generated on the device; optionally keeps
-    host copies of a few canonical rows per buffer (for the oracle sample)."""
-    bufs, kept = [], []
+def make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0, keep_rows=None, keep_bufs=()):
+    """n_rot packed weight buffers generated on the device; keeps host copies
+    of the canonical rows `keep_rows` of the buffers `keep_bufs` (for the
+    oracle gate)."""
+    bufs, kept = [], {}
     idx = None if keep_rows is None else torch.as_tensor(keep_rows, device="cuda")
     for b in range(n_rot):
         W = si.torch_weights(kind, N, K, seed0 + b, "cuda")
         P = skg.pack_weights(fmt, N, K, W)
-        if idx is not None and b < 4:
-            kept.append(W[idx].cpu().numpy())
+        if idx is not None and b in keep_bufs:
+            kept[b] = W[idx].cpu().numpy()
         bufs.append(P)
         del W
     torch.cuda.synchronize()
     return bufs, kept
 
 
-def check_outputs_sane(torch, ys):
-    """Pre-timing gate that needs no reference: outputs are finite, and two
-    launches on the same buffer agree bit for bit (checked by the caller)."""
-    for y in ys:
-        if not bool(torch.isfinite(y).all()):
-            raise RuntimeError("non-finite GEMV output; refusing to time")
+def gate_rows(N, n=24, seed=0):
+    """Rows checked against the oracle before an arm is timed: both ends, the
+    last workgroup's tail and a seeded sample."""
+    import numpy as np
+    rows = {0, 1, N - 2, N - 1} | set(range(max(0, N - 20), N))
+    rows |= set(np.random.default_rng(seed).choice(N, min(n, N), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
-def compare_abba(timer, launch_a, launch_b, n_rot, steps, cycles=3):
+def compare_abba(timer, launch_a, launch_b, n_rot, launches, cycles=3):
     """Interleaved comparison of two launch functions: `cycles` independent
     cycles in the fixed order A1 B1 B2 A2, and the ratio B / A as the mean of
     the per-cycle ratios (the RX 6700 XT write-up, Approach & Methodology;
@@ -242,24 +265,31 @@ def compare_abba(timer, launch_a, launch_b, n_rot, steps, cycles=3):
     than A/B).  Clock or temperature drift within a cycle cancels."""
     out = []
     for _ in range(cycles):
-        legs = [timer.run(f, n_rot, steps, 0)["us_per_launch"] for f in (launch_a, launch_b, launch_b, launch_a)]
+        legs = [timer.run(f, n_rot, repeats=max(1, launches // 200))["us_per_launch"]
+                for f in (launch_a, launch_b, launch_b, launch_a)]
         a, b = (legs[0] + legs[3]) / 2, (legs[1] + legs[2]) / 2
         out.append({"a_us": [round(legs[0], 4), round(legs[3], 4)], "b_us": [round(legs[1], 4), round(legs[2], 4)],
                     "b_over_a": b / a})
-    return {"order": "A1 B1 B2 A2", "cycles": out, "steps_per_leg": steps,
+    return {"order": "A1 B1 B2 A2", "cycles": out, "launches_per_leg": launches,
             "b_over_a": statistics.fmean(c["b_over_a"] for c in out)}
 
 
-def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmup, warm_s, x_host, keep_rows=None,
-                   graph=False, telemetry=None, abba=0):
-    import ctypes
+def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, x_host, repeats=10, warm_repeats=0,
+                   warm_s=1.0, graph=False, telemetry=None, abba=0, variants=()):
+    """One GEMV workload over a >= 2 GB rotation: oracle gate on sampled rows
+    of five rotation buffers, then the timed repeats, the streaming read of
+    the same buffers, and optionally an ABBA check against that read, graph
+    replay and further kernel variants (each gated before it is timed)."""
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
     log(f"[{name}] {n_rot} rotation buffers x {wbytes / 1e6:.1f} MB")
+    rows = gate_rows(N, seed=M)
+    keep_bufs = sorted({0, 1, 2, 3, n_rot - 1})
     bufs, kept = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=1000 * (fmt + 1) + 10 * M,
-                                      keep_rows=keep_rows)
+                                      keep_rows=rows, keep_bufs=keep_bufs)
     x = torch.from_numpy(x_host).cuda()
-    if fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1):
+    q8 = fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+    if q8:
         xin = skg.quantize_act_q8_1(x)
         xbytes = xin.numel()
     else:
@@ -270,25 +300,35 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
     xp, yp = xin.data_ptr(), [y.data_ptr() for y in ys]
     lib = skg.lib
     sh = torch.cuda.current_stream().cuda_stream
+    idx = torch.as_tensor(rows, device="cuda")
 
     def launch(i, sh):
         lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[i & 1], sh)
 
-    # gate: finite and deterministic on every rotation buffer
-    outs = []
-    for i in range(n_rot):
-        skg.check(lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[0], sh))
-        a = ys[0].clone()
-        skg.check(lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[1], sh))
-        if not torch.equal(a, ys[1]):
-            raise RuntimeError(f"[{name}] GEMV not deterministic on buffer {i}")
-        outs.append(a)
-    check_outputs_sane(torch, outs)
-    res = timer.run(launch, n_rot, steps, warmup, warm_s=warm_s, telemetry=telemetry)
+    def gate(label):
+        """Finite, deterministic on every rotation buffer, and within the
+        oracle's tolerance on the sampled rows of the kept buffers."""
+        outs = {}
+        for i in range(n_rot):
+            skg.check(lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[0], sh))
+            a = ys[0].clone()
+            skg.check(lib.skg_gemv(fmt, M, K, N, wp[i], xp, yp[1], sh))
+            if not torch.equal(a, ys[1]):
+                raise RuntimeError(f"[{label}] GEMV not deterministic on buffer {i}; refusing to time")
+            if not bool(torch.isfinite(a).all()):
+                raise RuntimeError(f"[{label}] non-finite GEMV output on buffer {i}; refusing to time")
+            if i in kept:
+                outs[i] = a[:, idx].cpu().numpy()
+        xq_gpu = xin.cpu().numpy() if q8 else None
+        return oracle_gate_gemv(label, kind, fmt, skg, x_host, xq_gpu, [(kept[b], outs[b]) for b in keep_bufs])
+
+    worst = gate(name)
+    res = timer.run(launch, n_rot, repeats=repeats, warm_repeats=warm_repeats, warm_s=warm_s, telemetry=telemetry)
     alg = wbytes + xbytes + M * N * 4
     res.update(name=name, fmt=skg.FMT_NAMES[fmt], M=M, N=N, K=K, rotation_buffers=n_rot,
                working_set_bytes=n_rot * wbytes, algorithmic_bytes=alg,
-               gbs=alg / (res["us_per_launch"] * 1e-6) / 1e9)
+               gbs=alg / (res["us_per_launch"] * 1e-6) / 1e9, oracle_gate_worst_err_over_tol=worst,
+               variant=skg.gemv_default_variant(fmt, M, skg.EPI_NONE, K))
     res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
     # achievable reference: the streaming-read kernel over the same buffers
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -297,7 +337,7 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
     def read(i, sh):
         lib.skg_stream_read(wp[i], wbytes, skp, sh)
 
-    ceil = timer.run(read, n_rot, steps, 0, warm_s=0.1)
+    ceil = timer.run(read, n_rot, repeats=repeats, warm_s=0.1)
     res["ceiling_us"] = ceil["us_per_launch"]
     res["ceiling_gbs"] = wbytes / (ceil["us_per_launch"] * 1e-6) / 1e9
     res["frac_ceiling"] = ceil["us_per_launch"] / res["us_per_launch"]
@@ -306,12 +346,20 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, steps, warmu
     if graph:
         res["graph"] = bench_graph(torch, launch, n_rot)
         res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
-    idx = None if keep_rows is None else torch.as_tensor(keep_rows, device="cuda")
-    extra = {"outputs": [o[:, idx].cpu().numpy() if idx is not None else None for o in outs[:4]],
-             "kept_rows": kept, "x": x_host}
+    res["variants"] = []
+    for v in variants:
+        skg.gemv_set_variant(fmt, M, skg.EPI_NONE, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+        try:
+            vw = gate(f"{name} variant {v}")
+            vr = timer.run(launch, n_rot, repeats=repeats, warm_s=0.3)
+        finally:
+            skg.gemv_set_variant(fmt, M, skg.EPI_NONE, 0)
+        res["variants"].append({"variant": v, "us_per_launch": vr["us_per_launch"], "spread": vr["spread"],
+                                "gbs": alg / (vr["us_per_launch"] * 1e-6) / 1e9,
+                                "oracle_gate_worst_err_over_tol": vw})
     del bufs
     torch.cuda.empty_cache()
-    return res, extra
+    return res
 
 
 def bench_graph(torch, launch, n_rot, per_graph=200, repeats=10):
@@ -342,7 +390,7 @@ def bench_graph(torch, launch, n_rot, per_graph=200, repeats=10):
     return summarize(rep_us, ev[0].elapsed_time(ev[-1]), per_graph * repeats)
 
 
-def bench_ceiling(skg, torch, timer, steps, warm_s):
+def bench_ceiling(skg, torch, timer, warm_s):
     """Streaming-read ceiling over a >= 2 GB rotation of 100.7 MB buffers."""
     nbytes = 12288 * 4096 * 2
     n_rot = rotation_count(nbytes)
@@ -357,7 +405,7 @@ def bench_ceiling(skg, torch, timer, steps, warm_s):
         lib.skg_stream_read(bp[i], nbytes, sp, sh)
 
     skg.check(lib.skg_stream_read(bp[0], nbytes, sp, sh))
-    res = timer.run(launch, n_rot, steps, 0, warm_s=warm_s)
+    res = timer.run(launch, n_rot, repeats=10, warm_s=warm_s)
     res.update(name="stream_read_ceiling", bytes=nbytes, rotation_buffers=n_rot,
                gbs=nbytes / (res["us_per_launch"] * 1e-6) / 1e9)
     res["frac_peak"] = res["gbs"] / PEAK_HBM_GBS
@@ -377,7 +425,7 @@ LAYER_MODES = {
 }
 
 
-def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
+def bench_layer(skg, si, torch, timer, warm_s, mode="plain"):
     """Llama-2-7B-shaped q4_0 x Q8_1 decode layer, M=1, 32 distinct layers.
     One step = one layer.
       plain (5 launches): quantize(x) -> QKV (one launch) -> gate/up + SwiGLU
@@ -477,7 +525,7 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
     torch.cuda.synchronize()
     if not bool(torch.isfinite(yo).all()) or (full and not bool(torch.isfinite(ya).all())):
         raise RuntimeError("layer chain produced non-finite output")
-    res = timer.run(launch, 32, steps, 0, per_repeat=32, warm_s=warm_s)
+    res = timer.run(launch, 32, repeats=20, per_repeat=32, warm_s=warm_s)
     wbytes = (skg.packed_size_multi(fmt, [D, D, D], D) + skg.packed_size_multi(fmt, [F, F], D)
               + skg.packed_size(fmt, D, F) + (skg.packed_size(fmt, D, D) if full else 0))
     alg = wbytes + sum(b for _, b in chain)
@@ -494,7 +542,7 @@ def bench_layer(skg, si, torch, timer, steps, warm_s, mode="plain"):
     return res
 
 
-def bench_norm(skg, si, torch, timer, steps, warm_s, M=1, K=4096):
+def bench_norm(skg, si, torch, timer, warm_s, M=1, K=4096):
     """The fused RMSNorm -> Q8_1 launch alone (M x K fp32 in, Q8_1 out), over
     32 distinct inputs and gains.  Launch-bound: 2 x 16 KB in, 4.6 KB out."""
     n = 32
@@ -512,19 +560,28 @@ def bench_norm(skg, si, torch, timer, steps, warm_s, M=1, K=4096):
 
     skg.check(lib.skg_rmsnorm_q8_1(M, K, ptrs[0][0], ptrs[0][1], 1e-5, None, qp, sh))
     torch.cuda.synchronize()
-    res = timer.run(launch, n, steps, 0, per_repeat=200, warm_s=warm_s)
+    # gate: the same launch also writing xn, its Q8_1 blocks the oracle's
+    # quantisation of that xn and xn within the RMSNorm tolerance
+    xn = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    skg.check(lib.skg_rmsnorm_q8_1(M, K, ptrs[0][0], ptrs[0][1], 1e-5, xn.data_ptr(), qp, sh))
+    oracle_gate_norm(f"rmsnorm_q8_1_m{M}_k{K}", xs[0].cpu().numpy(), gs[0].cpu().numpy(), 1e-5, xn.cpu().numpy(),
+                     xq.cpu().numpy())
+    res = timer.run(launch, n, repeats=10, per_repeat=200, warm_s=warm_s)
     res.update(name=f"rmsnorm_q8_1_m{M}_k{K}", algorithmic_bytes=4 * M * K + 4 * K + M * (K // 32) * 36)
     res["graph"] = bench_graph(torch, launch, n, per_graph=200)
     return res
 
 
-def bench_prefill(skg, si, torch, timer, steps, warm_s, kind="q4_0"):
+def bench_prefill(skg, si, torch, timer, warm_s, kind="q4_0"):
     M, N, K = 512, 14336, 4096
     fmt = skg.Q4_0_BF16 if kind == "q4_0" else skg.Q8_0_BF16
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
-    bufs, _ = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=70_000)
-    A = torch.from_numpy(si.activations_bf16(si.rng_for(0, 5, 9), M, K).view("int16")).cuda()
+    cols = gate_rows(N, n=40, seed=11)
+    bufs, kept = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=70_000, keep_rows=cols,
+                                      keep_bufs=(0, n_rot - 1))
+    A_host = si.activations_bf16(si.rng_for(0, 5, 9), M, K)
+    A = torch.from_numpy(A_host.view("int16")).cuda()
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     lib = skg.lib
     sh = torch.cuda.current_stream().cuda_stream
@@ -534,11 +591,16 @@ def bench_prefill(skg, si, torch, timer, steps, warm_s, kind="q4_0"):
     def launch(i, sh):
         lib.skg_gemm_tiled(fmt, M, K, N, wp[i], ap, yp, sh)
 
-    skg.check(lib.skg_gemm_tiled(fmt, M, K, N, wp[0], ap, yp, sh))
-    torch.cuda.synchronize()
-    if not bool(torch.isfinite(y).all()):
-        raise RuntimeError("prefill tile produced non-finite output")
-    res = timer.run(launch, n_rot, steps, 0, per_repeat=50, warm_s=warm_s)
+    mrows = gate_rows(M, n=24, seed=12)
+    for b in (0, n_rot - 1):
+        skg.check(lib.skg_gemm_tiled(fmt, M, K, N, wp[b], ap, yp, sh))
+        torch.cuda.synchronize()
+        if not bool(torch.isfinite(y).all()):
+            raise RuntimeError("prefill tile produced non-finite output; refusing to time")
+        oracle_gate_prefill(f"prefill_{kind} buffer {b}", kind, kept[b], A_host[mrows],
+                            y[torch.as_tensor(mrows, device="cuda")][:, torch.as_tensor(cols, device="cuda")]
+                            .cpu().numpy())
+    res = timer.run(launch, n_rot, repeats=10, per_repeat=50, warm_s=warm_s)
     flops = 2.0 * M * N * K
     res.update(name=f"prefill_{kind}_bf16_m512", M=M, N=N, K=K, rotation_buffers=n_rot, flop=flops,
                tflops=flops / (res["us_per_launch"] * 1e-6) / 1e12)
@@ -548,17 +610,116 @@ def bench_prefill(skg, si, torch, timer, steps, warm_s, kind="q4_0"):
     return res
 
 
+def bench_floor(skg, torch, timer, warm_s):
+    """What every launch costs before it moves a byte, and what a plain read
+    achieves per launch as the buffer grows: an empty kernel launched back to
+    back (one workgroup, and the headline's grid of 6144 x 512 threads),
+    eagerly and from a HIP graph, then the streaming read over rotations of
+    33.0 MB, 62.4 MB, 100.7 MB and 1 GiB buffers (>= 2 GB each)."""
+    lib = skg.lib
+    out = {"empty": [], "read": []}
+    for grid, block in ((1, 64), (6144, 512)):
+        def launch(i, sh, grid=grid, block=block):
+            lib.skg_empty_launch(grid, block, sh)
+
+        skg.check(lib.skg_empty_launch(grid, block, torch.cuda.current_stream().cuda_stream))
+        r = timer.run(launch, 1, repeats=10, warm_s=warm_s)
+        g = bench_graph(torch, launch, 1)
+        out["empty"].append({"grid": grid, "block": block, "us_per_launch": r["us_per_launch"],
+                             "spread": r["spread"], "graph_us_per_launch": g["us_per_launch"]})
+        log(f"[floor] empty kernel {grid} x {block}: {r['us_per_launch']:.2f} us eager, "
+            f"{g['us_per_launch']:.2f} us from a graph")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for nbytes in (33_030_144, 62_390_272, 100_663_296, 1 << 30):
+        n_rot = rotation_count(nbytes, minimum=2)
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n_rot)]
+        for b in bufs:
+            b.fill_(1)
+        bp = [b.data_ptr() for b in bufs]
+
+        def read(i, sh, nbytes=nbytes):
+            lib.skg_stream_read(bp[i], nbytes, sink.data_ptr(), sh)
+
+        r = timer.run(read, n_rot, repeats=10, per_repeat=200 if nbytes < (1 << 30) else 20, warm_s=0.2)
+        out["read"].append({"bytes": nbytes, "rotation_buffers": n_rot, "us_per_launch": r["us_per_launch"],
+                            "spread": r["spread"], "gbs": nbytes / (r["us_per_launch"] * 1e-6) / 1e9})
+        log(f"[floor] read {nbytes / 1e6:.1f} MB: {r['us_per_launch']:.2f} us "
+            f"({nbytes / (r['us_per_launch'] * 1e-6) / 1e9:.0f} GB/s)")
+        del bufs
+        torch.cuda.empty_cache()
+    # fixed cost per launch of the read: t(bytes) - bytes / (asymptotic rate of the 1 GiB read)
+    big = out["read"][-1]
+    rate = big["bytes"] / big["us_per_launch"]
+    for r in out["read"]:
+        r["fixed_us_vs_1gib_rate"] = r["us_per_launch"] - r["bytes"] / rate
+    return out
+
+
 # --------------------------------------------------------------------------
-# CPU baseline: the oracle itself, on a bounded sample of the headline workload
+# The oracle leg: the CPU oracle checks sampled outputs of every timed
+# workload before it is timed (no timing on a failure), and is itself timed
+# on a bounded sample of the headline workload on this host's cores.  Nothing
+# else in this file touches the oracle, and the GPU path never does.
 # --------------------------------------------------------------------------
 
-def cpu_baseline(si, gpu_sample, budget_s=12.0):
+def oracle_gate_gemv(label, kind, fmt, skg, x_host, xq_gpu, pairs):
+    """pairs: (canonical weight rows, GPU outputs [M, rows]) per kept rotation
+    buffer.  Q8_1 activations must equal the oracle's quantisation bit for
+    bit; every output must lie within the oracle's tolerance.  Returns the
+    worst error / tolerance; raises on any failure."""
+    import numpy as np
+
+    import oracle
+    q8 = fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+    if q8:
+        xq_ref = oracle.quantize_q8_1(x_host)
+        if not np.array_equal(xq_gpu.reshape(xq_ref.shape), xq_ref):
+            raise RuntimeError(f"[{label}] Q8_1 activation differs from the oracle; refusing to time")
+    worst = 0.0
+    for rows_w, y_gpu in pairs:
+        if kind == "bf16":
+            rows_w = rows_w.view(np.uint16)
+        if fmt == skg.Q4_0_Q8_1:
+            y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(rows_w, xq_ref)
+        elif fmt == skg.Q8_0_Q8_1:
+            y_ref, bound = oracle.gemv_q8_0_q8_1_ref(rows_w, xq_ref)
+        else:
+            x_kind = "bf16" if fmt == skg.BF16_BF16 else "f32"
+            xv = x_host.view(np.uint16) if x_kind == "bf16" else x_host
+            y_ref, bound = oracle.gemv_ref_fmt(kind, rows_w, xv, x_kind=x_kind)
+        ok, w = oracle.check_close(y_gpu, y_ref, oracle.tolerance(bound))
+        worst = max(worst, w)
+        if not ok:
+            raise RuntimeError(f"[{label}] GPU output outside the oracle's tolerance (worst err/tol {w:.3g}); "
+                               f"refusing to time")
+    return worst
+
+
+def oracle_gate_prefill(label, kind, cols_w, A_rows, y_gpu):
+    import oracle
+    y_ref, bound, _ = oracle.gemm_tiled_ref(cols_w, A_rows, kind)
+    ok, w = oracle.check_close(y_gpu, y_ref, oracle.tolerance(bound))
+    if not ok:
+        raise RuntimeError(f"[{label}] outside the oracle's tolerance (worst err/tol {w:.3g}); refusing to time")
+    return w
+
+
+def oracle_gate_norm(label, x, g, eps, xn_gpu, xq_gpu):
+    import numpy as np
+
+    import oracle
+    xn_ref = oracle.rmsnorm(x, g, eps)
+    if not np.all(np.abs(xn_gpu - xn_ref) <= oracle.rmsnorm_tolerance(xn_ref)):
+        raise RuntimeError(f"[{label}] RMSNorm outside the oracle's tolerance; refusing to time")
+    if not np.array_equal(xq_gpu.reshape(-1), oracle.quantize_q8_1(xn_gpu).reshape(-1)):
+        raise RuntimeError(f"[{label}] Q8_1 blocks differ from the oracle's quantisation; refusing to time")
+
+
+def cpu_baseline(si, x_host, budget_s=12.0):
     """The oracle as it stands, timed on this host's cores on a bounded
     sample of the headline workload: whole bf16 GEMVs (exact decode to fp64,
     numpy fp64 matvec) over two generated weight buffers, repeated until about
     budget_s seconds of oracle time; generation is not timed."""
-    import numpy as np
-
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -566,7 +727,7 @@ def cpu_baseline(si, gpu_sample, budget_s=12.0):
     except Exception:
         blas_threads = None
     N, K = 12288, 4096
-    x = gpu_sample["x"]
+    x = x_host
     Ws = [si.bf16_weights(si.rng_for(0, 2, 100 + b), N, K) for b in range(2)]
     times = []
     while sum(times) < budget_s and len(times) < 400:
@@ -587,14 +748,6 @@ def cpu_baseline(si, gpu_sample, budget_s=12.0):
             one = (time.perf_counter() - t1) / 3
     except ImportError:
         pass
-    # parity of the GPU's sampled rows on the timed rotation buffers
-    worst = 0.0
-    for rows_w, y_gpu in zip(gpu_sample["kept_rows"], gpu_sample["outputs"]):
-        y_ref, b = oracle.gemv_ref_fmt("bf16", rows_w.view(np.uint16), x, x_kind="bf16")
-        ok, w = oracle.check_close(y_gpu, y_ref, oracle.tolerance(b))
-        worst = max(worst, w)
-        if not ok:
-            raise RuntimeError(f"GPU output outside tolerance on a timed buffer (worst {w})")
     return {
         "value": alg / per / 1e9,
         "unit": "GB/s",
@@ -605,20 +758,34 @@ def cpu_baseline(si, gpu_sample, budget_s=12.0):
                    f"fp64 matvec on the BLAS threads given in cores); host has {os.cpu_count()} logical CPUs"),
         "us_per_gemv": per * 1e6,
         "one_blas_thread": None if one is None else {"us_per_gemv": one * 1e6, "value": alg / one / 1e9},
-        "gpu_parity_worst_err_over_tol": worst,
     }
 
 
 # --------------------------------------------------------------------------
 
+def two_term_variants(skg, fmt, M, K=4096):
+    """Compiled matrix-core variants of (fmt, M) that carry the fp32
+    activation as two fp16 terms (~22 significant bits) and take K, fastest
+    kind first: the LDS-ring kernel, then the register-fed one."""
+    vs = [v for v in skg.gemv_variants() if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE
+          and v["x_lds"] in (2, 3) and v["j"] == 2 and (v["x_lds"] != 3 or v["waves"] * v["kw"] == K // 32)
+          and (v["x_lds"] != 2 or ((K // 32) % v["kw"] == 0 and K // 32 <= v["waves"] * v["kw"]))]
+    return sorted(vs, key=lambda v: -v["x_lds"])[:1]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000, help="timed launches (repeats of 200)")
-    ap.add_argument("--warmup", type=int, default=60000, help="untimed warm-up launches (~1 s)")
-    ap.add_argument("--arms", default="all", help="all, none, or a comma list of: ceiling,q8_0,q4_0,q8_1,"
+    ap.add_argument("--steps", type=int, default=10,
+                    help="timed steps of the headline; one step = one repeat of 200 GEMV launches")
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed warm-up steps of the headline (topped up to at least 1 s)")
+    ap.add_argument("--arms", default="all", help="all, none, or a comma list of: floor,ceiling,q8_0,q4_0,q8_1,"
                                                   "multi_m,layer,small,norm,prefill")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ms", default="1,2,4,8", help="activation rows M of the multi_m arms (comma list, 1..8)")
+    ap.add_argument("--arm-warm-s", type=float, default=1.0, help="warm-up seconds of every further arm")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (its pre-timing parity gates still run)")
     ap.add_argument("--details", default=None, help="write the full results JSON here")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 5 plain 256 MiB device-to-device copies (a known-size reference for "
@@ -628,6 +795,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path is single-GPU "
               f"by design: no sharding or collectives).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -642,63 +812,79 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     timer = Timer(torch)
-    arms = set() if args.arms == "none" else (
-        {"ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill"} if args.arms == "all"
-        else set(args.arms.split(",")))
+    all_arms = {"floor", "ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill"}
+    arms = set() if args.arms == "none" else (all_arms if args.arms == "all" else set(args.arms.split(",")))
+    unknown = arms - all_arms
+    if unknown:
+        print(f"unknown arms {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    warm = args.arm_warm_s
 
-    # ---- headline: bf16 M=1 K=4096 N=12288 ----
+    # ---- headline: bf16 M=1 K=4096 N=12288; step = 200 launches ----
     N, K = 12288, 4096
     x_host = si.activations_bf16(si.rng_for(0, 2, 0), 1, K)
-    keep = np.array(sorted({0, 1, N - 1, N - 2} | set(np.random.default_rng(0).choice(N, 60, replace=False).tolist())))
-    head, sample = bench_gemv_arm(skg, si, torch, timer, "bf16_m1_k4096_n12288", "bf16", skg.BF16_BF16, 1, N, K,
-                                  args.steps, args.warmup, None, x_host.view(np.int16), keep_rows=keep, graph=True,
-                                  telemetry=Telemetry(torch), abba=1000)
-    sample["x"] = x_host
+    head = bench_gemv_arm(skg, si, torch, timer, "bf16_m1_k4096_n12288", "bf16", skg.BF16_BF16, 1, N, K,
+                          x_host.view(np.int16), repeats=args.steps, warm_repeats=args.warmup,
+                          warm_s=PROTOCOL["min_warm_s"], graph=True, telemetry=Telemetry(torch), abba=1000)
+    head["protocol_ok"] = protocol_ok(head)
     if head.get("telemetry"):
         log(f"[headline] telemetry over the timed repeats: {head['telemetry']}")
     log(f"[headline] ABBA against the streaming read of the same buffers: {head['abba_vs_read']}")
+    sp = "n/a" if head["spread"] is None else f"{100 * head['spread']:.2f}%"
     log(f"[headline] {head['us_per_launch']:.2f} us/launch  {head['gbs']:.0f} GB/s  "
-        f"({100 * head['frac_peak']:.1f}% of 8 TB/s)  spread {100 * head['spread']:.2f}%  "
-        f"graph {head['graph']['us_per_launch']:.2f} us  read-ceiling {head['ceiling_us']:.2f} us")
+        f"({100 * head['frac_peak']:.1f}% of 8 TB/s)  {head['repeats']} repeats of 200 after "
+        f"{head['warm_s']:.2f} s warm-up, spread {sp}  graph {head['graph']['us_per_launch']:.2f} us  "
+        f"read-ceiling {head['ceiling_us']:.2f} us")
 
     details = {"headline": head, "arms": {}}
-    short = dict(steps=2000, warmup=0, warm_s=0.3)
+    if "floor" in arms:
+        details["arms"]["floor"] = bench_floor(skg, torch, timer, warm)
     if "ceiling" in arms:
-        details["arms"]["ceiling"] = bench_ceiling(skg, torch, timer, short["steps"], short["warm_s"])
+        details["arms"]["ceiling"] = bench_ceiling(skg, torch, timer, warm)
         log(f"[ceiling] {details['arms']['ceiling']['gbs']:.0f} GB/s")
     for kind, fmt, key in (("q8_0", skg.Q8_0_F32, "q8_0"), ("q4_0", skg.Q4_0_F32, "q4_0"),
                            ("q4_0", skg.Q4_0_Q8_1, "q8_1"), ("q8_0", skg.Q8_0_Q8_1, "q8_1")):
         if key not in arms:
             continue
-        Ms = (1, 2, 4, 8) if "multi_m" in arms else (1,)
+        Ms = tuple(int(v) for v in args.ms.split(",")) if "multi_m" in arms else (1,)
         for M in Ms:
             xh = si.activations_f32(si.rng_for(0, 4, M), M, 4096)
-            r, _ = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
-                                  14336, 4096, short["steps"], 0, short["warm_s"], xh, graph=True)
+            # fp32-activation matrix-core defaults that round the activation to
+            # one fp16 term are timed beside the two-term (~22-bit) kernel
+            dv = skg.gemv_default_variant(fmt, M, skg.EPI_NONE, 4096)
+            extra = (two_term_variants(skg, fmt, M) if fmt in (skg.Q8_0_F32, skg.Q4_0_F32)
+                     and dv["x_lds"] in (2, 3) and dv["j"] == 1 else [])
+            r = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
+                               14336, 4096, xh, warm_s=warm, graph=True, variants=extra)
+            r["activation"] = ("fp32 rounded to one fp16 term per element" if dv["x_lds"] in (2, 3) and dv["j"] == 1
+                               and fmt in (skg.Q8_0_F32, skg.Q4_0_F32) else
+                               "fp32 as two fp16 terms" if dv["x_lds"] in (2, 3) and fmt in (skg.Q8_0_F32,
+                                                                                            skg.Q4_0_F32)
+                               else "Q8_1" if fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1) else "fp32")
             details["arms"][r["name"]] = r
-            log(f"[{r['name']}] {r['us_per_launch']:.2f} us  {r['gbs']:.0f} GB/s  graph "
-                f"{r['graph']['us_per_launch']:.2f} us ({r['graph']['gbs']:.0f} GB/s)  read-ceiling "
-                f"{r['ceiling_us']:.2f} us")
+            vs = "".join(f"  two-term {v['us_per_launch']:.2f} us" for v in r["variants"])
+            log(f"[{r['name']}] {r['us_per_launch']:.2f} us  {r['gbs']:.0f} GB/s  ({r['activation']})  graph "
+                f"{r['graph']['us_per_launch']:.2f} us  read-ceiling {r['ceiling_us']:.2f} us{vs}")
     if "small" in arms:
         xh = si.activations_f32(si.rng_for(0, 1, 0), 1, 256)
-        r, _ = bench_gemv_arm(skg, si, torch, timer, "q8_0_f32_m1_k256_n512", "q8_0", skg.Q8_0_F32, 1, 512, 256,
-                              short["steps"], 0, short["warm_s"], xh, graph=True)
+        r = bench_gemv_arm(skg, si, torch, timer, "q8_0_f32_m1_k256_n512", "q8_0", skg.Q8_0_F32, 1, 512, 256, xh,
+                           warm_s=warm, graph=True)
         details["arms"][r["name"]] = r
         log(f"[{r['name']}] {r['us_per_launch']:.2f} us (graph {r['graph']['us_per_launch']:.2f} us)")
     if "norm" in arms:
         for M in (1, 8):
-            r = bench_norm(skg, si, torch, timer, short["steps"], short["warm_s"], M=M)
+            r = bench_norm(skg, si, torch, timer, warm, M=M)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_launch']:.2f} us (graph {r['graph']['us_per_launch']:.2f} us)")
     if "layer" in arms:
         for mode in LAYER_MODES:
-            r = bench_layer(skg, si, torch, timer, 640, 0.3, mode=mode)
+            r = bench_layer(skg, si, torch, timer, warm, mode=mode)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
                 f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
     if "prefill" in arms:
         for kind in ("q4_0", "q8_0"):
-            r = bench_prefill(skg, si, torch, timer, 500, 0.3, kind=kind)
+            r = bench_prefill(skg, si, torch, timer, warm, kind=kind)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "
                 f"({100 * r['frac_peak_mfma_bf16']:.1f}% of bf16 peak)")
@@ -713,7 +899,7 @@ def main():
         log("[calibration] 5 x 256 MiB device copies")
         del src, dst
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(si, sample)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(si, x_host)
     if cpu:
         log(f"[cpu oracle] {cpu['value']:.2f} GB/s ({cpu['us_per_gemv']:.0f} us per GEMV, {cpu['cores']} threads)")
         if cpu["one_blas_thread"]:
@@ -721,6 +907,7 @@ def main():
             log(f"[cpu oracle] {o['value']:.2f} GB/s ({o['us_per_gemv']:.0f} us per GEMV) with one BLAS thread")
 
     traffic = counter_traffic()
+    floor = details["arms"].get("floor")
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 2),
@@ -728,7 +915,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["us_per_launch"] / 1000.0,
+        "ms_per_step": head["us_per_launch"] * head["launches_per_repeat"] / 1000.0,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -737,15 +924,25 @@ def main():
         "config": {
             "workload": "bf16 GEMV M=1 K=4096 N=12288, cold-cache rotation",
             "M": 1, "K": 4096, "N": 12288,
+            "step": "one repeat of 200 GEMV launches, each on the next rotation buffer",
             "rotation_buffers": head["rotation_buffers"],
             "working_set_bytes": head["working_set_bytes"],
+            "repeats": head["repeats"],
+            "launches_per_repeat": head["launches_per_repeat"],
+            "warm_s": head["warm_s"],
             "us_per_launch": round(head["us_per_launch"], 3),
             "frac_of_8TBs": round(head["frac_peak"], 4),
-            "spread": round(head["spread"], 4),
+            "spread": None if head["spread"] is None else round(head["spread"], 4),
             "spread_ok": head["spread_ok"],
+            "protocol_ok": head["protocol_ok"],
+            "oracle_gate_worst_err_over_tol": round(head["oracle_gate_worst_err_over_tol"], 4),
             "stream_read_ceiling_us": round(head["ceiling_us"], 3),
             "frac_of_stream_read_ceiling": round(head["frac_ceiling"], 4),
             "stream_read_over_gemv_abba": round(head["abba_vs_read"]["b_over_a"], 4),
+            "graph_us_per_launch": round(head["graph"]["us_per_launch"], 3),
+            "empty_launch_us": None if floor is None else
+            {f"{e['grid']}x{e['block']}": [round(e["us_per_launch"], 3), round(e["graph_us_per_launch"], 3)]
+             for e in floor["empty"]},
             "timer": "HIP events on the launch stream, eager launches, 200 per repeat",
         },
         "telemetry": head.get("telemetry"),

@@ -71,6 +71,8 @@ def _load() -> ctypes.CDLL:
         "skg_gemm_tiled": (i32, [i32, i64, i64, i64, vp, vp, vp, vp]),
         "skg_debug_block_dots": (i32, [i32, i64, i64, i64, i64, vp, vp, vp, vp]),
         "skg_stream_read": (i32, [vp, sz, vp, vp]),
+        "skg_empty_launch": (i32, [i64, i32, vp]),
+        "skg_gemv_default_variant": (i32, [i32, i32, i32, i64, ctypes.POINTER(i32)]),
         "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "skg_gemv_variants": (i32, [ctypes.POINTER(i32), i32]),
         "skg_set_lds_pad": (i32, [i64]),
@@ -309,6 +311,11 @@ def stream_read(buf, nbytes: int | None = None, out=None, stream=None):
     return out
 
 
+def empty_launch(grid: int = 1, block: int = 64, stream=None) -> None:
+    """One kernel that does nothing (the launch-floor reference)."""
+    check(lib.skg_empty_launch(grid, block, _stream(stream)))
+
+
 # ---- tuning hooks ------------------------------------------------------
 
 def gemv_variants():
@@ -318,6 +325,14 @@ def gemv_variants():
     lib.skg_gemv_variants(buf, n)
     keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves", "kw")
     return [dict(zip(keys, buf[8 * i: 8 * i + 8])) for i in range(n)]
+
+
+def gemv_default_variant(fmt: int, M: int, epi: int = EPI_NONE, K: int = 4096) -> dict:
+    """The variant record a gemv call with these arguments runs now."""
+    buf = (ctypes.c_int * 8)()
+    check(lib.skg_gemv_default_variant(fmt, M, epi, K, buf))
+    keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves", "kw")
+    return dict(zip(keys, buf[:8]))
 
 
 def gemv_set_variant(fmt: int, M: int, epi: int = EPI_NONE, ro: int = 0, j: int = 0, x_lds: int = 0,

@@ -18,6 +18,7 @@ hipError_t launch_rmsnorm_q8_1(int64_t M, int64_t K, const float* x, const float
 hipError_t launch_block_dots(int fmt, const void* W, const Layout& L, int64_t n0, int64_t nr, const void* xq,
                              int32_t* out, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int grid, hipStream_t stream);
+hipError_t launch_empty(int64_t grid, int block, hipStream_t stream);
 // Prefill kernel in use: 0 = one role per wave, 1 = producer/consumer waves.
 extern std::atomic<int> g_gemm_variant;
 extern const int kGemmDefaultVariant;

@@ -1,5 +1,6 @@
 // Test and measurement kernels: integer block dots through the GEMV's own
-// device functions, and the streaming-read bandwidth ceiling.
+// device functions, the streaming-read bandwidth ceiling and the empty kernel
+// that measures the launch floor.
 #include "gemv_impl.h"
 #include "kernels.h"
 
@@ -60,6 +61,14 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int 
   const int64_t blocks = (nwords + 255) / 256;
   hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
                      static_cast<const u32x4*>(buf), nwords, 0x9E3779B9u, out);
+  return hipGetLastError();
+}
+
+// Does nothing: back-to-back launches of it time the fixed cost of a launch.
+__global__ void empty_kernel() {}
+
+hipError_t launch_empty(int64_t grid, int block, hipStream_t stream) {
+  hipLaunchKernelGGL(empty_kernel, dim3(unsigned(grid)), dim3(unsigned(block)), 0, stream);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from synth import inputs as si
-from tests._gpu import assert_close, dev, host, note, poisoned
+from tests._gpu import assert_close, dev, host, note, poisoned, sample_rows
 from tests._q8_1_check import q8_1_violations
 
 pytestmark = pytest.mark.gpu
@@ -308,19 +308,20 @@ def test_gemv_mfma_shapes(skg, fmt, M):
     are exact int32 and only the fp32 scaling rounds, 2e-5 of sum|w a|."""
     cases = []
     for i, (N, K) in enumerate(MFMA_SHAPES):
-        if N * K * M > 20000 * 4096 * 2:
-            continue
         W, x = make_inputs(skg, fmt, M, N, K, seed=8000 + 100 * fmt + 10 * M + i)
         xq_ref = oracle.quantize_q8_1(x) if is_q8_1(skg, fmt) else None
-        y_ref, bound = reference(skg, fmt, W, x, xq_ref)
-        cases.append((N, K, W, x, y_ref, bound))
+        # large cases: the oracle evaluates a sample of rows (both ends, the
+        # ragged tail and a seeded sample), the kernel computes them all
+        rows = sample_rows(N, seed=M + i) if N * K * M > 20000 * 4096 * 2 else np.arange(N)
+        y_ref, bound = reference(skg, fmt, W[rows], x, xq_ref)
+        cases.append((N, K, W, x, y_ref, bound, rows))
         y, _ = run_gemv(skg, fmt, M, N, K, W, x)
-        assert_close(y, y_ref, bound, f"default fmt={fmt} M={M} N={N} K={K}")
+        assert_close(y[:, rows], y_ref, bound, f"default fmt={fmt} M={M} N={N} K={K}")
     try:
         for v in mfma_variants(skg, fmt, M):
             skg.gemv_set_variant(fmt, M, 0, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
             rel = 2e-5 if (v["j"] == 2 or is_q8_1(skg, fmt)) else 8e-4
-            for N, K, W, x, y_ref, bound in cases:
+            for N, K, W, x, y_ref, bound, rows in cases:
                 nb = K // 32
                 if nb % v["kw"] or nb > v["waves"] * v["kw"]:
                     continue
@@ -328,7 +329,7 @@ def test_gemv_mfma_shapes(skg, fmt, M):
                     continue  # the LDS-ring variant is compiled for K = 4096 only
                 note(f"variant {v} N={N} K={K}")
                 y, _ = run_gemv(skg, fmt, M, N, K, W, x)
-                assert_close(y, y_ref, bound, f"variant {v} N={N} K={K}", rel=rel)
+                assert_close(y[:, rows], y_ref, bound, f"variant {v} N={N} K={K}", rel=rel)
     finally:
         skg.gemv_set_variant(fmt, M, 0, 0)
 

@@ -31,11 +31,60 @@ def test_rotation_covers_two_gigabytes(nbytes):
 
 
 def test_summarize_spread_and_gate():
-    r = bench.summarize([10.0, 10.2, 9.8, 10.0], total_ms=8.0, steps=800)
+    r = bench.summarize([10.0, 10.2, 9.8, 10.0], total_ms=8.0, launches=800)
     assert r["us_per_launch"] == pytest.approx(10.0)
     assert r["spread"] == pytest.approx(0.4 / 10.0)
     assert r["spread_ok"]
     assert not bench.summarize([10.0, 11.0], 2.1, 200)["spread_ok"]
+    # one repeat has no spread, and no spread claim can be made from it
+    one = bench.summarize([10.0], 2.0, 200)
+    assert one["spread"] is None and not one["spread_ok"]
+
+
+def test_protocol_needs_warmup_repeats_and_spread():
+    good = {"warm_s": 1.2, "repeats": 10, "launches_per_repeat": 200, "spread_ok": True}
+    assert bench.protocol_ok(good)
+    for k, v in (("warm_s", 0.3), ("repeats", 9), ("launches_per_repeat", 20), ("spread_ok", False)):
+        assert not bench.protocol_ok(dict(good, **{k: v})), k
+
+
+def test_timer_runs_warmup_then_exact_repeats():
+    """Warm-up repeats (topped up to the requested seconds), then exactly the
+    requested repeats of per_repeat launches, each between two events."""
+    launched = []
+
+    class Ev:
+        n = 0
+
+        def __init__(self, enable_timing=True):
+            self.t = None
+
+        def record(self, stream):
+            self.t = float(len(launched))
+
+        def elapsed_time(self, other):
+            return (other.t - self.t) * 0.01           # 10 us per launch, in ms
+
+    class FakeCuda:
+        Event = Ev
+
+        @staticmethod
+        def current_stream():
+            return type("S", (), {"cuda_stream": 0})()
+
+        @staticmethod
+        def synchronize():
+            pass
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    r = bench.Timer(FakeTorch).run(lambda i, sh: launched.append(i), 7, repeats=3, per_repeat=50, warm_repeats=2,
+                                   warm_s=0.0)
+    assert len(launched) == 2 * 50 + 3 * 50
+    assert launched[:5] == [0, 1, 2, 3, 4] and launched[100] == 100 % 7
+    assert r["repeats"] == 3 and r["launches_per_repeat"] == 50 and r["warm_repeats"] == 2
+    assert r["us_per_launch"] == pytest.approx(10.0) and r["spread"] == pytest.approx(0.0)
 
 
 def test_counter_traffic_is_gated_by_the_gemv_sources(tmp_path, monkeypatch):
@@ -133,7 +182,7 @@ def test_abba_order_and_ratio():
     class FakeTimer:
         t = 0.0
 
-        def run(self, f, n_rot, steps, warmup):
+        def run(self, f, n_rot, repeats=10, **kw):
             calls.append(f.__name__)
             FakeTimer.t += 1.0                       # drift: every leg 1 us slower than the last
             base = 10.0 if f.__name__ == "a" else 12.0
