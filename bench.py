@@ -348,7 +348,7 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, x_host, repe
         res["graph"]["gbs"] = alg / (res["graph"]["us_per_launch"] * 1e-6) / 1e9
     res["variants"] = []
     for v in variants:
-        skg.gemv_set_variant(fmt, M, skg.EPI_NONE, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+        skg.gemv_select(v)
         try:
             vw = gate(f"{name} variant {v}")
             vr = timer.run(launch, n_rot, repeats=repeats, warm_s=0.3)
@@ -768,8 +768,8 @@ def two_term_variants(skg, fmt, M, K=4096):
     activation as two fp16 terms (~22 significant bits) and take K, fastest
     kind first: the LDS-ring kernel, then the register-fed one."""
     vs = [v for v in skg.gemv_variants() if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE
-          and v["x_lds"] in (2, 3) and v["j"] == 2 and (v["x_lds"] != 3 or v["waves"] * v["kw"] == K // 32)
-          and (v["x_lds"] != 2 or ((K // 32) % v["kw"] == 0 and K // 32 <= v["waves"] * v["kw"]))]
+          and v["x_lds"] in (2, 3, 4) and v["j"] == 2 and (v["x_lds"] != 3 or v["waves"] * v["kw"] == K // 32)
+          and (v["x_lds"] == 3 or ((K // 32) % v["kw"] == 0 and K // 32 <= v["waves"] * v["kw"]))]
     return sorted(vs, key=lambda v: -v["x_lds"])[:1]
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SKG_ABI_VERSION 1
+#define SKG_ABI_VERSION 2
 
 typedef enum skg_status {
   SKG_OK = 0,
@@ -292,10 +292,17 @@ skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream);
  *   16-row slots (the activation as for x_lds = 2); compiled for K = 4096 only
  *   (waves * kw = 128 blocks), so a call with any other K returns
  *   SKG_E_UNSUPPORTED while it is selected.
- * skg_gemv_variants: writes up to max_entries records of 8 ints
- *   {fmt, M, epi, ro, j, x_lds, waves, kw} to out (host) and returns the
- *   number of compiled variants.  For each (fmt, M, epi) and K the default is
- *   the first record whose variant takes that K.
+ *   x_lds = 4 names the same matrix-core computation with a private weight
+ *   ring per wave (each wave copies its own 16-block slice of every tile into
+ *   `depth` LDS slots; no workgroup barrier until the last tile); it takes K
+ *   with (K / 32) % 16 == 0 and K / 32 <= 128.
+ *   depth: weight tiles in flight (1 for the vector kernels; the prefetch
+ *   depth of x_lds = 2, 1 or 2; the ring slots of x_lds = 3, 2 or 3); 0
+ *   matches any depth.
+ * skg_gemv_variants: writes up to max_entries records of SKG_VARIANT_FIELDS
+ *   ints {fmt, M, epi, ro, j, x_lds, waves, kw, depth} to out (host) and
+ *   returns the number of compiled variants.  For each (fmt, M, epi) and K
+ *   the default is the first record whose variant takes that K.
  * skg_set_lds_pad: extra dynamic LDS bytes (0..65536) requested by every gemv
  *   launch, which lowers occupancy without changing the code (the MI50 case
  *   study's diagnostic control).  Initial value: $SKG_LDS_PAD_BYTES or 0.
@@ -306,9 +313,11 @@ skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream);
  * These settings are process-wide and must not change while another thread
  * is launching gemv work.
  */
-skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw);
+#define SKG_VARIANT_FIELDS 9
+skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw,
+                                int depth);
 int skg_gemv_variants(int* out, int max_entries);
-/* skg_gemv_default_variant: the record (8 ints, as skg_gemv_variants) of the
+/* skg_gemv_default_variant: the record (SKG_VARIANT_FIELDS ints, as skg_gemv_variants) of the
  * variant a skg_gemv / skg_gemv_multi call with this (fmt, M, epi, K) runs
  * now, honouring skg_gemv_set_variant; out is host memory.  SKG_E_UNSUPPORTED
  * when no compiled variant takes K; SKG_E_INVALID_ARG / SKG_E_SHAPE for an

@@ -73,7 +73,7 @@ def _load() -> ctypes.CDLL:
         "skg_stream_read": (i32, [vp, sz, vp, vp]),
         "skg_empty_launch": (i32, [i64, i32, vp]),
         "skg_gemv_default_variant": (i32, [i32, i32, i32, i64, ctypes.POINTER(i32)]),
-        "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
+        "skg_gemv_set_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, i32, i32]),
         "skg_gemv_variants": (i32, [ctypes.POINTER(i32), i32]),
         "skg_set_lds_pad": (i32, [i64]),
         "skg_gemm_tiled_set_variant": (i32, [i32]),
@@ -318,26 +318,38 @@ def empty_launch(grid: int = 1, block: int = 64, stream=None) -> None:
 
 # ---- tuning hooks ------------------------------------------------------
 
+VARIANT_KEYS = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves", "kw", "depth")
+
+
 def gemv_variants():
     """List of compiled GEMV variants as dicts (first per (fmt, M, epi) = default)."""
     n = lib.skg_gemv_variants(None, 0)
-    buf = (ctypes.c_int * (8 * n))()
+    w = len(VARIANT_KEYS)
+    buf = (ctypes.c_int * (w * n))()
     lib.skg_gemv_variants(buf, n)
-    keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves", "kw")
-    return [dict(zip(keys, buf[8 * i: 8 * i + 8])) for i in range(n)]
+    return [dict(zip(VARIANT_KEYS, buf[w * i: w * i + w])) for i in range(n)]
 
 
 def gemv_default_variant(fmt: int, M: int, epi: int = EPI_NONE, K: int = 4096) -> dict:
     """The variant record a gemv call with these arguments runs now."""
-    buf = (ctypes.c_int * 8)()
+    buf = (ctypes.c_int * len(VARIANT_KEYS))()
     check(lib.skg_gemv_default_variant(fmt, M, epi, K, buf))
-    keys = ("fmt", "M", "epi", "ro", "j", "x_lds", "waves", "kw")
-    return dict(zip(keys, buf[:8]))
+    return dict(zip(VARIANT_KEYS, buf[:len(VARIANT_KEYS)]))
 
 
 def gemv_set_variant(fmt: int, M: int, epi: int = EPI_NONE, ro: int = 0, j: int = 0, x_lds: int = 0,
-                     waves: int = 4, kw: int = 1) -> None:
-    check(lib.skg_gemv_set_variant(fmt, M, epi, ro, j, x_lds, waves, kw))
+                     waves: int = 4, kw: int = 1, depth: int = 0) -> None:
+    check(lib.skg_gemv_set_variant(fmt, M, epi, ro, j, x_lds, waves, kw, depth))
+
+
+def gemv_select(v: dict) -> None:
+    """Select the variant of a record from gemv_variants() for its (fmt, M, epi)."""
+    gemv_set_variant(v["fmt"], v["M"], v["epi"], v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"], v["depth"])
+
+
+def gemv_reset(fmt: int, M: int, epi: int = EPI_NONE) -> None:
+    """Back to the default variant of (fmt, M, epi)."""
+    gemv_set_variant(fmt, M, epi, 0)
 
 
 def set_lds_pad(nbytes: int) -> None:

@@ -16,6 +16,7 @@
 
 #include "gemv_registry.h"
 #include "gemv_mfma.h"
+#include "gemv_mfma_pw.h"
 #include "kernels.h"
 
 using namespace skg;
@@ -156,6 +157,7 @@ void init_registry() {
 bool variant_supports(const GemvEntry& e, int64_t K) {
   const int64_t nb = K / 32;
   if (e.xlds == 3) return nb == e.max_nb;
+  if (e.xlds == 4) return nb % PW_BPW == 0 && nb <= e.max_nb;
   if (e.xlds != 2) return true;
   return nb % e.kw == 0 && nb >= e.kw && nb <= e.max_nb;
 }
@@ -265,6 +267,48 @@ skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64
   return ok();
 }
 
+// Per-wave-ring matrix-core kernel: every workgroup owns a contiguous range
+// of the concatenated rows, spread over all CUs (16 .. 64 rows each).
+skg_status launch_gemv_mfma_pw(const GemvEntry& v, int64_t K, int nseg, const int64_t* Ns, const void* W,
+                               const void* x, float* const* ys, hipStream_t stream) {
+  const int wk = wkind_of(v.fmt);
+  PwArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.K = K;
+  a.nb = uint32_t(K / 32);
+  a.x = static_cast<const float*>(x);
+  a.nseg = nseg;
+  const uint8_t* base = static_cast<const uint8_t*>(W);
+  size_t off = 0;
+  int64_t rows = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const Layout L = layout_of(wk, Ns[i], K);
+    a.seg[i].w = packed_view(base + off, L);
+    a.seg[i].y = ys[i];
+    a.seg[i].N = Ns[i];
+    a.seg[i].row_begin = rows;
+    rows += Ns[i];
+    off += L.total;
+  }
+  a.ntot = rows;
+  int cus = 0;
+  skg_status st = check_device(&cus);
+  if (st != SKG_OK) return st;
+  int64_t per = (rows + cus - 1) / cus;
+  per = per < 16 ? 16 : (per > 16 * PW_MAXT ? 16 * PW_MAXT : per);
+  a.rows_per_wg = per;
+  const int64_t grid = (rows + per - 1) / per;
+  if (grid > 0x7FFFFFFF) return fail(SKG_E_SHAPE, "too many rows");
+  const int waves = int(a.nb / PW_BPW);
+  const size_t lds = pw_lds_bytes_of(v, waves);
+  if (hipError_t e = ensure_dynamic_lds(v.fn, lds); e != hipSuccess)
+    return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(v.fn, dim3(unsigned(grid)), dim3(unsigned(waves * 64)), args, lds, stream);
+  if (e != hipSuccess) return fail(SKG_E_HIP, "gemv launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t packed_size_multi(int fmt, int n, const int64_t* Ns, int64_t K) {
   size_t total = 0;
   for (int i = 0; i < n; ++i) total += layout_of(wkind_of(fmt), Ns[i], K).total;
@@ -278,6 +322,7 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
     return fail(SKG_E_UNSUPPORTED, "no compiled kernel (or the selected variant does not take K=%lld) for fmt=%d "
                 "M=%lld epi=%d", (long long)K, fmt, (long long)M, epi);
   if (v->xlds == 2 || v->xlds == 3) return launch_gemv_mfma(*v, K, nseg, Ns, W, x, ys, epi, stream);
+  if (v->xlds == 4) return launch_gemv_mfma_pw(*v, K, nseg, Ns, W, x, ys, stream);
   const int wk = wkind_of(fmt);
   GemvArgs a;
   std::memset(&a, 0, sizeof a);
@@ -560,12 +605,13 @@ skg_status skg_gemv_default_variant(skg_fmt fmt, int M, skg_epi epi, int64_t K, 
   if (!out) return fail(SKG_E_INVALID_ARG, "null out");
   const GemvEntry* e = find_variant(fmt, M, epi, K);
   if (!e) return fail(SKG_E_UNSUPPORTED, "no compiled variant takes K=%lld", (long long)K);
-  const int rec[8] = {e->fmt, e->M, e->epi, e->ro, e->j, e->xlds, e->waves, e->kw};
-  for (int i = 0; i < 8; ++i) out[i] = rec[i];
+  const int rec[SKG_VARIANT_FIELDS] = {e->fmt, e->M, e->epi, e->ro, e->j, e->xlds, e->waves, e->kw, e->depth};
+  for (int i = 0; i < SKG_VARIANT_FIELDS; ++i) out[i] = rec[i];
   return ok();
 }
 
-skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw) {
+skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, int x_lds, int waves, int kw,
+                                int depth) {
   if (!is_gemv_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown gemv fmt %d", int(fmt));
   if (M < 1 || M > 8) return fail(SKG_E_SHAPE, "M must be 1..8");
   if (epi != SKG_EPI_NONE && epi != SKG_EPI_SWIGLU && epi != SKG_EPI_SWIGLU_Q8_1)
@@ -576,14 +622,14 @@ skg_status skg_gemv_set_variant(skg_fmt fmt, int M, skg_epi epi, int ro, int j, 
     for (size_t i = 0; i < g_reg->size(); ++i) {
       const GemvEntry& e = (*g_reg)[i];
       if (e.fmt == fmt && e.M == M && e.epi == epi && e.ro == ro && e.j == j && e.xlds == x_lds && e.waves == waves &&
-          e.kw == kw) {
+          e.kw == kw && (depth == 0 || e.depth == depth)) {
         idx = int(i);
         break;
       }
     }
     if (idx < 0)
-      return fail(SKG_E_UNSUPPORTED, "no compiled variant ro=%d j=%d x_lds=%d waves=%d kw=%d", ro, j, x_lds, waves,
-                  kw);
+      return fail(SKG_E_UNSUPPORTED, "no compiled variant ro=%d j=%d x_lds=%d waves=%d kw=%d depth=%d", ro, j, x_lds,
+                  waves, kw, depth);
   }
   std::lock_guard<std::mutex> lk(g_sel_mu);
   g_sel[fmt][M][epi] = idx;
@@ -596,7 +642,7 @@ int skg_gemv_variants(int* out, int max_entries) {
   if (out) {
     for (int i = 0; i < n && i < max_entries; ++i) {
       const GemvEntry& e = (*g_reg)[size_t(i)];
-      int* o = out + 8 * i;
+      int* o = out + SKG_VARIANT_FIELDS * i;
       o[0] = e.fmt;
       o[1] = e.M;
       o[2] = e.epi;
@@ -605,6 +651,7 @@ int skg_gemv_variants(int* out, int max_entries) {
       o[5] = e.xlds;
       o[6] = e.waves;
       o[7] = e.kw;
+      o[8] = e.depth;
     }
   }
   return n;

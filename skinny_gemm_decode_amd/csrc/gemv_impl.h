@@ -635,6 +635,10 @@ struct GemvEntry {
   int fmt, M, epi, ro, j, xlds, waves, kw;
   int lds = 0;
   int max_nb = 0;
+  // tiles (or K chunks) of weight loads in flight per wave or workgroup:
+  // 1 for the vector kernels, the prefetch depth of the register-fed
+  // matrix-core kernel, the ring slots of the LDS-ring kernel
+  int depth = 1;
 };
 
 template <int FMT, int M, int RO, int J, bool XLDS, int WAVES, int EPI, int KW>

@@ -806,6 +806,7 @@ inline GemvEntry gemv_mfma_dma_entry() {
               FMT, M, SKG_EPI_NONE, MF_ROWS, XT, 3, 8, 16};
   e.lds = 0;
   e.max_nb = MfDmaGeom<FMT>::NB;
+  e.depth = R;
   return e;
 }
 
@@ -823,6 +824,7 @@ inline GemvEntry gemv_mfma_entry() {
     if (e.lds < q8_stage) e.lds = q8_stage;
   }
   e.max_nb = WAVES * BPW;
+  e.depth = PD;
   return e;
 }
 

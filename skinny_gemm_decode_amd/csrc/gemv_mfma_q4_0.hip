@@ -1,6 +1,7 @@
 // q4_0 weights x fp32 activations on the matrix cores, M = 1..8.
 #include "gemv_instances.h"
 #include "gemv_mfma.h"
+#include "gemv_mfma_pw.h"
 
 // MF(M, fp16 activation terms, prefetch depth)
 #define SKG_MF(M, XT, PD) out.push_back(skg::gemv_mfma_entry<SKG_Q4_0_F32, M, 8, 16, XT, SKG_EPI_NONE, PD>());
@@ -30,11 +31,30 @@ void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
 // Registered after them: measurement variants (at M = 1 the vector kernel
 // is faster; the LDS-ring kernel trails the register-fed one at every M).
 void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
+  // per-wave weight rings (measurement variants)
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 2, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 2, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 3, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 3, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 4, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 4, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 5, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 5, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 6, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 6, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 7, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 7, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 8, 1, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 8, 2, 3>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 4, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 8, 1, 2>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 1, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 2, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 4, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 2, 2, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 2, 2, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 1, 3, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 1, 3, false>());
   SKG_MF(1, 2, 1)
   SKG_MF(1, 1, 2)
   SKG_MF(8, 2, 1)

@@ -1,6 +1,7 @@
 // q8_0 weights x fp32 activations on the matrix cores, M = 1..8.
 #include "gemv_instances.h"
 #include "gemv_mfma.h"
+#include "gemv_mfma_pw.h"
 
 // MF(M, fp16 activation terms, prefetch depth)
 #define SKG_MF(M, XT, PD) out.push_back(skg::gemv_mfma_entry<SKG_Q8_0_F32, M, 8, 16, XT, SKG_EPI_NONE, PD>());
@@ -35,6 +36,21 @@ void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
 }
 // Registered after the vector-ALU instances: measurement variants.
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
+  // per-wave weight rings (measurement variants)
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 2, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 2, 2, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 3, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 3, 2, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 4, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 4, 2, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 5, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 5, 2, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 6, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 6, 2, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 7, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 7, 2, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 8, 1, 2>());
+  out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 8, 2, 2>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 1, 2, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 5, 2, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_F32, 6, 2, 2, true>());

@@ -152,4 +152,72 @@ def row_values(kind: str, row_bytes: bytes, K: int) -> list[Fraction]:
         for b in range(K // 32):
             out += q4_0_block_values(row_bytes[18 * b: 18 * b + 18])
         return out
+    if kind == "q4_K":
+        out = []
+        for b in range(K // 256):
+            out += q4_K_block_values(row_bytes[144 * b: 144 * b + 144])
+        return out
+    if kind == "q6_K":
+        out = []
+        for b in range(K // 256):
+            out += q6_K_block_values(row_bytes[210 * b: 210 * b + 210])
+        return out
     raise ValueError(kind)
+
+
+# --- K-quant super-blocks (256 elements), byte by byte -----------------------
+
+def q4_K_block_scales_mins(block: bytes):
+    """(sc, m) lists of the eight 6-bit sub-block scales and mins, read bit by
+    bit from the 12 packed bytes s = block[4:16]: the low six bits of s[j]
+    (scale) and s[j+4] (min) for j < 4; for j >= 4 the low / high nibble of
+    s[j+4] below the top two bits of s[j-4] (scale) and s[j] (min)."""
+    s = block[4:16]
+    sc, m = [], []
+    for j in range(8):
+        if j < 4:
+            sc.append(s[j] % 64)
+            m.append(s[j + 4] % 64)
+        else:
+            sc.append(s[j + 4] % 16 + 16 * (s[j - 4] // 64))
+            m.append(s[j + 4] // 16 + 16 * (s[j] // 64))
+    return sc, m
+
+
+def q4_K_block_values(block: bytes) -> list[Fraction]:
+    """Walks the 128 code bytes: byte 32c + i gives element 64c + i (low
+    nibble) and element 64c + 32 + i (high nibble)."""
+    assert len(block) == 144
+    d = f16_value(block[0] | (block[1] << 8))
+    dmin = f16_value(block[2] | (block[3] << 8))
+    sc, m = q4_K_block_scales_mins(block)
+    out = [None] * 256
+    for byte_index in range(128):
+        b = block[16 + byte_index]
+        c, i = divmod(byte_index, 32)
+        for e, code in ((64 * c + i, b % 16), (64 * c + 32 + i, b // 16)):
+            j = e // 32
+            out[e] = d * sc[j] * code - dmin * m[j]
+    return out
+
+
+def q6_K_block_values(block: bytes) -> list[Fraction]:
+    """Walks the ql bytes of each 128-element half: ql[64h + l] holds elements
+    l (low nibble) and l + 64 (high nibble), ql[64h + 32 + l] elements l + 32
+    and l + 96 (l < 32, relative to the half); qh[32h + l] holds the top two
+    bits of those four elements at bit pairs 0, 1 (element l), 2, 3 (l + 32),
+    4, 5 (l + 64), 6, 7 (l + 96)."""
+    assert len(block) == 210
+    ql, qh = block[0:128], block[128:192]
+    sc = [int8(v) for v in block[192:208]]
+    d = f16_value(block[208] | (block[209] << 8))
+    out = [None] * 256
+    for h in range(2):
+        for l in range(32):
+            a, b, hb = ql[64 * h + l], ql[64 * h + 32 + l], qh[32 * h + l]
+            lows = (a % 16, b % 16, a // 16, b // 16)
+            for k in range(4):
+                e = 128 * h + l + 32 * k
+                q = lows[k] + 16 * ((hb >> (2 * k)) % 4)
+                out[e] = d * sc[e // 16] * (q - 32)
+    return out

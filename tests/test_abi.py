@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(skg):
 
 
 def test_abi_version_and_status_strings(skg):
-    assert skg.abi_version() == 1
+    assert skg.abi_version() == 2
     assert skg.status_str(0) == "SKG_OK"
     assert skg.status_str(2) == "SKG_E_SHAPE"
     assert skg.status_str(99) == "SKG_E_UNKNOWN"
@@ -170,7 +170,7 @@ def test_other_entry_point_errors(skg):
     assert L.skg_debug_block_dots(3, 8, 64, 6, 3, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_stream_read(FAKE, 17, FAKE, None) == skg.E_SHAPE
     assert L.skg_set_lds_pad(1 << 20) == skg.E_INVALID_ARG
-    assert L.skg_gemv_set_variant(2, 1, 0, 3, 3, 0, 4, 1) == skg.E_UNSUPPORTED
+    assert L.skg_gemv_set_variant(2, 1, 0, 3, 3, 0, 4, 1, 0) == skg.E_UNSUPPORTED
 
 
 def test_variant_registry(skg):
@@ -185,6 +185,22 @@ def test_variant_registry(skg):
             assert (fmt, M, 2) in seen, (fmt, M, 2)
     skg.gemv_set_variant(2, 1, 0, 16, 2, 0, 4, 1)
     skg.gemv_set_variant(2, 1, 0, 0)
+    # every record selects itself, depth included; the default query returns
+    # the selected record and, after the reset, the first registered one
+    for v in vs:
+        assert v["depth"] >= 1
+    ring = [v for v in vs if v["x_lds"] == 3]
+    assert ring and {v["depth"] for v in ring} <= {2, 3}
+    v = ring[-1]
+    skg.gemv_select(v)
+    try:
+        assert skg.gemv_default_variant(v["fmt"], v["M"], v["epi"], 4096) == v
+    finally:
+        skg.gemv_reset(v["fmt"], v["M"], v["epi"])
+    first = next(w for w in vs if (w["fmt"], w["M"], w["epi"]) == (v["fmt"], v["M"], v["epi"]))
+    assert skg.gemv_default_variant(v["fmt"], v["M"], v["epi"], 4096) == first
+    with pytest.raises(skg.SkgError):
+        skg.gemv_set_variant(v["fmt"], v["M"], v["epi"], v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"], 7)
 
 
 @no_gpu

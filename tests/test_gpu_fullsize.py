@@ -68,12 +68,12 @@ def activation(skg, fmt, M, seed):
 def variants_at_k4096(skg, fmt, M):
     out = []
     for v in skg.gemv_variants():
-        if v["fmt"] != fmt or v["M"] != M or v["epi"] != skg.EPI_NONE or v["x_lds"] not in (2, 3):
+        if v["fmt"] != fmt or v["M"] != M or v["epi"] != skg.EPI_NONE or v["x_lds"] not in (2, 3, 4):
             continue
         nb = K // 32
         if v["x_lds"] == 3 and v["waves"] * v["kw"] != nb:
             continue
-        if v["x_lds"] == 2 and (nb % v["kw"] or nb > v["waves"] * v["kw"]):
+        if v["x_lds"] in (2, 4) and (nb % v["kw"] or nb > v["waves"] * v["kw"]):
             continue
         out.append(v)
     return out
@@ -99,7 +99,7 @@ def test_full_size_every_row(skg, fmt, M):
     assert_close(host(y), y_ref, bound, f"default fmt={fmt} M={M} {dv}")
     try:
         for v in variants_at_k4096(skg, fmt, M):
-            skg.gemv_set_variant(fmt, M, skg.EPI_NONE, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+            skg.gemv_select(v)
             note(f"full size fmt={fmt} M={M} variant {v}")
             y = poisoned((M, N_FULL))
             skg.gemv(fmt, M, K, N_FULL, Wp, xin, y)
@@ -120,7 +120,7 @@ def test_ragged_full_size_every_row(skg, fmt, M):
     try:
         for v in cases:
             if v is not None:
-                skg.gemv_set_variant(fmt, M, skg.EPI_NONE, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+                skg.gemv_select(v)
             note(f"ragged full size fmt={fmt} M={M} variant {v}")
             y = poisoned((M, N_RAGGED))
             skg.gemv(fmt, M, K, N_RAGGED, Wp, xin, y)

@@ -101,15 +101,15 @@ def test_every_compiled_variant(skg):
         for v in variants:
             fmt, M, epi = v["fmt"], v["M"], v["epi"]
             N = 320 if epi == skg.EPI_SWIGLU_Q8_1 else 300
-            # the matrix-core variants (x_lds == 2) take K % 256 == 0, K <= 4096
-            K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] in (2, 3) else 4128)
+            # the matrix-core variants (x_lds 2, 3, 4) take K % 512 == 0, K <= 4096
+            K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] in (2, 3, 4) else 4128)
             key = (fmt, M, epi, K)
             if key not in cache:
                 W0, x = make_inputs(skg, fmt, M, N, K, seed=5000 + 10 * fmt + M)
                 W1, _ = make_inputs(skg, fmt, 1, N, K, seed=6000 + 10 * fmt + M)
                 cache[key] = (W0, W1, x)
             W0, W1, x = cache[key]
-            skg.gemv_set_variant(fmt, M, epi, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+            skg.gemv_select(v)
             note(f"variant {v}")
             xin, xq_ref = gpu_activation(skg, fmt, x)
             if epi == skg.EPI_NONE:
@@ -294,7 +294,7 @@ MFMA_SHAPES = [(1, 512), (19, 512), (300, 4096), (1000, 1536), (37, 1280), (9000
 
 def mfma_variants(skg, fmt, M):
     return [v for v in skg.gemv_variants()
-            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3)]
+            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3, 4)]
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3, 4])
@@ -319,7 +319,7 @@ def test_gemv_mfma_shapes(skg, fmt, M):
         assert_close(y[:, rows], y_ref, bound, f"default fmt={fmt} M={M} N={N} K={K}")
     try:
         for v in mfma_variants(skg, fmt, M):
-            skg.gemv_set_variant(fmt, M, 0, v["ro"], v["j"], v["x_lds"], v["waves"], v["kw"])
+            skg.gemv_select(v)
             rel = 2e-5 if (v["j"] == 2 or is_q8_1(skg, fmt)) else 8e-4
             for N, K, W, x, y_ref, bound, rows in cases:
                 nb = K // 32
@@ -339,7 +339,7 @@ def test_gemv_mfma_activation_range(skg, fmt):
     """Activations far outside fp16 range, far below it, an all-zero row and
     a single huge outlier: the per-wave power-of-two scaling keeps the two
     fp16 terms exact enough everywhere."""
-    M, N, K = 5, 300, 4096
+    M, N, K = 6, 300, 4096
     rng = si.rng_for(0, 99, 8900 + fmt)
     W = si.weights(wkind(skg, fmt), rng, N, K)
     x = si.activations_f32(rng, M, K)
@@ -348,10 +348,24 @@ def test_gemv_mfma_activation_range(skg, fmt):
     x[2] *= np.float32(1e-30)        # far below fp16's smallest subnormal
     x[3, 1234] = np.float32(3e9)     # one outlier dominating its wave's range
     x[4, : K // 2] *= np.float32(1e20)
-    y, _ = run_gemv(skg, fmt, M, N, K, W, x)
+    # outliers in every quarter of a block (elements 4g..4g+3 and 16+4g..
+    # 16+4g+3 go to lane group g of the matrix-core kernels), so a scale
+    # taken from part of a row's lanes overflows fp16
+    for blk, e in ((3, 13), (40, 30), (77, 6), (100, 21), (126, 0)):
+        x[5, 32 * blk + e] = np.float32(7e4 * (1 + blk))
     y_ref, bound = reference(skg, fmt, W, x, None)
+    y, _ = run_gemv(skg, fmt, M, N, K, W, x)
     assert_close(y, y_ref, bound, f"fmt={fmt} range")
     assert np.all(y[1] == 0.0), "all-zero activation row must give exact zeros"
+    try:
+        for v in mfma_variants(skg, fmt, M):
+            skg.gemv_select(v)
+            note(f"range variant {v}")
+            y, _ = run_gemv(skg, fmt, M, N, K, W, x)
+            assert_close(y, y_ref, bound, f"fmt={fmt} range variant {v}")
+            assert np.all(y[1] == 0.0), f"variant {v}: all-zero activation row must give exact zeros"
+    finally:
+        skg.gemv_reset(fmt, M)
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
