@@ -158,6 +158,12 @@ bool variant_supports(const GemvEntry& e, int64_t K) {
   const int64_t nb = K / 32;
   if (e.xlds == 3) return nb == e.max_nb;
   if (e.xlds == 4) return nb % PW_BPW == 0 && nb <= e.max_nb;
+  if (e.xlds == 1 && e.kw > 1) {
+    // every K class of the LDS-staged split walks the same number of chunks
+    const int64_t nu = (e.fmt == SKG_BF16_BF16) ? K / 8 : nb;
+    const int64_t chunks = (nu + 64 * e.j - 1) / (64 * e.j);
+    return chunks % e.kw == 0;
+  }
   if (e.xlds != 2) return true;
   return nb % e.kw == 0 && nb >= e.kw && nb <= e.max_nb;
 }
@@ -361,7 +367,7 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
     }
   }
   if (blocks > 0x7FFFFFFF) return fail(SKG_E_SHAPE, "too many rows");
-  size_t lds = gemv_lds_bytes(fmt, int(M), v->j, v->xlds) + size_t(g_lds_pad.load());
+  size_t lds = gemv_lds_bytes(fmt, int(M), v->j, v->xlds, v->xlds ? v->kw : 1) + size_t(g_lds_pad.load());
   if (lds > 160 * 1024) return fail(SKG_E_UNSUPPORTED, "variant needs %zu bytes of LDS", lds);
   if (hipError_t e = ensure_dynamic_lds(v->fn, lds); e != hipSuccess)
     return fail(SKG_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));

@@ -189,6 +189,16 @@ __device__ inline void dma16(const void* src, uint32_t dst) {
                "v"(src)
                : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for data read exactly once per
+// launch (weights): it streams past the caches that hold what is re-read
+// (measured on the LDS-ring decode kernels: 12.85 -> 12.48 us for q4_0 at
+// M = 8, 17.08 -> 16.36 us for q8_0).
+__device__ inline void dma16_stream(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(
+                   __builtin_amdgcn_readfirstlane(dst)),
+               "v"(src)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) (N <= 63), other counters untouched.

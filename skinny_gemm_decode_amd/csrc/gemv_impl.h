@@ -394,7 +394,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   constexpr int PP = F::XB / 16;
   constexpr int GROUPS = WAVES / KW;  // row groups per workgroup
   static_assert(WAVES % KW == 0, "KW must divide WAVES");
-  static_assert(KW == 1 || !XLDS, "K split across waves keeps the activation in registers");
+  // With the activation in LDS and K split across waves, the waves of one
+  // K class (kw) stage their chunk into LDS region kw; the host launches such
+  // a variant only when every class has the same number of chunks.
+  constexpr int XCLS = XLDS ? KW : 1;  // LDS chunk regions
   extern __shared__ u32x4 xlds[];
   __shared__ float red[KW > 1 ? WAVES : 1][KW > 1 ? RT * M : 1];
   // SwiGLU outputs of the workgroup's rows, gathered for their Q8_1 blocks
@@ -444,19 +447,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     // weight stream second; the first wait then covers only the activation
     // and every weight load stays in flight until it is consumed.
     XRaw<FMT> xr[XLDS ? 1 : J][XLDS ? 1 : M];
-    u32x4 stage[XLDS && !F::XQ8 ? (M * UC * PP + WAVES * 64 - 1) / (WAVES * 64) : 1];
+    // staging threads: the waves of this K class
+    constexpr int ST = (WAVES / XCLS) * 64;
+    const int tl = (wave / XCLS) * 64 + lane;
+    u32x4 stage[XLDS && !F::XQ8 ? (M * UC * PP + ST - 1) / ST : 1];
     // Q8_1 activation staged whole blocks per thread (nine dwords each)
-    constexpr int NQ = (XLDS && F::XQ8) ? (M * UC + WAVES * 64 - 1) / (WAVES * 64) : 1;
+    constexpr int NQ = (XLDS && F::XQ8) ? (M * UC + ST - 1) / ST : 1;
     uint32_t qstage[NQ][9];
+    u32x4* xreg = xlds + size_t(XCLS > 1 ? kw : 0) * (M * PP * UC);
+    uint32_t* qreg = reinterpret_cast<uint32_t*>(xlds) + size_t(XCLS > 1 ? kw : 0) * (M * 9 * UC);
     if constexpr (XLDS && F::XQ8) {
       // Cooperative staging of this chunk's Q8_1 activation, all M rows: thread
       // t copies block t (36 contiguous bytes; a wave reads 2304 contiguous
       // bytes) into nine LDS planes [m][dword][unit], so both the writes here
       // and the lane-per-unit reads later hit consecutive banks.
-      if (c > 0) __syncthreads();
+      if (c != kw) __syncthreads();
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
-        const int i = int(threadIdx.x) + t * WAVES * 64;
+        const int i = tl + t * ST;
         const int m = i / UC, uu = i % UC;
         const uint32_t gu = ub + uint32_t(uu);
         const bool ok = (m < M) && (gu < nu);
@@ -475,12 +483,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
       // Cooperative staging of this chunk's activation, all M rows, into a
       // piece-planar LDS layout [m][piece][unit]: lanes reading consecutive
       // units then hit consecutive 16-byte LDS words (no bank conflicts).
-      if (c > 0) __syncthreads();
+      if (c != kw) __syncthreads();
       constexpr int ESZ = F::XB / F::E;
       constexpr int NS = sizeof(stage) / sizeof(stage[0]);
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        const int i = int(threadIdx.x) + t * WAVES * 64;
+        const int i = tl + t * ST;
         const int p = i % PP;
         const int uu = (i / PP) % UC;
         const int m = i / (PP * UC);
@@ -508,14 +516,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     // Every load of the chunk is issued before any result is used.
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (XLDS && F::XQ8) {
-      uint32_t* ql = reinterpret_cast<uint32_t*>(xlds);
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
-        const int i = int(threadIdx.x) + t * WAVES * 64;
+        const int i = tl + t * ST;
         if (i < M * UC) {
           const int m = i / UC, uu = i % UC;
 #pragma unroll
-          for (int k = 0; k < 9; ++k) ql[(m * 9 + k) * UC + uu] = qstage[t][k];
+          for (int k = 0; k < 9; ++k) qreg[(m * 9 + k) * UC + uu] = qstage[t][k];
         }
       }
       __syncthreads();
@@ -523,12 +530,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
       constexpr int NS = sizeof(stage) / sizeof(stage[0]);
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        const int i = int(threadIdx.x) + t * WAVES * 64;
+        const int i = tl + t * ST;
         if (i < M * UC * PP) {
           const int p = i % PP;
           const int uu = (i / PP) % UC;
           const int m = i / (PP * UC);
-          xlds[(m * PP + p) * UC + uu] = stage[t];
+          xreg[(m * PP + p) * UC + uu] = stage[t];
         }
       }
       __syncthreads();
@@ -541,15 +548,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
       for (int m = 0; m < M; ++m) {
         XUnit<FMT> xu;
         if constexpr (XLDS && F::XQ8) {
-          const uint32_t* ql = reinterpret_cast<const uint32_t*>(xlds);
           XRaw<FMT> r;
 #pragma unroll
-          for (int k = 0; k < 9; ++k) r.w[k] = ql[(m * 9 + k) * UC + j * 64 + lane];
+          for (int k = 0; k < 9; ++k) r.w[k] = qreg[(m * 9 + k) * UC + j * 64 + lane];
           x_from_raw<FMT>(xu, r, uok);
         } else if constexpr (XLDS) {
           u32x4 pc[PP];
 #pragma unroll
-          for (int p = 0; p < PP; ++p) pc[p] = xlds[(m * PP + p) * UC + j * 64 + lane];
+          for (int p = 0; p < PP; ++p) pc[p] = xreg[(m * PP + p) * UC + j * 64 + lane];
           x_from_pieces<FMT>(xu, pc);
         } else {
           x_from_raw<FMT>(xu, xr[j][m], uok);
@@ -648,10 +654,10 @@ inline GemvEntry gemv_entry() {
 }
 
 // LDS bytes an instance needs (0 when the activation lives in registers).
-inline size_t gemv_lds_bytes(int fmt, int M, int J, int xlds) {
+inline size_t gemv_lds_bytes(int fmt, int M, int J, int xlds, int kw = 1) {
   if (!xlds) return 0;
   const int xb = (fmt == SKG_BF16_BF16) ? 16 : (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1) ? 36 : 128;
-  return size_t(M) * size_t(64 * J) * size_t(xb);
+  return size_t(M) * size_t(64 * J) * size_t(xb) * size_t(kw);
 }
 
 }  // namespace skg

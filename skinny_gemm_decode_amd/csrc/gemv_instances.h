@@ -11,6 +11,8 @@
 #define SKG_I(F, M, RO, J, X, W, E) out.push_back(skg::gemv_entry<F, M, RO, J, X, W, E, 1>());
 // IK(..., KW): KW waves share each row group and split its K chunks.
 #define SKG_IK(F, M, RO, J, W, E, KW) out.push_back(skg::gemv_entry<F, M, RO, J, false, W, E, KW>());
+// IKL(..., KW): the same with the activation staged in LDS, one region per K class.
+#define SKG_IKL(F, M, RO, J, W, E, KW) out.push_back(skg::gemv_entry<F, M, RO, J, true, W, E, KW>());
 
 // Default instances, split by M so translation units compile in parallel.
 // Arguments: format; rows per wave and units per lane for M = 1, for M = 2,

@@ -675,7 +675,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       const uint8_t* rowp = sg.w0.payload + size_t(n) * sg.w0.row_bytes;
 #pragma unroll
       for (int ch = 0; ch < G::CH; ++ch)
-        dma16(rowp + ch * 1024 + lane * 16, lds_addr(slot) + uint32_t(r * G::PRS + ch * 1024));
+        dma16_stream(rowp + ch * 1024 + lane * 16, lds_addr(slot) + uint32_t(r * G::PRS + ch * 1024));
     }
     // Scales of rows 4 (wave % 4) .. +3, all 64 lanes (waves 4..7 repeat the
     // identical copies of waves 0..3, so every wave issues the same number of
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       const int r = 4 * (wave & 3) + (lane >> 4);
       const int64_t n = (rbase + r < sg.N) ? rbase + r : sg.N - 1;
       const uint16_t* srow = sg.w0.scales + size_t(n) * sg.w0.nb;
-      dma16(srow + (lane & 15) * 8, lds_addr(slot) + uint32_t(16 * G::PRS + 4 * (wave & 3) * G::SRS));
+      dma16_stream(srow + (lane & 15) * 8, lds_addr(slot) + uint32_t(16 * G::PRS + 4 * (wave & 3) * G::SRS));
     }
   };
 

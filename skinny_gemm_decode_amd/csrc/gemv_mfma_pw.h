@@ -145,7 +145,7 @@ __global__ __launch_bounds__(512, 1) void gemv_mfma_pw_kernel(const PwArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           if (valid || lane == 0)
-            dma16(pay + (size_t(p) * a.nb + blk0 + uint32_t(8 * b + jb)) * 16,
+            dma16_stream(pay + (size_t(p) * a.nb + blk0 + uint32_t(8 * b + jb)) * 16,
                   slot + uint32_t(p * G::PLANE + h * G::GRP + 1024 * b));
     }
     // scales: lane 2 r + e copies the eight scales of blocks 8e .. 8e + 7 of row r
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(512, 1) void gemv_mfma_pw_kernel(const PwArgs a) {
     const bool svalid = lane < 32 && srow < r1;
     const PwSeg s = seg_of(svalid ? srow : rbase);
     const uint16_t* sc = s.w.scales + size_t((svalid ? srow : rbase) - s.row_begin) * s.w.nb;
-    if (svalid) dma16(sc + blk0 + uint32_t(8 * (lane & 1)), slot + uint32_t(G::SCL_OFF));
+    if (svalid) dma16_stream(sc + blk0 + uint32_t(8 * (lane & 1)), slot + uint32_t(G::SCL_OFF));
   };
 
   // ---- the activation slice (asm loads), then the first R tiles, then one

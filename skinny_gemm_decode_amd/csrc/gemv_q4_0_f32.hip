@@ -27,5 +27,11 @@ void register_gemv_q4_0_f32(std::vector<GemvEntry>& out) {
   SKG_I(SKG_Q4_0_F32, 1, 4, 1, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 8, 2, true, 8, SKG_EPI_NONE)
   SKG_I(SKG_Q4_0_F32, 1, 2, 2, true, 4, SKG_EPI_NONE)
+  // activation in LDS with K split across the waves of a row group
+  SKG_IKL(SKG_Q4_0_F32, 1, 4, 1, 8, SKG_EPI_NONE, 2)
+  SKG_IKL(SKG_Q4_0_F32, 1, 2, 1, 8, SKG_EPI_NONE, 2)
+  SKG_IKL(SKG_Q4_0_F32, 1, 8, 1, 8, SKG_EPI_NONE, 2)
+  SKG_IKL(SKG_Q4_0_F32, 1, 4, 1, 4, SKG_EPI_NONE, 2)
+  SKG_IKL(SKG_Q4_0_F32, 1, 2, 1, 16, SKG_EPI_NONE, 2)
 }
 }  // namespace skg
