@@ -129,4 +129,7 @@ def dequantize(kind: str, W) -> np.ndarray:
         return decode_q8_0(W)
     if kind == "q4_0":
         return decode_q4_0(W)
+    if kind in ("q4_K", "q6_K"):
+        from . import kquant
+        return kquant.decode_q4_K(W) if kind == "q4_K" else kquant.decode_q6_K(W)
     raise ValueError(f"unknown weight kind {kind!r}")

@@ -14,6 +14,9 @@ in order, K contiguous):
   Random code bytes are drawn uniformly over 0..255, which makes both 4-bit
   codes of every byte independent and uniform over 0..15; which code of the
   byte is which element is the decoder's business, not the generator's.
+* q4_K super-block, 144 bytes, and q6_K super-block, 210 bytes (256 elements
+  each): the field layout is the decoder's business; the generator fills the
+  fp16 scale fields with scale-like values and every other byte uniformly.
 * fp32 activations: float32 [M][K].
 
 Value distributions follow the decode workloads of the source pages (token
@@ -85,6 +88,36 @@ def q4_0_weights(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
     return out
 
 
+QK_K = 256  # elements per K-quant super-block
+
+
+def q4_K_weights(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """uint8 [N, K/256, 144]: fp16 d and dmin |N(0, 1e-4)|, 12 uniform random
+    bytes of packed 6-bit sub-block scales and mins, 128 uniform random code
+    bytes.  The pages do not characterise K-quant tensors; these magnitudes put
+    typical weights near those of the other formats (|w| ~ 0.02)."""
+    assert K % QK_K == 0
+    nsb = K // QK_K
+    out = np.empty((N, nsb, 144), dtype=np.uint8)
+    out[..., 0:2] = _fp16_bytes(np.abs(rng.normal(0.0, 1e-4, size=(N, nsb))).astype(np.float32))
+    out[..., 2:4] = _fp16_bytes(np.abs(rng.normal(0.0, 1e-4, size=(N, nsb))).astype(np.float32))
+    out[..., 4:] = rng.integers(0, 256, size=(N, nsb, 140), dtype=np.uint16).astype(np.uint8)
+    return out
+
+
+def q6_K_weights(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """uint8 [N, K/256, 210]: 192 uniform random code bytes (low and high
+    planes), 16 int8 sub-block scales uniform in [-128, 127], fp16 d
+    |N(0, 2e-5)| (typical |w| ~ 0.02; stated choices, as for q4_K)."""
+    assert K % QK_K == 0
+    nsb = K // QK_K
+    out = np.empty((N, nsb, 210), dtype=np.uint8)
+    out[..., 0:192] = rng.integers(0, 256, size=(N, nsb, 192), dtype=np.uint16).astype(np.uint8)
+    out[..., 192:208] = rng.integers(-128, 128, size=(N, nsb, 16), dtype=np.int16).astype(np.int8).view(np.uint8)
+    out[..., 208:210] = _fp16_bytes(np.abs(rng.normal(0.0, 2e-5, size=(N, nsb))).astype(np.float32))
+    return out
+
+
 def bf16_weights(rng: np.random.Generator, N: int, K: int, std: float = 0.02) -> np.ndarray:
     """uint16 [N, K] bf16 bit patterns of N(0, std) values."""
     return _f32_to_bf16_bits(rng.normal(0.0, std, size=(N, K)).astype(np.float32))
@@ -124,6 +157,10 @@ def weights(kind: str, rng: np.random.Generator, N: int, K: int) -> np.ndarray:
         return q8_0_weights(rng, N, K)
     if kind == "q4_0":
         return q4_0_weights(rng, N, K)
+    if kind == "q4_K":
+        return q4_K_weights(rng, N, K)
+    if kind == "q6_K":
+        return q6_K_weights(rng, N, K)
     raise ValueError(f"unknown weight kind {kind!r}")
 
 
@@ -155,5 +192,19 @@ def torch_weights(kind: str, N: int, K: int, seed: int, device):
         out[..., 0:2] = d.view(torch.uint8).view(N, nb, 2)
         q = torch.randint(-127, 128, (N, nb, 32), generator=g, device=device, dtype=torch.int8)
         out[..., 2:] = q.view(torch.uint8)
+        return out
+    if kind in ("q4_K", "q6_K"):
+        nsb = K // QK_K
+        if kind == "q4_K":
+            out = torch.empty((N, nsb, 144), dtype=torch.uint8, device=device)
+            for o in (0, 2):
+                d = (torch.randn((N, nsb), generator=g, device=device) * 1e-4).abs().to(torch.float16)
+                out[..., o:o + 2] = d.view(torch.uint8).view(N, nsb, 2)
+            out[..., 4:] = torch.randint(0, 256, (N, nsb, 140), generator=g, device=device, dtype=torch.uint8)
+        else:
+            out = torch.empty((N, nsb, 210), dtype=torch.uint8, device=device)
+            out[..., 0:208] = torch.randint(0, 256, (N, nsb, 208), generator=g, device=device, dtype=torch.uint8)
+            d = (torch.randn((N, nsb), generator=g, device=device) * 2e-5).abs().to(torch.float16)
+            out[..., 208:210] = d.view(torch.uint8).view(N, nsb, 2)
         return out
     raise ValueError(f"unknown weight kind {kind!r}")
