@@ -27,8 +27,10 @@ fp16 term are timed beside the two-term kernel), the Llama-2-7B-shaped q4_0 x
 Q8_1 decode layer over 32 distinct layers (plain, with the SwiGLU launch
 writing Q8_1, and with the layer's RMSNorm as its own launch or writing Q8_1
 itself), the fused RMSNorm -> Q8_1 launch alone, the q8_0 M=1 K=256 N=512
-launch-bound case, and the M=512 MFMA prefill tile.  The CPU oracle is timed
-on a bounded sample of the headline workload on this host's cores.
+launch-bound case, the M=512 MFMA prefill tile, and the K-quant (q4_K, q6_K
+super-block) weights x fp32 and x Q8_1 at the same decode shape.  The CPU
+oracle is timed on a bounded sample of the headline workload on this host's
+cores.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 5] [--arms all|none|a,b] [--ms 1,2,4,8]
 Prints one JSON line on stdout; per-arm details go to the --details file when
@@ -288,7 +290,7 @@ def bench_gemv_arm(skg, si, torch, timer, name, kind, fmt, M, N, K, x_host, repe
     bufs, kept = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=1000 * (fmt + 1) + 10 * M,
                                       keep_rows=rows, keep_bufs=keep_bufs)
     x = torch.from_numpy(x_host).cuda()
-    q8 = fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+    q8 = fmt in skg.Q8_1_FMTS
     if q8:
         xin = skg.quantize_act_q8_1(x)
         xbytes = xin.numel()
@@ -670,7 +672,7 @@ def oracle_gate_gemv(label, kind, fmt, skg, x_host, xq_gpu, pairs):
     import numpy as np
 
     import oracle
-    q8 = fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+    q8 = fmt in skg.Q8_1_FMTS
     if q8:
         xq_ref = oracle.quantize_q8_1(x_host)
         if not np.array_equal(xq_gpu.reshape(xq_ref.shape), xq_ref):
@@ -683,6 +685,8 @@ def oracle_gate_gemv(label, kind, fmt, skg, x_host, xq_gpu, pairs):
             y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(rows_w, xq_ref)
         elif fmt == skg.Q8_0_Q8_1:
             y_ref, bound = oracle.gemv_q8_0_q8_1_ref(rows_w, xq_ref)
+        elif q8:
+            y_ref, bound = oracle.gemv_ref(oracle.dequantize(kind, rows_w), oracle.decode_q8_1(xq_ref))
         else:
             x_kind = "bf16" if fmt == skg.BF16_BF16 else "f32"
             xv = x_host.view(np.uint16) if x_kind == "bf16" else x_host
@@ -781,7 +785,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5,
                     help="untimed warm-up steps of the headline (topped up to at least 1 s)")
     ap.add_argument("--arms", default="all", help="all, none, or a comma list of: floor,ceiling,q8_0,q4_0,q8_1,"
-                                                  "multi_m,layer,small,norm,prefill")
+                                                  "multi_m,layer,small,norm,prefill,kquant")
     ap.add_argument("--ms", default="1,2,4,8", help="activation rows M of the multi_m arms (comma list, 1..8)")
     ap.add_argument("--arm-warm-s", type=float, default=1.0, help="warm-up seconds of every further arm")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -812,7 +816,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     timer = Timer(torch)
-    all_arms = {"floor", "ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill"}
+    all_arms = {"floor", "ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill", "kquant"}
     arms = set() if args.arms == "none" else (all_arms if args.arms == "all" else set(args.arms.split(",")))
     unknown = arms - all_arms
     if unknown:
@@ -843,7 +847,9 @@ def main():
         details["arms"]["ceiling"] = bench_ceiling(skg, torch, timer, warm)
         log(f"[ceiling] {details['arms']['ceiling']['gbs']:.0f} GB/s")
     for kind, fmt, key in (("q8_0", skg.Q8_0_F32, "q8_0"), ("q4_0", skg.Q4_0_F32, "q4_0"),
-                           ("q4_0", skg.Q4_0_Q8_1, "q8_1"), ("q8_0", skg.Q8_0_Q8_1, "q8_1")):
+                           ("q4_0", skg.Q4_0_Q8_1, "q8_1"), ("q8_0", skg.Q8_0_Q8_1, "q8_1"),
+                           ("q4_K", skg.Q4_K_F32, "kquant"), ("q6_K", skg.Q6_K_F32, "kquant"),
+                           ("q4_K", skg.Q4_K_Q8_1, "kquant"), ("q6_K", skg.Q6_K_Q8_1, "kquant")):
         if key not in arms:
             continue
         Ms = tuple(int(v) for v in args.ms.split(",")) if "multi_m" in arms else (1,)
@@ -860,7 +866,7 @@ def main():
                                and fmt in (skg.Q8_0_F32, skg.Q4_0_F32) else
                                "fp32 as two fp16 terms" if dv["x_lds"] in (2, 3) and fmt in (skg.Q8_0_F32,
                                                                                             skg.Q4_0_F32)
-                               else "Q8_1" if fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1) else "fp32")
+                               else "Q8_1" if fmt in skg.Q8_1_FMTS else "fp32")
             details["arms"][r["name"]] = r
             vs = "".join(f"  two-term {v['us_per_launch']:.2f} us" for v in r["variants"])
             log(f"[{r['name']}] {r['us_per_launch']:.2f} us  {r['gbs']:.0f} GB/s  ({r['activation']})  graph "

@@ -21,6 +21,20 @@
  *           c_i = low nibble of qs[i] for i < 16, high nibble of qs[i-16] else.
  *   Q8_1  : 36-byte block {fp16 d; fp16 s; int8 q[32]},      a_i = d * q_i,
  *           s = fp16(d_f32 * sum_i q_i).
+ * K-quant super-blocks (256 elements along K): "Chapter 2.2 - speed - 64-lane
+ * Metal" (In twenty seconds - The fix) runs q4_K and q6_K weights without
+ * defining them; these are the GGUF super-block layouts such files carry.
+ *   q4_K  : 144 bytes {fp16 d; fp16 dmin; uint8 s[12]; uint8 qs[128]}: eight
+ *           6-bit scales sc_j and mins m_j (j < 4: sc_j = s[j] & 63,
+ *           m_j = s[j+4] & 63; j >= 4: sc_j = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+ *           m_j = (s[j+4] >> 4) | (s[j] >> 6) << 4); element 64c + i (i < 32)
+ *           is the low nibble of qs[32c + i], element 64c + 32 + i its high
+ *           nibble; w = d * sc_j * q - dmin * m_j for element e in j = e / 32.
+ *   q6_K  : 210 bytes {uint8 ql[128]; uint8 qh[64]; int8 sc[16]; fp16 d}:
+ *           element e, h = e / 128, r = e % 128, g = r / 32, l = r % 32, takes
+ *           nibble (g >> 1) of ql[64h + 32(g & 1) + l] and bits 2g, 2g+1 of
+ *           qh[32h + l] as its high two bits: q in 0..63,
+ *           w = d * sc[e / 16] * (q - 32).
  *
  * Memory: every pointer argument named W/x/y/xq/src/dst/buf/out is a DEVICE
  * pointer on the current HIP device; pointer arrays (Ns, srcs, ys) are HOST
@@ -77,7 +91,11 @@ typedef enum skg_fmt {
   SKG_Q4_0_Q8_1 = 3, /* q4_0 W  x Q8_1 x, integer dot (gemv)                */
   SKG_Q8_0_Q8_1 = 4, /* q8_0 W  x Q8_1 x, integer dot (gemv)                */
   SKG_Q4_0_BF16 = 5, /* q4_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
-  SKG_Q8_0_BF16 = 6  /* q8_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
+  SKG_Q8_0_BF16 = 6, /* q8_0 W  x bf16 x, MFMA tile (gemm_tiled)            */
+  SKG_Q4_K_F32 = 7,  /* q4_K W  x float32 x       (gemv)                    */
+  SKG_Q6_K_F32 = 8,  /* q6_K W  x float32 x       (gemv)                    */
+  SKG_Q4_K_Q8_1 = 9, /* q4_K W  x Q8_1 x, integer dot (gemv)                */
+  SKG_Q6_K_Q8_1 = 10 /* q6_K W  x Q8_1 x, integer dot (gemv)                */
 } skg_fmt;
 
 typedef enum skg_epi {
@@ -109,7 +127,7 @@ const char* skg_last_error(void);
  * skg_packed_size: bytes of the packed buffer for an N x K matrix of the
  *   weight format of `fmt`, or 0 if (fmt, N, K) is invalid.  1 <= N <=
  *   2^31 - 1; K <= 2^30 and K >= 32, K % 32 == 0 for q8_0/q4_0, K >= 8 and
- *   K % 8 == 0 for bf16.
+ *   K % 8 == 0 for bf16, K >= 256 and K % 256 == 0 for q4_K/q6_K.
  * skg_pack_weights: src = canonical N x K weights (device, 2-byte aligned),
  *   N * K / 32 / 256 < 2^31 - 1 for q8_0/q4_0 (one launch; else SKG_E_SHAPE),
  *   dst = packed buffer of skg_packed_size bytes (device, 256-byte aligned).

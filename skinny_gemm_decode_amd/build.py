@@ -38,6 +38,8 @@ SOURCES = [
     "gemv_q8_0_f32.hip",
     "gemv_q4_0_f32.hip",
     "gemv_q8_1.hip",
+    "gemv_q4_K.hip",
+    "gemv_q6_K.hip",
 ]
 
 # Packed fp32 arithmetic is disabled for every HIP translation unit; the host

@@ -63,8 +63,11 @@ skg_status check_device(int* cus = nullptr) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool is_gemv_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1; }
-bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_BF16; }
+bool is_gemv_fmt(int fmt) {
+  return (fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1) || (fmt >= SKG_Q4_K_F32 && fmt <= SKG_Q6_K_Q8_1);
+}
+bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q6_K_Q8_1; }
+constexpr int kNumFmts = SKG_Q6_K_Q8_1 + 1;
 
 // K and N rules shared by packing and products.
 skg_status check_nk(int fmt, int64_t N, int64_t K) {
@@ -73,6 +76,9 @@ skg_status check_nk(int fmt, int64_t N, int64_t K) {
   if (N < 1) return fail(SKG_E_SHAPE, "N must be >= 1 (got %lld)", (long long)N);
   if (wk == WK_BF16) {
     if (K < 8 || K % 8) return fail(SKG_E_SHAPE, "bf16 needs K >= 8 and K %% 8 == 0 (got %lld)", (long long)K);
+  } else if (wk == WK_Q4_K || wk == WK_Q6_K) {
+    if (K < QK_K || K % QK_K)
+      return fail(SKG_E_SHAPE, "q4_K/q6_K need K >= 256 and K %% 256 == 0 (got %lld)", (long long)K);
   } else {
     if (K < 32 || K % 32) return fail(SKG_E_SHAPE, "q8_0/q4_0 need K >= 32 and K %% 32 == 0 (got %lld)", (long long)K);
   }
@@ -95,7 +101,7 @@ std::once_flag g_reg_once;
 std::vector<GemvEntry>* g_reg = nullptr;
 std::mutex g_sel_mu;
 // selected registry index per (fmt, M, epi); -1 = default (first registered)
-int g_sel[5][9][3];
+int g_sel[kNumFmts][9][3];
 std::atomic<int64_t> g_lds_pad{0};
 // Set when SKG_LDS_PAD_BYTES holds something other than an integer in
 // 0..kMaxLdsPad: every GEMV call is then refused until skg_set_lds_pad
@@ -136,6 +142,8 @@ void init_registry() {
     register_gemv_mfma_q8_1_alt(*v);
     register_gemv_mfma_q4_0_alt(*v);
     register_gemv_mfma_q8_0_alt(*v);
+    register_gemv_q4_K(*v);
+    register_gemv_q6_K(*v);
     for (auto& a : g_sel)
       for (auto& b : a)
         for (int& c : b) c = -1;
@@ -389,7 +397,7 @@ skg_status check_gemv_common(int fmt, int64_t M, int64_t K, const void* W, const
                 (long long)kMaxLdsPad);
   if (!W || !x) return fail(SKG_E_INVALID_ARG, "null W or x");
   if (!aligned(W, 16)) return fail(SKG_E_ALIGN, "W must be 16-byte aligned");
-  const bool q8 = (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1);
+  const bool q8 = (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1 || fmt == SKG_Q4_K_Q8_1 || fmt == SKG_Q6_K_Q8_1);
   if (!aligned(x, q8 ? 4 : 16)) return fail(SKG_E_ALIGN, "x must be %d-byte aligned", q8 ? 4 : 16);
   (void)K;
   return SKG_OK;

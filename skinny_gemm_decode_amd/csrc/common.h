@@ -14,7 +14,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int QK = 32;  // elements per quantisation block along K
 
-enum WKind { WK_BF16 = 0, WK_Q8_0 = 1, WK_Q4_0 = 2, WK_INVALID = -1 };
+enum WKind { WK_BF16 = 0, WK_Q8_0 = 1, WK_Q4_0 = 2, WK_Q4_K = 3, WK_Q6_K = 4, WK_INVALID = -1 };
+
+constexpr int QK_K = 256;  // elements per K-quant super-block
 
 __host__ __device__ inline int wkind_of(int fmt) {
   switch (fmt) {
@@ -25,6 +27,10 @@ __host__ __device__ inline int wkind_of(int fmt) {
     case SKG_Q4_0_F32:
     case SKG_Q4_0_Q8_1:
     case SKG_Q4_0_BF16: return WK_Q4_0;
+    case SKG_Q4_K_F32:
+    case SKG_Q4_K_Q8_1: return WK_Q4_K;
+    case SKG_Q6_K_F32:
+    case SKG_Q6_K_Q8_1: return WK_Q6_K;
     default: return WK_INVALID;
   }
 }
@@ -38,10 +44,20 @@ __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_
 //     q8_0 -> two planes of nb units: plane 0 holds codes 0..15 of every
 //             block, plane 1 codes 16..31, so each plane streams contiguously.
 //   scales (q8_0, q4_0): fp16 [N][nb] at scale_off (256-byte aligned).
+//   q4_K: payload one 16-byte unit per 32-element sub-block, its codes in the
+//     q4_0 order (byte i: element i in the low nibble, element 16 + i in the
+//     high nibble); at scale_off the 16-byte header {d, dmin, 12 scale bytes}
+//     of every super-block [N][K/256], i.e. 2 bytes per 32 elements as q4_0.
+//   q6_K: per row nb low units (16 bytes, the low four bits of each code in
+//     the q4_0 order) then nb high units (8 bytes: dword t holds, for code
+//     dwords k = 2t + s of the low unit, the top two bits of element 4k + b
+//     at bits 8b + 4 - 4s and of element 16 + 4k + b at bits 8b + 6 - 4s);
+//     int8 sub-block scales [N][K/16] at scale_off; fp16 d [N][K/256] at
+//     d_off.
 struct Layout {
   int64_t N = 0, K = 0, nb = 0;
   int wk = WK_INVALID;
-  size_t row_bytes = 0, payload_bytes = 0, scale_off = 0, total = 0;
+  size_t row_bytes = 0, payload_bytes = 0, scale_off = 0, d_off = 0, total = 0;
 };
 
 __host__ __device__ inline Layout layout_of(int wk, int64_t N, int64_t K) {
@@ -56,10 +72,14 @@ __host__ __device__ inline Layout layout_of(int wk, int64_t N, int64_t K) {
     L.scale_off = align256(L.payload_bytes);
     L.total = L.scale_off;
   } else {
-    L.row_bytes = size_t(L.nb) * (wk == WK_Q8_0 ? 32 : 16);
+    L.row_bytes = size_t(L.nb) * (wk == WK_Q8_0 ? 32 : wk == WK_Q6_K ? 24 : 16);
     L.payload_bytes = size_t(N) * L.row_bytes;
     L.scale_off = align256(L.payload_bytes);
     L.total = align256(L.scale_off + size_t(N) * size_t(L.nb) * 2);
+    if (wk == WK_Q6_K) {
+      L.d_off = L.total;
+      L.total = align256(L.d_off + size_t(N) * size_t(K / QK_K) * 2);
+    }
   }
   return L;
 }
@@ -67,7 +87,8 @@ __host__ __device__ inline Layout layout_of(int wk, int64_t N, int64_t K) {
 // A packed matrix as the kernels see it.
 struct PackedW {
   const uint8_t* payload;
-  const uint16_t* scales;
+  const uint16_t* scales;  // 2 bytes per 32-element block per row (q6_K: two int8 scales)
+  const uint16_t* dsup;    // q6_K: fp16 d per super-block [N][K/256]; else null
   uint32_t row_bytes;
   uint32_t nb;
 };
@@ -76,6 +97,7 @@ inline PackedW packed_view(const void* base, const Layout& L) {
   PackedW p;
   p.payload = static_cast<const uint8_t*>(base);
   p.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(base) + L.scale_off);
+  p.dsup = L.d_off ? reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(base) + L.d_off) : nullptr;
   p.row_bytes = uint32_t(L.row_bytes);
   p.nb = uint32_t(L.nb);
   return p;

@@ -28,37 +28,83 @@ namespace skg {
 template <int FMT>
 struct Fmt;
 
+// E: elements per 16-byte weight unit; WV: payload dwords per unit; XB, XF:
+// activation bytes and floats per unit; KQ: 4 or 6 for the K-quant
+// super-block formats q4_K / q6_K, else 0.
 template <>
 struct Fmt<SKG_BF16_BF16> {
-  static constexpr int E = 8, WV = 4, XB = 16, XF = 8;
+  static constexpr int E = 8, WV = 4, XB = 16, XF = 8, KQ = 0;
   static constexpr bool SCALE = false, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q8_0_F32> {
-  static constexpr int E = 32, WV = 8, XB = 128, XF = 32;
+  static constexpr int E = 32, WV = 8, XB = 128, XF = 32, KQ = 0;
   static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
 };
 template <>
 struct Fmt<SKG_Q4_0_F32> {
-  static constexpr int E = 32, WV = 4, XB = 128, XF = 32;
+  static constexpr int E = 32, WV = 4, XB = 128, XF = 32, KQ = 0;
   static constexpr bool SCALE = true, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q4_0_Q8_1> {
-  static constexpr int E = 32, WV = 4, XB = 36, XF = 0;
+  static constexpr int E = 32, WV = 4, XB = 36, XF = 0, KQ = 0;
   static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q8_0_Q8_1> {
-  static constexpr int E = 32, WV = 8, XB = 36, XF = 0;
+  static constexpr int E = 32, WV = 8, XB = 36, XF = 0, KQ = 0;
   static constexpr bool SCALE = true, XQ8 = true, XSUM = false;
+};
+// K-quant super-block weights (256 elements): one unit per 32-element
+// sub-block; their scales are decoded per unit from the super-block header
+// (q4_K) or the int8 scale and fp16 d streams (q6_K).
+template <>
+struct Fmt<SKG_Q4_K_F32> {
+  static constexpr int E = 32, WV = 4, XB = 128, XF = 32, KQ = 4;
+  static constexpr bool SCALE = false, XQ8 = false, XSUM = true;
+};
+template <>
+struct Fmt<SKG_Q6_K_F32> {
+  static constexpr int E = 32, WV = 4, XB = 128, XF = 32, KQ = 6;
+  static constexpr bool SCALE = false, XQ8 = false, XSUM = true;
+};
+template <>
+struct Fmt<SKG_Q4_K_Q8_1> {
+  static constexpr int E = 32, WV = 4, XB = 36, XF = 0, KQ = 4;
+  static constexpr bool SCALE = false, XQ8 = true, XSUM = false;
+};
+template <>
+struct Fmt<SKG_Q6_K_Q8_1> {
+  static constexpr int E = 32, WV = 4, XB = 36, XF = 0, KQ = 6;
+  static constexpr bool SCALE = false, XQ8 = true, XSUM = false;
 };
 
 // One 16-byte (bf16, q4_0) or 2x16-byte (q8_0) weight unit and its scale.
-template <int FMT>
+// The K-quant units keep their scale words raw until the unit is consumed, so
+// that no load result is needed while the chunk's loads are being issued.
+template <int FMT, int KQ = Fmt<FMT>::KQ>
 struct WUnit {
   uint32_t w[Fmt<FMT>::WV];
   float d;
+};
+// q4_K: lane l always owns units u with u = l (mod 64), so the eight lanes
+// 8s .. 8s+7 hold the eight sub-blocks of one super-block and each quad of
+// them can hold its whole 16-byte header: lane l loads header dword l & 3 and
+// the quad exchanges them (DPP) when the unit is consumed.
+template <int FMT>
+struct WUnit<FMT, 4> {
+  uint32_t w[4];  // codes, q4_0 order
+  uint32_t hd;    // header dword (lane & 3): d | dmin << 16, or 4 of the 12 scale/min bytes
+  float a, b;     // d * sc and dmin * m of the unit's sub-block (set by prep_w)
+};
+template <int FMT>
+struct WUnit<FMT, 6> {
+  uint32_t w[4];  // low four bits of the codes, q4_0 order
+  uint32_t h[2];  // top two bits (crumbs, see the packed layout)
+  uint32_t sc;    // int8 scales of elements 0..15 (low byte) and 16..31
+  uint32_t d;     // fp16 bits of the super-block's d
+  float alo, ahi;  // d * scale of each half (set by prep_w)
 };
 
 // One activation unit in compute form.
@@ -67,12 +113,14 @@ struct XUnit;
 template <int FMT>
 struct XUnit<FMT, false> {
   float v[Fmt<FMT>::XF];
-  float sum;
+  float sum;   // sum of the block (q6_K: of elements 0..15)
+  float sum2;  // q6_K: sum of elements 16..31
 };
 template <int FMT>
 struct XUnit<FMT, true> {
   uint32_t q[8];
   float d, s;
+  int qs_lo, qs_hi;  // q6_K: integer sums of codes 0..15 and 16..31
 };
 
 template <int FMT>
@@ -89,26 +137,51 @@ __device__ inline u32x4 ld_u32x4_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// rowp: start of the row's payload; srow: the row's fp16 scales.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// rowp: start of the row's payload; srow: the row's scale stream (fp16
+// scales; q4_K super-block headers; q6_K int8 scale pairs); drow: the row's
+// q6_K d stream.
 template <int FMT>
 __device__ inline void load_w(WUnit<FMT>& u, const uint8_t* rowp, const uint16_t* srow, uint32_t nb,
-                              uint32_t unit) {
+                              uint32_t unit, const uint16_t* drow = nullptr) {
   const u32x4 p = ld_u32x4_stream(rowp + size_t(unit) * 16);
-  u.w[0] = p.x;
-  u.w[1] = p.y;
-  u.w[2] = p.z;
-  u.w[3] = p.w;
-  if constexpr (Fmt<FMT>::WV == 8) {
-    const u32x4 q = ld_u32x4_stream(rowp + (size_t(nb) + unit) * 16);
-    u.w[4] = q.x;
-    u.w[5] = q.y;
-    u.w[6] = q.z;
-    u.w[7] = q.w;
-  }
-  if constexpr (Fmt<FMT>::SCALE) {
-    u.d = h2f(__builtin_nontemporal_load(srow + unit));
+  if constexpr (Fmt<FMT>::KQ == 4) {
+    u.w[0] = p.x;
+    u.w[1] = p.y;
+    u.w[2] = p.z;
+    u.w[3] = p.w;
+    // dword lane & 3 (= unit & 3, also for a clamped unit past the row's end,
+    // so the quad always exchanges one whole header)
+    u.hd = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(srow + size_t(unit >> 3) * 8) +
+                                      (threadIdx.x & 3u));
+  } else if constexpr (Fmt<FMT>::KQ == 6) {
+    u.w[0] = p.x;
+    u.w[1] = p.y;
+    u.w[2] = p.z;
+    u.w[3] = p.w;
+    const u32x2 h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rowp + size_t(nb) * 16 + size_t(unit) * 8));
+    u.h[0] = h.x;
+    u.h[1] = h.y;
+    u.sc = __builtin_nontemporal_load(srow + unit);
+    u.d = __builtin_nontemporal_load(drow + (unit >> 3));
   } else {
-    u.d = 0.f;
+    u.w[0] = p.x;
+    u.w[1] = p.y;
+    u.w[2] = p.z;
+    u.w[3] = p.w;
+    if constexpr (Fmt<FMT>::WV == 8) {
+      const u32x4 q = ld_u32x4_stream(rowp + (size_t(nb) + unit) * 16);
+      u.w[4] = q.x;
+      u.w[5] = q.y;
+      u.w[6] = q.z;
+      u.w[7] = q.w;
+    }
+    if constexpr (Fmt<FMT>::SCALE) {
+      u.d = h2f(__builtin_nontemporal_load(srow + unit));
+    } else {
+      u.d = 0.f;
+    }
   }
 }
 
@@ -159,7 +232,15 @@ __device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
     // activation chain of unit_acc, so that a block whose codes are all 0
     // (q8_0) cancels to exactly zero: scaling every term by a power of two
     // commutes with each rounding.
-    if constexpr (Fmt<FMT>::XSUM) {
+    if constexpr (Fmt<FMT>::KQ == 6) {
+      // half-block sums, each in the element order of its product chain
+      float s2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += x.v[i];
+#pragma unroll
+      for (int i = 16; i < 32; ++i) s2 += x.v[i];
+      x.sum2 = s2;
+    } else if constexpr (Fmt<FMT>::XSUM) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) s += x.v[i];
     }
@@ -206,6 +287,16 @@ __device__ inline void x_from_raw(XUnit<FMT>& x, const XRaw<FMT>& r, bool ok) {
     const uint32_t ds = ok ? r.w[0] : 0u;
     x.d = h2f(ds & 0xFFFFu);
     x.s = h2f(ds >> 16);
+    if constexpr (Fmt<FMT>::KQ == 6) {
+      int lo = 0, hi = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lo = __builtin_amdgcn_sdot4(int(x.q[k]), 0x01010101, lo, false);
+        hi = __builtin_amdgcn_sdot4(int(x.q[4 + k]), 0x01010101, hi, false);
+      }
+      x.qs_lo = lo;
+      x.qs_hi = hi;
+    }
   } else {
     constexpr int PP = Fmt<FMT>::XB / 16;
     u32x4 pc[PP];
@@ -228,7 +319,7 @@ __device__ inline void fetch_x_global(XUnit<FMT>& x, const uint8_t* xb, int64_t 
 template <int FMT>
 __device__ inline int unit_idot(const WUnit<FMT>& w, const XUnit<FMT, true>& x) {
   int si = 0;
-  if constexpr (FMT == SKG_Q4_0_Q8_1) {
+  if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q4_K_Q8_1) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       si = __builtin_amdgcn_sdot4(int(w.w[k] & 0x0F0F0F0Fu), int(x.q[k]), si, false);
@@ -253,6 +344,55 @@ __device__ inline DecodeK decode_consts() {
   asm volatile("" : "+s"(k.mhi));
   asm volatile("" : "+v"(k.magic));
   return k;
+}
+
+// d * sc_j and dmin * m_j of the calling lane's q4_K sub-block j = lane & 7
+// (both exact in binary32: 11-bit by 6-bit products).  The quad's header
+// dwords arrive by DPP broadcast (all 64 lanes take part).  From the 12 packed
+// bytes s[0..11]: for j < 4, sc = s[j] & 63 and m = s[j + 4] & 63; for
+// j >= 4, the low four bits come from s[j + 4] (sc: low nibble, m: high
+// nibble) and the top two from bits 6..7 of s[j - 4] (sc) and s[j] (m).
+template <int CTRL>
+__device__ inline uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline void q4_K_scales(uint32_t hd, float& a, float& b) {
+  const uint32_t dd = dpp_u<0x00>(hd);  // quad_perm [0,0,0,0]
+  const uint32_t s0 = dpp_u<0x55>(hd);  // [1,1,1,1]: s[0..3]
+  const uint32_t s1 = dpp_u<0xAA>(hd);  // [2,2,2,2]: s[4..7]
+  const uint32_t s2 = dpp_u<0xFF>(hd);  // [3,3,3,3]: s[8..11]
+  const uint32_t j = threadIdx.x & 7u;
+  const uint32_t sh = 8u * (j & 3u);
+  const uint32_t b0 = (s0 >> sh) & 0xFFu, b1 = (s1 >> sh) & 0xFFu, b2 = (s2 >> sh) & 0xFFu;
+  const bool lo = j < 4u;
+  const uint32_t sc = lo ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+  const uint32_t m = lo ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+  a = h2f(dd & 0xFFFFu) * float(sc);
+  b = h2f(dd >> 16) * float(m);
+}
+
+// Full 6-bit codes of a q6_K unit as bytes: code dword k of elements 4k..4k+3
+// (A) and of elements 16+4k..16+4k+3 (B).
+__device__ inline void q6_K_codes(const uint32_t (&w)[4], const uint32_t (&h)[2], int k, uint32_t& a,
+                                  uint32_t& b) {
+  const uint32_t H = h[k >> 1];
+  const uint32_t hA = (k & 1) ? (H << 4) : H;
+  const uint32_t hB = (k & 1) ? (H << 2) : (H >> 2);
+  a = (w[k] & 0x0F0F0F0Fu) | (hA & 0x30303030u);
+  b = ((w[k] >> 4) & 0x0F0F0F0Fu) | (hB & 0x30303030u);
+}
+
+// Once per loaded unit, before it meets the M activation rows: the K-quant
+// scales are decoded here rather than once per row of the activation.
+template <int FMT>
+__device__ inline void prep_w(WUnit<FMT>& w) {
+  if constexpr (Fmt<FMT>::KQ == 4) {
+    q4_K_scales(w.hd, w.a, w.b);
+  } else if constexpr (Fmt<FMT>::KQ == 6) {
+    const float d = h2f(w.d);
+    w.alo = d * float(int8_t(w.sc & 0xFFu));  // exact: 11 x 8 bits
+    w.ahi = d * float(int8_t(w.sc >> 8));
+  }
 }
 
 // acc + (contribution of one weight unit against one activation unit).
@@ -311,6 +451,69 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
   } else if constexpr (FMT == SKG_Q4_0_Q8_1) {
     const int si = unit_idot<FMT>(w, x);
     return fmaf(w.d, fmaf(x.d, float(si), -8.f * x.s), acc);
+  } else if constexpr (FMT == SKG_Q4_K_F32) {
+    // w = d sc q - dmin m: the codes decode exactly to fp16 (as for q4_0,
+    // without the offset) and the min term takes the block sum of x.
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t v = w.w[k], v8 = v >> 8;
+      const q4h lo02 = q4h_of((v & dk.mlo) | dk.magic);
+      const q4h lo13 = q4h_of((v8 & dk.mlo) | dk.magic);
+      const q4h hi02 = q4h_of((v & dk.mhi) | dk.magic);
+      const q4h hi13 = q4h_of((v8 & dk.mhi) | dk.magic);
+      const q4h off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+      const q4h sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      const q4h off16 = {(_Float16)-64.0f, (_Float16)-64.0f};
+      const q4h a = lo02 + off, b = lo13 + off;
+      const q4h c = __builtin_elementwise_fma(hi02, sixteenth, off16);
+      const q4h e = __builtin_elementwise_fma(hi13, sixteenth, off16);
+      s = fmaf(float(a[0]), x.v[4 * k + 0], s);
+      s = fmaf(float(b[0]), x.v[4 * k + 1], s);
+      s = fmaf(float(a[1]), x.v[4 * k + 2], s);
+      s = fmaf(float(b[1]), x.v[4 * k + 3], s);
+      t = fmaf(float(c[0]), x.v[16 + 4 * k + 0], t);
+      t = fmaf(float(e[0]), x.v[16 + 4 * k + 1], t);
+      t = fmaf(float(c[1]), x.v[16 + 4 * k + 2], t);
+      t = fmaf(float(e[1]), x.v[16 + 4 * k + 3], t);
+    }
+    return fmaf(w.a, s + t, fmaf(-w.b, x.sum, acc));
+  } else if constexpr (FMT == SKG_Q4_K_Q8_1) {
+    const int si = unit_idot<FMT>(w, x);
+    return fmaf(w.a, x.d * float(si), fmaf(-w.b, x.s, acc));
+  } else if constexpr (FMT == SKG_Q6_K_F32) {
+    // w = d sc (q - 32) per 16 elements: unsigned code bytes times x, less
+    // 32 times the half-block sum of x (accumulated in the same order, so a
+    // half whose codes are all 32 cancels exactly).
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t ca, cb;
+      q6_K_codes(w.w, w.h, k, ca, cb);
+      s = fmaf(cvt_ubyte<0>(ca), x.v[4 * k + 0], s);
+      s = fmaf(cvt_ubyte<1>(ca), x.v[4 * k + 1], s);
+      s = fmaf(cvt_ubyte<2>(ca), x.v[4 * k + 2], s);
+      s = fmaf(cvt_ubyte<3>(ca), x.v[4 * k + 3], s);
+      t = fmaf(cvt_ubyte<0>(cb), x.v[16 + 4 * k + 0], t);
+      t = fmaf(cvt_ubyte<1>(cb), x.v[16 + 4 * k + 1], t);
+      t = fmaf(cvt_ubyte<2>(cb), x.v[16 + 4 * k + 2], t);
+      t = fmaf(cvt_ubyte<3>(cb), x.v[16 + 4 * k + 3], t);
+    }
+    acc = fmaf(w.alo, fmaf(-32.f, x.sum, s), acc);
+    return fmaf(w.ahi, fmaf(-32.f, x.sum2, t), acc);
+  } else if constexpr (FMT == SKG_Q6_K_Q8_1) {
+    // codes 0..63 are non-negative int8, so the signed 4x8-bit dot is exact
+    int sa = 0, sb = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t ca, cb;
+      q6_K_codes(w.w, w.h, k, ca, cb);
+      sa = __builtin_amdgcn_sdot4(int(ca), int(x.q[k]), sa, false);
+      sb = __builtin_amdgcn_sdot4(int(cb), int(x.q[4 + k]), sb, false);
+    }
+    // d * sc * dA * (sum q qa - 32 sum qa) per half: the integer parts are exact
+    acc = fmaf(w.alo * x.d, float(sa - 32 * x.qs_lo), acc);
+    return fmaf(w.ahi * x.d, float(sb - 32 * x.qs_hi), acc);
   } else {
     const int si = unit_idot<FMT>(w, x);
     return fmaf(w.d * x.d, float(si), acc);
@@ -420,6 +623,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 
   const uint8_t* rowp[RT];
   const uint16_t* srow[RT];
+  const uint16_t* drow[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const PackedW& P = (r < RO) ? sg.w0 : sg.w1;
@@ -427,6 +631,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     const int64_t nn = (n < sg.N) ? n : 0;
     rowp[r] = P.payload + size_t(nn) * P.row_bytes;
     srow[r] = P.scales + size_t(nn) * P.nb;
+    drow[r] = (F::KQ == 6) ? P.dsup + size_t(nn) * (P.nb / 8) : nullptr;
   }
   const uint32_t nb = sg.w0.nb;
   const uint32_t nu = a.nu;
@@ -438,7 +643,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
   DecodeK dk{};
-  if constexpr (FMT == SKG_Q4_0_F32) dk = decode_consts();
+  if constexpr (FMT == SKG_Q4_0_F32 || FMT == SKG_Q4_K_F32) dk = decode_consts();
   const int nchunks = int((nu + UC - 1) / UC);
   for (int c = kw; c < nchunks; c += KW) {
     const uint32_t ub = uint32_t(c) * UC;
@@ -511,7 +716,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
       const uint32_t u = ub + uint32_t(j * 64 + lane);
       const uint32_t uc = (u < nu) ? u : 0u;
 #pragma unroll
-      for (int r = 0; r < RT; ++r) load_w<FMT>(w[r][j], rowp[r], srow[r], nb, uc);
+      for (int r = 0; r < RT; ++r) load_w<FMT>(w[r][j], rowp[r], srow[r], nb, uc, drow[r]);
     }
     // Every load of the chunk is issued before any result is used.
     __builtin_amdgcn_sched_barrier(0);
@@ -544,6 +749,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     for (int j = 0; j < J; ++j) {
       const uint32_t u = ub + uint32_t(j * 64 + lane);
       const bool uok = u < nu;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) prep_w<FMT>(w[r][j]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         XUnit<FMT> xu;
@@ -656,7 +863,8 @@ inline GemvEntry gemv_entry() {
 // LDS bytes an instance needs (0 when the activation lives in registers).
 inline size_t gemv_lds_bytes(int fmt, int M, int J, int xlds, int kw = 1) {
   if (!xlds) return 0;
-  const int xb = (fmt == SKG_BF16_BF16) ? 16 : (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1) ? 36 : 128;
+  const bool q8 = fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1 || fmt == SKG_Q4_K_Q8_1 || fmt == SKG_Q6_K_Q8_1;
+  const int xb = (fmt == SKG_BF16_BF16) ? 16 : q8 ? 36 : 128;
   return size_t(M) * size_t(64 * J) * size_t(xb) * size_t(kw);
 }
 

@@ -34,3 +34,12 @@
   SKG_M(F, 6, ROL, JL, XL, SROL)       \
   SKG_M(F, 7, ROL, JL, XL, SROL)       \
   SKG_M(F, 8, ROL, JL, XL, SROL)
+
+// plain GEMV only, M = 3..8
+#define SKG_N3_8(F, RO, J, X)           \
+  SKG_I(F, 3, RO, J, X, 4, SKG_EPI_NONE) \
+  SKG_I(F, 4, RO, J, X, 4, SKG_EPI_NONE) \
+  SKG_I(F, 5, RO, J, X, 4, SKG_EPI_NONE) \
+  SKG_I(F, 6, RO, J, X, 4, SKG_EPI_NONE) \
+  SKG_I(F, 7, RO, J, X, 4, SKG_EPI_NONE) \
+  SKG_I(F, 8, RO, J, X, 4, SKG_EPI_NONE)

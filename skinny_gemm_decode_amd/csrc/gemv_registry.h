@@ -19,6 +19,8 @@ void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out);
+void register_gemv_q4_K(std::vector<GemvEntry>& out);
+void register_gemv_q6_K(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q8_1(std::vector<GemvEntry>& out);
 void register_gemv_mfma_q8_1_alt(std::vector<GemvEntry>& out);
 }  // namespace skg

@@ -55,6 +55,18 @@ def test_packed_sizes(skg):
     assert skg.packed_size(skg.BF16_BF16, 0, 64) == 0       # N < 1
     assert skg.packed_size(17, 4, 64) == 0                  # unknown format
     assert skg.packed_size_multi(skg.Q4_0_Q8_1, [4096, 4096, 4096], 4096) == 3 * 4096 * 128 * 18
+    # K-quants: q4_K 16-byte units + 16-byte header per 256 elements; q6_K
+    # 24 bytes per 32 elements, int8 scale pairs, then fp16 d per 256 elements,
+    # each stream starting on a 256-byte boundary
+    a256 = lambda v: (v + 255) // 256 * 256
+    assert skg.packed_size(skg.Q4_K_F32, 14336, 4096) == 14336 * 128 * 18
+    assert skg.packed_size(skg.Q4_K_Q8_1, 3, 256) == a256(a256(3 * 8 * 16) + 3 * 8 * 2)
+    q6 = a256(14336 * 128 * 24) + 14336 * 128 * 2
+    assert skg.packed_size(skg.Q6_K_F32, 14336, 4096) == a256(q6) + 14336 * 16 * 2
+    assert skg.packed_size(skg.Q6_K_Q8_1, 5, 512) == a256(a256(a256(5 * 16 * 24) + 5 * 16 * 2) + 5 * 2 * 2)
+    for fmt in (skg.Q4_K_F32, skg.Q6_K_F32, skg.Q4_K_Q8_1, skg.Q6_K_Q8_1):
+        assert skg.packed_size(fmt, 4, 4128) == 0           # K not a multiple of 256
+        assert skg.packed_size(fmt, 4, 128) == 0
     # three 4096x4096 + two 11008x4096 + one 4096x11008 q4_0 matrices: one decode layer
     layer = (skg.packed_size_multi(3, [4096] * 3, 4096) + skg.packed_size_multi(3, [11008] * 2, 4096)
              + skg.packed_size(3, 4096, 11008))

@@ -23,7 +23,9 @@ pytestmark = pytest.mark.gpu
 K = 4096
 N_FULL = 14336
 N_RAGGED = 14331          # last tile holds 11 rows
-KIND = {1: "q8_0", 2: "q4_0", 3: "q4_0", 4: "q8_0"}
+KIND = {1: "q8_0", 2: "q4_0", 3: "q4_0", 4: "q8_0", 7: "q4_K", 8: "q6_K", 9: "q4_K", 10: "q6_K"}
+SEED = {"q8_0": 2, "q4_0": 1, "q4_K": 3, "q6_K": 4}
+FMTS = [1, 2, 3, 4, 7, 8, 9, 10]
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +43,7 @@ def weights(skg, fmt, N):
     key = (KIND[fmt], N)
     if key not in _CACHE:
         _CACHE.clear()  # one matrix (~470 MB decoded) at a time
-        rng = si.rng_for(0, 4, 500 + N + (1 if KIND[fmt] == "q4_0" else 2))
+        rng = si.rng_for(0, 4, 500 + N + SEED[KIND[fmt]])
         W = si.weights(KIND[fmt], rng, N, K)
         Wd = oracle.dequantize(KIND[fmt], W)
         _CACHE[key] = (W, {}, Wd)
@@ -57,7 +59,7 @@ def activation(skg, fmt, M, seed):
     activation the reference multiplies (Q8_1 blocks checked bit-exactly
     against the oracle's quantiser first)."""
     x = si.activations_f32(si.rng_for(0, 4, 900 + seed), M, K)
-    if fmt in (3, 4):
+    if fmt in skg.Q8_1_FMTS:
         xq = skg.quantize_act_q8_1(dev(x))
         ref = oracle.quantize_q8_1(x)
         assert np.array_equal(host(xq), ref), "Q8_1 activation differs from the oracle"
@@ -83,10 +85,10 @@ def rel_of(skg, fmt, v):
     """Tolerance a matrix-core variant is held to: two fp16 activation terms
     or exact int8 block dots 2e-5 of sum|w x|; one fp16 term (one rounding of
     2^-11 relative per element plus fp32 accumulation) 8e-4."""
-    return 2e-5 if (v["j"] == 2 or fmt in (3, 4)) else 8e-4
+    return 2e-5 if (v["j"] == 2 or fmt in skg.Q8_1_FMTS) else 8e-4
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_full_size_every_row(skg, fmt, M):
     W, Wp, Wd = weights(skg, fmt, N_FULL)
@@ -108,7 +110,7 @@ def test_full_size_every_row(skg, fmt, M):
         skg.gemv_set_variant(fmt, M, skg.EPI_NONE, 0)
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [3, 8])
 def test_ragged_full_size_every_row(skg, fmt, M):
     """N = 14331: the last 16-row tile is partial (its rows past N are

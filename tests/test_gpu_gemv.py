@@ -24,12 +24,21 @@ def skg():
 
 
 def wkind(skg, fmt):
-    return {skg.BF16_BF16: "bf16", skg.Q8_0_F32: "q8_0", skg.Q4_0_F32: "q4_0",
-            skg.Q4_0_Q8_1: "q4_0", skg.Q8_0_Q8_1: "q8_0"}[fmt]
+    return skg.WEIGHT_KIND[fmt]
 
 
 def is_q8_1(skg, fmt):
-    return fmt in (skg.Q4_0_Q8_1, skg.Q8_0_Q8_1)
+    return fmt in skg.Q8_1_FMTS
+
+
+def is_kquant(fmt):
+    return fmt >= 7
+
+
+def k_of(skg, fmt, bf16_k=4104, q_k=4128, kq_k=4352):
+    """A K with a ragged last chunk for each weight kind (K-quants: a
+    multiple of 256)."""
+    return bf16_k if fmt == skg.BF16_BF16 else (kq_k if is_kquant(fmt) else q_k)
 
 
 def make_inputs(skg, fmt, M, N, K, seed):
@@ -60,6 +69,8 @@ def reference(skg, fmt, W, x, xq_ref):
         return y, bound
     if fmt == skg.Q8_0_Q8_1:
         return oracle.gemv_q8_0_q8_1_ref(W, xq_ref)
+    if is_q8_1(skg, fmt):
+        return oracle.gemv_ref(oracle.dequantize(kind, W), oracle.decode_q8_1(xq_ref))
     return oracle.gemv_ref_fmt(kind, W, x, x_kind="bf16" if fmt == skg.BF16_BF16 else "f32")
 
 
@@ -72,12 +83,14 @@ def run_gemv(skg, fmt, M, N, K, W, x):
     return host(y), xq_ref
 
 
-GEMV_FMTS = [0, 1, 2, 3, 4]
+GEMV_FMTS = [0, 1, 2, 3, 4, 7, 8, 9, 10]
 
 
 def shapes_for(fmt):
     if fmt == 0:
         return [(1, 8), (5, 40), (17, 520), (131, 4104)]
+    if is_kquant(fmt):
+        return [(1, 256), (3, 512), (17, 768), (131, 4352)]
     return [(1, 32), (3, 96), (17, 288), (131, 4128)]
 
 
@@ -102,10 +115,10 @@ def test_every_compiled_variant(skg):
             fmt, M, epi = v["fmt"], v["M"], v["epi"]
             N = 320 if epi == skg.EPI_SWIGLU_Q8_1 else 300
             # the matrix-core variants (x_lds 2, 3, 4) take K % 512 == 0, K <= 4096
-            K = 4104 if fmt == skg.BF16_BF16 else (4096 if v["x_lds"] in (2, 3, 4) else 4128)
+            K = 4096 if v["x_lds"] in (2, 3, 4) else k_of(skg, fmt)
             if v["x_lds"] == 1 and v["kw"] > 1:
                 # every K class walks the same number of chunks, the last one partial
-                K = 32 * (64 * v["j"] * (2 * v["kw"] - 1) + 10)
+                K = 32 * (64 * v["j"] * (2 * v["kw"] - 1) + (8 if is_kquant(fmt) else 10))
             key = (fmt, M, epi, K)
             if key not in cache:
                 W0, x = make_inputs(skg, fmt, M, N, K, seed=5000 + 10 * fmt + M)
@@ -143,7 +156,7 @@ def test_every_compiled_variant(skg):
 
 @pytest.mark.parametrize("fmt", GEMV_FMTS)
 def test_gemv_multi_qkv_three_outputs(skg, fmt):
-    K = 4104 if fmt == skg.BF16_BF16 else 4128
+    K = k_of(skg, fmt)
     Ns = [96, 33, 130]
     Ws = [make_inputs(skg, fmt, 1, n, K, seed=7000 + 10 * fmt + i)[0] for i, n in enumerate(Ns)]
     _, x = make_inputs(skg, fmt, 2, 1, K, seed=7100 + fmt)
@@ -207,7 +220,7 @@ def test_swiglu_q8_1_epilogue(skg, fmt, M):
 @pytest.mark.parametrize("fmt", GEMV_FMTS)
 @pytest.mark.parametrize("M", [1, 2, 5])
 def test_gemv_multi_swiglu_and_its_halves(skg, fmt, M):
-    K = 4104 if fmt == skg.BF16_BF16 else 4128
+    K = k_of(skg, fmt)
     N = 257
     Wg, x = make_inputs(skg, fmt, M, N, K, seed=8000 + 10 * fmt + M)
     Wu, _ = make_inputs(skg, fmt, M, N, K, seed=8100 + 10 * fmt + M)
