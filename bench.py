@@ -27,8 +27,9 @@ fp16 term are timed beside the two-term kernel), the Llama-2-7B-shaped q4_0 x
 Q8_1 decode layer over 32 distinct layers (plain, with the SwiGLU launch
 writing Q8_1, and with the layer's RMSNorm as its own launch or writing Q8_1
 itself), the fused RMSNorm -> Q8_1 launch alone, the q8_0 M=1 K=256 N=512
-launch-bound case, the M=512 MFMA prefill tile, and the K-quant (q4_K, q6_K
-super-block) weights x fp32 and x Q8_1 at the same decode shape.  The CPU
+launch-bound case, the M=512 MFMA prefill tile (q4_0, q8_0, q4_K and q6_K
+weights), and the K-quant (q4_K, q6_K super-block) weights x fp32 and x Q8_1
+at the same decode shape.  The CPU
 oracle is timed on a bounded sample of the headline workload on this host's
 cores.
 
@@ -576,7 +577,7 @@ def bench_norm(skg, si, torch, timer, warm_s, M=1, K=4096):
 
 def bench_prefill(skg, si, torch, timer, warm_s, kind="q4_0"):
     M, N, K = 512, 14336, 4096
-    fmt = skg.Q4_0_BF16 if kind == "q4_0" else skg.Q8_0_BF16
+    fmt = {"q4_0": skg.Q4_0_BF16, "q8_0": skg.Q8_0_BF16, "q4_K": skg.Q4_K_BF16, "q6_K": skg.Q6_K_BF16}[kind]
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
     cols = gate_rows(N, n=40, seed=11)
@@ -889,7 +890,7 @@ def main():
             log(f"[{r['name']}] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
                 f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
     if "prefill" in arms:
-        for kind in ("q4_0", "q8_0"):
+        for kind in ("q4_0", "q8_0", "q4_K", "q6_K"):
             r = bench_prefill(skg, si, torch, timer, warm, kind=kind)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "

@@ -95,7 +95,9 @@ typedef enum skg_fmt {
   SKG_Q4_K_F32 = 7,  /* q4_K W  x float32 x       (gemv)                    */
   SKG_Q6_K_F32 = 8,  /* q6_K W  x float32 x       (gemv)                    */
   SKG_Q4_K_Q8_1 = 9, /* q4_K W  x Q8_1 x, integer dot (gemv)                */
-  SKG_Q6_K_Q8_1 = 10 /* q6_K W  x Q8_1 x, integer dot (gemv)                */
+  SKG_Q6_K_Q8_1 = 10, /* q6_K W  x Q8_1 x, integer dot (gemv)               */
+  SKG_Q4_K_BF16 = 11, /* q4_K W  x bf16 x, MFMA tile (gemm_tiled)           */
+  SKG_Q6_K_BF16 = 12  /* q6_K W  x bf16 x, MFMA tile (gemm_tiled)           */
 } skg_fmt;
 
 typedef enum skg_epi {
@@ -240,16 +242,21 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
  * the weights once per activation row: each 64x64 weight tile is decoded once
  * into padded on-chip memory and serves every row of its output tile.
  *
- * fmt : SKG_Q4_0_BF16 or SKG_Q8_0_BF16 (the q8_0 tile of the same page's
- *       q8_0 measurements).  W : skg_pack_weights(fmt, N, K) output.
+ * fmt : SKG_Q4_0_BF16, SKG_Q8_0_BF16 (the q8_0 tile of the same page's
+ *       q8_0 measurements), SKG_Q4_K_BF16 or SKG_Q6_K_BF16 (the q4_K / q6_K
+ *       weights the same page's tile is built for).
+ * W   : skg_pack_weights(fmt, N, K) output.
  * x   : bf16 [M][K] device, 16-byte aligned.  y : float32 [M][N], overwritten.
  * Weights are decoded to bf16 (w = bf16_rne(d * (c - 8)) for q4_0,
- * bf16_rne(d * q) for q8_0) and multiplied on bf16 MFMA with fp32
- * accumulation.  1 <= M <= 2^31 - 1, N >= 1, K % 32 == 0, and the output
- * must fit one launch: ceil(M / 256) * ceil(N / 112) <= 2^31 - 1 (else
- * SKG_E_SHAPE).  q8_0 weights run on the
- * pipelined organisations (skg_gemm_tiled_set_variant 3 or 4); with another
- * organisation selected a q8_0 call returns SKG_E_UNSUPPORTED.
+ * bf16_rne(d * q) for q8_0, both exact before the rounding; for q4_K
+ * bf16_rne(fp32_rn(d sc q - dmin m)) and for q6_K
+ * bf16_rne(fp32_rn(d sc (q - 32))), the value formed once in binary32) and
+ * multiplied on bf16 MFMA with fp32 accumulation.  1 <= M <= 2^31 - 1,
+ * N >= 1, K % 32 == 0 (K % 256 == 0 for q4_K/q6_K), and the output must fit
+ * one launch: ceil(M / 256) * ceil(N / 112) <= 2^31 - 1 (else SKG_E_SHAPE).
+ * q8_0, q4_K and q6_K weights run on the pipelined organisations
+ * (skg_gemm_tiled_set_variant 3 or 4); with another organisation selected
+ * such a call returns SKG_E_UNSUPPORTED.
  */
 skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x,
                           float* y, hipStream_t stream);

@@ -179,7 +179,8 @@ def swiglu_tolerance(g_ref, u_ref, tol_g, tol_u) -> np.ndarray:
 
 def gemm_tiled_ref(Wq, A_bf16, kind: str = "q4_0"):
     """Quantised weights [N, nb, block] ("q4_0" 18-byte or "q8_0" 34-byte
-    blocks) x bf16 bit patterns [M, K] -> (y, bound, y_bf16w) [M, N].
+    blocks, "q4_K" / "q6_K" super-blocks) x bf16 bit patterns [M, K] ->
+    (y, bound, y_bf16w) [M, N].
 
     "Chapter 2.2 - speed - 64-lane Metal" (the tile) decodes each weight tile
     once and multiplies it against every activation row; the product itself
@@ -187,10 +188,13 @@ def gemm_tiled_ref(Wq, A_bf16, kind: str = "q4_0"):
     y_bf16w rounds every decoded weight to bf16 (nearest-even) before the
     float64 product: the value a kernel that stages bf16 weights computes
     exactly up to summation order.  It is a second reference for classifying
-    deviations, not the gate.
+    deviations, not the gate.  The page does not say how a K-quant weight
+    reaches bf16; the reading taken here is the plainest one for a kernel
+    that decodes in binary32: the decoded value is rounded once to binary32
+    (nearest-even; exact for q4_0 and q8_0), then to bf16.
     """
-    if kind not in ("q4_0", "q8_0"):
-        raise ValueError(f"tile weights are q4_0 or q8_0, not {kind!r}")
+    if kind not in ("q4_0", "q8_0", "q4_K", "q6_K"):
+        raise ValueError(f"tile weights are q4_0, q8_0, q4_K or q6_K, not {kind!r}")
     Wd = dequantize(kind, Wq)
     A = decode_bf16(A_bf16)
     y, bound = gemv_ref(Wd, A)

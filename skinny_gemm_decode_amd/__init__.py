@@ -32,13 +32,16 @@ Q4_K_F32 = 7
 Q6_K_F32 = 8
 Q4_K_Q8_1 = 9
 Q6_K_Q8_1 = 10
+Q4_K_BF16 = 11
+Q6_K_BF16 = 12
 FMT_NAMES = {BF16_BF16: "bf16_bf16", Q8_0_F32: "q8_0_f32", Q4_0_F32: "q4_0_f32",
              Q4_0_Q8_1: "q4_0_q8_1", Q8_0_Q8_1: "q8_0_q8_1", Q4_0_BF16: "q4_0_bf16", Q8_0_BF16: "q8_0_bf16",
-             Q4_K_F32: "q4_K_f32", Q6_K_F32: "q6_K_f32", Q4_K_Q8_1: "q4_K_q8_1", Q6_K_Q8_1: "q6_K_q8_1"}
+             Q4_K_F32: "q4_K_f32", Q6_K_F32: "q6_K_f32", Q4_K_Q8_1: "q4_K_q8_1", Q6_K_Q8_1: "q6_K_q8_1",
+             Q4_K_BF16: "q4_K_bf16", Q6_K_BF16: "q6_K_bf16"}
 # weight kind of each format (the canonical encoding pack_weights reads)
 WEIGHT_KIND = {BF16_BF16: "bf16", Q8_0_F32: "q8_0", Q4_0_F32: "q4_0", Q4_0_Q8_1: "q4_0", Q8_0_Q8_1: "q8_0",
                Q4_0_BF16: "q4_0", Q8_0_BF16: "q8_0", Q4_K_F32: "q4_K", Q6_K_F32: "q6_K", Q4_K_Q8_1: "q4_K",
-               Q6_K_Q8_1: "q6_K"}
+               Q6_K_Q8_1: "q6_K", Q4_K_BF16: "q4_K", Q6_K_BF16: "q6_K"}
 Q8_1_FMTS = (Q4_0_Q8_1, Q8_0_Q8_1, Q4_K_Q8_1, Q6_K_Q8_1)
 # skg_epi
 EPI_NONE = 0
@@ -130,11 +133,12 @@ def _nbytes(t) -> int:
 # Bytes per K element of an activation row, by product format (Q8_1: 36-byte
 # blocks of 32 elements), and of a canonical weight row element.
 _X_BYTES_PER_32 = {BF16_BF16: 64, Q8_0_F32: 128, Q4_0_F32: 128, Q4_0_Q8_1: 36, Q8_0_Q8_1: 36,
-                   Q4_0_BF16: 64, Q8_0_BF16: 64, Q4_K_F32: 128, Q6_K_F32: 128, Q4_K_Q8_1: 36, Q6_K_Q8_1: 36}
+                   Q4_0_BF16: 64, Q8_0_BF16: 64, Q4_K_F32: 128, Q6_K_F32: 128, Q4_K_Q8_1: 36, Q6_K_Q8_1: 36,
+                   Q4_K_BF16: 64, Q6_K_BF16: 64}
 _W_BYTES_PER_32 = {BF16_BF16: 64, Q8_0_F32: 34, Q4_0_F32: 18, Q4_0_Q8_1: 18, Q8_0_Q8_1: 34,
                    Q4_0_BF16: 18, Q8_0_BF16: 34}
 # K-quant super-blocks: bytes per 256 elements
-_W_BYTES_PER_256 = {Q4_K_F32: 144, Q4_K_Q8_1: 144, Q6_K_F32: 210, Q6_K_Q8_1: 210}
+_W_BYTES_PER_256 = {Q4_K_F32: 144, Q4_K_Q8_1: 144, Q4_K_BF16: 144, Q6_K_F32: 210, Q6_K_Q8_1: 210, Q6_K_BF16: 210}
 
 
 def _need(t, nbytes: int, what: str) -> int:
@@ -292,7 +296,7 @@ def gemv_multi(fmt: int, M: int, K: int, Ns: Sequence[int], W, x, ys=None, epi: 
 
 
 def gemm_tiled(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
-    """y[M, N] = x W^T on MFMA for large M (q4_0 weights, bf16 x)."""
+    """y[M, N] = x W^T on MFMA for large M (q4_0, q8_0, q4_K or q6_K weights, bf16 x)."""
     import torch
 
     if y is None:

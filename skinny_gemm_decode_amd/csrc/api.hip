@@ -66,8 +66,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool is_gemv_fmt(int fmt) {
   return (fmt >= SKG_BF16_BF16 && fmt <= SKG_Q8_0_Q8_1) || (fmt >= SKG_Q4_K_F32 && fmt <= SKG_Q6_K_Q8_1);
 }
-bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q6_K_Q8_1; }
-constexpr int kNumFmts = SKG_Q6_K_Q8_1 + 1;
+bool is_any_fmt(int fmt) { return fmt >= SKG_BF16_BF16 && fmt <= SKG_Q6_K_BF16; }
+constexpr int kNumFmts = SKG_Q6_K_BF16 + 1;
 
 // K and N rules shared by packing and products.
 skg_status check_nk(int fmt, int64_t N, int64_t K) {
@@ -547,11 +547,12 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
 skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x, float* y,
                           hipStream_t stream) {
   if (!is_any_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown fmt %d", int(fmt));
-  if (fmt != SKG_Q4_0_BF16 && fmt != SKG_Q8_0_BF16)
-    return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16 and SKG_Q8_0_BF16");
+  if (fmt != SKG_Q4_0_BF16 && fmt != SKG_Q8_0_BF16 && fmt != SKG_Q4_K_BF16 && fmt != SKG_Q6_K_BF16)
+    return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16, SKG_Q8_0_BF16, SKG_Q4_K_BF16 and SKG_Q6_K_BF16");
   const int variant = g_gemm_variant.load(std::memory_order_relaxed);
-  if (fmt == SKG_Q8_0_BF16 && variant != 3 && variant != 4)
-    return fail(SKG_E_UNSUPPORTED, "q8_0 tiles run on prefill organisations 3 and 4 (selected: %d)", variant);
+  if (fmt != SKG_Q4_0_BF16 && variant != 3 && variant != 4)
+    return fail(SKG_E_UNSUPPORTED, "q8_0, q4_K and q6_K tiles run on prefill organisations 3 and 4 (selected: %d)",
+                variant);
   skg_status st = check_nk(fmt, N, K);
   if (st != SKG_OK) return st;
   if (M < 1 || M > INT32_MAX) return fail(SKG_E_SHAPE, "M must be in [1, 2^31 - 1] (got %lld)", (long long)M);

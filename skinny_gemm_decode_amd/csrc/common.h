@@ -28,9 +28,11 @@ __host__ __device__ inline int wkind_of(int fmt) {
     case SKG_Q4_0_Q8_1:
     case SKG_Q4_0_BF16: return WK_Q4_0;
     case SKG_Q4_K_F32:
-    case SKG_Q4_K_Q8_1: return WK_Q4_K;
+    case SKG_Q4_K_Q8_1:
+    case SKG_Q4_K_BF16: return WK_Q4_K;
     case SKG_Q6_K_F32:
-    case SKG_Q6_K_Q8_1: return WK_Q6_K;
+    case SKG_Q6_K_Q8_1:
+    case SKG_Q6_K_BF16: return WK_Q6_K;
     default: return WK_INVALID;
   }
 }
@@ -104,6 +106,31 @@ inline PackedW packed_view(const void* base, const Layout& L) {
 }
 
 __device__ inline u32x4 ld_u32x4(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Full 6-bit codes of a packed q6_K unit as bytes, from its low unit w and
+// high unit h: code dword k of elements 4k..4k+3 (a) and of elements
+// 16+4k..16+4k+3 (b).
+__device__ inline void q6_K_codes(const uint32_t (&w)[4], const uint32_t (&h)[2], int k, uint32_t& a,
+                                  uint32_t& b) {
+  const uint32_t H = h[k >> 1];
+  const uint32_t hA = (k & 1) ? (H << 4) : H;
+  const uint32_t hB = (k & 1) ? (H << 2) : (H >> 2);
+  a = (w[k] & 0x0F0F0F0Fu) | (hA & 0x30303030u);
+  b = ((w[k] >> 4) & 0x0F0F0F0Fu) | (hB & 0x30303030u);
+}
+
+// Scale and min of sub-block j of a q4_K super-block from its 12 packed
+// scale bytes s[0..11] (s0 = s[0..3], s1 = s[4..7], s2 = s[8..11]): for
+// j < 4, sc = s[j] & 63 and m = s[j + 4] & 63; for j >= 4, the low four bits
+// come from s[j + 4] (sc: low nibble, m: high nibble) and the top two from
+// bits 6..7 of s[j - 4] (sc) and s[j] (m).
+__device__ inline void q4_K_sc_m(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t j, uint32_t& sc, uint32_t& m) {
+  const uint32_t sh = 8u * (j & 3u);
+  const uint32_t b0 = (s0 >> sh) & 0xFFu, b1 = (s1 >> sh) & 0xFFu, b2 = (s2 >> sh) & 0xFFu;
+  const bool lo = j < 4u;
+  sc = lo ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
+  m = lo ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+}
 
 // Byte i of v as a float, one v_cvt_f32_ubyte<i> instruction.  Written as
 // asm because the compiler otherwise narrows the byte mask it can prove and

@@ -1,5 +1,6 @@
-// Tiled prefill GEMM on MFMA: y[m][n] = sum_k W[n][k] x[m][k], q4_0 weights,
-// bf16 activations, fp32 output.
+// Tiled prefill GEMM on MFMA: y[m][n] = sum_k W[n][k] x[m][k], q4_0 weights
+// (q8_0, q4_K and q6_K on the pipelined organisation), bf16 activations, fp32
+// output.
 //
 // "Chapter 2.2 - speed - 64-lane Metal" (the tile) stops re-reading and
 // re-unpacking the weights for every activation row: a workgroup decodes a
@@ -398,13 +399,15 @@ __global__ __launch_bounds__((CW + 4) * 64) void gemm_q4_0_bf16_pc_kernel(Packed
 // the fragments of step s+1 are read.  Each lane fetches the chunk whose
 // swizzled slot is its own destination, so the slots keep the swizzled
 // layout the fragment reads expect.
-// WK selects the weight format: q4_0 (one 16-byte unit per block) or q8_0
-// (two planes of 16 bytes per block: codes 0-15 and 16-31).
+// WK selects the weight format: q4_0 (one 16-byte unit per block), q8_0
+// (two planes of 16 bytes per block: codes 0-15 and 16-31), q4_K (the 16-byte
+// unit of a 32-element sub-block and its super-block header) or q6_K (the
+// low unit, the 8-byte high unit, the int8 scale pair and d).
 template <int NB16, int PW, bool ADMA, int WK = WK_Q4_0>
 __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, const uint16_t* __restrict__ A,
                                                                   float* __restrict__ y, int M, int N, int K) {
-  static_assert(WK == WK_Q4_0 || WK == WK_Q8_0, "q4_0 or q8_0 weights");
-  constexpr int NPL = (WK == WK_Q8_0) ? 2 : 1;  // 16-byte planes per block
+  static_assert(WK == WK_Q4_0 || WK == WK_Q8_0 || WK == WK_Q4_K || WK == WK_Q6_K, "weight format");
+  constexpr int NPL = (WK == WK_Q4_0) ? 1 : 2;  // 16-byte words held per block
   constexpr int BN = 16 * NB16;
   constexpr int ASLOTS = ADMA ? 3 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t Bs[3][128 * GT_LDS_ROW];
@@ -430,6 +433,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     const int dn = min(n0 + drow, N - 1);
     const uint8_t* dpay = P.payload + size_t(dn) * P.row_bytes;
     const uint16_t* dsc = P.scales + size_t(dn) * P.nb;
+    const uint16_t* dsup = (WK == WK_Q6_K) ? P.dsup + size_t(dn) * (P.nb / 8) : nullptr;
     u32x4 wraw[PW][NPL];
     uint32_t wsc[PW];
     bool wok[PW];
@@ -437,9 +441,19 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
       constexpr int SL = decltype(slot_c)::value;
       const int kb = s * 2 + dblk;
       const int kc = min(kb, nbk - 1);
+      if constexpr (WK == WK_Q4_K) {
+        wraw[SL][0] = ld_u32x4(dpay + size_t(kc) * 16);
+        wraw[SL][1] = ld_u32x4(dsc + size_t(kc >> 3) * 8);  // super-block header
+        wsc[SL] = uint32_t(kc) & 7u;                          // sub-block index
+      } else if constexpr (WK == WK_Q6_K) {
+        wraw[SL][0] = ld_u32x4(dpay + size_t(kc) * 16);
+        const uint32_t* hp = reinterpret_cast<const uint32_t*>(dpay + size_t(nbk) * 16 + size_t(kc) * 8);
+        wraw[SL][1] = u32x4{hp[0], hp[1], dsc[kc], dsup[kc >> 3]};
+      } else {
 #pragma unroll
-      for (int p = 0; p < NPL; ++p) wraw[SL][p] = ld_u32x4(dpay + (size_t(p) * size_t(nbk) + size_t(kc)) * 16);
-      wsc[SL] = dsc[kc];
+        for (int p = 0; p < NPL; ++p) wraw[SL][p] = ld_u32x4(dpay + (size_t(p) * size_t(nbk) + size_t(kc)) * 16);
+        wsc[SL] = dsc[kc];
+      }
       wok[SL] = kb < nbk;
     };
     // o[j] = bf16 pair (element 2j, element 2j+1) of the block, each
@@ -447,9 +461,44 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     auto store_w = [&](auto slot_c, auto buf_c) {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int BUF = decltype(buf_c)::value;
-      const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
       uint32_t o[16];
-      if constexpr (WK == WK_Q4_0) {
+      if constexpr (WK == WK_Q4_K) {
+        // w = fp32_rn(a q - b), a = d sc_j, b = dmin m_j (both exact), q in
+        // the q4_0 unit order
+        uint32_t sc, m;
+        q4_K_sc_m(wraw[SL][1].y, wraw[SL][1].z, wraw[SL][1].w, wsc[SL], sc, m);
+        const float a = wok[SL] ? h2f(wraw[SL][1].x & 0xFFFFu) * float(sc) : 0.0f;
+        const float nb = wok[SL] ? -(h2f(wraw[SL][1].x >> 16) * float(m)) : 0.0f;
+        const uint32_t pw[4] = {wraw[SL][0].x, wraw[SL][0].y, wraw[SL][0].z, wraw[SL][0].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = pw[k] & 0x0F0F0F0Fu;
+          const uint32_t hi = (pw[k] >> 4) & 0x0F0F0F0Fu;
+          o[2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(lo), a, nb), fmaf(cvt_ubyte<1>(lo), a, nb));
+          o[2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(lo), a, nb), fmaf(cvt_ubyte<3>(lo), a, nb));
+          o[8 + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(hi), a, nb), fmaf(cvt_ubyte<1>(hi), a, nb));
+          o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(hi), a, nb), fmaf(cvt_ubyte<3>(hi), a, nb));
+        }
+      } else if constexpr (WK == WK_Q6_K) {
+        // w = fp32_rn(a (q - 32)), a = d * scale of the half (exact)
+        const float d = h2f(wraw[SL][1].w);
+        const uint32_t sc = wraw[SL][1].z;
+        const float alo = wok[SL] ? d * float(int8_t(sc & 0xFFu)) : 0.0f;
+        const float ahi = wok[SL] ? d * float(int8_t(sc >> 8)) : 0.0f;
+        const float nlo = -32.0f * alo, nhi = -32.0f * ahi;
+        const uint32_t lw[4] = {wraw[SL][0].x, wraw[SL][0].y, wraw[SL][0].z, wraw[SL][0].w};
+        const uint32_t hw[2] = {wraw[SL][1].x, wraw[SL][1].y};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t ca, cb;
+          q6_K_codes(lw, hw, k, ca, cb);
+          o[2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(ca), alo, nlo), fmaf(cvt_ubyte<1>(ca), alo, nlo));
+          o[2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(ca), alo, nlo), fmaf(cvt_ubyte<3>(ca), alo, nlo));
+          o[8 + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(cb), ahi, nhi), fmaf(cvt_ubyte<1>(cb), ahi, nhi));
+          o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(cb), ahi, nhi), fmaf(cvt_ubyte<3>(cb), ahi, nhi));
+        }
+      } else if constexpr (WK == WK_Q4_0) {
+        const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
         // w = d (c - 8); element i < 16 is the low nibble of byte i, i + 16 its high nibble
         const float nd8 = -8.0f * d;
         const uint32_t pw[4] = {wraw[SL][0].x, wraw[SL][0].y, wraw[SL][0].z, wraw[SL][0].w};
@@ -464,6 +513,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
         }
       } else {
         // w = d q; q + 128 is the unsigned byte of q ^ 0x80, so w = d (u - 128)
+        const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
         const float nd128 = -128.0f * d;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -646,11 +696,33 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
 extern const int kGemmDefaultVariant = 4;
 std::atomic<int> g_gemm_variant{kGemmDefaultVariant};
 
+// The pipelined organisations (3: activation through registers, 4: copied
+// straight into LDS) for weight format WK.
+template <int WK>
+void launch_pipe(int variant, bool seven, unsigned grid, const PackedW& P, const uint16_t* xa, float* y, int64_t M,
+                 int64_t N, int64_t K, hipStream_t stream) {
+  if (variant == 3) {
+    if (seven)
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, false, WK>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+                         int(M), int(N), int(K));
+    else
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, false, WK>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+                         int(M), int(N), int(K));
+  } else {
+    if (seven)
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, true, WK>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+                         int(M), int(N), int(K));
+    else
+      hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, true, WK>), dim3(grid), dim3(512), 0, stream, P, xa, y,
+                         int(M), int(N), int(K));
+  }
+}
+
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,
                              float* y, hipStream_t stream) {
   const int variant = g_gemm_variant.load(std::memory_order_relaxed);
-  if (L.wk == WK_Q8_0) {
-    // q8_0 weights: the pipelined organisations only
+  if (L.wk != WK_Q4_0) {
+    // q8_0, q4_K and q6_K weights: the pipelined organisations only
     const PackedW P = packed_view(W, L);
     const int64_t mtiles = (M + GT_BM - 1) / GT_BM;
     const int64_t t7 = mtiles * ((N + 111) / 112), t8 = mtiles * ((N + 127) / 128);
@@ -660,21 +732,12 @@ hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, con
     const bool seven = e7 > e8;
     const unsigned grid = unsigned(seven ? t7 : t8);
     const uint16_t* xa = static_cast<const uint16_t*>(x);
-    if (variant == 3) {
-      if (seven)
-        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, false, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
-                           xa, y, int(M), int(N), int(K));
-      else
-        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, false, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
-                           xa, y, int(M), int(N), int(K));
-    } else {
-      if (seven)
-        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<7, GT_PW, true, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
-                           xa, y, int(M), int(N), int(K));
-      else
-        hipLaunchKernelGGL((gemm_q4_0_bf16_pipe_kernel<8, GT_PW, true, WK_Q8_0>), dim3(grid), dim3(512), 0, stream, P,
-                           xa, y, int(M), int(N), int(K));
-    }
+    if (L.wk == WK_Q8_0)
+      launch_pipe<WK_Q8_0>(variant, seven, grid, P, xa, y, M, N, K, stream);
+    else if (L.wk == WK_Q4_K)
+      launch_pipe<WK_Q4_K>(variant, seven, grid, P, xa, y, M, N, K, stream);
+    else
+      launch_pipe<WK_Q6_K>(variant, seven, grid, P, xa, y, M, N, K, stream);
     return hipGetLastError();
   }
   const PackedW P = packed_view(W, L);

@@ -348,10 +348,7 @@ __device__ inline DecodeK decode_consts() {
 
 // d * sc_j and dmin * m_j of the calling lane's q4_K sub-block j = lane & 7
 // (both exact in binary32: 11-bit by 6-bit products).  The quad's header
-// dwords arrive by DPP broadcast (all 64 lanes take part).  From the 12 packed
-// bytes s[0..11]: for j < 4, sc = s[j] & 63 and m = s[j + 4] & 63; for
-// j >= 4, the low four bits come from s[j + 4] (sc: low nibble, m: high
-// nibble) and the top two from bits 6..7 of s[j - 4] (sc) and s[j] (m).
+// dwords arrive by DPP broadcast (all 64 lanes take part).
 template <int CTRL>
 __device__ inline uint32_t dpp_u(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
@@ -361,25 +358,10 @@ __device__ inline void q4_K_scales(uint32_t hd, float& a, float& b) {
   const uint32_t s0 = dpp_u<0x55>(hd);  // [1,1,1,1]: s[0..3]
   const uint32_t s1 = dpp_u<0xAA>(hd);  // [2,2,2,2]: s[4..7]
   const uint32_t s2 = dpp_u<0xFF>(hd);  // [3,3,3,3]: s[8..11]
-  const uint32_t j = threadIdx.x & 7u;
-  const uint32_t sh = 8u * (j & 3u);
-  const uint32_t b0 = (s0 >> sh) & 0xFFu, b1 = (s1 >> sh) & 0xFFu, b2 = (s2 >> sh) & 0xFFu;
-  const bool lo = j < 4u;
-  const uint32_t sc = lo ? (b0 & 63u) : ((b2 & 15u) | ((b0 >> 6) << 4));
-  const uint32_t m = lo ? (b1 & 63u) : ((b2 >> 4) | ((b1 >> 6) << 4));
+  uint32_t sc, m;
+  q4_K_sc_m(s0, s1, s2, threadIdx.x & 7u, sc, m);
   a = h2f(dd & 0xFFFFu) * float(sc);
   b = h2f(dd >> 16) * float(m);
-}
-
-// Full 6-bit codes of a q6_K unit as bytes: code dword k of elements 4k..4k+3
-// (A) and of elements 16+4k..16+4k+3 (B).
-__device__ inline void q6_K_codes(const uint32_t (&w)[4], const uint32_t (&h)[2], int k, uint32_t& a,
-                                  uint32_t& b) {
-  const uint32_t H = h[k >> 1];
-  const uint32_t hA = (k & 1) ? (H << 4) : H;
-  const uint32_t hB = (k & 1) ? (H << 2) : (H >> 2);
-  a = (w[k] & 0x0F0F0F0Fu) | (hA & 0x30303030u);
-  b = ((w[k] >> 4) & 0x0F0F0F0Fu) | (hB & 0x30303030u);
 }
 
 // Once per loaded unit, before it meets the M activation rows: the K-quant

@@ -197,3 +197,32 @@ def test_prefill_tile_q8_0(skg, variant, M, N, K):
     y_ref, bound, y_b = oracle.gemm_tiled_ref(W[ncols], A[mrows], "q8_0")
     assert_close(yh[np.ix_(mrows, ncols)], y_ref, bound, "q8_0 tile vs exact weights")
     assert_close(yh[np.ix_(mrows, ncols)], y_b, bound, "q8_0 tile vs bf16 weights", rel=1e-4)
+
+
+@pytest.mark.parametrize("variant", [3, 4])
+@pytest.mark.parametrize("kind", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("M,N,K", [(512, 14336, 4096), (300, 250, 2304), (17, 129, 256), (2048, 256, 2048)])
+def test_prefill_tile_kquant(skg, variant, kind, M, N, K):
+    """q4_K / q6_K weight tiles (pipelined organisations), sampled at the
+    M=512 workload size, with ragged tiles; the bf16-weight reference (each
+    weight rounded through binary32 to bf16) bounds the remaining deviation
+    to summation order."""
+    fmt = skg.Q4_K_BF16 if kind == "q4_K" else skg.Q6_K_BF16
+    rng = si.rng_for(0, 7, M + N + K + (kind == "q6_K"))
+    W = si.weights(kind, rng, N, K)
+    A = si.activations_bf16(rng, M, K)
+    note(f"gemm_tiled {kind} M={M} N={N} K={K} variant {variant}")
+    skg.gemm_tiled_set_variant(variant)
+    try:
+        Wp = skg.pack_weights(fmt, N, K, dev(W))
+        y = poisoned((M, N))
+        skg.gemm_tiled(fmt, M, K, N, Wp, dev(A), y)
+        yh = host(y)
+    finally:
+        skg.gemm_tiled_set_variant(-1)
+    assert np.all(np.isfinite(yh))
+    mrows = sample_rows(M, n=32, seed=10)
+    ncols = sample_rows(N, n=1024, seed=11) if N > 1024 else np.arange(N)
+    y_ref, bound, y_b = oracle.gemm_tiled_ref(W[ncols], A[mrows], kind)
+    assert_close(yh[np.ix_(mrows, ncols)], y_ref, bound, f"{kind} tile vs exact weights")
+    assert_close(yh[np.ix_(mrows, ncols)], y_b, bound, f"{kind} tile vs bf16 weights", rel=1e-4)

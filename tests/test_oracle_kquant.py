@@ -152,3 +152,37 @@ def test_kquant_block_sizes():
     assert kquant.Q6_K_BLOCK_BYTES * 8 / kquant.QK_K == 6.5625
     for kind, nbytes in (("q4_K", 144), ("q6_K", 210)):
         assert si.weights(kind, si.rng_for(0, 99, 60), 3, 768).shape == (3, 3, nbytes)
+
+
+@pytest.mark.parametrize("kind", ["q4_K", "q6_K"])
+def test_tile_bf16_weight_reference_rounds_through_binary32(kind):
+    """y_bf16w of the tile reference for K-quant weights: each decoded weight
+    rounded to binary32 (nearest-even) and then to bf16 (nearest-even), exact
+    rational products.  The q4_K row 0 is built so the two roundings differ
+    from one: w = (1 + 2^-8) - (-2^-24) = 1 + 2^-8 + 2^-24 lies half a binary32
+    ulp above 1 + 2^-8, which rounds to even (1 + 2^-8), a bf16 tie that
+    rounds to even again: 1, where rounding the exact value once would give
+    1 + 2^-7."""
+    rng = si.rng_for(0, 99, 70 + (kind == "q6_K"))
+    M, N, K = 2, 4, 256
+    W = si.weights(kind, rng, N, K)
+    if kind == "q4_K":
+        W[0, 0, 0:2] = [0x04, 0x3C]          # d = 1 + 2^-8
+        W[0, 0, 2:4] = [0x01, 0x80]          # dmin = -2^-24 (smallest subnormal, negative)
+        W[0, 0, 4] = (W[0, 0, 4] & 0xC0) | 1     # sc_0 = 1
+        W[0, 0, 8] = (W[0, 0, 8] & 0xC0) | 1     # m_0 = 1
+        W[0, 0, 16] = (W[0, 0, 16] & 0xF0) | 1   # element 0: code 1
+    A = si.activations_bf16(rng, M, K)
+    _, _, y_b = oracle.gemm_tiled_ref(W, A, kind)
+    for n in range(N):
+        vals = ex.row_values(kind, W[n].tobytes(), K)
+        wr = [ex.round_binary(ex.round_binary(v, ex.F32), (8, -126)) for v in vals]
+        if kind == "q4_K" and n == 0:
+            assert vals[0] == 1 + Fraction(1, 256) + Fraction(1, 2 ** 24)
+            assert ex.round_binary(vals[0], (8, -126)) == 1 + Fraction(1, 128)
+            assert wr[0] == 1
+        for m in range(M):
+            av = [ex.bf16_value(int(v)) for v in A[m]]
+            ye = sum(w * a for w, a in zip(wr, av))
+            be = sum(abs(w * a) for w, a in zip(wr, av))
+            assert abs(float(ye) - y_b[m, n]) <= 1e-13 * float(be) + 1e-300, (m, n)
