@@ -29,9 +29,8 @@ writing Q8_1, and with the layer's RMSNorm as its own launch or writing Q8_1
 itself), the fused RMSNorm -> Q8_1 launch alone, the q8_0 M=1 K=256 N=512
 launch-bound case, the M=512 MFMA prefill tile (q4_0, q8_0, q4_K and q6_K
 weights), and the K-quant (q4_K, q6_K super-block) weights x fp32 and x Q8_1
-at the same decode shape.  The CPU
-oracle is timed on a bounded sample of the headline workload on this host's
-cores.
+at the same decode shape.  The CPU oracle is timed on a bounded sample of the
+headline workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 5] [--arms all|none|a,b] [--ms 1,2,4,8]
 Prints one JSON line on stdout; per-arm details go to the --details file when
