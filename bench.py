@@ -51,6 +51,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 ROTATION_BYTES = 2 * 1000**3   # >= 2 GB working set per arm
 METRIC = "achieved HBM GB/s (% of peak) + µs per M=1 GEMV, cold-cache rotation"
 
@@ -574,16 +575,26 @@ def bench_norm(skg, si, torch, timer, warm_s, M=1, K=4096):
     return res
 
 
-def bench_prefill(skg, si, torch, timer, warm_s, kind="q4_0"):
+def bench_prefill(skg, si, torch, timer, warm_s, kind="q4_0", act="bf16"):
+    """The M=512 tile: bf16 activations on the bf16 matrix cores, or (act
+    "q8_1") Q8_1 activation blocks on the integer matrix cores."""
     M, N, K = 512, 14336, 4096
-    fmt = {"q4_0": skg.Q4_0_BF16, "q8_0": skg.Q8_0_BF16, "q4_K": skg.Q4_K_BF16, "q6_K": skg.Q6_K_BF16}[kind]
+    if act == "q8_1":
+        fmt = {"q4_0": skg.Q4_0_Q8_1, "q8_0": skg.Q8_0_Q8_1}[kind]
+    else:
+        fmt = {"q4_0": skg.Q4_0_BF16, "q8_0": skg.Q8_0_BF16, "q4_K": skg.Q4_K_BF16, "q6_K": skg.Q6_K_BF16}[kind]
     wbytes = skg.packed_size(fmt, N, K)
     n_rot = rotation_count(wbytes)
     cols = gate_rows(N, n=40, seed=11)
     bufs, kept = make_packed_rotation(skg, si, torch, kind, fmt, N, K, n_rot, seed0=70_000, keep_rows=cols,
                                       keep_bufs=(0, n_rot - 1))
-    A_host = si.activations_bf16(si.rng_for(0, 5, 9), M, K)
-    A = torch.from_numpy(A_host.view("int16")).cuda()
+    if act == "q8_1":
+        x_host = si.activations_f32(si.rng_for(0, 5, 9), M, K)
+        A = skg.quantize_act_q8_1(torch.from_numpy(x_host).cuda())
+        A_host = A.cpu().numpy().reshape(M, K // 32, 36)   # checked against the oracle's quantiser below
+    else:
+        A_host = si.activations_bf16(si.rng_for(0, 5, 9), M, K)
+        A = torch.from_numpy(A_host.view("int16")).cuda()
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     lib = skg.lib
     sh = torch.cuda.current_stream().cuda_stream
@@ -594,19 +605,26 @@ def bench_prefill(skg, si, torch, timer, warm_s, kind="q4_0"):
         lib.skg_gemm_tiled(fmt, M, K, N, wp[i], ap, yp, sh)
 
     mrows = gate_rows(M, n=24, seed=12)
+    if act == "q8_1":
+        import numpy as np
+        import oracle
+        if not np.array_equal(A_host, oracle.quantize_q8_1(x_host).reshape(A_host.shape)):
+            raise RuntimeError("Q8_1 activation differs from the oracle; refusing to time")
     for b in (0, n_rot - 1):
         skg.check(lib.skg_gemm_tiled(fmt, M, K, N, wp[b], ap, yp, sh))
         torch.cuda.synchronize()
         if not bool(torch.isfinite(y).all()):
             raise RuntimeError("prefill tile produced non-finite output; refusing to time")
-        oracle_gate_prefill(f"prefill_{kind} buffer {b}", kind, kept[b], A_host[mrows],
+        oracle_gate_prefill(f"prefill_{kind}_{act} buffer {b}", kind, kept[b], A_host[mrows], act,
                             y[torch.as_tensor(mrows, device="cuda")][:, torch.as_tensor(cols, device="cuda")]
                             .cpu().numpy())
     res = timer.run(launch, n_rot, repeats=10, per_repeat=50, warm_s=warm_s)
     flops = 2.0 * M * N * K
-    res.update(name=f"prefill_{kind}_bf16_m512", M=M, N=N, K=K, rotation_buffers=n_rot, flop=flops,
+    res.update(name=f"prefill_{kind}_{act}_m512", M=M, N=N, K=K, rotation_buffers=n_rot, flop=flops,
                tflops=flops / (res["us_per_launch"] * 1e-6) / 1e12)
     res["frac_peak_mfma_bf16"] = res["tflops"] / PEAK_BF16_TFLOPS
+    if act == "q8_1":
+        res["frac_peak_mfma_int8"] = res["tflops"] / PEAK_INT8_TOPS
     del bufs
     torch.cuda.empty_cache()
     return res
@@ -699,9 +717,15 @@ def oracle_gate_gemv(label, kind, fmt, skg, x_host, xq_gpu, pairs):
     return worst
 
 
-def oracle_gate_prefill(label, kind, cols_w, A_rows, y_gpu):
+def oracle_gate_prefill(label, kind, cols_w, A_rows, act, y_gpu):
     import oracle
-    y_ref, bound, _ = oracle.gemm_tiled_ref(cols_w, A_rows, kind)
+    if act == "q8_1":
+        if kind == "q4_0":
+            y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(cols_w, A_rows)
+        else:
+            y_ref, bound = oracle.gemv_q8_0_q8_1_ref(cols_w, A_rows)
+    else:
+        y_ref, bound, _ = oracle.gemm_tiled_ref(cols_w, A_rows, kind)
     ok, w = oracle.check_close(y_gpu, y_ref, oracle.tolerance(bound))
     if not ok:
         raise RuntimeError(f"[{label}] outside the oracle's tolerance (worst err/tol {w:.3g}); refusing to time")
@@ -889,8 +913,9 @@ def main():
             log(f"[{r['name']}] {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s  graph "
                 f"{r['graph']['us_per_launch']:.2f} us/layer ({r['graph']['gbs']:.0f} GB/s)")
     if "prefill" in arms:
-        for kind in ("q4_0", "q8_0", "q4_K", "q6_K"):
-            r = bench_prefill(skg, si, torch, timer, warm, kind=kind)
+        for kind, act in (("q4_0", "bf16"), ("q8_0", "bf16"), ("q4_K", "bf16"), ("q6_K", "bf16"),
+                          ("q4_0", "q8_1"), ("q8_0", "q8_1")):
+            r = bench_prefill(skg, si, torch, timer, warm, kind=kind, act=act)
             details["arms"][r["name"]] = r
             log(f"[{r['name']}] {r['us_per_launch']:.1f} us  {r['tflops']:.0f} TFLOP/s "
                 f"({100 * r['frac_peak_mfma_bf16']:.1f}% of bf16 peak)")

@@ -257,6 +257,15 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
  * q8_0, q4_K and q6_K weights run on the pipelined organisations
  * (skg_gemm_tiled_set_variant 3 or 4); with another organisation selected
  * such a call returns SKG_E_UNSUPPORTED.
+ *
+ * fmt SKG_Q4_0_Q8_1 / SKG_Q8_0_Q8_1 runs the integer matrix-core tile (the
+ * int8 arm of the same tile): x is then the Q8_1 blocks of the activation
+ * ([M][K/32] blocks of 36 bytes, 4-byte aligned, as skg_quantize_act_q8_1
+ * writes them), each 32-element block's integer dot is exact, and
+ * y = sum over blocks of dW * dA * dot in fp32 (q4_0: dot of the codes
+ * minus 8).  K % 64 == 0 (else SKG_E_SHAPE), one launch takes
+ * ceil(M / 256) * ceil(N / 64) <= 2^31 - 1 tiles, and the organisation
+ * selected by skg_gemm_tiled_set_variant does not apply.
  */
 skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x,
                           float* y, hipStream_t stream);

@@ -296,12 +296,14 @@ def gemv_multi(fmt: int, M: int, K: int, Ns: Sequence[int], W, x, ys=None, epi: 
 
 
 def gemm_tiled(fmt: int, M: int, K: int, N: int, W, x, y=None, stream=None):
-    """y[M, N] = x W^T on MFMA for large M (q4_0, q8_0, q4_K or q6_K weights, bf16 x)."""
+    """y[M, N] = x W^T on MFMA for large M: q4_0, q8_0, q4_K or q6_K weights
+    against bf16 x, or q4_0 / q8_0 weights against Q8_1 blocks of x (integer
+    matrix cores)."""
     import torch
 
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=W.device)
-    check(lib.skg_gemm_tiled(fmt, M, K, N, _need(W, packed_size(fmt, N, K), "W"), _need(x, M * K * 2, "x"),
+    check(lib.skg_gemm_tiled(fmt, M, K, N, _need(W, packed_size(fmt, N, K), "W"), _need(x, _x_bytes(fmt, M, K), "x"),
                              _need(y, M * N * 4, "y"), _stream(stream)))
     return y
 

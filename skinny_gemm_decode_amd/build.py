@@ -34,6 +34,7 @@ SOURCES = [
     "norm.hip",
     "misc.hip",
     "gemm_tiled.hip",
+    "gemm_i8.hip",
     "gemv_bf16.hip",
     "gemv_q8_0_f32.hip",
     "gemv_q4_0_f32.hip",

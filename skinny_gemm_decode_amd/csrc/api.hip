@@ -547,8 +547,26 @@ skg_status skg_gemv_multi(skg_fmt fmt, int64_t M, int64_t K, int n, const int64_
 skg_status skg_gemm_tiled(skg_fmt fmt, int64_t M, int64_t K, int64_t N, const void* W, const void* x, float* y,
                           hipStream_t stream) {
   if (!is_any_fmt(fmt)) return fail(SKG_E_INVALID_ARG, "unknown fmt %d", int(fmt));
+  if (fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1) {
+    // integer matrix-core tile: Q8_1 activation blocks
+    skg_status st = check_nk(fmt, N, K);
+    if (st != SKG_OK) return st;
+    if (K % 64) return fail(SKG_E_SHAPE, "the Q8_1 tile needs K %% 64 == 0 (got %lld)", (long long)K);
+    if (M < 1 || M > INT32_MAX) return fail(SKG_E_SHAPE, "M must be in [1, 2^31 - 1] (got %lld)", (long long)M);
+    if (((M + 255) / 256) * ((N + 63) / 64) > INT32_MAX)
+      return fail(SKG_E_SHAPE, "M=%lld x N=%lld needs more output tiles than one launch takes", (long long)M,
+                  (long long)N);
+    if (!W || !x || !y) return fail(SKG_E_INVALID_ARG, "null W, x or y");
+    if (!aligned(W, 16)) return fail(SKG_E_ALIGN, "W must be 16-byte aligned");
+    if (!aligned(x, 4) || !aligned(y, 4)) return fail(SKG_E_ALIGN, "x and y must be 4-byte aligned");
+    if ((st = check_device()) != SKG_OK) return st;
+    hipError_t e = launch_gemm_i8(M, K, N, W, layout_of(wkind_of(fmt), N, K), x, y, stream);
+    if (e != hipSuccess) return fail(SKG_E_HIP, "gemm_tiled: %s", hipGetErrorString(e));
+    return ok();
+  }
   if (fmt != SKG_Q4_0_BF16 && fmt != SKG_Q8_0_BF16 && fmt != SKG_Q4_K_BF16 && fmt != SKG_Q6_K_BF16)
-    return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16, SKG_Q8_0_BF16, SKG_Q4_K_BF16 and SKG_Q6_K_BF16");
+    return fail(SKG_E_UNSUPPORTED, "gemm_tiled supports SKG_Q4_0_BF16, SKG_Q8_0_BF16, SKG_Q4_K_BF16, SKG_Q6_K_BF16, "
+                "SKG_Q4_0_Q8_1 and SKG_Q8_0_Q8_1");
   const int variant = g_gemm_variant.load(std::memory_order_relaxed);
   if (fmt != SKG_Q4_0_BF16 && variant != 3 && variant != 4)
     return fail(SKG_E_UNSUPPORTED, "q8_0, q4_K and q6_K tiles run on prefill organisations 3 and 4 (selected: %d)",

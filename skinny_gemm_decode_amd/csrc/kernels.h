@@ -23,6 +23,8 @@ hipError_t launch_empty(int64_t grid, int block, hipStream_t stream);
 extern std::atomic<int> g_gemm_variant;
 extern const int kGemmDefaultVariant;
 
+hipError_t launch_gemm_i8(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* xq, float* y,
+                          hipStream_t stream);
 hipError_t launch_gemm_tiled(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* x,
                              float* y, hipStream_t stream);
 

@@ -176,6 +176,9 @@ def test_other_entry_point_errors(skg):
     assert L.skg_gemm_tiled(11, 512, 4128, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE  # K % 256
     assert L.skg_gemm_tiled(12, 512, 128, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_gemv(11, 1, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_UNSUPPORTED    # tile format
+    assert L.skg_gemm_tiled(3, 512, 4128, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE   # Q8_1 tile: K % 64
+    assert L.skg_gemm_tiled(4, 512, 4096, 4096, FAKE, MISALIGNED, FAKE, None) == skg.E_ALIGN
+    assert L.skg_gemm_tiled(3, 0, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_SHAPE
     assert L.skg_gemv(13, 1, 4096, 4096, FAKE, FAKE, FAKE, None) == skg.E_INVALID_ARG
     # more output tiles than one launch takes, and M or N beyond 32-bit indices
     assert L.skg_gemm_tiled(5, 1 << 30, 4096, 1 << 20, FAKE, FAKE, FAKE, None) == skg.E_SHAPE

@@ -226,3 +226,37 @@ def test_prefill_tile_kquant(skg, variant, kind, M, N, K):
     y_ref, bound, y_b = oracle.gemm_tiled_ref(W[ncols], A[mrows], kind)
     assert_close(yh[np.ix_(mrows, ncols)], y_ref, bound, f"{kind} tile vs exact weights")
     assert_close(yh[np.ix_(mrows, ncols)], y_b, bound, f"{kind} tile vs bf16 weights", rel=1e-4)
+
+
+@pytest.mark.parametrize("fmt", [3, 4])
+@pytest.mark.parametrize("M,N,K", [(512, 14336, 4096), (300, 250, 2048), (17, 129, 64), (2048, 256, 2048),
+                                   (257, 1000, 4160)])
+def test_prefill_tile_q8_1_integer(skg, fmt, M, N, K):
+    """The integer matrix-core tile (q4_0 / q8_0 weights x Q8_1 activation
+    blocks): every block dot exact, then one binary32 scaling by dA dW per
+    block, so the result stays within 2e-5 of sum|w a| of the exact product of
+    the decoded operands (which fails if a block's scale, sign or code order
+    were wrong); sampled at the M=512 workload size, ragged tiles."""
+    kind = "q4_0" if fmt == skg.Q4_0_Q8_1 else "q8_0"
+    rng = si.rng_for(0, 8, M + N + K + fmt)
+    W = si.weights(kind, rng, N, K)
+    x = si.activations_f32(rng, M, K)
+    note(f"gemm_tiled Q8_1 {kind} M={M} N={N} K={K}")
+    import torch
+    Wp = skg.pack_weights(fmt, N, K, dev(W))
+    xq = skg.quantize_act_q8_1(dev(x))
+    xq_ref = oracle.quantize_q8_1(x)
+    assert np.array_equal(host(xq), xq_ref), "Q8_1 activation differs from the oracle"
+    y = poisoned((M, N))
+    skg.gemm_tiled(fmt, M, K, N, Wp, xq, y)
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+    mrows = sample_rows(M, n=32, seed=12)
+    ncols = sample_rows(N, n=1024, seed=13) if N > 1024 else np.arange(N)
+    xs = xq_ref.reshape(M, K // 32, 36)[mrows]
+    if fmt == skg.Q4_0_Q8_1:
+        y_ref, _, bound = oracle.gemv_q4_0_q8_1_ref(W[ncols], xs)
+    else:
+        y_ref, bound = oracle.gemv_q8_0_q8_1_ref(W[ncols], xs)
+    assert_close(yh[np.ix_(mrows, ncols)], y_ref, bound, f"Q8_1 tile {kind}", rel=2e-5)
+    del torch
