@@ -33,16 +33,14 @@
 
 namespace skg {
 
-namespace {
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GI_BM = 256;
-constexpr int GI_BROW = 80;    // LDS bytes per weight row: 2 x 32 codes + 16 pad
-constexpr int GI_AROW = 18;    // LDS dwords per activation row: 2 x 8 code dwords + 2 pad
-constexpr int GI_PW = 4;       // weight prefetch distance in K steps
+static constexpr int GI_BM = 256;
+static constexpr int GI_BROW = 80;  // LDS bytes per weight row: 2 x 32 codes + 16 pad
+static constexpr int GI_AROW = 18;  // LDS dwords per activation row: 2 x 8 code dwords + 2 pad
+static constexpr int GI_PW = 4;     // weight prefetch distance in K steps
 
-__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+static __device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int WK, int NB16, int PW>
 __global__ __launch_bounds__(256) void gemm_q8_1_i8_kernel(PackedW P, const uint8_t* __restrict__ xq,
@@ -235,8 +233,6 @@ __global__ __launch_bounds__(256) void gemm_q8_1_i8_kernel(PackedW P, const uint
       }
     }
 }
-
-}  // namespace
 
 hipError_t launch_gemm_i8(int64_t M, int64_t K, int64_t N, const void* W, const Layout& L, const void* xq, float* y,
                           hipStream_t stream) {

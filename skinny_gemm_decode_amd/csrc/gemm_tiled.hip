@@ -298,8 +298,11 @@ __global__ __launch_bounds__((CW + 4) * 64) void gemm_q4_0_bf16_pc_kernel(Packed
   // Each consumer wave loads its own WR rows x 64 columns of x per step with
   // full-cache-line loads (instruction i: rows 8i..8i+7, 128 contiguous bytes
   // each), parks them in a wave-private LDS slice, and reads the MFMA
-  // fragments from there.  Slot of (row r, 16-byte chunk c) = 8r + (c ^ (r & 7)):
-  // the 16 rows of a fragment read land on distinct banks.  Only the owning
+  // fragments from there.  Slot of (row r, 16-byte chunk c) =
+  // 8r + (c ^ ((r >> 1) & 7)): a fragment read takes one chunk of 16
+  // consecutive rows; rows of equal parity share a half of the 64 banks (a
+  // row is 128 bytes), and within each parity the 8 rows' chunks land on 8
+  // different 4-bank groups, so the 16 reads cover all 64 banks once.  Only the owning
   // wave touches its slice, and a wave's LDS operations complete in order, so
   // the slice needs no barrier.  Rows past M read row M-1; columns past K read
   // the last 8 (their weights decode to zero).
@@ -321,7 +324,7 @@ __global__ __launch_bounds__((CW + 4) * 64) void gemm_q4_0_bf16_pc_kernel(Packed
     for (int i = 0; i < AL; ++i) {
       const int r = i * 8 + (lane >> 3);
       const int c = lane & 7;
-      As[buf * SLICE + r * 8 + (c ^ (r & 7))] = araw[i];
+      As[buf * SLICE + r * 8 + (c ^ ((r >> 1) & 7))] = araw[i];
     }
   };
   f32x4 acc[MI][NB16];
@@ -344,7 +347,7 @@ __global__ __launch_bounds__((CW + 4) * 64) void gemm_q4_0_bf16_pc_kernel(Packed
       for (int mi = 0; mi < MI; ++mi) {
         const int r = mi * 16 + (lane & 15);
         const int c = kk * 4 + (lane >> 4);
-        afr[mi] = As[CUR * SLICE + r * 8 + (c ^ (r & 7))];
+        afr[mi] = As[CUR * SLICE + r * 8 + (c ^ ((r >> 1) & 7))];
       }
 #pragma unroll
       for (int nj = 0; nj < NB16; ++nj)
@@ -427,9 +430,12 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
 
   if (wave >= 4) {
     // ---------------- producer: weight ring + decode, two steps ahead ----------------
+    // Thread (row, block): each 16-lane group writes one block of 16
+    // consecutive tile rows, whose 144-byte rows start on 16 different 4-bank
+    // groups, so every 16-byte store instruction covers the 64 banks once.
     const int ptid = tid - 256;
-    const int drow = ptid >> 1;
-    const int dblk = ptid & 1;
+    const int drow = (ptid & 15) + 16 * (ptid >> 5);
+    const int dblk = (ptid >> 4) & 1;
     const int dn = min(n0 + drow, N - 1);
     const uint8_t* dpay = P.payload + size_t(dn) * P.row_bytes;
     const uint16_t* dsc = P.scales + size_t(dn) * P.nb;
@@ -577,7 +583,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     for (int i = 0; i < 8; ++i) {
       const int r = i * 8 + (lane >> 3);
       const int c = lane & 7;
-      As[slot * 512 + r * 8 + (c ^ (r & 7))] = araw[i];
+      As[slot * 512 + r * 8 + (c ^ ((r >> 1) & 7))] = araw[i];
     }
   };
   // fragment sets: [set][mi] activation, [set][nj] weights
@@ -588,7 +594,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     for (int mi = 0; mi < 4; ++mi) {
       const int r = mi * 16 + (lane & 15);
       const int c = kk * 4 + (lane >> 4);
-      af[SET][mi] = As[aslot * 512 + r * 8 + (c ^ (r & 7))];
+      af[SET][mi] = As[aslot * 512 + r * 8 + (c ^ ((r >> 1) & 7))];
     }
 #pragma unroll
     for (int nj = 0; nj < NB16; ++nj)
@@ -612,12 +618,12 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   };
   // slice of step s into slot `slot` by direct copies: instruction i fills
   // slots 64 i .. 64 i + 63 (row 8 i + l / 8, physical chunk l % 8 for lane l),
-  // so lane l fetches logical chunk (l % 8) ^ (row & 7) of its row
+  // so lane l fetches logical chunk (l % 8) ^ ((row >> 1) & 7) of its row
   auto dma_a = [&](int slot, int s) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = i * 8 + (lane >> 3);
-      const int cl = (lane & 7) ^ (r & 7);
+      const int cl = (lane & 7) ^ ((r >> 1) & 7);
       const int m = min(mw + r, M - 1);
       const int k = min(s * GT_BK + cl * 8, K - 8);
       dma16(A + size_t(m) * size_t(K) + size_t(k), as_lds + uint32_t(slot) * 8192u + uint32_t(i) * 1024u);

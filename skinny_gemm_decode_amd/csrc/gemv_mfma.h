@@ -231,6 +231,15 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // A operands of the wave's BPW blocks and the activation scales of the four
 // output rows 4g..4g+3 this lane accumulates (zero for rows >= M).  The wave's
+// LDS row stride (dwords) of the Q8_1 staging: RW = 9 BPW, plus one where
+// rows 4 apart would start on the same bank (RW = 144: 4 x 144 = 9 x 64), so
+// the scales a lane gathers from rows 4 g .. 4 g + 3 and the 16 rows of a
+// fragment read start on different banks.
+template <int BPW>
+constexpr int q8_stage_row() {
+  return (4 * 9 * BPW) % 64 == 0 ? 9 * BPW + 1 : 9 * BPW;
+}
+
 // M x BPW blocks (BPW * 36 contiguous bytes per activation row) are copied
 // with coalesced dword loads into the wave-private LDS area and picked apart
 // there; between() runs once those loads are issued (the first tiles' weight
@@ -242,6 +251,7 @@ __device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk
                                    f32x4 (&da)[BPW], Between between, AfterX after_x) {
   constexpr int RW = BPW * 9;                 // dwords per activation row of the wave's span
   constexpr int NL = (M * RW + 63) / 64;      // dword loads per lane
+  constexpr int RWP = q8_stage_row<BPW>();
   const int g = lane >> 4, c = lane & 15;
   const int mr = (c < M) ? c : c % M;
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(a.x);
@@ -260,18 +270,18 @@ __device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int f = i * 64 + lane;
-    if (f < M * RW) area[f] = v[i];
+    if (f < M * RW) area[(f / RW) * RWP + f % RW] = v[i];
   }
   after_x();
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
-    const uint32_t* blk = area + mr * RW + j * 9;
+    const uint32_t* blk = area + mr * RWP + j * 9;
     aq[j] = uint64_t(blk[1 + g]) | (uint64_t(blk[5 + g]) << 32);
     float d4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * g + i;
-      d4[i] = (m < M) ? h2f(area[(m < M ? m : 0) * RW + j * 9] & 0xFFFFu) : 0.f;
+      d4[i] = (m < M) ? h2f(area[(m < M ? m : 0) * RWP + j * 9] & 0xFFFFu) : 0.f;
     }
     da[j] = f32x4{d4[0], d4[1], d4[2], d4[3]};
   }
@@ -336,8 +346,9 @@ __device__ inline void mf_tile_q8(MfW<NP, BPW>& r, const uint64_t (&aq)[BPW], co
 // staging, reused afterwards for the two reduction buffers.
 template <int M, int WAVES, int BPW, int XT, int NR>
 struct MfLds {
-  // one pass of 8 blocks (hi and lo A entries)
-  static constexpr int WAVE_STAGE = XT * 8 * 4 * M * 16;
+  // one pass of 8 blocks (hi and lo A entries); entries of (M | 1) 16-byte
+  // units, see mf_stage
+  static constexpr int WAVE_STAGE = XT * 8 * 4 * (M | 1) * 16;
   static constexpr int STAGE = WAVES * WAVE_STAGE;
   static constexpr int RED = 2 * WAVES * NR * MF_ROWS * M * 4;
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
@@ -351,12 +362,17 @@ struct MfLds {
 // compiler drains those before any later use of a register load), and leaves
 // the fp16 A operands of the wave's BPW blocks in ah / al.  Passes of 8
 // blocks go through the wave-private LDS area `area`.
-template <int M, int BPW, int XT, class Between, class AfterX>
+template <int M, int BPW, int XT, int MS = (M | 1), class Between, class AfterX>
 __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ah)[BPW],
                                 f16x8 (&al)[BPW], float (&unscale)[4], Between between, AfterX after_x) {
   const int g = lane >> 4, c = lane & 15;
+  // A entry (block, quarter) holds M 16-byte units at a stride of MS units;
+  // an odd stride (M | 1, the default) makes the 32 entries a pass writes
+  // (and the 4 a read takes) start on different bank groups: with an even
+  // stride such as M = 8 (128 bytes, half the 64 banks) they pile onto two.
+  static_assert(MS >= M, "entry stride");
   uint8_t* hi_base = area;
-  uint8_t* lo_base = hi_base + 8 * 4 * M * 16;
+  uint8_t* lo_base = hi_base + 8 * 4 * MS * 16;
   const int mr = (c < M) ? c : c % M;
   f32x4 xv[M][BPW / 8];
 #pragma unroll
@@ -404,7 +420,7 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
       const f32x4 v = xv[m][e] * sc[m];
       const f16x2 h02 = __builtin_convertvector((f32x2{v.x, v.z}), f16x2);
       const f16x2 h13 = __builtin_convertvector((f32x2{v.y, v.w}), f16x2);
-      const size_t off = size_t(((bl * 4 + gq) * M + m) * 16 + 8 * h);
+      const size_t off = size_t(((bl * 4 + gq) * MS + m) * 16 + 8 * h);
       *reinterpret_cast<u32x2*>(hi_base + off) = u32x2{bits(h02), bits(h13)};
       if constexpr (XT == 2) {
         const f32x2 r02 = f32x2{v.x, v.z} - __builtin_convertvector(h02, f32x2);
@@ -415,7 +431,7 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
     }
 #pragma unroll
     for (int jl = 0; jl < 8; ++jl) {
-      const size_t off = size_t(((jl * 4 + g) * M + mr) * 16);
+      const size_t off = size_t(((jl * 4 + g) * MS + mr) * 16);
       ah[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hi_base + off));
       if constexpr (XT == 2)
         al[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lo_base + off));
@@ -510,7 +526,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
     }
   };
   if constexpr (Q8)
-    mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(lds) + size_t(wave) * (M * BPW * 9), blk0, lane, aq, da,
+    mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(lds) + size_t(wave) * (M * q8_stage_row<BPW>()), blk0, lane,
+                        aq, da,
                         first_loads, [] {});
   else
     mf_stage<M, BPW, XT>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al, unscale,
@@ -616,8 +633,13 @@ struct MfDmaGeom {
   static constexpr int NB = 128;                     // blocks per row (K = 4096)
   static constexpr int RB = NB * 16 * NP;            // payload bytes per row
   static constexpr int PRS = RB + 16;                // padded LDS row stride
-  static constexpr int SRS = NB * 2;                 // LDS scale-row stride (4 rows per transfer)
-  static constexpr int SLOT = 16 * PRS + 16 * SRS;   // one tile
+  // Scales: row r's 16 chunks of 16 bytes at LDS chunks 17 r .. 17 r + 15 of
+  // the scale area (one pad chunk per row), so the 16 rows a B-operand group
+  // reads start on 16 different 4-bank groups (a 256-byte stride would put
+  // them all on one bank).  Five 1 KB transfers fill the 272 chunks.
+  static constexpr int SRS = NB * 2 + 16;            // LDS scale-row stride
+  static constexpr int SCH = 5;                      // scale transfers per tile
+  static constexpr int SLOT = 16 * PRS + SCH * 1024; // one tile
   static constexpr int CH = RB / 1024;               // 1 KB transfers per row
   static constexpr int P = 2 * CH + 1;               // transfers per wave per tile (2 rows + 4 scale rows)
 };
@@ -632,9 +654,14 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   static_assert(R == 2 || R == 3, "ring slots");
   using G = MfDmaGeom<FMT>;
   constexpr int NP = G::NP, BPW = 16, WAVES = 8, P = G::P;
+  static_assert(WAVES >= G::SCH, "every scale transfer has a wave");
   constexpr int RR = M < 4 ? M : 4;
   // per-wave activation staging: fp16 A operands, or the raw Q8_1 blocks
-  constexpr int WAVE_STAGE = Q8 ? M * BPW * 36 : MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE;
+  // fp16 staging entries at the odd stride where the staging still fits the
+  // shared slot (every case but two fp16 terms at M = 8 with q8_0 weights)
+  constexpr int MSO = M | 1;
+  constexpr int MSD = (!ALIAS || WAVES * (XT * 8 * 4 * MSO * 16) <= G::SLOT) ? MSO : M;
+  constexpr int WAVE_STAGE = Q8 ? M * q8_stage_row<BPW>() * 4 : XT * 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   __shared__ __attribute__((aligned(16))) uint8_t slot0[G::SLOT];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[G::SLOT];
@@ -677,14 +704,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       for (int ch = 0; ch < G::CH; ++ch)
         dma16_stream(rowp + ch * 1024 + lane * 16, lds_addr(slot) + uint32_t(r * G::PRS + ch * 1024));
     }
-    // Scales of rows 4 (wave % 4) .. +3, all 64 lanes (waves 4..7 repeat the
-    // identical copies of waves 0..3, so every wave issues the same number of
-    // transfers per tile).
+    // Scales: transfer u = wave % 5 fills chunks 64 u .. 64 u + 63 of the
+    // scale area (waves 5..7 repeat the identical copies of waves 0..2, so
+    // every wave issues the same number of transfers per tile).  Chunk
+    // h = 17 r + j holds chunk j of row r's scales; pad chunks (j = 16) and
+    // the chunks past row 15 take a valid duplicate and are never read.
     {
-      const int r = 4 * (wave & 3) + (lane >> 4);
+      const int u = wave % G::SCH;
+      const int h = 64 * u + lane;
+      const int r = h / 17 < 16 ? h / 17 : 15;
+      const int j = h % 17 < 16 ? h % 17 : 15;
       const int64_t n = (rbase + r < sg.N) ? rbase + r : sg.N - 1;
       const uint16_t* srow = sg.w0.scales + size_t(n) * sg.w0.nb;
-      dma16_stream(srow + (lane & 15) * 8, lds_addr(slot) + uint32_t(16 * G::PRS + 4 * (wave & 3) * G::SRS));
+      dma16_stream(srow + j * 8, lds_addr(slot) + uint32_t(16 * G::PRS + u * 1024));
     }
   };
 
@@ -706,7 +738,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da,
                         [] {}, first_dma);
   else
-    mf_stage<M, BPW, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {}, first_dma);
+    mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {},
+                              first_dma);
   if constexpr (ALIAS) {
     // every wave has read its staged operands before the shared slot refills
     asm volatile("" ::: "memory");
@@ -820,7 +853,7 @@ inline GemvEntry gemv_mfma_entry() {
               FMT, M, EPI, MF_ROWS, XT, 2, WAVES, BPW};
   e.lds = MfLds<M, WAVES, BPW, XT, NR>::BYTES;
   if constexpr (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1) {
-    constexpr int q8_stage = WAVES * M * BPW * 36;  // each wave's Q8_1 blocks
+    constexpr int q8_stage = WAVES * M * q8_stage_row<BPW>() * 4;  // each wave's Q8_1 blocks
     if (e.lds < q8_stage) e.lds = q8_stage;
   }
   e.max_nb = WAVES * BPW;
