@@ -7,17 +7,21 @@
 
 namespace skg {
 // Registered before the vector-ALU Q8_1 instances: the defaults where they
-// measure faster on MI355X (K = 4096, N = 14336, cold-cache rotation): q4_0
-// M = 7 / 8 14.1 / 13.8 us against 14.6 / 16.0 us on the vector ALU, q8_0
-// 18.1 / 17.6 (weights through an LDS ring) against 19.1 / 19.7 us.  From M = 6 down the vector kernels win
-// (M = 4: 10.6 against 13.4 us for q4_0).  Other K (not a multiple of 256, or
-// above 4096) fall through to the vector kernels.
+// measure faster on MI355X (K = 4096, N = 14336, cold-cache rotation).  The
+// weights streamed into an LDS ring: q4_0 M = 6 / 7 / 8 12.93 / 12.81 /
+// 12.97 us against 13.44 / 14.06 / 13.52 for the next best (vector kernel at
+// M = 6, register-fed integer MFMA at 7, 8); q8_0 M = 6 17.34 against 17.83
+// (vector), M = 7 / 8 18.08 / 17.55 against 18.45 / 18.12 (register-fed).
+// From M = 5 down the vector kernels win (M = 5: 12.15 against 13.49 us for
+// q4_0).  The ring kernels take K = 4096 only; other K (not a multiple of
+// 256, or above 4096) fall through to the register-fed or vector kernels.
 void register_gemv_mfma_q8_1(std::vector<GemvEntry>& out) {
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 6, 1, 2, true>());
   SKG_MF8(SKG_Q4_0_Q8_1, 7, 16, 8, 1)
   SKG_MF8(SKG_Q4_0_Q8_1, 8, 16, 8, 1)
-  // q8_0 at M = 7, 8: the weights streamed into an LDS ring, 18.08 / 17.55 us
-  // against 18.45 / 18.12 for the register-fed kernel (three A1 B1 B2 A2
-  // cycles; K = 4096 only, other K take the register-fed kernel)
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 7, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 8, 1, 2, true>());
   SKG_MF8(SKG_Q8_0_Q8_1, 7, 16, 8, 1)
@@ -41,9 +45,8 @@ void register_gemv_mfma_q8_1_alt(std::vector<GemvEntry>& out) {
   SKG_MF8(SKG_Q4_0_Q8_1, 8, 8, 16, 2)
   SKG_MF8(SKG_Q8_0_Q8_1, 4, 8, 16, 1)
   SKG_MF8(SKG_Q8_0_Q8_1, 8, 8, 16, 1)
-  // weights streamed into an LDS ring (K = 4096 only): ties the vector
-  // kernel for q8_0 at M = 6; slower for q8_0 at M = 4, 5 (15-16%) and for
-  // q4_0 at M = 6..8 (5-9%), which are not compiled
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 6, 1, 2, true>());
+  // weights streamed into an LDS ring at M = 5: slower than the vector
+  // kernel (q8_0 17.06 against 15.86 us)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 5, 1, 2, true>());
 }
 }  // namespace skg
