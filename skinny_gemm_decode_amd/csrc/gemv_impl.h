@@ -504,6 +504,10 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
 
 __device__ inline float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// Units per activation piece plane in LDS for PP pieces of UC units (see
+// gemv_kernel).
+__host__ __device__ constexpr int gemv_x_plane_stride(int pp, int uc) { return pp > 1 ? uc + 2 : uc; }
+
 // One output segment of a launch: a matrix (two for SwiGLU) and its output
 // (plus the Q8_1 form of the SwiGLU output for SKG_EPI_SWIGLU_Q8_1).
 struct Seg {
@@ -583,6 +587,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
   // K class (kw) stage their chunk into LDS region kw; the host launches such
   // a variant only when every class has the same number of chunks.
   constexpr int XCLS = XLDS ? KW : 1;  // LDS chunk regions
+  // Stride (16-byte units) of an activation piece plane in LDS.  The staging
+  // threads write the PP pieces of a unit with consecutive lanes (so the
+  // global loads stay contiguous); a plane stride of UC + 2 units puts the 16
+  // stores of 16 lanes (8 pieces x 2 units) on 16 different bank groups,
+  // where a stride of UC (a multiple of the 64 banks) put a unit's 8 pieces
+  // on one.  The lanes reading a plane take consecutive units either way.
+  constexpr int XPS = gemv_x_plane_stride(PP, UC);
   extern __shared__ u32x4 xlds[];
   __shared__ float red[KW > 1 ? WAVES : 1][KW > 1 ? RT * M : 1];
   // SwiGLU outputs of the workgroup's rows, gathered for their Q8_1 blocks
@@ -641,7 +652,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     // Q8_1 activation staged whole blocks per thread (nine dwords each)
     constexpr int NQ = (XLDS && F::XQ8) ? (M * UC + ST - 1) / ST : 1;
     uint32_t qstage[NQ][9];
-    u32x4* xreg = xlds + size_t(XCLS > 1 ? kw : 0) * (M * PP * UC);
+    u32x4* xreg = xlds + size_t(XCLS > 1 ? kw : 0) * (M * PP * XPS);
     uint32_t* qreg = reinterpret_cast<uint32_t*>(xlds) + size_t(XCLS > 1 ? kw : 0) * (M * 9 * UC);
     if constexpr (XLDS && F::XQ8) {
       // Cooperative staging of this chunk's Q8_1 activation, all M rows: thread
@@ -722,7 +733,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
           const int p = i % PP;
           const int uu = (i / PP) % UC;
           const int m = i / (PP * UC);
-          xreg[(m * PP + p) * UC + uu] = stage[t];
+          xreg[(m * PP + p) * XPS + uu] = stage[t];
         }
       }
       __syncthreads();
@@ -744,7 +755,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
         } else if constexpr (XLDS) {
           u32x4 pc[PP];
 #pragma unroll
-          for (int p = 0; p < PP; ++p) pc[p] = xreg[(m * PP + p) * UC + j * 64 + lane];
+          for (int p = 0; p < PP; ++p) pc[p] = xreg[(m * PP + p) * XPS + j * 64 + lane];
           x_from_pieces<FMT>(xu, pc);
         } else {
           x_from_raw<FMT>(xu, xr[j][m], uok);
@@ -846,8 +857,9 @@ inline GemvEntry gemv_entry() {
 inline size_t gemv_lds_bytes(int fmt, int M, int J, int xlds, int kw = 1) {
   if (!xlds) return 0;
   const bool q8 = fmt == SKG_Q4_0_Q8_1 || fmt == SKG_Q8_0_Q8_1 || fmt == SKG_Q4_K_Q8_1 || fmt == SKG_Q6_K_Q8_1;
-  const int xb = (fmt == SKG_BF16_BF16) ? 16 : q8 ? 36 : 128;
-  return size_t(M) * size_t(64 * J) * size_t(xb) * size_t(kw);
+  if (q8) return size_t(M) * size_t(64 * J) * 36 * size_t(kw);
+  const int pp = (fmt == SKG_BF16_BF16) ? 1 : 8;  // 16-byte pieces per unit
+  return size_t(M) * size_t(pp) * size_t(gemv_x_plane_stride(pp, 64 * J)) * 16 * size_t(kw);
 }
 
 }  // namespace skg

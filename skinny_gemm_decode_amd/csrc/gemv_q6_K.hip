@@ -6,22 +6,39 @@
 
 namespace skg {
 void register_gemv_q6_K(std::vector<GemvEntry>& out) {
-  // q6_K x fp32, activation in LDS: 4 rows per wave where the kernel keeps two
-  // waves per SIMD (M = 1, 3, 5, 6: M = 6 28.6 us against 34.2 us), 2 rows
-  // where 4 rows would leave one (M = 2, 4, 7, 8: M = 4 24.5 against 36.4 us)
-  SKG_I(SKG_Q6_K_F32, 1, 4, 1, true, 4, SKG_EPI_NONE)
+  // q6_K x fp32, activation in LDS: 2 rows per wave (M = 1: 2 units per
+  // lane, 11.09 us against 11.83-12.20; M = 6 27.29 against 40.19 with 4
+  // rows), 4 rows at M = 3, 5 (M = 5 22.44 against 24.46)
+  SKG_I(SKG_Q6_K_F32, 1, 2, 2, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q6_K_F32, 2, 2, 1, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q6_K_F32, 3, 4, 1, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q6_K_F32, 4, 2, 1, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q6_K_F32, 5, 4, 1, true, 4, SKG_EPI_NONE)
-  SKG_I(SKG_Q6_K_F32, 6, 4, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 6, 2, 1, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q6_K_F32, 7, 2, 1, true, 4, SKG_EPI_NONE)
   SKG_I(SKG_Q6_K_F32, 8, 2, 1, true, 4, SKG_EPI_NONE)
-  SKG_M12(SKG_Q6_K_F32, 4, 2, 4, 1, 2, 2)
-  SKG_M3_8(SKG_Q6_K_F32, 4, 1, true, 2)
+  // SwiGLU: M = 1, 2 from registers, M >= 3 in LDS, 2 output rows per wave
+  SKG_I(SKG_Q6_K_F32, 1, 2, 2, false, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 2, 2, 1, false, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 3, 2, 1, true, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 4, 2, 1, true, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 5, 2, 1, true, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 6, 2, 1, true, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 7, 2, 1, true, 4, SKG_EPI_SWIGLU)
+  SKG_I(SKG_Q6_K_F32, 8, 2, 1, true, 4, SKG_EPI_SWIGLU)
+  // measurement variants
+  SKG_I(SKG_Q6_K_F32, 1, 4, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 1, 2, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 1, 4, 2, false, 4, SKG_EPI_NONE)
   SKG_IKL(SKG_Q6_K_F32, 1, 4, 1, 8, SKG_EPI_NONE, 2)
   SKG_I(SKG_Q6_K_F32, 2, 4, 1, true, 4, SKG_EPI_NONE)
-  SKG_N3_8(SKG_Q6_K_F32, 2, 1, true)
+  SKG_I(SKG_Q6_K_F32, 2, 4, 1, false, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 3, 2, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 4, 4, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 5, 2, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 6, 4, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 7, 4, 1, true, 4, SKG_EPI_NONE)
+  SKG_I(SKG_Q6_K_F32, 8, 4, 1, true, 4, SKG_EPI_NONE)
   // q6_K x Q8_1: M = 1 9.4 us; M >= 3 8 rows per wave, activation in LDS
   // (M = 8: 21.4 us against 23.0-24.5 us)
   SKG_IK(SKG_Q6_K_Q8_1, 1, 4, 1, 4, SKG_EPI_NONE, 2)
