@@ -246,12 +246,12 @@ constexpr int q8_stage_row() {
 // loads go there), after_x() once they have been written to LDS (direct
 // global-to-LDS weight transfers go there: the compiler would drain them
 // before any later use of a register load).
-template <int M, int BPW, class Between, class AfterX>
+template <int M, int BPW, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
 __device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, uint64_t (&aq)[BPW],
                                    f32x4 (&da)[BPW], Between between, AfterX after_x) {
   constexpr int RW = BPW * 9;                 // dwords per activation row of the wave's span
   constexpr int NL = (M * RW + 63) / 64;      // dword loads per lane
-  constexpr int RWP = q8_stage_row<BPW>();
+  static_assert(RWP >= RW, "row stride");
   const int g = lane >> 4, c = lane & 15;
   const int mr = (c < M) ? c : c % M;
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(a.x);
@@ -620,10 +620,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
 // register-fed kernel above touch 16 rows x 64 bytes per wave instruction;
 // here each wave instruction moves 1 KB of one row straight from HBM into LDS
 // (global_load_lds_dwordx4), so every request is whole cache lines and no
-// weight registers are held.  Rows sit 16 bytes apart from a multiple of the
-// LDS bank period, so the B operand reads (16 rows per 16-lane group) are
-// conflict-free.  A ring of R tile slots (16 rows x all of K, plus scales)
-// keeps R - 1 tiles in flight while one is decoded; one barrier per tile.
+// weight registers are held.  A ring of R tile slots (16 rows x all of K,
+// plus scales) keeps R - 1 tiles in flight while one is decoded; one barrier
+// per tile.
+//
+// LDS rows are not padded: a row's 16-byte chunks are permuted within each
+// aligned group of 16 (chunk j of row r sits at position j ^ (r % 16)), so the
+// 16 rows a B-operand group reads at one chunk index land on 16 different
+// 4-bank groups.  Each lane of a transfer fetches the chunk its destination
+// position holds.  (Two workgroups per CU would fit the LDS of the q4_0
+// variants with aliased staging, but not their registers: held to 128 VGPRs
+// they spill, and ran 2.4-3.3x slower.)
 
 constexpr int MF_DMA_TILES = 4;  // most tiles one workgroup processes
 
@@ -631,18 +638,15 @@ template <int FMT>
 struct MfDmaGeom {
   static constexpr int NP = (FMT == SKG_Q8_0_F32 || FMT == SKG_Q8_0_Q8_1) ? 2 : 1;
   static constexpr int NB = 128;                     // blocks per row (K = 4096)
-  static constexpr int RB = NB * 16 * NP;            // payload bytes per row
-  static constexpr int PRS = RB + 16;                // padded LDS row stride
-  // Scales: row r's 16 chunks of 16 bytes at LDS chunks 17 r .. 17 r + 15 of
-  // the scale area (one pad chunk per row), so the 16 rows a B-operand group
-  // reads start on 16 different 4-bank groups (a 256-byte stride would put
-  // them all on one bank).  Five 1 KB transfers fill the 272 chunks.
-  static constexpr int SRS = NB * 2 + 16;            // LDS scale-row stride
-  static constexpr int SCH = 5;                      // scale transfers per tile
-  static constexpr int SLOT = 16 * PRS + SCH * 1024; // one tile
+  static constexpr int RB = NB * 16 * NP;            // payload bytes per row (LDS row stride)
+  static constexpr int SRS = NB * 2;                 // scale bytes per row (16 chunks)
+  static constexpr int SLOT = 16 * RB + 16 * SRS;    // one tile
   static constexpr int CH = RB / 1024;               // 1 KB transfers per row
   static constexpr int P = 2 * CH + 1;               // transfers per wave per tile (2 rows + 4 scale rows)
 };
+
+// LDS position of chunk j of row r (16-byte chunks, see above).
+__device__ inline int mf_swz(int j, int r) { return j ^ (r & 15); }
 
 // R: ring slots; ALIAS: the activation staging area shares the last slot
 // (its first load is issued after staging).
@@ -654,20 +658,23 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   static_assert(R == 2 || R == 3, "ring slots");
   using G = MfDmaGeom<FMT>;
   constexpr int NP = G::NP, BPW = 16, WAVES = 8, P = G::P;
-  static_assert(WAVES >= G::SCH, "every scale transfer has a wave");
   constexpr int RR = M < 4 ? M : 4;
-  // per-wave activation staging: fp16 A operands, or the raw Q8_1 blocks
-  // fp16 staging entries at the odd stride where the staging still fits the
-  // shared slot (every case but two fp16 terms at M = 8 with q8_0 weights)
+  // per-wave activation staging: fp16 A operands, or the raw Q8_1 blocks;
+  // the bank-spreading strides where the staging still fits the shared slot
   constexpr int MSO = M | 1;
   constexpr int MSD = (!ALIAS || WAVES * (XT * 8 * 4 * MSO * 16) <= G::SLOT) ? MSO : M;
-  constexpr int WAVE_STAGE = Q8 ? M * q8_stage_row<BPW>() * 4 : XT * 8 * 4 * MSD * 16;
+  constexpr int QRP = (!ALIAS || WAVES * M * q8_stage_row<BPW>() * 4 <= G::SLOT) ? q8_stage_row<BPW>() : 9 * BPW;
+  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : XT * 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
-  __shared__ __attribute__((aligned(16))) uint8_t slot0[G::SLOT];
-  __shared__ __attribute__((aligned(16))) uint8_t slot1[G::SLOT];
-  __shared__ __attribute__((aligned(16))) uint8_t slot2[R == 3 ? G::SLOT : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t stage_own[ALIAS ? 16 : WAVES * WAVE_STAGE];
-  __shared__ __attribute__((aligned(16))) float red[2 * WAVES * MF_ROWS * M];
+  // one LDS array, carved: R slots, the own staging area, the partial sums
+  constexpr int RED_BYTES = 2 * WAVES * MF_ROWS * M * 4;
+  constexpr int STAGE_BYTES = ALIAS ? 0 : WAVES * WAVE_STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[R * G::SLOT + STAGE_BYTES + RED_BYTES];
+  uint8_t* const slot0 = lds_all;
+  uint8_t* const slot1 = lds_all + G::SLOT;
+  uint8_t* const slot2 = lds_all + (R == 3 ? 2 * G::SLOT : 0);
+  uint8_t* const stage_own = lds_all + R * G::SLOT;
+  float* const red = reinterpret_cast<float*>(lds_all + R * G::SLOT + STAGE_BYTES);
 
   uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
   asm volatile("" : "+s"(mlo));
@@ -702,21 +709,17 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       const uint8_t* rowp = sg.w0.payload + size_t(n) * sg.w0.row_bytes;
 #pragma unroll
       for (int ch = 0; ch < G::CH; ++ch)
-        dma16_stream(rowp + ch * 1024 + lane * 16, lds_addr(slot) + uint32_t(r * G::PRS + ch * 1024));
+        dma16_stream(rowp + mf_swz(ch * 64 + lane, r) * 16, lds_addr(slot) + uint32_t(r * G::RB + ch * 1024));
     }
-    // Scales: transfer u = wave % 5 fills chunks 64 u .. 64 u + 63 of the
-    // scale area (waves 5..7 repeat the identical copies of waves 0..2, so
-    // every wave issues the same number of transfers per tile).  Chunk
-    // h = 17 r + j holds chunk j of row r's scales; pad chunks (j = 16) and
-    // the chunks past row 15 take a valid duplicate and are never read.
+    // Scales of rows 4 (wave % 4) .. +3, all 64 lanes (waves 4..7 repeat the
+    // identical copies of waves 0..3, so every wave issues the same number of
+    // transfers per tile); lane l fills position l % 16 of row 4 (wave % 4) +
+    // l / 16.
     {
-      const int u = wave % G::SCH;
-      const int h = 64 * u + lane;
-      const int r = h / 17 < 16 ? h / 17 : 15;
-      const int j = h % 17 < 16 ? h % 17 : 15;
+      const int r = 4 * (wave & 3) + (lane >> 4);
       const int64_t n = (rbase + r < sg.N) ? rbase + r : sg.N - 1;
       const uint16_t* srow = sg.w0.scales + size_t(n) * sg.w0.nb;
-      dma16_stream(srow + j * 8, lds_addr(slot) + uint32_t(16 * G::PRS + u * 1024));
+      dma16_stream(srow + mf_swz(lane & 15, r) * 8, lds_addr(slot) + uint32_t(16 * G::RB + 4 * (wave & 3) * G::SRS));
     }
   };
 
@@ -735,7 +738,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if constexpr (R == 3 && !ALIAS) dma_tile(slot2, clamp(2));
   };
   if constexpr (Q8)
-    mf_stage_q8<M, BPW>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da,
+    mf_stage_q8<M, BPW, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq,
+                             da,
                         [] {}, first_dma);
   else
     mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {},
@@ -781,11 +785,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       for (int q = 0; q < BPW / 4; ++q)
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-          w.u[q][p] =
-              *reinterpret_cast<const u32x4*>(slot + c * G::PRS + (p * G::NB + int(blk0) + 4 * q + g) * 16);
+          w.u[q][p] = *reinterpret_cast<const u32x4*>(slot + c * G::RB + mf_swz(p * G::NB + int(blk0) + 4 * q + g, c) * 16);
 #pragma unroll
       for (int k = 0; k < BPW / 8; ++k)
-        w.sc[k] = *reinterpret_cast<const u32x4*>(slot + 16 * G::PRS + c * G::SRS + int(blk0) * 2 + k * 16);
+        w.sc[k] = *reinterpret_cast<const u32x4*>(slot + 16 * G::RB + c * G::SRS + mf_swz(int(blk0) / 8 + k, c) * 16);
       const MfNext none{};
       if constexpr (Q8)
         mf_tile_q8<NP, BPW, RR, false>(w, aq, da, acc, none, blk0, g);
