@@ -640,7 +640,9 @@ struct MfDmaGeom {
   static constexpr int NB = 128;                     // blocks per row (K = 4096)
   static constexpr int RB = NB * 16 * NP;            // payload bytes per row (LDS row stride)
   static constexpr int SRS = NB * 2;                 // scale bytes per row (16 chunks)
-  static constexpr int SLOT = 16 * RB + 16 * SRS;    // one tile
+  // one tile, plus 256 bytes so that the aliased Q8_1 staging of 8 rows keeps
+  // its bank-spreading row stride (8 waves x 8 rows x 145 dwords)
+  static constexpr int SLOT = 16 * RB + 16 * SRS + 256;
   static constexpr int CH = RB / 1024;               // 1 KB transfers per row
   static constexpr int P = 2 * CH + 1;               // transfers per wave per tile (2 rows + 4 scale rows)
 };

@@ -100,9 +100,9 @@ def traffic_md(fetch_dir, write_dir):
         "Two counter runs of the same command, one counter each (run from the repository root on one MI355X):",
         "",
         f"    rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python -u bench.py --arms none "
-        "--no-cpu-baseline --steps 200 --warmup 200 --calibrate-copy",
+        "--no-cpu-baseline --steps 10 --warmup 0 --calibrate-copy",
         f"    rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python -u bench.py --arms none "
-        "--no-cpu-baseline --steps 200 --warmup 200 --calibrate-copy",
+        "--no-cpu-baseline --steps 10 --warmup 0 --calibrate-copy",
         f"    python -m skinny_gemm_decode_amd.rocprof_summary traffic-md {fetch_dir} {write_dir}",
         "",
         "Per-dispatch means (KiB):",
