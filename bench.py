@@ -29,10 +29,13 @@ writing Q8_1, and with the layer's RMSNorm as its own launch or writing Q8_1
 itself), the fused RMSNorm -> Q8_1 launch alone, the q8_0 M=1 K=256 N=512
 launch-bound case, the M=512 MFMA prefill tile (q4_0, q8_0, q4_K and q6_K
 weights), and the K-quant (q4_K, q6_K super-block) weights x fp32 and x Q8_1
-at the same decode shape.  The CPU oracle is timed on a bounded sample of the
-headline workload on this host's cores.
+at the same decode shape.  The `sweep` arm (not part of `all`) times the
+default of each (format, M) named by --sweep / --ms against every compiled
+alternative, each gated against the oracle first.  The CPU oracle is timed on
+a bounded sample of the headline workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 5] [--arms all|none|a,b] [--ms 1,2,4,8]
+                      [--sweep q4_0_f32,...]
 Prints one JSON line on stdout; per-arm details go to the --details file when
 one is given.
 """
@@ -791,6 +794,33 @@ def cpu_baseline(si, x_host, budget_s=12.0):
 
 # --------------------------------------------------------------------------
 
+def takes_k4096(v, nb=128):
+    """Whether a compiled GEMV variant handles K = 4096 (nb = 128 blocks):
+    the library's own shape rules, restated for choosing what to time."""
+    if v["x_lds"] == 3:
+        return v["waves"] * v["kw"] == nb
+    if v["x_lds"] == 2:
+        return nb % v["kw"] == 0 and nb <= v["waves"] * v["kw"]
+    if v["x_lds"] == 4:
+        return nb % 16 == 0
+    if v["x_lds"] == 1 and v["kw"] > 1:
+        return ((nb + 64 * v["j"] - 1) // (64 * v["j"])) % v["kw"] == 0
+    return True
+
+
+def sweep_variants(skg, fmt, M):
+    """Every compiled plain-output variant of (fmt, M) that takes K = 4096,
+    the default excluded (it is timed as the arm itself)."""
+    dv = skg.gemv_default_variant(fmt, M, skg.EPI_NONE, 4096)
+    seen, out = {tuple(dv[k] for k in skg.VARIANT_KEYS)}, []
+    for v in skg.gemv_variants():
+        key = tuple(v[k] for k in skg.VARIANT_KEYS)
+        if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and takes_k4096(v) and key not in seen:
+            seen.add(key)
+            out.append(v)
+    return out
+
+
 def two_term_variants(skg, fmt, M, K=4096):
     """Compiled matrix-core variants of (fmt, M) that carry the fp32
     activation as two fp16 terms (~22 significant bits) and take K, fastest
@@ -809,8 +839,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5,
                     help="untimed warm-up steps of the headline (topped up to at least 1 s)")
     ap.add_argument("--arms", default="all", help="all, none, or a comma list of: floor,ceiling,q8_0,q4_0,q8_1,"
-                                                  "multi_m,layer,small,norm,prefill,kquant")
-    ap.add_argument("--ms", default="1,2,4,8", help="activation rows M of the multi_m arms (comma list, 1..8)")
+                                                  "multi_m,layer,small,norm,prefill,kquant,sweep (not in all)")
+    ap.add_argument("--ms", default="1,2,4,8", help="activation rows M of the multi_m and sweep arms (comma list, 1..8)")
+    ap.add_argument("--sweep", default="q4_0_f32",
+                    help="formats of the sweep arm (comma list of names: bf16_bf16, q8_0_f32, q4_0_f32, q4_0_q8_1, "
+                         "q8_0_q8_1, q4_K_f32, q6_K_f32, q4_K_q8_1, q6_K_q8_1)")
     ap.add_argument("--arm-warm-s", type=float, default=1.0, help="warm-up seconds of every further arm")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (its pre-timing parity gates still run)")
@@ -840,8 +873,9 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     timer = Timer(torch)
-    all_arms = {"floor", "ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill", "kquant"}
-    arms = set() if args.arms == "none" else (all_arms if args.arms == "all" else set(args.arms.split(",")))
+    all_arms = {"floor", "ceiling", "q8_0", "q4_0", "q8_1", "multi_m", "layer", "small", "norm", "prefill", "kquant",
+                "sweep"}
+    arms = set() if args.arms == "none" else (all_arms - {"sweep"} if args.arms == "all" else set(args.arms.split(",")))
     unknown = arms - all_arms
     if unknown:
         print(f"unknown arms {sorted(unknown)}", file=sys.stderr)
@@ -895,6 +929,20 @@ def main():
             vs = "".join(f"  two-term {v['us_per_launch']:.2f} us" for v in r["variants"])
             log(f"[{r['name']}] {r['us_per_launch']:.2f} us  {r['gbs']:.0f} GB/s  ({r['activation']})  graph "
                 f"{r['graph']['us_per_launch']:.2f} us  read-ceiling {r['ceiling_us']:.2f} us{vs}")
+    if "sweep" in arms:
+        # the default of each (format, M) against every compiled alternative,
+        # each gated against the oracle before it is timed: how the defaults
+        # were chosen, reproducible from this file
+        for name in args.sweep.split(","):
+            fmt = {v: k for k, v in skg.FMT_NAMES.items()}[name]
+            for M in (int(v) for v in args.ms.split(",")):
+                xh = si.activations_f32(si.rng_for(0, 4, M), M, 4096)
+                r = bench_gemv_arm(skg, si, torch, timer, f"sweep_{name}_m{M}_k4096_n14336", skg.WEIGHT_KIND[fmt],
+                                   fmt, M, 14336, 4096, xh, warm_s=warm, variants=sweep_variants(skg, fmt, M))
+                details["arms"][r["name"]] = r
+                log(f"[{r['name']}] default {r['variant']}: {r['us_per_launch']:.2f} us")
+                for v in sorted(r["variants"], key=lambda v: v["us_per_launch"]):
+                    log(f"    {v['variant']}: {v['us_per_launch']:.2f} us")
     if "small" in arms:
         xh = si.activations_f32(si.rng_for(0, 1, 0), 1, 256)
         r = bench_gemv_arm(skg, si, torch, timer, "q8_0_f32_m1_k256_n512", "q8_0", skg.Q8_0_F32, 1, 512, 256, xh,

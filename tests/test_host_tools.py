@@ -199,3 +199,19 @@ def test_abba_order_and_ratio():
     # cycle 1: A legs 11, 14 -> 12.5; B legs 14, 15 -> 14.5 (drift cancels in the means' centres)
     assert r["cycles"][0]["b_over_a"] == pytest.approx(14.5 / 12.5)
     assert r["b_over_a"] == pytest.approx((14.5 / 12.5 + 18.5 / 16.5) / 2)
+
+
+def test_sweep_takes_k4096_restates_the_shape_rules():
+    """The bench's sweep arm times only variants that accept K = 4096: the
+    LDS ring needs waves x kw = 128 blocks, the register-fed matrix-core
+    kernel kw | 128 <= waves x kw, the LDS-staged K split an equal number of
+    chunks per K class."""
+    import bench
+    v = dict(fmt=2, M=8, epi=0, ro=16, j=1, x_lds=3, waves=8, kw=16, depth=2)
+    assert bench.takes_k4096(v)
+    assert not bench.takes_k4096(dict(v, kw=8))
+    assert bench.takes_k4096(dict(v, x_lds=2, waves=16, kw=8))
+    assert not bench.takes_k4096(dict(v, x_lds=2, waves=4, kw=8))
+    assert bench.takes_k4096(dict(v, x_lds=1, j=1, kw=2, ro=4, waves=4))      # 2 chunks of 64 units
+    assert not bench.takes_k4096(dict(v, x_lds=1, j=2, kw=2, ro=4, waves=4))  # 1 chunk of 128
+    assert bench.takes_k4096(dict(v, x_lds=0, j=2, kw=1, ro=4, waves=4))
