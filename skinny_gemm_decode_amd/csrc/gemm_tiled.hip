@@ -642,17 +642,56 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   }
   lds_barrier();  // weight buffers 0 and 1 decoded
   read_frags(integral_constant<int, 0>{}, 0, 0, 0);
+  // One fragment read of set SET, in the order the next half-step's MFMAs
+  // consume them: r = 0 -> weights nj 0, r = 1..4 -> activation mi 0..3,
+  // r >= 5 -> weights nj r-4.
+  auto read1 = [&](auto set_c, auto r_c, int aslot, int bbuf, int kk) {
+    constexpr int SET = decltype(set_c)::value;
+    constexpr int R = decltype(r_c)::value;
+    if constexpr (R >= 1 && R <= 4) {
+      const int r = (R - 1) * 16 + (lane & 15);
+      const int c = kk * 4 + (lane >> 4);
+      af[SET][R - 1] = As[aslot * 512 + r * 8 + (c ^ ((r >> 1) & 7))];
+    } else {
+      constexpr int NJ = R == 0 ? 0 : R - 4;
+      bf[SET][NJ] = *reinterpret_cast<const u32x4*>(&Bs[bbuf][(NJ * 16 + (lane & 15)) * GT_LDS_ROW + kk * 32 + (lane >> 4) * 8]);
+    }
+  };
+  // The MFMAs of set USE (nj-major) with the 4 + NB16 fragment reads of the
+  // other set spread one per two MFMAs, pinned in that order (the scheduler
+  // otherwise gathers the reads next to their uses and the LDS latency shows
+  // between MFMA groups).
+  auto half = [&](auto use_c, int aslot, int bbuf, int kk) {
+    constexpr int USE = decltype(use_c)::value;
+    constexpr int NR = 4 + NB16;
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (([&] {
+         constexpr int nj = J / 4, mi = J % 4;
+         acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[USE][mi]),
+                                                               __builtin_bit_cast(bf16x8, bf[USE][nj]), acc[mi][nj], 0,
+                                                               0, 0);
+         if constexpr (J % 2 == 1 && J / 2 < NR)
+           read1(integral_constant<int, 1 - USE>{}, integral_constant<int, J / 2>{}, aslot, bbuf, kk);
+         __builtin_amdgcn_sched_barrier(0);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, 4 * NB16>{});
+  };
   auto dstep = [&](auto ca_c, auto cb_c, int s) {
     constexpr int CA = decltype(ca_c)::value;  // activation slot of step s (mod 3)
     constexpr int CB = decltype(cb_c)::value;  // weight buffer of step s
     dma_a((CA + 2) % 3, s + 2);  // that slot was last read during step s-1
-    read_frags(integral_constant<int, 1>{}, CA, CB, 1);
-    mfmas(integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    half(integral_constant<int, 0>{}, CA, CB, 1);
     wait_vmcnt<8>();  // slice s+1 (requested one step ago) has landed
     asm volatile("" ::: "memory");
-    read_frags(integral_constant<int, 0>{}, (CA + 1) % 3, (CB + 1) % 3, 0);
-    mfmas(integral_constant<int, 1>{});
-    lds_barrier();
+    half(integral_constant<int, 1>{}, (CA + 1) % 3, (CB + 1) % 3, 0);
+    // No LDS wait here: the reads still in flight are those of step s+1
+    // (weight buffer (s+1) % 3, written before the previous barrier; slot
+    // (CA+1) % 3), which nothing overwrites before the next barrier; every read
+    // of buffer s % 3 fed an MFMA of this step, so has completed before the
+    // producers overwrite it in step s+1.
+    asm volatile("s_barrier" ::: "memory");
   };
   auto cstep = [&](auto ca_c, auto cb_c, int s) {
     constexpr int CA = decltype(ca_c)::value;  // activation slot of step s
@@ -698,7 +737,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
 // rows; 2: producer/consumer waves, 8 consumer waves of 32 rows; 3: pipelined
 // producer/consumer waves (triple-buffered weight tile); 4: as 3 with the
 // activation slices copied straight into LDS
-// measured on MI355X at M=512, K=4096, N=14336: 80.8 / 71.3 / 71.4 / 67.6 / 64.8 us
+// measured on MI355X at M=512, K=4096, N=14336: 80.8 / 71.3 / 71.4 / 67.6 / 64.2-64.8 us
 extern const int kGemmDefaultVariant = 4;
 std::atomic<int> g_gemm_variant{kGemmDefaultVariant};
 
