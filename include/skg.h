@@ -331,8 +331,8 @@ skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream);
  *   `depth` LDS slots; no workgroup barrier until the last tile); it takes K
  *   with (K / 32) % 16 == 0 and K / 32 <= 128.
  *   depth: weight tiles in flight (1 for the vector kernels; the prefetch
- *   depth of x_lds = 2, 1 or 2; the ring slots of x_lds = 3, 2 or 3); 0
- *   matches any depth.
+ *   depth of x_lds = 2, 1 or 2; the ring slots of x_lds = 3, 2 or 3, or 4
+ *   for q4_0 weights); 0 matches any depth.
  * skg_gemv_variants: writes up to max_entries records of SKG_VARIANT_FIELDS
  *   ints {fmt, M, epi, ro, j, x_lds, waves, kw, depth} to out (host) and
  *   returns the number of compiled variants.  For each (fmt, M, epi) and K

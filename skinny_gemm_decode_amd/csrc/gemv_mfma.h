@@ -622,7 +622,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
 // (global_load_lds_dwordx4), so every request is whole cache lines and no
 // weight registers are held.  A ring of R tile slots (16 rows x all of K,
 // plus scales) keeps R - 1 tiles in flight while one is decoded; one barrier
-// per tile.
+// per tile.  With R = 4 (q4_0 only: four 37 KB slots fit the 160 KB) every
+// tile a workgroup owns is requested before the first is decoded, so no
+// transfer waits for a slot to drain.
 //
 // LDS rows are not padded: a row's 16-byte chunks are permuted within each
 // aligned group of 16 (chunk j of row r sits at position j ^ (r % 16)), so the
@@ -657,7 +659,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
   static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
   static_assert(!Q8 || XT == 1, "Q8_1 activations: one integer term");
-  static_assert(R == 2 || R == 3, "ring slots");
+  static_assert(R >= 2 && R <= MF_DMA_TILES, "ring slots");
+  static_assert(R * MfDmaGeom<FMT>::SLOT <= 160 * 1024, "ring exceeds the LDS");
   using G = MfDmaGeom<FMT>;
   constexpr int NP = G::NP, BPW = 16, WAVES = 8, P = G::P;
   constexpr int RR = M < 4 ? M : 4;
@@ -674,7 +677,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[R * G::SLOT + STAGE_BYTES + RED_BYTES];
   uint8_t* const slot0 = lds_all;
   uint8_t* const slot1 = lds_all + G::SLOT;
-  uint8_t* const slot2 = lds_all + (R == 3 ? 2 * G::SLOT : 0);
+  uint8_t* const slot2 = lds_all + (R >= 3 ? 2 * G::SLOT : 0);
+  uint8_t* const slot3 = lds_all + (R == 4 ? 3 * G::SLOT : 0);
   uint8_t* const stage_own = lds_all + R * G::SLOT;
   float* const red = reinterpret_cast<float*>(lds_all + R * G::SLOT + STAGE_BYTES);
 
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     }
   };
 
-  uint8_t* stage_area = ALIAS ? (R == 3 ? slot2 : slot1) : stage_own;
+  uint8_t* stage_area = ALIAS ? (R == 4 ? slot3 : R == 3 ? slot2 : slot1) : stage_own;
   f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
   uint64_t aq[Q8 ? BPW : 1];
   f32x4 da[Q8 ? BPW : 1];
@@ -737,7 +741,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   auto first_dma = [&] {
     dma_tile(slot0, 0);
     if constexpr (!(R == 2 && ALIAS)) dma_tile(slot1, clamp(1));
-    if constexpr (R == 3 && !ALIAS) dma_tile(slot2, clamp(2));
+    if constexpr ((R == 3 && !ALIAS) || R == 4) dma_tile(slot2, clamp(2));
+    if constexpr (R == 4 && !ALIAS) dma_tile(slot3, clamp(3));
   };
   if constexpr (Q8)
     mf_stage_q8<M, BPW, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq,
@@ -754,6 +759,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     asm volatile("" ::: "memory");
     if constexpr (R == 2) dma_tile(slot1, clamp(1));
     if constexpr (R == 3) dma_tile(slot2, clamp(2));
+    if constexpr (R == 4) dma_tile(slot3, clamp(3));
   }
 
   // Waits until this wave's transfers of tile i have landed: tiles
@@ -762,7 +768,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   auto wait_tile = [&](int i, int issued) {
     const int last = (issued > R ? (issued < nmine ? issued : nmine) : R) - 1;
     const int after = last - i;
-    if (after >= 2)
+    if (after >= 3)
+      wait_vmcnt<3 * P>();
+    else if (after == 2)
       wait_vmcnt<2 * P>();
     else if (after == 1)
       wait_vmcnt<P>();
@@ -826,7 +834,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   static_assert(MF_DMA_TILES == 4, "unrolled for four tiles");
   run(slot0, 0);
   if (1 < nmine) run(slot1, 1);
-  if constexpr (R == 3) {
+  if constexpr (R == 4) {
+    if (2 < nmine) run(slot2, 2);
+    if (3 < nmine) run(slot3, 3);
+  } else if constexpr (R == 3) {
     if (2 < nmine) run(slot2, 2);
     if (3 < nmine) run(slot0, 3);
   } else {

@@ -55,6 +55,13 @@ void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 2, 2, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 1, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 1, 3, false>());
+  // four slots, every tile of a workgroup in flight from the start: slower
+  // at every M (M = 4 / 6 / 7 / 8: 12.34 / 12.94 / 13.15 / 13.02 us against
+  // 11.71 / 12.38 / 11.77 / 11.75 for the defaults)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 4, 1, 4, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 6, 1, 4, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 1, 4, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 1, 4, true>());
   SKG_MF(1, 2, 1)
   SKG_MF(1, 1, 2)
   SKG_MF(8, 2, 1)

@@ -48,5 +48,11 @@ void register_gemv_mfma_q8_1_alt(std::vector<GemvEntry>& out) {
   // weights streamed into an LDS ring at M = 5: slower than the vector
   // kernel (q8_0 17.06 against 15.86 us)
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 5, 1, 2, true>());
+  // q4_0 with four slots, every tile of a workgroup in flight from the
+  // start: slower (M = 6 / 7 / 8: 14.90 / 14.75 / 14.87 us against 12.80 /
+  // 12.92 / 12.73 for the two-slot defaults)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 4, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 4, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 4, true>());
 }
 }  // namespace skg
