@@ -238,6 +238,22 @@ __device__ inline void dma16(const void* src, uint32_t dst) {
                "v"(src)
                : "memory", "m0");
 }
+// Forces a lambda's call operator inline (kernels built from many lambdas
+// otherwise get some outlined as calls with stack traffic).
+#define SKG_INL __attribute__((always_inline))
+
+// The same copy addressed as a wave-uniform base (scalar register pair) plus
+// a 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ inline void dma16_sv(const void* base, uint32_t off, uint32_t dst) {
+  // readfirstlane returns a signed int: widen through uint32_t, or a low
+  // word >= 2^31 would sign-extend into the high word
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t sb = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)))) |
+                      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)))) << 32);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(dst)),
+               "v"(off), "s"(sb)
+               : "memory", "m0");
+}
 // The same copy with the non-temporal hint, for data read exactly once per
 // launch (weights): it streams past the caches that hold what is re-read
 // (measured on the LDS-ring decode kernels: 12.85 -> 12.48 us for q4_0 at

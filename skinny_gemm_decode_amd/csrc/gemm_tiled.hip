@@ -32,6 +32,7 @@ namespace skg {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GT_BM = 256;
 constexpr int GT_BK = 64;
@@ -417,7 +418,8 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   __shared__ __attribute__((aligned(16))) uint8_t As_raw[4 * ASLOTS * 64 * 8 * 16];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform (scalar registers): the copy bases below derive from it
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int mtiles = (M + GT_BM - 1) / GT_BM;
   const int m0 = (blockIdx.x % mtiles) * GT_BM;
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     u32x4 wraw[PW][NPL];
     uint32_t wsc[PW];
     bool wok[PW];
-    auto load_w = [&](auto slot_c, int s) {
+    auto load_w = [&](auto slot_c, int s) SKG_INL {
       constexpr int SL = decltype(slot_c)::value;
       const int kb = s * 2 + dblk;
       const int kc = min(kb, nbk - 1);
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     };
     // o[j] = bf16 pair (element 2j, element 2j+1) of the block, each
     // bf16_rne(d * code) with the product exact in fp32 (fma: one rounding).
-    auto store_w = [&](auto slot_c, auto buf_c) {
+    auto store_w = [&](auto slot_c, auto buf_c) SKG_INL {
       constexpr int SL = decltype(slot_c)::value;
       constexpr int BUF = decltype(buf_c)::value;
       uint32_t o[16];
@@ -504,18 +506,35 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
           o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(cb), ahi, nhi), fmaf(cvt_ubyte<3>(cb), ahi, nhi));
         }
       } else if constexpr (WK == WK_Q4_0) {
+        // w = d (c - 8); element i < 16 is the low nibble of byte i, i + 16
+        // its high nibble.  Each nibble pair becomes two exact fp16 values by
+        // one mask-and-or: 1024 + c (low nibbles) or 1024 + 16 c (high
+        // nibbles, still in place), and one mixed-precision fma per element
+        // gives the exact fp32 product: (1024 + c) d - 1032 d and
+        // (1024 + 16 c) (d / 16) - 72 d, where 1032 d, 72 d and d / 16 are
+        // exact in fp32 (d has 11 significant bits).
         const float d = wok[SL] ? h2f(wsc[SL]) : 0.0f;
-        // w = d (c - 8); element i < 16 is the low nibble of byte i, i + 16 its high nibble
-        const float nd8 = -8.0f * d;
+        const float d16 = d * 0.0625f;
+        const float blo = -1032.0f * d, bhi = -72.0f * d;
         const uint32_t pw[4] = {wraw[SL][0].x, wraw[SL][0].y, wraw[SL][0].z, wraw[SL][0].w};
+        // masks and the exponent pattern as register operands, so each
+        // mask-and-or is one v_and_or_b32 (it takes no two literals)
+        uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+        asm volatile("" : "+s"(mlo));
+        asm volatile("" : "+s"(mhi));
+        asm volatile("" : "+v"(magic));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t lo = pw[k] & 0x0F0F0F0Fu;
-          const uint32_t hi = (pw[k] >> 4) & 0x0F0F0F0Fu;
-          o[2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(lo), d, nd8), fmaf(cvt_ubyte<1>(lo), d, nd8));
-          o[2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(lo), d, nd8), fmaf(cvt_ubyte<3>(lo), d, nd8));
-          o[8 + 2 * k + 0] = pack_bf16x2(fmaf(cvt_ubyte<0>(hi), d, nd8), fmaf(cvt_ubyte<1>(hi), d, nd8));
-          o[8 + 2 * k + 1] = pack_bf16x2(fmaf(cvt_ubyte<2>(hi), d, nd8), fmaf(cvt_ubyte<3>(hi), d, nd8));
+          const uint32_t v = pw[k], v8 = pw[k] >> 8;
+          // elements 4k, 4k+2 | 4k+1, 4k+3 | 16+4k, 16+4k+2 | 16+4k+1, 16+4k+3
+          const h16x2 l02 = __builtin_bit_cast(h16x2, (v & mlo) | magic);
+          const h16x2 l13 = __builtin_bit_cast(h16x2, (v8 & mlo) | magic);
+          const h16x2 h02 = __builtin_bit_cast(h16x2, (v & mhi) | magic);
+          const h16x2 h13 = __builtin_bit_cast(h16x2, (v8 & mhi) | magic);
+          o[2 * k + 0] = pack_bf16x2(fmaf(float(l02[0]), d, blo), fmaf(float(l13[0]), d, blo));
+          o[2 * k + 1] = pack_bf16x2(fmaf(float(l02[1]), d, blo), fmaf(float(l13[1]), d, blo));
+          o[8 + 2 * k + 0] = pack_bf16x2(fmaf(float(h02[0]), d16, bhi), fmaf(float(h13[0]), d16, bhi));
+          o[8 + 2 * k + 1] = pack_bf16x2(fmaf(float(h02[1]), d16, bhi), fmaf(float(h13[1]), d16, bhi));
         }
       } else {
         // w = d q; q + 128 is the unsigned byte of q ^ 0x80, so w = d (u - 128)
@@ -537,7 +556,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
       for (int q = 0; q < 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
     };
     using std::integral_constant;
-    [&]<int... I>(std::integer_sequence<int, I...>) {
+    [&]<int... I>(std::integer_sequence<int, I...>) SKG_INL {
       (load_w(integral_constant<int, I>{}, I), ...);
     }(std::make_integer_sequence<int, PW>{});
     store_w(integral_constant<int, 0>{}, integral_constant<int, 0>{});
@@ -545,13 +564,13 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     store_w(integral_constant<int, 1 % PW>{}, integral_constant<int, 1>{});
     load_w(integral_constant<int, 1 % PW>{}, PW + 1);
     lds_barrier();
-    auto pstep = [&](auto slot_c, auto buf_c, int s) {
+    auto pstep = [&](auto slot_c, auto buf_c, int s) SKG_INL {
       store_w(slot_c, buf_c);
       load_w(slot_c, s + 2 + PW);
       lds_barrier();
     };
     for (int s0 = 0; s0 < steps; s0 += U) {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
+      [&]<int... I>(std::integer_sequence<int, I...>) SKG_INL {
         ((s0 + I < steps ? pstep(integral_constant<int, (I + 2) % PW>{}, integral_constant<int, (I + 2) % 3>{},
                                  s0 + I)
                          : void()),
@@ -569,7 +588,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
       __builtin_amdgcn_readfirstlane(lds_addr(As_raw) + uint32_t(wave) * (ASLOTS * 64 * 8 * 16));
   const int mw = m0 + wave * 64;
   u32x4 araw[8];
-  auto load_a = [&](int s) {
+  auto load_a = [&](int s) SKG_INL {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = i * 8 + (lane >> 3);
@@ -578,7 +597,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
       araw[i] = ld_u32x4(A + size_t(m) * size_t(K) + size_t(k));
     }
   };
-  auto park_a = [&](int slot) {
+  auto park_a = [&](int slot) SKG_INL {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = i * 8 + (lane >> 3);
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   };
   // fragment sets: [set][mi] activation, [set][nj] weights
   u32x4 af[2][4], bf[2][NB16];
-  auto read_frags = [&](auto set_c, int aslot, int bbuf, int kk) {
+  auto read_frags = [&](auto set_c, int aslot, int bbuf, int kk) SKG_INL {
     constexpr int SET = decltype(set_c)::value;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -605,7 +624,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int nj = 0; nj < NB16; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mfmas = [&](auto set_c) {
+  auto mfmas = [&](auto set_c) SKG_INL {
     constexpr int SET = decltype(set_c)::value;
 #pragma unroll
     for (int nj = 0; nj < NB16; ++nj) {
@@ -619,7 +638,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   // slice of step s into slot `slot` by direct copies: instruction i fills
   // slots 64 i .. 64 i + 63 (row 8 i + l / 8, physical chunk l % 8 for lane l),
   // so lane l fetches logical chunk (l % 8) ^ ((row >> 1) & 7) of its row
-  auto dma_a = [&](int slot, int s) {
+  auto dma_a = [&](int slot, int s) SKG_INL {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = i * 8 + (lane >> 3);
@@ -628,6 +647,27 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
       const int k = min(s * GT_BK + cl * 8, K - 8);
       dma16(A + size_t(m) * size_t(K) + size_t(k), as_lds + uint32_t(slot) * 8192u + uint32_t(i) * 1024u);
     }
+  };
+  // The same copies where no row or column is clamped (the wave's 64 rows
+  // lie below M and step s ends inside K): one wave-uniform base per copy
+  // and two per-lane offsets (copy i takes the even or odd one: the chunk
+  // swizzle of row 8 i + l / 8 depends on i only through i % 2), so the copy
+  // addresses cost scalar additions only.
+  const bool rows_in = mw + 64 <= M;
+  const uint32_t off_even = uint32_t(lane >> 3) * uint32_t(K) * 2u + uint32_t((lane & 7) ^ (lane >> 4)) * 16u;
+  const uint32_t off_odd = uint32_t(lane >> 3) * uint32_t(K) * 2u + uint32_t((lane & 7) ^ (4 + (lane >> 4))) * 16u;
+  const uint16_t* const a_wave = A + size_t(mw) * size_t(K);
+  auto dma_a_fast = [&](int slot, int s) SKG_INL {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dma16_sv(a_wave + size_t(i) * 8u * size_t(K) + size_t(s) * GT_BK, (i & 1) ? off_odd : off_even,
+               as_lds + uint32_t(slot) * 8192u + uint32_t(i) * 1024u);
+  };
+  auto dma_step = [&](int slot, int s) SKG_INL {
+    if (rows_in && (s + 1) * GT_BK <= K)
+      dma_a_fast(slot, s);
+    else
+      dma_a(slot, s);
   };
   using std::integral_constant;
   if constexpr (ADMA) {
@@ -645,7 +685,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   // One fragment read of set SET, in the order the next half-step's MFMAs
   // consume them: r = 0 -> weights nj 0, r = 1..4 -> activation mi 0..3,
   // r >= 5 -> weights nj r-4.
-  auto read1 = [&](auto set_c, auto r_c, int aslot, int bbuf, int kk) {
+  auto read1 = [&](auto set_c, auto r_c, int aslot, int bbuf, int kk) SKG_INL {
     constexpr int SET = decltype(set_c)::value;
     constexpr int R = decltype(r_c)::value;
     if constexpr (R >= 1 && R <= 4) {
@@ -661,11 +701,11 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   // other set spread one per two MFMAs, pinned in that order (the scheduler
   // otherwise gathers the reads next to their uses and the LDS latency shows
   // between MFMA groups).
-  auto half = [&](auto use_c, int aslot, int bbuf, int kk) {
+  auto half = [&](auto use_c, int aslot, int bbuf, int kk) SKG_INL {
     constexpr int USE = decltype(use_c)::value;
     constexpr int NR = 4 + NB16;
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-      (([&] {
+    [&]<int... J>(std::integer_sequence<int, J...>) SKG_INL {
+      (([&]() SKG_INL {
          constexpr int nj = J / 4, mi = J % 4;
          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[USE][mi]),
                                                                __builtin_bit_cast(bf16x8, bf[USE][nj]), acc[mi][nj], 0,
@@ -677,10 +717,10 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
        ...);
     }(std::make_integer_sequence<int, 4 * NB16>{});
   };
-  auto dstep = [&](auto ca_c, auto cb_c, int s) {
+  auto dstep = [&](auto ca_c, auto cb_c, int s) SKG_INL {
     constexpr int CA = decltype(ca_c)::value;  // activation slot of step s (mod 3)
     constexpr int CB = decltype(cb_c)::value;  // weight buffer of step s
-    dma_a((CA + 2) % 3, s + 2);  // that slot was last read during step s-1
+    dma_step((CA + 2) % 3, s + 2);  // that slot was last read during step s-1
     __builtin_amdgcn_sched_barrier(0);
     half(integral_constant<int, 0>{}, CA, CB, 1);
     wait_vmcnt<8>();  // slice s+1 (requested one step ago) has landed
@@ -693,7 +733,7 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
     // producers overwrite it in step s+1.
     asm volatile("s_barrier" ::: "memory");
   };
-  auto cstep = [&](auto ca_c, auto cb_c, int s) {
+  auto cstep = [&](auto ca_c, auto cb_c, int s) SKG_INL {
     constexpr int CA = decltype(ca_c)::value;  // activation slot of step s
     constexpr int CB = decltype(cb_c)::value;  // weight buffer of step s
     park_a(CA ^ 1);  // slice of step s+1 (loaded one step ago)
@@ -706,12 +746,12 @@ __global__ __launch_bounds__(512) void gemm_q4_0_bf16_pipe_kernel(PackedW P, con
   };
   for (int s0 = 0; s0 < steps; s0 += U) {
     if constexpr (ADMA) {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
+      [&]<int... I>(std::integer_sequence<int, I...>) SKG_INL {
         ((s0 + I < steps ? dstep(integral_constant<int, I % 3>{}, integral_constant<int, I % 3>{}, s0 + I) : void()),
          ...);
       }(std::make_integer_sequence<int, U>{});
     } else {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
+      [&]<int... I>(std::integer_sequence<int, I...>) SKG_INL {
         ((s0 + I < steps ? cstep(integral_constant<int, I % 2>{}, integral_constant<int, I % 3>{}, s0 + I) : void()),
          ...);
       }(std::make_integer_sequence<int, U>{});
