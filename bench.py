@@ -916,14 +916,13 @@ def main():
             # fp32-activation matrix-core defaults that round the activation to
             # one fp16 term are timed beside the two-term (~22-bit) kernel
             dv = skg.gemv_default_variant(fmt, M, skg.EPI_NONE, 4096)
-            extra = (two_term_variants(skg, fmt, M) if fmt in (skg.Q8_0_F32, skg.Q4_0_F32)
-                     and dv["x_lds"] in (2, 3) and dv["j"] == 1 else [])
+            mf_f32 = fmt in (skg.Q8_0_F32, skg.Q4_0_F32, skg.Q4_K_F32)
+            extra = (two_term_variants(skg, fmt, M) if mf_f32 and dv["x_lds"] in (2, 3) and dv["j"] == 1 else [])
             r = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
                                14336, 4096, xh, warm_s=warm, graph=True, variants=extra)
-            r["activation"] = ("fp32 rounded to one fp16 term per element" if dv["x_lds"] in (2, 3) and dv["j"] == 1
-                               and fmt in (skg.Q8_0_F32, skg.Q4_0_F32) else
-                               "fp32 as two fp16 terms" if dv["x_lds"] in (2, 3) and fmt in (skg.Q8_0_F32,
-                                                                                            skg.Q4_0_F32)
+            r["activation"] = ("fp32 rounded to one fp16 term per element" if mf_f32 and dv["x_lds"] in (2, 3)
+                               and dv["j"] == 1 else
+                               "fp32 as two fp16 terms" if mf_f32 and dv["x_lds"] in (2, 3)
                                else "Q8_1" if fmt in skg.Q8_1_FMTS else "fp32")
             details["arms"][r["name"]] = r
             vs = "".join(f"  two-term {v['us_per_launch']:.2f} us" for v in r["variants"])

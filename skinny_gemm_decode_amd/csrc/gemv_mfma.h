@@ -133,6 +133,15 @@ __device__ inline f16x8 decode_q8_0(uint32_t p0, uint32_t p1) {
   return f16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
+// B operand of one q4_K sub-block from dword g of its unit (the q4_0 nibble
+// order): each code c as the exact fp16 subnormal c 2^-24, one shift-free AND
+// or a shift and an AND per pair (the matrix cores take fp16 subnormals
+// exactly, checked on MI355X; the products stay exact in fp32).  q4_K has no
+// code offset (w = d sc c - dmin m), so nothing cancels.
+__device__ inline f16x8 decode_q4_K_sub(uint32_t w, uint32_t mlo) {
+  return __builtin_bit_cast(f16x8, u32x4{w & mlo, (w >> 8) & mlo, (w >> 4) & mlo, (w >> 12) & mlo});
+}
+
 // Weight registers of one tile for one matrix: NP planes x BPW/4 quads of 16
 // bytes and the fp16 scales of the wave's BPW blocks (aligned 16-byte loads:
 // the kernel requires nb % BPW == 0).
@@ -168,9 +177,18 @@ struct MfNext {
 // with the same quad of the next tile as soon as they have been transposed,
 // and the scales after their last use, so about one tile of loads stays in
 // flight with a single register set.
-template <int NP, int BPW, int RR, int XT, bool RELOAD>
+//
+// KQ (q4_K): the scale words are the 16-byte super-block headers {d, dmin,
+// 12 scale bytes} of the wave's BPW / 8 super-blocks; block j's product is
+// scaled by d sc_j, and the min term - sum_j dmin m_j S_j (S_j: the block's
+// activation sum) is one MFMA per super-block over ksum, the block sums'
+// operand from mf_stage: A slot 8g + i holds the high (g even) or low (g odd)
+// fp16 part of 2^-6 S of block 8 (g / 2) + i, B the codes m_j as subnormals
+// in the slots of that super-block.
+template <int NP, int BPW, int RR, int XT, bool RELOAD, bool KQ = false>
 __device__ inline void mf_tile(MfW<NP, BPW>& r, const f16x8 (&ah)[BPW], const f16x8 (&al)[BPW], float (&acc)[4],
-                               uint32_t mlo, uint32_t mhi, uint32_t magic, const MfNext& nx, uint32_t blk0, int g) {
+                               uint32_t mlo, uint32_t mhi, uint32_t magic, const MfNext& nx, uint32_t blk0, int g,
+                               const f16x8& ksum = f16x8{}) {
   uint32_t scw[BPW / 2];
 #pragma unroll
   for (int i = 0; i < BPW / 8; ++i) {
@@ -202,17 +220,53 @@ __device__ inline void mf_tile(MfW<NP, BPW>& r, const f16x8 (&ah)[BPW], const f1
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * q + jj;
       f16x8 bw;
-      if constexpr (NP == 1)
+      if constexpr (KQ)
+        bw = decode_q4_K_sub(t[0][jj], mlo);
+      else if constexpr (NP == 1)
         bw = decode_q4_0(t[0][jj], mlo, mhi, magic);
       else
         bw = decode_q8_0(t[0][jj], t[1][jj]);
       f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j], bw, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       if constexpr (XT == 2) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[j], bw, d, 0, 0, 0);
-      const uint32_t sw = scw[j >> 1];
-      const float s = h2f((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+      float s;
+      if constexpr (KQ) {
+        // d sc_j (exact in fp32: 11 x 6 bits)
+        const int hb = 4 * (j >> 3);
+        uint32_t sc, mn;
+        q4_K_sc_m(scw[hb + 1], scw[hb + 2], scw[hb + 3], uint32_t(j & 7), sc, mn);
+        s = h2f(scw[hb] & 0xFFFFu) * float(sc);
+      } else {
+        const uint32_t sw = scw[j >> 1];
+        s = h2f((j & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+      }
 #pragma unroll
       for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, d[i], acc[i]);
     }
+  }
+  if constexpr (KQ) {
+    // acc holds 2^-24 sum_j d sc_j sum_k c_k x_k; the min term's MFMA gives
+    // 2^-30 sum_j m_j S_j per super-block
+    float mt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sb = 0; sb < BPW / 8; ++sb) {
+      uint32_t mp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t sc0, m0, sc1, m1;
+        q4_K_sc_m(scw[4 * sb + 1], scw[4 * sb + 2], scw[4 * sb + 3], uint32_t(2 * i), sc0, m0);
+        q4_K_sc_m(scw[4 * sb + 1], scw[4 * sb + 2], scw[4 * sb + 3], uint32_t(2 * i + 1), sc1, m1);
+        mp[i] = m0 | (m1 << 16);
+      }
+      const bool mine = (g >> 1) == sb;
+      const u32x4 bm = mine ? u32x4{mp[0], mp[1], mp[2], mp[3]} : u32x4{0u, 0u, 0u, 0u};
+      const f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(ksum, __builtin_bit_cast(f16x8, bm),
+                                                               f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const float dmin = h2f(scw[4 * sb] >> 16);
+#pragma unroll
+      for (int i = 0; i < RR; ++i) mt[i] = fmaf(dmin, cr[i], mt[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < RR; ++i) acc[i] = fmaf(acc[i], 16777216.0f, -1073741824.0f * mt[i]);
   }
 }
 
@@ -362,9 +416,16 @@ struct MfLds {
 // compiler drains those before any later use of a register load), and leaves
 // the fp16 A operands of the wave's BPW blocks in ah / al.  Passes of 8
 // blocks go through the wave-private LDS area `area`.
-template <int M, int BPW, int XT, int MS = (M | 1), class Between, class AfterX>
+//
+// SUMS (q4_K): ksum receives the A operand of the min term (mf_tile): lane
+// (g, c) the block sums S of activation row c (of the values the MFMA sees),
+// times 2^-6 so that they stay inside fp16 (|S| < 32 2^15), for blocks
+// 8 (g / 2) .. +7 of the span, as their high fp16 part (g even) or the fp16
+// rounding of the rest (g odd); zero past the span.
+template <int M, int BPW, int XT, int MS = (M | 1), bool SUMS = false, class Between, class AfterX>
 __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ah)[BPW],
-                                f16x8 (&al)[BPW], float (&unscale)[4], Between between, AfterX after_x) {
+                                f16x8 (&al)[BPW], float (&unscale)[4], f16x8& ksum, Between between,
+                                AfterX after_x) {
   const int g = lane >> 4, c = lane & 15;
   // A entry (block, quarter) holds M 16-byte units at a stride of MS units;
   // an odd stride (M | 1, the default) makes the 32 entries a pass writes
@@ -409,6 +470,7 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
   // A wave's LDS accesses complete in order, so its own writes are visible
   // to its reads without a barrier, and a pass's reads finish before the
   // next pass overwrites.
+  float part[SUMS ? BPW / 8 : 1][SUMS ? M : 1];
 #pragma unroll
   for (int e = 0; e < BPW / 8; ++e) {
     // element 256 e + 4 lane + i of the wave lies in block 8 e + bl, quarter
@@ -422,11 +484,19 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
       const f16x2 h13 = __builtin_convertvector((f32x2{v.y, v.w}), f16x2);
       const size_t off = size_t(((bl * 4 + gq) * MS + m) * 16 + 8 * h);
       *reinterpret_cast<u32x2*>(hi_base + off) = u32x2{bits(h02), bits(h13)};
+      f16x2 l02 = {(_Float16)0.0f, (_Float16)0.0f}, l13 = l02;
       if constexpr (XT == 2) {
         const f32x2 r02 = f32x2{v.x, v.z} - __builtin_convertvector(h02, f32x2);
         const f32x2 r13 = f32x2{v.y, v.w} - __builtin_convertvector(h13, f32x2);
-        *reinterpret_cast<u32x2*>(lo_base + off) =
-            u32x2{bits(__builtin_convertvector(r02, f16x2)), bits(__builtin_convertvector(r13, f16x2))};
+        l02 = __builtin_convertvector(r02, f16x2);
+        l13 = __builtin_convertvector(r13, f16x2);
+        *reinterpret_cast<u32x2*>(lo_base + off) = u32x2{bits(l02), bits(l13)};
+      }
+      if constexpr (SUMS) {
+        // this lane's share (4 elements) of the block sum of what the MFMA sees
+        float p = (float(h02[0]) + float(h02[1])) + (float(h13[0]) + float(h13[1]));
+        if constexpr (XT == 2) p += (float(l02[0]) + float(l02[1])) + (float(l13[0]) + float(l13[1]));
+        part[e][m] = p;
       }
     }
 #pragma unroll
@@ -439,6 +509,33 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
         al[8 * e + jl] = ah[8 * e + jl];
     }
   }
+  if constexpr (SUMS) {
+    // the 8 lanes of a block (lane / 8) add their shares (two quad exchanges
+    // and the half-row mirror); lane 8 bl stores the sums [m][block] in the
+    // area, free now (its last reads are above), and each lane reads its 8
+    static_assert(BPW == 8 || BPW == 16, "operand layout");
+    static_assert(M * BPW * 4 <= 8 * 4 * MS * 16, "block sums fit the staging area");
+    float* sarea = reinterpret_cast<float*>(area);
+#pragma unroll
+    for (int e = 0; e < BPW / 8; ++e)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float p = part[e][m];
+        p += dpp_f<SKG_DPP_QUAD_XOR1>(p);
+        p += dpp_f<SKG_DPP_QUAD_XOR2>(p);
+        p += dpp_f<SKG_DPP_ROW_HALF_MIRROR>(p);
+        if ((lane & 7) == 0) sarea[m * BPW + 8 * e + (lane >> 3)] = p;
+      }
+    const int sb = g >> 1;
+    f16x8 t;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float sv = (8 * sb < BPW) ? sarea[mr * BPW + (8 * sb) % BPW + j] * 0.015625f : 0.0f;
+      const _Float16 hi = (_Float16)sv;
+      t[j] = (g & 1) ? (_Float16)(sv - float(hi)) : hi;
+    }
+    ksum = t;
+  }
 }
 
 // Launched with nb / BPW waves (at most WAVES), so every wave owns BPW
@@ -448,7 +545,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
   static_assert(PD == 1 || PD == 2, "prefetch depth: tiles in flight per wave");
   static_assert(BPW % 8 == 0, "whole 16-byte scale loads");
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
-  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
+  // q4_K: the q4_0 unit layout, with the 16-byte super-block headers as the
+  // scale words (one per 8 blocks)
+  constexpr bool KQ = (FMT == SKG_Q4_K_F32);
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || KQ || Q8, "quantised weight formats only");
+  static_assert(!KQ || EPI == SKG_EPI_NONE, "q4_K: plain output");
   static_assert(!Q8 || (XT == 1 && EPI == SKG_EPI_NONE), "Q8_1 activations: one integer term, plain output");
   constexpr int NP = (FMT == SKG_Q8_0_F32 || FMT == SKG_Q8_0_Q8_1) ? 2 : 1;
   constexpr int NR = (EPI == SKG_EPI_SWIGLU) ? 2 : 1;
@@ -503,6 +604,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
   uint64_t aq[Q8 ? BPW : 1];
   f32x4 da[Q8 ? BPW : 1];
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};  // 2^e of the activation rows this lane's outputs belong to
+  f16x8 ksum = {};                            // q4_K: block sums, the A operand of the min term
   auto first_loads = [&] {
     next_of(nx, t0);
 #pragma unroll
@@ -530,8 +632,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
                         aq, da,
                         first_loads, [] {});
   else
-    mf_stage<M, BPW, XT>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al, unscale,
-                         first_loads, [] {});
+    mf_stage<M, BPW, XT, (M | 1), KQ>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al,
+                                      unscale, ksum, first_loads, [] {});
   __syncthreads();  // the staging area becomes the reduction buffers
 
   float* red = reinterpret_cast<float*>(lds);
@@ -547,7 +649,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
       if constexpr (Q8)
         mf_tile_q8<NP, BPW, RR, RELOAD>(w[r], aq, da, acc[r], nx[r], blk0, g);
       else
-        mf_tile<NP, BPW, RR, XT, RELOAD>(w[r], ah, al, acc[r], mlo, mhi, magic, nx[r], blk0, g);
+        mf_tile<NP, BPW, RR, XT, RELOAD, KQ>(w[r], ah, al, acc[r], mlo, mhi, magic, nx[r], blk0, g, ksum);
     }
     // partial sums: lane (g, c) holds rows m = 4g + i of output row c
     float* rb = red + size_t(parity) * (WAVES * NR * MF_ROWS * M);
@@ -734,6 +836,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   uint64_t aq[Q8 ? BPW : 1];
   f32x4 da[Q8 ? BPW : 1];
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};
+  f16x8 ksum = {};  // unused: no q4_K here
   // The first R tiles' transfers are unconditional (a workgroup with fewer
   // tiles copies its last one again): conditional transfers here would make
   // the compiler drain them all before the staging arithmetic.
@@ -749,7 +852,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
                              da,
                         [] {}, first_dma);
   else
-    mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {},
+    mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, ksum, [] {},
                               first_dma);
   if constexpr (ALIAS) {
     // every wave has read its staged operands before the shared slot refills

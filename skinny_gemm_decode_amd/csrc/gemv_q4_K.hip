@@ -3,9 +3,28 @@
 // chosen by measurement on MI355X at K = 4096, N = 14336 under cold-cache
 // rotation.
 #include "gemv_instances.h"
+#include "gemv_mfma.h"
+
+// q4_K x fp32 on the matrix cores: MF(M, waves, blocks per wave, fp16
+// activation terms, prefetch depth)
+#define SKG_MFK(M, W, B, XT, PD) out.push_back(skg::gemv_mfma_entry<SKG_Q4_K_F32, M, W, B, XT, SKG_EPI_NONE, PD>());
 
 namespace skg {
 void register_gemv_q4_K(std::vector<GemvEntry>& out) {
+  // q4_K x fp32 at M = 2..8 on the matrix cores (K a multiple of 256 up to
+  // 4096; others fall through to the vector kernels below): the activation
+  // as two fp16 terms at M = 2, 3 (13.01 / 14.11 us against 13.28 / 17.62 for
+  // the vector kernel) and as one term from M = 4, inside the accuracy bound
+  // as for q4_0 (M = 4 / 5 / 6 / 7 / 8: 13.17 / 13.86 / 14.13 / 14.63 / 14.58
+  // us against 21.07 / 24.82 / 27.69 / 30.67 / 34.21; two terms 15.30 /
+  // 18.69 / 17.34 / 18.15 / 17.51)
+  SKG_MFK(2, 16, 8, 2, 1)
+  SKG_MFK(3, 8, 16, 2, 1)
+  SKG_MFK(4, 16, 8, 1, 1)
+  SKG_MFK(5, 16, 8, 1, 1)
+  SKG_MFK(6, 16, 8, 1, 1)
+  SKG_MFK(7, 16, 8, 1, 1)
+  SKG_MFK(8, 16, 8, 1, 1)
   // q4_K x fp32, activation in LDS: 2 rows per wave at M = 1, 2, 4 (M = 1
   // 9.63 us against 9.83-10.31; M = 2 13.19 against 14.25; M = 4 20.72
   // against 21.85), 4 rows at M = 3, 5..8 (M = 8 34.13 against 39.2-39.4)
@@ -50,5 +69,23 @@ void register_gemv_q4_K(std::vector<GemvEntry>& out) {
   SKG_M3_8(SKG_Q4_K_Q8_1, 8, 1, true, 2)
   SKG_N3_8(SKG_Q4_K_Q8_1, 4, 1, true)
   SKG_N3_8(SKG_Q4_K_Q8_1, 4, 1, false)
+  // q4_K x fp32 on the matrix cores: measurement variants (16 waves with two
+  // terms spill at M = 3: 20.33 us)
+  SKG_MFK(2, 8, 16, 1, 1)
+  SKG_MFK(2, 8, 16, 2, 1)
+  SKG_MFK(3, 8, 16, 1, 1)
+  SKG_MFK(3, 16, 8, 2, 1)
+  SKG_MFK(3, 16, 8, 1, 1)
+  SKG_MFK(4, 8, 16, 1, 1)
+  SKG_MFK(4, 8, 16, 2, 1)
+  SKG_MFK(5, 8, 16, 1, 1)
+  SKG_MFK(5, 8, 16, 2, 1)
+  SKG_MFK(6, 8, 16, 1, 1)
+  SKG_MFK(6, 8, 16, 2, 1)
+  SKG_MFK(7, 8, 16, 1, 1)
+  SKG_MFK(7, 8, 16, 2, 1)
+  SKG_MFK(8, 8, 16, 1, 1)
+  SKG_MFK(8, 8, 16, 1, 2)
+  SKG_MFK(8, 8, 16, 2, 1)
 }
 }  // namespace skg

@@ -313,7 +313,7 @@ def mfma_variants(skg, fmt, M):
             if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3, 4)]
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 7])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemv_mfma_shapes(skg, fmt, M):
     """Default path at the shapes the matrix-core kernel takes, then every
@@ -350,7 +350,7 @@ def test_gemv_mfma_shapes(skg, fmt, M):
         skg.gemv_set_variant(fmt, M, 0, 0)
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 7])
 def test_gemv_mfma_activation_range(skg, fmt):
     """Activations far outside fp16 range, far below it, an all-zero row and
     a single huge outlier: the per-wave power-of-two scaling keeps the two
@@ -384,7 +384,7 @@ def test_gemv_mfma_activation_range(skg, fmt):
         skg.gemv_reset(fmt, M)
 
 
-@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("fmt", [1, 2, 7])
 def test_gemv_multi_mfma(skg, fmt):
     """Several matrices in one matrix-core launch (fused QKV shape)."""
     K, M = 4096, 3
