@@ -39,7 +39,7 @@ struct Fmt<SKG_BF16_BF16> {
 template <>
 struct Fmt<SKG_Q8_0_F32> {
   static constexpr int E = 32, WV = 8, XB = 128, XF = 32, KQ = 0;
-  static constexpr bool SCALE = true, XQ8 = false, XSUM = true;
+  static constexpr bool SCALE = true, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q4_0_F32> {
@@ -67,7 +67,7 @@ struct Fmt<SKG_Q4_K_F32> {
 template <>
 struct Fmt<SKG_Q6_K_F32> {
   static constexpr int E = 32, WV = 4, XB = 128, XF = 32, KQ = 6;
-  static constexpr bool SCALE = false, XQ8 = false, XSUM = true;
+  static constexpr bool SCALE = false, XQ8 = false, XSUM = false;
 };
 template <>
 struct Fmt<SKG_Q4_K_Q8_1> {
@@ -232,7 +232,7 @@ __device__ inline void x_from_pieces(XUnit<FMT>& x, const u32x4* pc) {
     // activation chain of unit_acc, so that a block whose codes are all 0
     // (q8_0) cancels to exactly zero: scaling every term by a power of two
     // commutes with each rounding.
-    if constexpr (Fmt<FMT>::KQ == 6) {
+    if constexpr (Fmt<FMT>::KQ == 6 && Fmt<FMT>::XSUM) {
       // half-block sums, each in the element order of its product chain
       float s2 = 0.f;
 #pragma unroll
@@ -336,13 +336,14 @@ __device__ inline int unit_idot(const WUnit<FMT>& w, const XUnit<FMT, true>& x) 
 // (SGPR masks, fp16 1024.0 pair in a VGPR) so each code pair decodes in one
 // v_and_or_b32: an instruction of that encoding takes at most one literal.
 struct DecodeK {
-  uint32_t mlo, mhi, magic;
+  uint32_t mlo, mhi, magic, mbyte;
 };
 __device__ inline DecodeK decode_consts() {
-  DecodeK k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+  DecodeK k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x00FF00FFu};
   asm volatile("" : "+s"(k.mlo));
   asm volatile("" : "+s"(k.mhi));
   asm volatile("" : "+v"(k.magic));
+  asm volatile("" : "+s"(k.mbyte));
   return k;
 }
 
@@ -420,16 +421,26 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
     }
     return fmaf(w.d, s + t, acc);
   } else if constexpr (FMT == SKG_Q8_0_F32) {
-    // int8 q + 128 is the unsigned byte of q ^ 0x80: sum_i q_i x_i =
-    // sum_i (q_i + 128) x_i - 128 sum_i x_i
+    // The codes as exact fp16 pairs: q ^ 0x80 is the unsigned byte q + 128, a
+    // byte permute puts two of them under the exponent of 1024 (1024 + q +
+    // 128) and one packed subtraction of 1152 leaves q; each product takes
+    // the fp16 code and the fp32 activation in one mixed-precision fma.  A
+    // code of 0 then contributes exactly zero whatever its activation (taking
+    // sum (q + 128) x - 128 sum x instead, an activation outlier with a zero
+    // weight cancels against itself and erases the rest of its block).
+    const q4h off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t b = w.w[k] ^ 0x80808080u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(ubyte(b, i), x.v[4 * k + i], s);
+      const uint32_t u = w.w[k] ^ 0x80808080u;
+      const q4h e02 = q4h_of(__builtin_amdgcn_perm(dk.magic | 0x00640064u, u, 0x04020400u)) + off;
+      const q4h e13 = q4h_of(__builtin_amdgcn_perm(dk.magic | 0x00640064u, u, 0x04030401u)) + off;
+      s = fmaf(float(e02[0]), x.v[4 * k + 0], s);
+      s = fmaf(float(e13[0]), x.v[4 * k + 1], s);
+      s = fmaf(float(e02[1]), x.v[4 * k + 2], s);
+      s = fmaf(float(e13[1]), x.v[4 * k + 3], s);
     }
-    return fmaf(w.d, fmaf(-128.f, x.sum, s), acc);
+    return fmaf(w.d, s, acc);
   } else if constexpr (FMT == SKG_Q4_0_Q8_1) {
     const int si = unit_idot<FMT>(w, x);
     return fmaf(w.d, fmaf(x.d, float(si), -8.f * x.s), acc);
@@ -464,25 +475,35 @@ __device__ inline float unit_acc(const WUnit<FMT>& w, const XUnit<FMT>& x, float
     const int si = unit_idot<FMT>(w, x);
     return fmaf(w.a, x.d * float(si), fmaf(-w.b, x.s, acc));
   } else if constexpr (FMT == SKG_Q6_K_F32) {
-    // w = d sc (q - 32) per 16 elements: unsigned code bytes times x, less
-    // 32 times the half-block sum of x (accumulated in the same order, so a
-    // half whose codes are all 32 cancels exactly).
+    // w = d sc (q - 32) per 16 elements.  The 6-bit codes decode exactly to
+    // the fp16 pairs q - 32 (one mask-and-or to 1024 + q, one packed
+    // subtraction of 1056) and each product takes the fp16 code and the fp32
+    // activation in one mixed-precision fma, so a code of 32 contributes
+    // exactly zero whatever its activation (taking sum q x - 32 sum x
+    // instead, an activation outlier with a zero weight cancels against
+    // itself and erases the rest of its half).
+    const q4h off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
     float s = 0.f, t = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t ca, cb;
       q6_K_codes(w.w, w.h, k, ca, cb);
-      s = fmaf(cvt_ubyte<0>(ca), x.v[4 * k + 0], s);
-      s = fmaf(cvt_ubyte<1>(ca), x.v[4 * k + 1], s);
-      s = fmaf(cvt_ubyte<2>(ca), x.v[4 * k + 2], s);
-      s = fmaf(cvt_ubyte<3>(ca), x.v[4 * k + 3], s);
-      t = fmaf(cvt_ubyte<0>(cb), x.v[16 + 4 * k + 0], t);
-      t = fmaf(cvt_ubyte<1>(cb), x.v[16 + 4 * k + 1], t);
-      t = fmaf(cvt_ubyte<2>(cb), x.v[16 + 4 * k + 2], t);
-      t = fmaf(cvt_ubyte<3>(cb), x.v[16 + 4 * k + 3], t);
+      // elements 4k, 4k+2 | 4k+1, 4k+3 of each half
+      const q4h a02 = q4h_of((ca & dk.mbyte) | dk.magic) + off;
+      const q4h a13 = q4h_of(((ca >> 8) & dk.mbyte) | dk.magic) + off;
+      const q4h b02 = q4h_of((cb & dk.mbyte) | dk.magic) + off;
+      const q4h b13 = q4h_of(((cb >> 8) & dk.mbyte) | dk.magic) + off;
+      s = fmaf(float(a02[0]), x.v[4 * k + 0], s);
+      s = fmaf(float(a13[0]), x.v[4 * k + 1], s);
+      s = fmaf(float(a02[1]), x.v[4 * k + 2], s);
+      s = fmaf(float(a13[1]), x.v[4 * k + 3], s);
+      t = fmaf(float(b02[0]), x.v[16 + 4 * k + 0], t);
+      t = fmaf(float(b13[0]), x.v[16 + 4 * k + 1], t);
+      t = fmaf(float(b02[1]), x.v[16 + 4 * k + 2], t);
+      t = fmaf(float(b13[1]), x.v[16 + 4 * k + 3], t);
     }
-    acc = fmaf(w.alo, fmaf(-32.f, x.sum, s), acc);
-    return fmaf(w.ahi, fmaf(-32.f, x.sum2, t), acc);
+    acc = fmaf(w.alo, s, acc);
+    return fmaf(w.ahi, t, acc);
   } else if constexpr (FMT == SKG_Q6_K_Q8_1) {
     // codes 0..63 are non-negative int8, so the signed 4x8-bit dot is exact
     int sa = 0, sb = 0;
@@ -636,7 +657,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
   DecodeK dk{};
-  if constexpr (FMT == SKG_Q4_0_F32 || FMT == SKG_Q4_K_F32) dk = decode_consts();
+  if constexpr (FMT == SKG_Q4_0_F32 || FMT == SKG_Q4_K_F32 || FMT == SKG_Q8_0_F32 || FMT == SKG_Q6_K_F32)
+    dk = decode_consts();
   const int nchunks = int((nu + UC - 1) / UC);
   for (int c = kw; c < nchunks; c += KW) {
     const uint32_t ub = uint32_t(c) * UC;

@@ -350,14 +350,9 @@ def test_gemv_mfma_shapes(skg, fmt, M):
         skg.gemv_set_variant(fmt, M, 0, 0)
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 7])
-def test_gemv_mfma_activation_range(skg, fmt):
-    """Activations far outside fp16 range, far below it, an all-zero row and
-    a single huge outlier: the per-wave power-of-two scaling keeps the two
-    fp16 terms exact enough everywhere."""
-    M, N, K = 6, 300, 4096
-    rng = si.rng_for(0, 99, 8900 + fmt)
-    W = si.weights(wkind(skg, fmt), rng, N, K)
+def range_activations(rng, M, K):
+    """Rows far outside fp16 range, zero, far below it, one huge outlier, a
+    half scaled by 1e20 and outliers in every quarter of some blocks."""
     x = si.activations_f32(rng, M, K)
     x[0] *= np.float32(1e6)          # |x| up to ~5e6 (fp16 max is 65504)
     x[1] = 0.0
@@ -369,6 +364,68 @@ def test_gemv_mfma_activation_range(skg, fmt):
     # taken from part of a row's lanes overflows fp16
     for blk, e in ((3, 13), (40, 30), (77, 6), (100, 21), (126, 0)):
         x[5, 32 * blk + e] = np.float32(7e4 * (1 + blk))
+    return x
+
+
+def zero_weight(kind, W, n, k):
+    """Set element k of row n of canonical weights W to the code whose weight
+    is exactly zero (q8_0: 0, q4_0: 8, q6_K: 32); returns whether the format
+    has one."""
+    if kind == "q8_0":
+        W[n, k // 32, 2 + k % 32] = 0
+    elif kind == "q4_0":
+        b, i = k // 32, k % 32
+        byte = W[n, b, 2 + i % 16]
+        W[n, b, 2 + i % 16] = (byte & 0xF0) | 8 if i < 16 else (byte & 0x0F) | 0x80
+    elif kind == "q6_K":
+        sb, e = k // 256, k % 256
+        h, r = e // 128, e % 128
+        g, l = r // 32, r % 32
+        qi = 64 * h + 32 * (g & 1) + l        # low four bits: 0
+        sh = 4 * (g >> 1)
+        W[n, sb, qi] &= np.uint8(~(0xF << sh) & 0xFF)
+        hi = 128 + 32 * h + l                 # top two bits: 0b10
+        W[n, sb, hi] = (W[n, sb, hi] & np.uint8(~(3 << (2 * g)) & 0xFF)) | np.uint8(2 << (2 * g))
+    else:
+        return False
+    return True
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 7, 8])
+def test_gemv_activation_range_single_rows(skg, fmt):
+    """The M = 1 defaults (vector ALU) on each pathological activation row
+    alone, with the weights of every other output row made exactly zero at
+    the outliers' positions (q8_0 code 0, q4_0 code 8, q6_K code 32): such an
+    outlier must contribute nothing, not cancel against itself and erase the
+    rest of its block."""
+    N, K = 300, 4096
+    rng = si.rng_for(0, 99, 8950 + fmt)
+    kind = wkind(skg, fmt)
+    W = si.weights(kind, rng, N, K)
+    x = range_activations(rng, 6, K)
+    for k in [1234] + [32 * blk + e for blk, e in ((3, 13), (40, 30), (77, 6), (100, 21), (126, 0))]:
+        for n in range(0, N, 2):
+            zero_weight(kind, W, n, k)
+    if kind in ("q8_0", "q4_0", "q6_K"):
+        assert np.all(oracle.dequantize(kind, W)[::2, 1234] == 0.0)
+    for m in range(6):
+        xm = np.ascontiguousarray(x[m:m + 1])
+        y_ref, bound = reference(skg, fmt, W, xm, None)
+        y, _ = run_gemv(skg, fmt, 1, N, K, W, xm)
+        assert_close(y, y_ref, bound, f"fmt={fmt} M=1 row {m}")
+        if m == 1:
+            assert np.all(y == 0.0), "all-zero activation row must give exact zeros"
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 7, 8])
+def test_gemv_mfma_activation_range(skg, fmt):
+    """Activations far outside fp16 range, far below it, an all-zero row and
+    a single huge outlier: the per-wave power-of-two scaling keeps the two
+    fp16 terms exact enough everywhere."""
+    M, N, K = 6, 300, 4096
+    rng = si.rng_for(0, 99, 8900 + fmt)
+    W = si.weights(wkind(skg, fmt), rng, N, K)
+    x = range_activations(rng, M, K)
     y_ref, bound = reference(skg, fmt, W, x, None)
     y, _ = run_gemv(skg, fmt, M, N, K, W, x)
     assert_close(y, y_ref, bound, f"fmt={fmt} range")
