@@ -300,14 +300,11 @@ constexpr int q8_stage_row() {
 // loads go there), after_x() once they have been written to LDS (direct
 // global-to-LDS weight transfers go there: the compiler would drain them
 // before any later use of a register load).
-template <int M, int BPW, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
-__device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, uint64_t (&aq)[BPW],
-                                   f32x4 (&da)[BPW], Between between, AfterX after_x) {
+template <int M, int BPW, int RWP, class Between>
+__device__ inline void mf_copy_q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, Between between) {
   constexpr int RW = BPW * 9;                 // dwords per activation row of the wave's span
   constexpr int NL = (M * RW + 63) / 64;      // dword loads per lane
   static_assert(RWP >= RW, "row stride");
-  const int g = lane >> 4, c = lane & 15;
-  const int mr = (c < M) ? c : c % M;
   const uint32_t* xw = reinterpret_cast<const uint32_t*>(a.x);
   uint32_t v[NL];
 #pragma unroll
@@ -326,7 +323,15 @@ __device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk
     const int f = i * 64 + lane;
     if (f < M * RW) area[(f / RW) * RWP + f % RW] = v[i];
   }
+}
+
+template <int M, int BPW, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
+__device__ inline void mf_stage_q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, uint64_t (&aq)[BPW],
+                                   f32x4 (&da)[BPW], Between between, AfterX after_x) {
+  mf_copy_q8<M, BPW, RWP>(a, area, blk0, lane, between);
   after_x();
+  const int g = lane >> 4, c = lane & 15;
+  const int mr = (c < M) ? c : c % M;
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
     const uint32_t* blk = area + mr * RWP + j * 9;
@@ -393,6 +398,116 @@ __device__ inline void mf_tile_q8(MfW<NP, BPW>& r, const uint64_t (&aq)[BPW], co
 #pragma unroll
       for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, da[j][i] * float(sdot[i]), acc[i]);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two Q8_1 blocks per v_mfma_i32_16x16x64_i8 (weight-ring kernel, M <= 8).
+// One block per 16 x 16 integer MFMA leaves result rows M..15 unused, and
+// every lane scales four results of which at most two rows of four carry
+// output.  The 64-deep instruction takes blocks b and b + 1 at once as a
+// block-diagonal product: the B operand holds block b in lane groups g = 0, 1
+// and block b + 1 in g = 2, 3; A rows 0..7 hold the activation rows of block
+// b in groups 0, 1 and zeros in 2, 3, rows 8..15 those of block b + 1 in
+// groups 2, 3 and zeros in 0, 1.  Result row r is then block b + r / 8's dot
+// of activation row r % 8, exact in int32: an element of A lane (g, i) only
+// ever meets the element in the same position of B lane (g, j), so which k
+// the hardware gives each position does not matter.  Every lane's four
+// results are output rows (for M > 4), half the scaling per block, and the B
+// operand comes straight from the LDS slot with no transpose: lane (g, c)
+// takes half g % 2 of block b + g / 2 of row c (8 bytes of nibbles, or one
+// 16-byte q8_0 plane unit).  The two halves of an output row's sum (lane
+// groups g and g + 2) are added once per tile.
+
+// LDS position of chunk j of row r in a weight-ring slot (16-byte chunks,
+// permuted within each aligned group of 16; see the ring kernel below).
+__device__ inline int mf_swz(int j, int r) { return j ^ (r & 15); }
+
+// A operands of the wave's BPW / 2 block pairs in that layout, and the
+// activation scales of the four result rows of each lane (zero for rows >=
+// M; over 16 for q4_0, whose B codes are 16 (code - 8)).
+template <int M, int BPW, bool Q4, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
+__device__ inline void mf_stage_q8p(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, i32x4 (&aq)[BPW / 2],
+                                    f32x4 (&da)[BPW / 2], Between between, AfterX after_x) {
+  static_assert(M <= 8 && BPW % 2 == 0, "two blocks of eight rows");
+  mf_copy_q8<M, BPW, RWP>(a, area, blk0, lane, between);
+  after_x();
+  const int g = lane >> 4, c = lane & 15;
+  const int h = g & 1, e = g >> 1;  // half of the block, block of the pair
+  const int m = c & 7;
+  const bool on = (c >> 3) == e && m < M;
+  const uint32_t* row = area + (m < M ? m : 0) * RWP;
+  constexpr float WS = Q4 ? 0.0625f : 1.0f;
+#pragma unroll
+  for (int p = 0; p < BPW / 2; ++p) {
+    const uint32_t* blk = row + (2 * p + e) * 9;
+    // q4_0: nibble bytes 8h..8h+7 hold elements 8h..8h+7 (low) and
+    // 16+8h..16+8h+7 (high), decoded dword by dword as low, high; q8_0: plane
+    // h holds elements 16h..16h+15 in order.  Element i sits in dword 1 + i/4.
+    uint32_t v[4];
+    if constexpr (Q4) {
+      v[0] = blk[1 + 2 * h];
+      v[1] = blk[5 + 2 * h];
+      v[2] = blk[2 + 2 * h];
+      v[3] = blk[6 + 2 * h];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = blk[1 + 4 * h + i];
+    }
+    aq[p] = on ? i32x4{int(v[0]), int(v[1]), int(v[2]), int(v[3])} : i32x4{0, 0, 0, 0};
+    float d4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mo = 4 * h + i;
+      d4[i] = (mo < M) ? h2f(area[(mo < M ? mo : 0) * RWP + (2 * p + e) * 9] & 0xFFFFu) * WS : 0.f;
+    }
+    da[p] = f32x4{d4[0], d4[1], d4[2], d4[3]};
+  }
+}
+
+// One tile of the weight-ring kernel against Q8_1 activations in block pairs.
+// slot: the tile's LDS slot (rows of RB payload bytes, mf_swz chunk order,
+// then 16 rows of SRS scale bytes); RR: result rows per lane that can be
+// output rows.  On return every lane holds the full sums of rows 4 (g % 2) ..
+// 4 (g % 2) + 3 of column c.
+template <class G, int BPW, int RR>
+__device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, int c, const i32x4 (&aq)[BPW / 2],
+                                   const f32x4 (&da)[BPW / 2], float (&acc)[4]) {
+  uint32_t scw[BPW / 2];
+#pragma unroll
+  for (int k = 0; k < BPW / 8; ++k) {
+    const u32x4 s4 = *reinterpret_cast<const u32x4*>(slot + 16 * G::RB + c * G::SRS + mf_swz(int(blk0) / 8 + k, c) * 16);
+    scw[4 * k + 0] = s4.x;
+    scw[4 * k + 1] = s4.y;
+    scw[4 * k + 2] = s4.z;
+    scw[4 * k + 3] = s4.w;
+  }
+  const int h = g & 1, e = g >> 1;
+  const uint32_t sh = uint32_t(e) * 16u;  // block b + 1's scale is the high half
+  const uint8_t* row = slot + c * G::RB;
+#pragma unroll
+  for (int p = 0; p < BPW / 2; ++p) {
+    const int b = int(blk0) + 2 * p + e;
+    i32x4 bv;
+    if constexpr (G::NP == 1) {
+      // 16 (code - 8) as int8: the nibble moved to the high half of its
+      // byte, sign bit flipped
+      const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(b, c) * 16 + 8 * h);
+      bv = i32x4{int(((u.x << 4) & 0xF0F0F0F0u) ^ 0x80808080u), int((u.x & 0xF0F0F0F0u) ^ 0x80808080u),
+                 int(((u.y << 4) & 0xF0F0F0F0u) ^ 0x80808080u), int((u.y & 0xF0F0F0F0u) ^ 0x80808080u)};
+    } else {
+      bv = *reinterpret_cast<const i32x4*>(row + mf_swz(h * G::NB + b, c) * 16);
+    }
+    const i32x4 sdot = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[p], bv, i32x4{0, 0, 0, 0}, 0, 0, 0);
+    const float s = h2f(scw[p] >> sh);
+#pragma unroll
+    for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, da[p][i] * float(sdot[i]), acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < RR; ++i) {
+    const uint32_t v = __float_as_uint(acc[i]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    acc[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
 }
 
@@ -726,7 +841,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
 // plus scales) keeps R - 1 tiles in flight while one is decoded; one barrier
 // per tile.  With R = 4 (q4_0 only: four 37 KB slots fit the 160 KB) every
 // tile a workgroup owns is requested before the first is decoded, so no
-// transfer waits for a slot to drain.
+// transfer waits for a slot to drain.  Q8_1 activations take two blocks per
+// 64-deep integer MFMA (mf_stage_q8p / mf_tile_q8p above), with the B
+// operand read from the slot in its final layout.
 //
 // LDS rows are not padded: a row's 16-byte chunks are permuted within each
 // aligned group of 16 (chunk j of row r sits at position j ^ (r % 16)), so the
@@ -751,8 +868,6 @@ struct MfDmaGeom {
   static constexpr int P = 2 * CH + 1;               // transfers per wave per tile (2 rows + 4 scale rows)
 };
 
-// LDS position of chunk j of row r (16-byte chunks, see above).
-__device__ inline int mf_swz(int j, int r) { return j ^ (r & 15); }
 
 // R: ring slots; ALIAS: the activation staging area shares the last slot
 // (its first load is issued after staging).
@@ -833,8 +948,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
 
   uint8_t* stage_area = ALIAS ? (R == 4 ? slot3 : R == 3 ? slot2 : slot1) : stage_own;
   f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
-  uint64_t aq[Q8 ? BPW : 1];
-  f32x4 da[Q8 ? BPW : 1];
+  i32x4 aq[Q8 ? BPW / 2 : 1];
+  f32x4 da[Q8 ? BPW / 2 : 1];
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};
   f16x8 ksum = {};  // unused: no q4_K here
   // The first R tiles' transfers are unconditional (a workgroup with fewer
@@ -848,9 +963,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if constexpr (R == 4 && !ALIAS) dma_tile(slot3, clamp(3));
   };
   if constexpr (Q8)
-    mf_stage_q8<M, BPW, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq,
-                             da,
-                        [] {}, first_dma);
+    mf_stage_q8p<M, BPW, FMT == SKG_Q4_0_Q8_1, QRP>(
+        a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da, [] {}, first_dma);
   else
     mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, ksum, [] {},
                               first_dma);
@@ -892,7 +1006,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   int parity = 0;
   auto run = [&](uint8_t* slot, int i) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    {
+    if constexpr (Q8) {
+      mf_tile_q8p<G, BPW, (M > 4 ? 4 : M)>(slot, blk0, g, c, aq, da, acc);
+    } else {
       MfW<NP, BPW> w;
 #pragma unroll
       for (int q = 0; q < BPW / 4; ++q)
@@ -903,10 +1019,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       for (int k = 0; k < BPW / 8; ++k)
         w.sc[k] = *reinterpret_cast<const u32x4*>(slot + 16 * G::RB + c * G::SRS + mf_swz(int(blk0) / 8 + k, c) * 16);
       const MfNext none{};
-      if constexpr (Q8)
-        mf_tile_q8<NP, BPW, RR, false>(w, aq, da, acc, none, blk0, g);
-      else
-        mf_tile<NP, BPW, RR, XT, false>(w, ah, al, acc, mlo, mhi, magic, none, blk0, g);
+      mf_tile<NP, BPW, RR, XT, false>(w, ah, al, acc, mlo, mhi, magic, none, blk0, g);
     }
     float* rb = red + parity * (WAVES * MF_ROWS * M);
     parity ^= 1;

@@ -8,13 +8,13 @@
 namespace skg {
 // Registered before the vector-ALU Q8_1 instances: the defaults where they
 // measure faster on MI355X (K = 4096, N = 14336, cold-cache rotation).  The
-// weights streamed into an LDS ring: q4_0 M = 6 / 7 / 8 12.93 / 12.81 /
-// 12.97 us against 13.44 / 14.06 / 13.52 for the next best (vector kernel at
-// M = 6, register-fed integer MFMA at 7, 8); q8_0 M = 6 17.34 against 17.83
-// (vector), M = 7 / 8 18.08 / 17.55 against 18.45 / 18.12 (register-fed).
-// From M = 5 down the vector kernels win (M = 5: 12.15 against 13.49 us for
-// q4_0).  The ring kernels take K = 4096 only; other K (not a multiple of
-// 256, or above 4096) fall through to the register-fed or vector kernels.
+// weights streamed into an LDS ring, two blocks per 64-deep integer MFMA:
+// q4_0 M = 6 / 7 / 8 10.45 / 10.15 / 10.05 us, q8_0 14.21 / 14.04 / 13.80 us
+// (one block per MFMA before: 12.79 / 12.92 / 12.71 and 16.93 / 17.07 /
+// 16.72; the next best kernels, vector at M = 6 and register-fed integer
+// MFMA at 7, 8, took 13.44 / 14.06 / 13.52 and 17.83 / 18.45 / 18.12).  The
+// ring kernels take K = 4096 only; other K (not a multiple of 256, or above
+// 4096) fall through to the register-fed or vector kernels.
 void register_gemv_mfma_q8_1(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 2, true>());
