@@ -24,8 +24,10 @@
 //   and per wave so that the largest |x| of the row in the wave's span of K
 //   maps into [2^14, 2^15).  The pair carries ~22 significant bits for every
 //   element within 2^-28 of that largest magnitude; smaller elements keep an
-//   absolute error below 2^-39 of it.  Every product is exact in fp32.  Each
-//   block takes two MFMAs (hi, then lo accumulated on top).
+//   absolute error below 2^-39 of it.  Every product is exact in fp32.  With
+//   M <= 8 the two terms share one MFMA: A rows 0..7 hold the hi parts of the
+//   activation rows, rows 8..15 the lo parts, and the two halves of each
+//   output row's sum (lane groups 0, 1 and 2, 3) are added once per tile.
 // * Loads keep the row-major packed layout of the vector kernels: lane
 //   (g, c) of a wave (g = lane / 16, c = lane % 16) reads the 16-byte unit of
 //   block 4 q + g of row c, i.e. four consecutive blocks per row per load.
@@ -226,8 +228,7 @@ __device__ inline void mf_tile(MfW<NP, BPW>& r, const f16x8 (&ah)[BPW], const f1
         bw = decode_q4_0(t[0][jj], mlo, mhi, magic);
       else
         bw = decode_q8_0(t[0][jj], t[1][jj]);
-      f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j], bw, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      if constexpr (XT == 2) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[j], bw, d, 0, 0, 0);
+      const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[j], bw, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       float s;
       if constexpr (KQ) {
         // d sc_j (exact in fp32: 11 x 6 bits)
@@ -267,6 +268,15 @@ __device__ inline void mf_tile(MfW<NP, BPW>& r, const f16x8 (&ah)[BPW], const f1
     }
 #pragma unroll
     for (int i = 0; i < RR; ++i) acc[i] = fmaf(acc[i], 16777216.0f, -1073741824.0f * mt[i]);
+  }
+  if constexpr (XT == 2) {
+    // high-part rows (lane groups 0, 1) plus low-part rows (2, 3)
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      const uint32_t v = __float_as_uint(acc[i]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      acc[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
   }
 }
 
@@ -515,9 +525,9 @@ __device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, in
 // staging, reused afterwards for the two reduction buffers.
 template <int M, int WAVES, int BPW, int XT, int NR>
 struct MfLds {
-  // one pass of 8 blocks (hi and lo A entries); entries of (M | 1) 16-byte
-  // units, see mf_stage
-  static constexpr int WAVE_STAGE = XT * 8 * 4 * (M | 1) * 16;
+  // one pass of 8 blocks; A entries of (XT M | 1) 16-byte units (the hi rows,
+  // then the lo rows), see mf_stage
+  static constexpr int WAVE_STAGE = 8 * 4 * ((XT * M) | 1) * 16;
   static constexpr int STAGE = WAVES * WAVE_STAGE;
   static constexpr int RED = 2 * WAVES * NR * MF_ROWS * M * 4;
   static constexpr int BYTES = STAGE > RED ? STAGE : RED;
@@ -537,19 +547,24 @@ struct MfLds {
 // times 2^-6 so that they stay inside fp16 (|S| < 32 2^15), for blocks
 // 8 (g / 2) .. +7 of the span, as their high fp16 part (g even) or the fp16
 // rounding of the rest (g odd); zero past the span.
-template <int M, int BPW, int XT, int MS = (M | 1), bool SUMS = false, class Between, class AfterX>
+template <int M, int BPW, int XT, int MS = ((XT * M) | 1), bool SUMS = false, class Between, class AfterX>
 __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ah)[BPW],
                                 f16x8 (&al)[BPW], float (&unscale)[4], f16x8& ksum, Between between,
                                 AfterX after_x) {
   const int g = lane >> 4, c = lane & 15;
-  // A entry (block, quarter) holds M 16-byte units at a stride of MS units;
-  // an odd stride (M | 1, the default) makes the 32 entries a pass writes
+  // A entry (block, quarter) holds XT M 16-byte units (the hi rows, then the
+  // lo rows) at a stride of MS units; an odd stride (XT M | 1, the default)
+  // makes the 32 entries a pass writes
   // (and the 4 a read takes) start on different bank groups: with an even
   // stride such as M = 8 (128 bytes, half the 64 banks) they pile onto two.
-  static_assert(MS >= M, "entry stride");
+  static_assert(MS >= XT * M, "entry stride");
   uint8_t* hi_base = area;
-  uint8_t* lo_base = hi_base + 8 * 4 * MS * 16;
+  uint8_t* lo_base = area + M * 16;  // lo rows follow the hi rows of each entry
   const int mr = (c < M) ? c : c % M;
+  // two terms: A rows 0..7 take the high parts of activation rows 0..7, rows
+  // 8..15 the low parts (rows past M repeat a row; their results are unused)
+  const int mp = ((c & 7) < M) ? (c & 7) : (c & 7) % M;
+  const uint8_t* a_base = (XT == 2 && c >= 8) ? lo_base : hi_base;
   f32x4 xv[M][BPW / 8];
 #pragma unroll
   for (int m = 0; m < M; ++m)
@@ -616,12 +631,9 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
     }
 #pragma unroll
     for (int jl = 0; jl < 8; ++jl) {
-      const size_t off = size_t(((jl * 4 + g) * MS + mr) * 16);
-      ah[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hi_base + off));
-      if constexpr (XT == 2)
-        al[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(lo_base + off));
-      else
-        al[8 * e + jl] = ah[8 * e + jl];
+      const size_t off = size_t(((jl * 4 + g) * MS + (XT == 2 ? mp : mr)) * 16);
+      ah[8 * e + jl] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(a_base + off));
+      al[8 * e + jl] = ah[8 * e + jl];
     }
   }
   if constexpr (SUMS) {
@@ -645,7 +657,10 @@ __device__ inline void mf_stage(const MfArgs& a, uint8_t* area, uint32_t blk0, i
     f16x8 t;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float sv = (8 * sb < BPW) ? sarea[mr * BPW + (8 * sb) % BPW + j] * 0.015625f : 0.0f;
+      // two terms: the high and low rows share one block sum, carried by rows
+      // 0..7 only
+      const bool live = 8 * sb < BPW && !(XT == 2 && c >= 8);
+      const float sv = live ? sarea[(XT == 2 ? mp : mr) * BPW + (8 * sb) % BPW + j] * 0.015625f : 0.0f;
       const _Float16 hi = (_Float16)sv;
       t[j] = (g & 1) ? (_Float16)(sv - float(hi)) : hi;
     }
@@ -747,7 +762,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const MfArgs a) {
                         aq, da,
                         first_loads, [] {});
   else
-    mf_stage<M, BPW, XT, (M | 1), KQ>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al,
+    mf_stage<M, BPW, XT, ((XT * M) | 1), KQ>(a, lds + size_t(wave) * MfLds<M, WAVES, BPW, XT, 1>::WAVE_STAGE, blk0, lane, ah, al,
                                       unscale, ksum, first_loads, [] {});
   __syncthreads();  // the staging area becomes the reduction buffers
 
@@ -883,10 +898,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr int RR = M < 4 ? M : 4;
   // per-wave activation staging: fp16 A operands, or the raw Q8_1 blocks;
   // the bank-spreading strides where the staging still fits the shared slot
-  constexpr int MSO = M | 1;
-  constexpr int MSD = (!ALIAS || WAVES * (XT * 8 * 4 * MSO * 16) <= G::SLOT) ? MSO : M;
+  constexpr int MSO = (XT * M) | 1;
+  constexpr int MSD = (!ALIAS || WAVES * (8 * 4 * MSO * 16) <= G::SLOT) ? MSO : XT * M;
   constexpr int QRP = (!ALIAS || WAVES * M * q8_stage_row<BPW>() * 4 <= G::SLOT) ? q8_stage_row<BPW>() : 9 * BPW;
-  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : XT * 8 * 4 * MSD * 16;
+  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   // one LDS array, carved: R slots, the own staging area, the partial sums
   constexpr int RED_BYTES = 2 * WAVES * MF_ROWS * M * 4;
