@@ -10,6 +10,12 @@ namespace skg {
 // Registered before the vector-ALU instances: the defaults for M = 2..8,
 // measured on MI355X under cold-cache rotation (K = 4096, N = 14336).
 void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
+  // M = 2: the LDS-ring kernel with two fp16 activation terms, 11.35 us
+  // against 11.82 (register-fed, two terms); M = 3 / 5: the ring with one
+  // term, 11.61 / 12.41 us against 12.16 / 12.59 (register-fed, two terms)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 2, 2, 3, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 3, 1, 3, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 5, 1, 3, false>());
   SKG_MF(2, 2, 1)
   SKG_MF(3, 2, 1)
   // M = 4, 6: the LDS-ring kernel with one fp16 activation term, 12.00 /
@@ -49,12 +55,13 @@ void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 4, 1, 2>());
   out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 8, 1, 2>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 1, 2, 3, false>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 2, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 4, 2, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 2, 2, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 2, 2, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 8, 1, 3, false>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 7, 1, 3, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 3, 2, 3, false>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 5, 2, 3, false>());
   // four slots, every tile of a workgroup in flight from the start: slower
   // at every M (M = 4 / 6 / 7 / 8: 12.34 / 12.94 / 13.15 / 13.02 us against
   // 11.71 / 12.38 / 11.77 / 11.75 for the defaults)

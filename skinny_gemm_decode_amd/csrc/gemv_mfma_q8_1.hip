@@ -14,8 +14,16 @@ namespace skg {
 // 16.72; the next best kernels, vector at M = 6 and register-fed integer
 // MFMA at 7, 8, took 13.44 / 14.06 / 13.52 and 17.83 / 18.45 / 18.12).  The
 // ring kernels take K = 4096 only; other K (not a multiple of 256, or above
-// 4096) fall through to the register-fed or vector kernels.
+// 4096) fall through to the register-fed or vector kernels.  At M = 4 / 5 the
+// ring kernel is the default too: q4_0 10.28 / 10.84 us against 10.63 /
+// 12.19 for the vector kernel, q8_0 14.43 / 14.65 against 14.73 / 15.89; at
+// M = 2 / 3 the vector kernel stays ahead (q4_0 8.77 / 9.62 against 9.33 /
+// 10.18, q8_0 12.18 / 13.49 against 13.38 / 13.98).
 void register_gemv_mfma_q8_1(std::vector<GemvEntry>& out) {
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 4, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 5, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 4, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 5, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 2, true>());
@@ -45,9 +53,12 @@ void register_gemv_mfma_q8_1_alt(std::vector<GemvEntry>& out) {
   SKG_MF8(SKG_Q4_0_Q8_1, 8, 8, 16, 2)
   SKG_MF8(SKG_Q8_0_Q8_1, 4, 8, 16, 1)
   SKG_MF8(SKG_Q8_0_Q8_1, 8, 8, 16, 1)
-  // weights streamed into an LDS ring at M = 5: slower than the vector
-  // kernel (q8_0 17.06 against 15.86 us)
-  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 5, 1, 2, true>());
+  // weights streamed into an LDS ring at M = 2 / 3: slower than the vector
+  // kernels (figures above)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 2, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 3, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 2, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 3, 1, 2, true>());
   // q4_0 with four slots, every tile of a workgroup in flight from the
   // start: slower (M = 6 / 7 / 8: 14.90 / 14.75 / 14.87 us against 12.80 /
   // 12.92 / 12.73 for the two-slot defaults)
