@@ -797,7 +797,7 @@ def cpu_baseline(si, x_host, budget_s=12.0):
 def takes_k4096(v, nb=128):
     """Whether a compiled GEMV variant handles K = 4096 (nb = 128 blocks):
     the library's own shape rules, restated for choosing what to time."""
-    if v["x_lds"] == 3:
+    if v["x_lds"] in (3, 5):
         return v["waves"] * v["kw"] == nb
     if v["x_lds"] == 2:
         return nb % v["kw"] == 0 and nb <= v["waves"] * v["kw"]
@@ -824,11 +824,14 @@ def sweep_variants(skg, fmt, M):
 def two_term_variants(skg, fmt, M, K=4096):
     """Compiled matrix-core variants of (fmt, M) that carry the fp32
     activation as two fp16 terms (~22 significant bits) and take K, fastest
-    kind first: the LDS-ring kernel, then the register-fed one."""
+    kind first: the LDS-ring kernel with grouped blocks, then the ring with
+    one block per MFMA, the register-fed kernel and the per-wave rings."""
     vs = [v for v in skg.gemv_variants() if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE
-          and v["x_lds"] in (2, 3, 4) and v["j"] == 2 and (v["x_lds"] != 3 or v["waves"] * v["kw"] == K // 32)
-          and (v["x_lds"] == 3 or ((K // 32) % v["kw"] == 0 and K // 32 <= v["waves"] * v["kw"]))]
-    return sorted(vs, key=lambda v: -v["x_lds"])[:1]
+          and v["x_lds"] in (2, 3, 4, 5) and v["j"] == 2
+          and (v["x_lds"] not in (3, 5) or v["waves"] * v["kw"] == K // 32)
+          and (v["x_lds"] in (3, 5) or ((K // 32) % v["kw"] == 0 and K // 32 <= v["waves"] * v["kw"]))]
+    order = {5: 0, 3: 1, 2: 2, 4: 3}
+    return sorted(vs, key=lambda v: order[v["x_lds"]])[:1]
 
 
 def main():
@@ -917,12 +920,12 @@ def main():
             # one fp16 term are timed beside the two-term (~22-bit) kernel
             dv = skg.gemv_default_variant(fmt, M, skg.EPI_NONE, 4096)
             mf_f32 = fmt in (skg.Q8_0_F32, skg.Q4_0_F32, skg.Q4_K_F32)
-            extra = (two_term_variants(skg, fmt, M) if mf_f32 and dv["x_lds"] in (2, 3) and dv["j"] == 1 else [])
+            extra = (two_term_variants(skg, fmt, M) if mf_f32 and dv["x_lds"] in (2, 3, 5) and dv["j"] == 1 else [])
             r = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
                                14336, 4096, xh, warm_s=warm, graph=True, variants=extra)
-            r["activation"] = ("fp32 rounded to one fp16 term per element" if mf_f32 and dv["x_lds"] in (2, 3)
+            r["activation"] = ("fp32 rounded to one fp16 term per element" if mf_f32 and dv["x_lds"] in (2, 3, 5)
                                and dv["j"] == 1 else
-                               "fp32 as two fp16 terms" if mf_f32 and dv["x_lds"] in (2, 3)
+                               "fp32 as two fp16 terms" if mf_f32 and dv["x_lds"] in (2, 3, 5)
                                else "Q8_1" if fmt in skg.Q8_1_FMTS else "fp32")
             details["arms"][r["name"]] = r
             vs = "".join(f"  two-term {v['us_per_launch']:.2f} us" for v in r["variants"])

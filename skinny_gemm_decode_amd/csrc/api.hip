@@ -161,10 +161,10 @@ void init_registry() {
 }
 
 // The matrix-core kernels run nb / kw waves of kw blocks each; the LDS-ring
-// variant (x_lds = 3) is compiled for one K.
+// variants (x_lds = 3, 5) are compiled for one K.
 bool variant_supports(const GemvEntry& e, int64_t K) {
   const int64_t nb = K / 32;
-  if (e.xlds == 3) return nb == e.max_nb;
+  if (e.xlds == 3 || e.xlds == 5) return nb == e.max_nb;
   if (e.xlds == 4) return nb % PW_BPW == 0 && nb <= e.max_nb;
   if (e.xlds == 1 && e.kw > 1) {
     // every K class of the LDS-staged split walks the same number of chunks
@@ -270,7 +270,7 @@ skg_status launch_gemv_mfma(const GemvEntry& v, int64_t K, int nseg, const int64
   // 448 workgroups of two tiles, rather than 384 of two and 128 of one).
   const int64_t passes = (tiles + resident - 1) / resident;
   int64_t grid = (tiles + passes - 1) / passes;
-  if (v.xlds == 3) {
+  if (v.xlds == 3 || v.xlds == 5) {
     // the LDS-ring kernel processes at most MF_DMA_TILES tiles per workgroup
     const int64_t need = (tiles + MF_DMA_TILES - 1) / MF_DMA_TILES;
     if (grid < need) grid = need;
@@ -335,7 +335,7 @@ skg_status launch_gemv_segments(int fmt, int64_t M, int64_t K, int nseg, const i
   if (!v)
     return fail(SKG_E_UNSUPPORTED, "no compiled kernel (or the selected variant does not take K=%lld) for fmt=%d "
                 "M=%lld epi=%d", (long long)K, fmt, (long long)M, epi);
-  if (v->xlds == 2 || v->xlds == 3) return launch_gemv_mfma(*v, K, nseg, Ns, W, x, ys, epi, stream);
+  if (v->xlds == 2 || v->xlds == 3 || v->xlds == 5) return launch_gemv_mfma(*v, K, nseg, Ns, W, x, ys, epi, stream);
   if (v->xlds == 4) return launch_gemv_mfma_pw(*v, K, nseg, Ns, W, x, ys, stream);
   const int wk = wkind_of(fmt);
   GemvArgs a;

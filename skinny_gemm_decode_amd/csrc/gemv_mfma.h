@@ -521,6 +521,231 @@ __device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped blocks for fp16 activations (weight-ring kernel, one fp16 term).
+// With one term, A rows M..15 of the one-block-per-MFMA layout are padding.
+// Here E = 16 / RB blocks share a chain of E v_mfma_f32_16x16x32_f16, RB = 8
+// result rows per block for M <= 8 (E = 2) or RB = 4 for M <= 4 (E = 4):
+// A rows RB e .. RB e + RB - 1 carry the activation rows of block b + e in lane
+// group(s) of that block and zeros elsewhere, and the B operand of lane (g, c)
+// holds only block b + g / (4 / E) of weight row c.  Each MFMA of the chain
+// takes 32 / E elements of every block of the group, so after the chain
+// result row r is block b + r / RB's full dot with activation row r % RB, and
+// every lane's four results belong to one block: one scale per lane and
+// group.  As in the integer version, only the pairing of positions matters:
+// position i of A lane (g, r) meets position i of B lane (g, c).
+//
+// B operand of lane (g, c), chain step j, from the weight unit of its block
+// (q4_0: byte i holds element i in the low and i + 16 in the high nibble;
+// q8_0: plane p holds elements 16 p .. 16 p + 15):
+//   E = 2, h = g % 2: elements 16 j + 8 h + (0..7) (q4_0: bytes 8h..8h+7,
+//     low nibbles for j = 0, high for j = 1; q8_0: plane j, bytes 8h..8h+7);
+//   E = 4: elements 8 j + (0..7) (q4_0: bytes 8 (j % 2) .. +7, low nibbles for
+//     j < 2, high for j >= 2; q8_0: plane j / 2, bytes 8 (j % 2) .. +7).
+// Within the eight, decode_q4_0 / decode_q8_0 leave the slot order
+// 0, 2, 1, 3, 4, 6, 5, 7, and the A operand takes the same order.
+
+// Element offset (in the wave's span of 8 blocks of one staging pass) of
+// chain step j of lane group g for the group gl of the pass.
+template <int E>
+__device__ inline int grp_elem(int gl, int g, int j) {
+  if constexpr (E == 2)
+    return 32 * (2 * gl + (g >> 1)) + 16 * j + 8 * (g & 1);
+  else
+    return 32 * (4 * gl + g) + 8 * j;
+}
+
+// Bytes of one activation row in a staging pass (8 blocks of fp16, plus 16 so
+// that the rows a fragment read takes start 4 banks apart).
+constexpr int GRP_ROW = 8 * 32 * 2 + 16;
+
+// A operands of the wave's BPW blocks in the grouped layout (ap[E gi + j] is
+// chain step j of group gi) and the power-of-two unscale of each lane's
+// result rows; loads, scaling and hooks as mf_stage with one term.  The
+// fp16 rows go through the wave-private area (M x GRP_ROW bytes) one pass of
+// 8 blocks at a time.
+//
+// XT = 2 (E = 2, M <= 4): the activation as two fp16 terms, hi = fp16(x s)
+// and lo = fp16(x s - hi); the eight A rows of a block carry the hi parts of
+// activation rows 0..3, then their lo parts, so lane groups g and g ^ 1 hold
+// the two halves of the same sums.  The area then holds the hi rows, then
+// the lo rows (2 M x GRP_ROW bytes).
+template <int M, int BPW, int E, int XT = 1, class Between, class AfterX>
+__device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ap)[BPW],
+                                    float (&unscale)[4], Between between, AfterX after_x) {
+  static_assert((E == 2 && M <= 8) || (E == 4 && M <= 4), "result rows per block of a group");
+  static_assert(XT == 1 || (E == 2 && M <= 4), "two terms: four hi and four lo rows per block");
+  static_assert(BPW % 8 == 0, "whole staging passes");
+  constexpr int RB = 16 / E;
+  const int g = lane >> 4, c = lane & 15;
+  f32x4 xv[M][BPW / 8];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int e = 0; e < BPW / 8; ++e)
+      xv[m][e] = *reinterpret_cast<const f32x4*>(a.x + size_t(m) * size_t(a.K) + size_t(blk0) * 32 + 256 * e + 4 * lane);
+  __builtin_amdgcn_sched_barrier(0);
+  between();
+  __builtin_amdgcn_sched_barrier(0);
+  float sc[M], us[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < BPW / 8; ++e)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][e].x), fabsf(xv[m][e].y)), fmaxf(fabsf(xv[m][e].z), fabsf(xv[m][e].w))));
+    mx = wave_max(mx);
+    int se = 15 - __builtin_amdgcn_frexp_expf(mx);
+    se = se > 126 ? 126 : (se < -126 ? -126 : se);
+    sc[m] = __builtin_ldexpf(1.0f, se);
+    us[m] = __builtin_ldexpf(1.0f, -se);
+  }
+  // result rows of lane (g, c): activation rows RB (g % (4 / E)) .. + 3 when
+  // RB = 8, rows 0 .. 3 when RB = 4
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = (E == 2 && XT == 1 ? 4 * (g & 1) : 0) + i;
+    unscale[i] = 1.f;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm)
+      if (mm == m) unscale[i] = us[mm];
+  }
+  after_x();
+  // A row c of the lane: area row mrow (two terms: the hi rows, then the lo
+  // rows)
+  const int sub = c % RB;
+  const int mrow = (XT == 2) ? (sub < 4 ? sub : M + sub - 4) : sub;
+  const bool on = (c / RB) == (E == 2 ? (g >> 1) : g) && (XT == 2 ? (sub & 3) : sub) < M;
+  const uint8_t* rd = area + (on ? mrow : 0) * GRP_ROW;
+#pragma unroll
+  for (int e = 0; e < BPW / 8; ++e) {
+    // a wave's LDS accesses complete in order: this pass's writes are seen by
+    // its reads, and its reads finish before the next pass writes
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const f32x4 v = xv[m][e] * sc[m];
+      const f16x2 p01 = __builtin_convertvector((f32x2{v.x, v.y}), f16x2);
+      const f16x2 p23 = __builtin_convertvector((f32x2{v.z, v.w}), f16x2);
+      *reinterpret_cast<u32x2*>(area + m * GRP_ROW + 8 * lane) = u32x2{bits(p01), bits(p23)};
+      if constexpr (XT == 2) {
+        const f16x2 l01 = __builtin_convertvector((f32x2{v.x, v.y} - __builtin_convertvector(p01, f32x2)), f16x2);
+        const f16x2 l23 = __builtin_convertvector((f32x2{v.z, v.w} - __builtin_convertvector(p23, f32x2)), f16x2);
+        *reinterpret_cast<u32x2*>(area + (M + m) * GRP_ROW + 8 * lane) = u32x2{bits(l01), bits(l23)};
+      }
+    }
+#pragma unroll
+    for (int gl = 0; gl < 8 / E; ++gl)
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const u32x4 r = *reinterpret_cast<const u32x4*>(rd + 2 * grp_elem<E>(gl, g, j));
+        // elements 0..7 in order -> slots 0, 2, 1, 3, 4, 6, 5, 7
+        const u32x4 s = {__builtin_amdgcn_perm(r.y, r.x, 0x05040100u), __builtin_amdgcn_perm(r.y, r.x, 0x07060302u),
+                         __builtin_amdgcn_perm(r.w, r.z, 0x05040100u), __builtin_amdgcn_perm(r.w, r.z, 0x07060302u)};
+        ap[E * (e * (8 / E) + gl) + j] = __builtin_bit_cast(f16x8, on ? s : u32x4{0u, 0u, 0u, 0u});
+      }
+  }
+}
+
+// One tile of the weight-ring kernel with grouped blocks (layout above); RR:
+// result rows per lane that can be output rows.  On return every lane holds
+// the full sums of its result rows (lane groups holding the same activation
+// rows have been added).
+template <class G, int BPW, int E, int RR, int XT = 1>
+__device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, int c, const f16x8 (&ap)[BPW],
+                                   float (&acc)[4], uint32_t mlo, uint32_t mhi, uint32_t magic) {
+  uint32_t scw[E == 2 ? BPW / 2 : 1];
+  if constexpr (E == 2) {
+#pragma unroll
+    for (int k = 0; k < BPW / 8; ++k) {
+      const u32x4 s4 =
+          *reinterpret_cast<const u32x4*>(slot + 16 * G::RB + c * G::SRS + mf_swz(int(blk0) / 8 + k, c) * 16);
+      scw[4 * k + 0] = s4.x;
+      scw[4 * k + 1] = s4.y;
+      scw[4 * k + 2] = s4.z;
+      scw[4 * k + 3] = s4.w;
+    }
+  }
+  const uint8_t* row = slot + c * G::RB;
+  const int gb = (E == 2) ? (g >> 1) : g;  // this lane's block within a group
+  const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2 off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  // q4_0 nibbles of two dwords (bytes 0..7 of the eight) as n - 8, low or
+  // high nibbles, in slot order
+  auto q4lo = [&](uint32_t w0, uint32_t w1) {
+    const f16x2 r0 = half2_of((w0 & mlo) | magic) + off, r1 = half2_of(((w0 >> 8) & mlo) | magic) + off;
+    const f16x2 r2 = half2_of((w1 & mlo) | magic) + off, r3 = half2_of(((w1 >> 8) & mlo) | magic) + off;
+    return f16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  };
+  auto q4hi = [&](uint32_t w0, uint32_t w1) {
+    const f16x2 r0 = __builtin_elementwise_fma(half2_of((w0 & mhi) | magic), sixteenth, off16);
+    const f16x2 r1 = __builtin_elementwise_fma(half2_of(((w0 >> 8) & mhi) | magic), sixteenth, off16);
+    const f16x2 r2 = __builtin_elementwise_fma(half2_of((w1 & mhi) | magic), sixteenth, off16);
+    const f16x2 r3 = __builtin_elementwise_fma(half2_of(((w1 >> 8) & mhi) | magic), sixteenth, off16);
+    return f16x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  };
+#pragma unroll
+  for (int gi = 0; gi < BPW / E; ++gi) {
+    const int b = int(blk0) + E * gi + gb;
+    f16x8 bw[E];
+    if constexpr (G::NP == 1) {
+      if constexpr (E == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(b, c) * 16 + 8 * (g & 1));
+        bw[0] = q4lo(u.x, u.y);
+        bw[1] = q4hi(u.x, u.y);
+      } else {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(row + mf_swz(b, c) * 16);
+        bw[0] = q4lo(u.x, u.y);
+        bw[1] = q4lo(u.z, u.w);
+        bw[2] = q4hi(u.x, u.y);
+        bw[3] = q4hi(u.z, u.w);
+      }
+    } else {
+      if constexpr (E == 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(j * G::NB + b, c) * 16 + 8 * (g & 1));
+          bw[j] = decode_q8_0(u.x, u.y);
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const u32x4 u = *reinterpret_cast<const u32x4*>(row + mf_swz(p * G::NB + b, c) * 16);
+          bw[2 * p] = decode_q8_0(u.x, u.y);
+          bw[2 * p + 1] = decode_q8_0(u.z, u.w);
+        }
+      }
+    }
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < E; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[E * gi + j], bw[j], d, 0, 0, 0);
+    // fp16 scale of block b: with E = 2 half gb of word gi of the quads read
+    // above; with E = 4 the lane's own 2-byte read (a word chosen per lane
+    // would go through scratch)
+    uint32_t sw;
+    if constexpr (E == 2)
+      sw = scw[gi] >> (16u * uint32_t(gb));
+    else
+      sw = *reinterpret_cast<const uint16_t*>(slot + 16 * G::RB + c * G::SRS + mf_swz(b >> 3, c) * 16 + (b & 7) * 2);
+    const float s = h2f(sw & 0xFFFFu);
+#pragma unroll
+    for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, d[i], acc[i]);
+  }
+  // lane groups g and g + 2 (and, with E = 4 or two terms, g ^ 1) hold
+  // parts of the same sums
+#pragma unroll
+  for (int i = 0; i < RR; ++i) {
+    uint32_t v = __float_as_uint(acc[i]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    acc[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if constexpr (E == 4 || XT == 2) {
+      v = __float_as_uint(acc[i]);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      acc[i] = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    }
+  }
+}
+
 // LDS bytes of one launch with up to WAVES waves: per-wave activation
 // staging, reused afterwards for the two reduction buffers.
 template <int M, int WAVES, int BPW, int XT, int NR>
@@ -885,12 +1110,15 @@ struct MfDmaGeom {
 
 
 // R: ring slots; ALIAS: the activation staging area shares the last slot
-// (its first load is issued after staging).
-template <int FMT, int M, int XT, int R, bool ALIAS>
+// (its first load is issued after staging); E: 0 for one block per MFMA, or
+// 2 / 4 blocks per chain of MFMAs (fp32 activations as one fp16 term; see
+// mf_stage_grp).
+template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
   static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
   static_assert(!Q8 || XT == 1, "Q8_1 activations: one integer term");
+  static_assert(E == 0 || (!Q8 && (XT == 1 || (E == 2 && M <= 4))), "grouped blocks: fp32 activations");
   static_assert(R >= 2 && R <= MF_DMA_TILES, "ring slots");
   static_assert(R * MfDmaGeom<FMT>::SLOT <= 160 * 1024, "ring exceeds the LDS");
   using G = MfDmaGeom<FMT>;
@@ -901,7 +1129,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr int MSO = (XT * M) | 1;
   constexpr int MSD = (!ALIAS || WAVES * (8 * 4 * MSO * 16) <= G::SLOT) ? MSO : XT * M;
   constexpr int QRP = (!ALIAS || WAVES * M * q8_stage_row<BPW>() * 4 <= G::SLOT) ? q8_stage_row<BPW>() : 9 * BPW;
-  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : 8 * 4 * MSD * 16;
+  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : E > 0 ? XT * M * GRP_ROW : 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   // one LDS array, carved: R slots, the own staging area, the partial sums
   constexpr int RED_BYTES = 2 * WAVES * MF_ROWS * M * 4;
@@ -980,6 +1208,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   if constexpr (Q8)
     mf_stage_q8p<M, BPW, FMT == SKG_Q4_0_Q8_1, QRP>(
         a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da, [] {}, first_dma);
+  else if constexpr (E > 0)
+    mf_stage_grp<M, BPW, E, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, unscale, [] {}, first_dma);
   else
     mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, ksum, [] {},
                               first_dma);
@@ -1023,6 +1253,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (Q8) {
       mf_tile_q8p<G, BPW, (M > 4 ? 4 : M)>(slot, blk0, g, c, aq, da, acc);
+    } else if constexpr (E > 0) {
+      mf_tile_grp<G, BPW, E, RR, XT>(slot, blk0, g, c, ah, acc, mlo, mhi, magic);
     } else {
       MfW<NP, BPW> w;
 #pragma unroll
@@ -1084,6 +1316,20 @@ template <int FMT, int M, int XT, int R, bool ALIAS>
 inline GemvEntry gemv_mfma_dma_entry() {
   GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<FMT, M, XT, R, ALIAS>),
               FMT, M, SKG_EPI_NONE, MF_ROWS, XT, 3, 8, 16};
+  e.lds = 0;
+  e.max_nb = MfDmaGeom<FMT>::NB;
+  e.depth = R;
+  return e;
+}
+
+// The ring kernel with grouped blocks (x_lds = 5): one fp16 activation term
+// with two blocks per MFMA chain for M = 5..8 and four for M <= 4, or two
+// terms (XT = 2, M <= 4) with two blocks per chain.
+template <int FMT, int M, int R, bool ALIAS, int XT = 1>
+inline GemvEntry gemv_mfma_grp_entry() {
+  constexpr int E = (M <= 4 && XT == 1) ? 4 : 2;
+  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<FMT, M, XT, R, ALIAS, E>),
+              FMT, M, SKG_EPI_NONE, MF_ROWS, XT, 5, 8, 16};
   e.lds = 0;
   e.max_nb = MfDmaGeom<FMT>::NB;
   e.depth = R;

@@ -10,7 +10,19 @@ namespace skg {
 // Registered before the vector-ALU instances: the defaults for M = 2..8,
 // measured on MI355X under cold-cache rotation (K = 4096, N = 14336).
 void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
-  // M = 2: the LDS-ring kernel with two fp16 activation terms, 11.35 us
+  // M = 2..8: the LDS-ring kernel with grouped blocks (four per MFMA chain
+  // for M <= 4, two for M = 5..8), two ring slots, the activation as one
+  // fp16 term (one rounding, 2^-11, inside the accuracy bound).  Alternating
+  // timings against the kernels below, us (grouped / previous default):
+  // M = 2 10.25 / 11.35 (ring, two terms), 3 10.64 / 11.57, 4 10.70 /
+  // 11.76, 5 11.12 / 12.44, 6 11.16 / 12.40, 7 11.39 / 11.78, 8 11.39 /
+  // 11.78 (ring, one block per MFMA); three slots: 10.8-12.3.
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 2, false>()})
+    out.push_back(e);
+  // Before them: M = 2: the LDS-ring kernel with two fp16 activation terms, 11.35 us
   // against 11.82 (register-fed, two terms); M = 3 / 5: the ring with one
   // term, 11.61 / 12.41 us against 12.16 / 12.59 (register-fed, two terms)
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_F32, 2, 2, 3, false>());
@@ -37,6 +49,17 @@ void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
 // Registered after them: measurement variants (at M = 1 the vector kernel
 // is faster; the LDS-ring kernel trails the register-fed one at every M).
 void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
+  // grouped blocks with the activation as two fp16 terms (two blocks per
+  // MFMA chain, four hi and four lo rows each), M <= 4
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 2, false, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 2, false, 2>()})
+    out.push_back(e);
+  // grouped blocks with three ring slots
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 3, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 3, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 3, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 3, false>()})
+    out.push_back(e);
   // per-wave weight rings (measurement variants)
   out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 2, 1, 3>());
   out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 2, 2, 3>());

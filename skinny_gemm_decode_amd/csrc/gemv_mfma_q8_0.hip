@@ -12,6 +12,18 @@ namespace skg {
 // two planes per block the two-term activation does not fit the register
 // file beyond M = 2, so these carry the activation as one fp16 term.
 void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
+  // M = 2..8: the LDS-ring kernel with grouped blocks (four per MFMA chain
+  // for M <= 4, two for M = 5..8), two slots, the activation staged in the
+  // second one, one fp16 term.  Alternating timings against the kernels
+  // below, us (grouped / previous default, the ring with one block per
+  // MFMA): M = 2 13.85 / 14.67, 3 14.19 / 15.00, 4 14.23 / 15.02, 5 15.15 /
+  // 15.76, 6 14.97 / 15.58, 7 15.46 / 16.02, 8 15.10 / 15.65.
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q8_0_F32, 2, 2, true>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 3, 2, true>(),
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 4, 2, true>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 5, 2, true>(),
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 6, 2, true>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 7, 2, true>(),
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 8, 2, true>()})
+    out.push_back(e);
+  // Before them:
   // M = 2..8: the LDS-ring kernel (weights copied straight into LDS) with
   // one fp16 activation term (one rounding, 2^-11, inside the accuracy
   // bound) beats the ring with two terms, the register-fed and the vector
@@ -36,6 +48,11 @@ void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
 }
 // Registered after the vector-ALU instances: measurement variants.
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
+  // grouped blocks with the activation as two fp16 terms (two blocks per
+  // MFMA chain, four hi and four lo rows each), M <= 4
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q8_0_F32, 2, 2, true, 2>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 3, 2, true, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 4, 2, true, 2>()})
+    out.push_back(e);
   // per-wave weight rings (measurement variants)
   out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 2, 1, 2>());
   out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 2, 2, 2>());

@@ -212,7 +212,7 @@ def test_variant_registry(skg):
     # the selected record and, after the reset, the first registered one
     for v in vs:
         assert v["depth"] >= 1
-    ring = [v for v in vs if v["x_lds"] == 3]
+    ring = [v for v in vs if v["x_lds"] in (3, 5)]
     assert ring and {v["depth"] for v in ring} <= {2, 3, 4}
     v = ring[-1]
     skg.gemv_select(v)

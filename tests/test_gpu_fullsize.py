@@ -70,10 +70,10 @@ def activation(skg, fmt, M, seed):
 def variants_at_k4096(skg, fmt, M):
     out = []
     for v in skg.gemv_variants():
-        if v["fmt"] != fmt or v["M"] != M or v["epi"] != skg.EPI_NONE or v["x_lds"] not in (2, 3, 4):
+        if v["fmt"] != fmt or v["M"] != M or v["epi"] != skg.EPI_NONE or v["x_lds"] not in (2, 3, 4, 5):
             continue
         nb = K // 32
-        if v["x_lds"] == 3 and v["waves"] * v["kw"] != nb:
+        if v["x_lds"] in (3, 5) and v["waves"] * v["kw"] != nb:
             continue
         if v["x_lds"] in (2, 4) and (nb % v["kw"] or nb > v["waves"] * v["kw"]):
             continue

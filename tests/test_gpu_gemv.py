@@ -114,8 +114,8 @@ def test_every_compiled_variant(skg):
         for v in variants:
             fmt, M, epi = v["fmt"], v["M"], v["epi"]
             N = 320 if epi == skg.EPI_SWIGLU_Q8_1 else 300
-            # the matrix-core variants (x_lds 2, 3, 4) take K % 512 == 0, K <= 4096
-            K = 4096 if v["x_lds"] in (2, 3, 4) else k_of(skg, fmt)
+            # the matrix-core variants (x_lds 2..5) take K % 512 == 0, K <= 4096
+            K = 4096 if v["x_lds"] in (2, 3, 4, 5) else k_of(skg, fmt)
             if v["x_lds"] == 1 and v["kw"] > 1:
                 # every K class walks the same number of chunks, the last one partial
                 K = 32 * (64 * v["j"] * (2 * v["kw"] - 1) + (8 if is_kquant(fmt) else 10))
@@ -310,7 +310,7 @@ MFMA_SHAPES = [(1, 512), (19, 512), (300, 4096), (1000, 1536), (37, 1280), (9000
 
 def mfma_variants(skg, fmt, M):
     return [v for v in skg.gemv_variants()
-            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3, 4)]
+            if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3, 4, 5)]
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3, 4, 7])
@@ -341,7 +341,7 @@ def test_gemv_mfma_shapes(skg, fmt, M):
                 nb = K // 32
                 if nb % v["kw"] or nb > v["waves"] * v["kw"]:
                     continue
-                if v["x_lds"] == 3 and nb != v["waves"] * v["kw"]:
+                if v["x_lds"] in (3, 5) and nb != v["waves"] * v["kw"]:
                     continue  # the LDS-ring variant is compiled for K = 4096 only
                 note(f"variant {v} N={N} K={K}")
                 y, _ = run_gemv(skg, fmt, M, N, K, W, x)
