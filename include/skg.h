@@ -330,9 +330,13 @@ skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream);
  *   ring per wave (each wave copies its own 16-block slice of every tile into
  *   `depth` LDS slots; no workgroup barrier until the last tile); it takes K
  *   with (K / 32) % 16 == 0 and K / 32 <= 128.
+ *   x_lds = 5 names the ring kernel of x_lds = 3 with several quantisation
+ *   blocks per chain of MFMAs (a block-diagonal A operand: four blocks for
+ *   M <= 4 and two for M = 5..8 with j = 1; two blocks of four hi and four lo
+ *   rows with j = 2, M <= 4); compiled for K = 4096 only, like x_lds = 3.
  *   depth: weight tiles in flight (1 for the vector kernels; the prefetch
- *   depth of x_lds = 2, 1 or 2; the ring slots of x_lds = 3, 2 or 3, or 4
- *   for q4_0 weights); 0 matches any depth.
+ *   depth of x_lds = 2, 1 or 2; the ring slots of x_lds = 3 or 5, 2 or 3, or
+ *   4 for q4_0 weights); 0 matches any depth.
  * skg_gemv_variants: writes up to max_entries records of SKG_VARIANT_FIELDS
  *   ints {fmt, M, epi, ro, j, x_lds, waves, kw, depth} to out (host) and
  *   returns the number of compiled variants.  For each (fmt, M, epi) and K

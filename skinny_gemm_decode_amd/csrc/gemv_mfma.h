@@ -565,18 +565,22 @@ constexpr int GRP_ROW = 8 * 32 * 2 + 16;
 // fp16 rows go through the wave-private area (M x GRP_ROW bytes) one pass of
 // 8 blocks at a time.
 //
-// XT = 2 (E = 2, M <= 4): the activation as two fp16 terms, hi = fp16(x s)
-// and lo = fp16(x s - hi); the eight A rows of a block carry the hi parts of
-// activation rows 0..3, then their lo parts, so lane groups g and g ^ 1 hold
-// the two halves of the same sums.  The area then holds the hi rows, then
-// the lo rows (2 M x GRP_ROW bytes).
+// XT = 2 (E = 2): the activation as two fp16 terms, hi = fp16(x s) and lo =
+// fp16(x s - hi).  For M <= 4 the eight A rows of a block carry the hi parts
+// of activation rows 0..3, then their lo parts, so lane groups g and g ^ 1
+// hold the two halves of the same sums; for M = 5..8 the lo parts are a
+// second set of operands (al), a second MFMA chain against the same B
+// operand into the same result.  The area holds the hi rows, then the lo
+// rows (2 M x GRP_ROW bytes).
 template <int M, int BPW, int E, int XT = 1, class Between, class AfterX>
 __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ap)[BPW],
-                                    float (&unscale)[4], Between between, AfterX after_x) {
+                                    f16x8 (&al)[BPW], float (&unscale)[4], Between between, AfterX after_x) {
   static_assert((E == 2 && M <= 8) || (E == 4 && M <= 4), "result rows per block of a group");
-  static_assert(XT == 1 || (E == 2 && M <= 4), "two terms: four hi and four lo rows per block");
+  static_assert(XT == 1 || E == 2, "two terms: two blocks per chain");
   static_assert(BPW % 8 == 0, "whole staging passes");
   constexpr int RB = 16 / E;
+  constexpr bool LOROWS = XT == 2 && M <= 4;  // lo parts in the block's rows 4..7
+  constexpr bool LOCHAIN = XT == 2 && M > 4;  // lo parts as a second chain
   const int g = lane >> 4, c = lane & 15;
   f32x4 xv[M][BPW / 8];
 #pragma unroll
@@ -604,7 +608,7 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
   // RB = 8, rows 0 .. 3 when RB = 4
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = (E == 2 && XT == 1 ? 4 * (g & 1) : 0) + i;
+    const int m = (E == 2 && !LOROWS ? 4 * (g & 1) : 0) + i;
     unscale[i] = 1.f;
 #pragma unroll
     for (int mm = 0; mm < M; ++mm)
@@ -614,9 +618,10 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
   // A row c of the lane: area row mrow (two terms: the hi rows, then the lo
   // rows)
   const int sub = c % RB;
-  const int mrow = (XT == 2) ? (sub < 4 ? sub : M + sub - 4) : sub;
-  const bool on = (c / RB) == (E == 2 ? (g >> 1) : g) && (XT == 2 ? (sub & 3) : sub) < M;
+  const int mrow = LOROWS ? (sub < 4 ? sub : M + sub - 4) : sub;
+  const bool on = (c / RB) == (E == 2 ? (g >> 1) : g) && (LOROWS ? (sub & 3) : sub) < M;
   const uint8_t* rd = area + (on ? mrow : 0) * GRP_ROW;
+  const uint8_t* rdl = area + (on ? M + mrow : 0) * GRP_ROW;  // LOCHAIN
 #pragma unroll
   for (int e = 0; e < BPW / 8; ++e) {
     // a wave's LDS accesses complete in order: this pass's writes are seen by
@@ -637,11 +642,15 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
     for (int gl = 0; gl < 8 / E; ++gl)
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        const u32x4 r = *reinterpret_cast<const u32x4*>(rd + 2 * grp_elem<E>(gl, g, j));
         // elements 0..7 in order -> slots 0, 2, 1, 3, 4, 6, 5, 7
-        const u32x4 s = {__builtin_amdgcn_perm(r.y, r.x, 0x05040100u), __builtin_amdgcn_perm(r.y, r.x, 0x07060302u),
-                         __builtin_amdgcn_perm(r.w, r.z, 0x05040100u), __builtin_amdgcn_perm(r.w, r.z, 0x07060302u)};
-        ap[E * (e * (8 / E) + gl) + j] = __builtin_bit_cast(f16x8, on ? s : u32x4{0u, 0u, 0u, 0u});
+        auto slots = [&](const uint8_t* src) {
+          const u32x4 r = *reinterpret_cast<const u32x4*>(src + 2 * grp_elem<E>(gl, g, j));
+          const u32x4 s = {__builtin_amdgcn_perm(r.y, r.x, 0x05040100u), __builtin_amdgcn_perm(r.y, r.x, 0x07060302u),
+                           __builtin_amdgcn_perm(r.w, r.z, 0x05040100u), __builtin_amdgcn_perm(r.w, r.z, 0x07060302u)};
+          return __builtin_bit_cast(f16x8, on ? s : u32x4{0u, 0u, 0u, 0u});
+        };
+        ap[E * (e * (8 / E) + gl) + j] = slots(rd);
+        if constexpr (LOCHAIN) al[E * (e * (8 / E) + gl) + j] = slots(rdl);
       }
   }
 }
@@ -650,9 +659,11 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
 // result rows per lane that can be output rows.  On return every lane holds
 // the full sums of its result rows (lane groups holding the same activation
 // rows have been added).
-template <class G, int BPW, int E, int RR, int XT = 1>
+// LOCHAIN: the lo operands al are a second chain (two terms, M = 5..8).
+template <class G, int BPW, int E, int RR, bool LOROWS = false, bool LOCHAIN = false>
 __device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, int c, const f16x8 (&ap)[BPW],
-                                   float (&acc)[4], uint32_t mlo, uint32_t mhi, uint32_t magic) {
+                                   const f16x8 (&al)[BPW], float (&acc)[4], uint32_t mlo, uint32_t mhi,
+                                   uint32_t magic) {
   uint32_t scw[E == 2 ? BPW / 2 : 1];
   if constexpr (E == 2) {
 #pragma unroll
@@ -719,6 +730,10 @@ __device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, in
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < E; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[E * gi + j], bw[j], d, 0, 0, 0);
+    if constexpr (LOCHAIN) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[E * gi + j], bw[j], d, 0, 0, 0);
+    }
     // fp16 scale of block b: with E = 2 half gb of word gi of the quads read
     // above; with E = 4 the lane's own 2-byte read (a word chosen per lane
     // would go through scratch)
@@ -738,7 +753,7 @@ __device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, in
     uint32_t v = __float_as_uint(acc[i]);
     const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     acc[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if constexpr (E == 4 || XT == 2) {
+    if constexpr (E == 4 || LOROWS) {
       v = __float_as_uint(acc[i]);
       const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
       acc[i] = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
@@ -1118,7 +1133,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
   static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
   static_assert(!Q8 || XT == 1, "Q8_1 activations: one integer term");
-  static_assert(E == 0 || (!Q8 && (XT == 1 || (E == 2 && M <= 4))), "grouped blocks: fp32 activations");
+  static_assert(E == 0 || (!Q8 && (XT == 1 || E == 2)), "grouped blocks: fp32 activations");
   static_assert(R >= 2 && R <= MF_DMA_TILES, "ring slots");
   static_assert(R * MfDmaGeom<FMT>::SLOT <= 160 * 1024, "ring exceeds the LDS");
   using G = MfDmaGeom<FMT>;
@@ -1209,7 +1224,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     mf_stage_q8p<M, BPW, FMT == SKG_Q4_0_Q8_1, QRP>(
         a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da, [] {}, first_dma);
   else if constexpr (E > 0)
-    mf_stage_grp<M, BPW, E, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, unscale, [] {}, first_dma);
+    mf_stage_grp<M, BPW, E, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {},
+                                first_dma);
   else
     mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, ksum, [] {},
                               first_dma);
@@ -1254,7 +1270,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if constexpr (Q8) {
       mf_tile_q8p<G, BPW, (M > 4 ? 4 : M)>(slot, blk0, g, c, aq, da, acc);
     } else if constexpr (E > 0) {
-      mf_tile_grp<G, BPW, E, RR, XT>(slot, blk0, g, c, ah, acc, mlo, mhi, magic);
+      constexpr bool LOROWS = XT == 2 && M <= 4, LOCHAIN = XT == 2 && !LOROWS;
+      mf_tile_grp<G, BPW, E, RR, LOROWS, LOCHAIN>(slot, blk0, g, c, ah, al, acc, mlo, mhi, magic);
     } else {
       MfW<NP, BPW> w;
 #pragma unroll
@@ -1324,7 +1341,7 @@ inline GemvEntry gemv_mfma_dma_entry() {
 
 // The ring kernel with grouped blocks (x_lds = 5): one fp16 activation term
 // with two blocks per MFMA chain for M = 5..8 and four for M <= 4, or two
-// terms (XT = 2, M <= 4) with two blocks per chain.
+// terms (XT = 2) with two blocks per chain.
 template <int FMT, int M, int R, bool ALIAS, int XT = 1>
 inline GemvEntry gemv_mfma_grp_entry() {
   constexpr int E = (M <= 4 && XT == 1) ? 4 : 2;

@@ -50,9 +50,12 @@ void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
 // is faster; the LDS-ring kernel trails the register-fed one at every M).
 void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
   // grouped blocks with the activation as two fp16 terms (two blocks per
-  // MFMA chain, four hi and four lo rows each), M <= 4
+  // MFMA chain; four hi and four lo rows per block for M <= 4, a second
+  // chain of lo operands for M = 5..8)
   for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 2, false, 2>(),
-                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 2, false, 2>()})
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 2, false, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 2, false, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 2, false, 2>()})
     out.push_back(e);
   // grouped blocks with three ring slots
   for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 3, false>(),

@@ -49,9 +49,12 @@ void register_gemv_mfma_q8_0(std::vector<GemvEntry>& out) {
 // Registered after the vector-ALU instances: measurement variants.
 void register_gemv_mfma_q8_0_alt(std::vector<GemvEntry>& out) {
   // grouped blocks with the activation as two fp16 terms (two blocks per
-  // MFMA chain, four hi and four lo rows each), M <= 4
+  // MFMA chain; four hi and four lo rows per block for M <= 4, a second
+  // chain of lo operands for M = 5..8)
   for (auto e : {gemv_mfma_grp_entry<SKG_Q8_0_F32, 2, 2, true, 2>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 3, 2, true, 2>(),
-                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 4, 2, true, 2>()})
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 4, 2, true, 2>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 5, 2, true, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 6, 2, true, 2>(), gemv_mfma_grp_entry<SKG_Q8_0_F32, 7, 2, true, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q8_0_F32, 8, 2, true, 2>()})
     out.push_back(e);
   // per-wave weight rings (measurement variants)
   out.push_back(gemv_mfma_pw_entry<SKG_Q8_0_F32, 2, 1, 2>());
