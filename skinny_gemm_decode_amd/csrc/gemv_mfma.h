@@ -435,10 +435,14 @@ __device__ inline int mf_swz(int j, int r) { return j ^ (r & 15); }
 
 // A operands of the wave's BPW / 2 block pairs in that layout, and the
 // activation scales of the four result rows of each lane (zero for rows >=
-// M; over 16 for q4_0, whose B codes are 16 (code - 8)).
-template <int M, int BPW, bool Q4, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
+// M; over 16 for q4_0, whose B codes are 16 (code - 8)) and, for q4_K, the
+// activation block sums s = dA sum(q) of those rows (the min term).
+// WK: the weight kind (WK_Q4_0, WK_Q8_0 or WK_Q4_K; q4_K codes are q4_0's
+// nibbles without the offset).
+template <int M, int BPW, int WK, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
 __device__ inline void mf_stage_q8p(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane, i32x4 (&aq)[BPW / 2],
-                                    f32x4 (&da)[BPW / 2], Between between, AfterX after_x) {
+                                    f32x4 (&da)[BPW / 2], f32x4 (&sa)[BPW / 2], Between between, AfterX after_x) {
+  constexpr bool Q4 = WK == WK_Q4_0 || WK == WK_Q4_K;
   static_assert(M <= 8 && BPW % 2 == 0, "two blocks of eight rows");
   mf_copy_q8<M, BPW, RWP>(a, area, blk0, lane, between);
   after_x();
@@ -447,7 +451,7 @@ __device__ inline void mf_stage_q8p(const MfArgs& a, uint32_t* area, uint32_t bl
   const int m = c & 7;
   const bool on = (c >> 3) == e && m < M;
   const uint32_t* row = area + (m < M ? m : 0) * RWP;
-  constexpr float WS = Q4 ? 0.0625f : 1.0f;
+  constexpr float WS = WK == WK_Q4_0 ? 0.0625f : 1.0f;
 #pragma unroll
   for (int p = 0; p < BPW / 2; ++p) {
     const uint32_t* blk = row + (2 * p + e) * 9;
@@ -465,13 +469,16 @@ __device__ inline void mf_stage_q8p(const MfArgs& a, uint32_t* area, uint32_t bl
       for (int i = 0; i < 4; ++i) v[i] = blk[1 + 4 * h + i];
     }
     aq[p] = on ? i32x4{int(v[0]), int(v[1]), int(v[2]), int(v[3])} : i32x4{0, 0, 0, 0};
-    float d4[4];
+    float d4[4], s4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int mo = 4 * h + i;
-      d4[i] = (mo < M) ? h2f(area[(mo < M ? mo : 0) * RWP + (2 * p + e) * 9] & 0xFFFFu) * WS : 0.f;
+      const uint32_t ds = area[(mo < M ? mo : 0) * RWP + (2 * p + e) * 9];
+      d4[i] = (mo < M) ? h2f(ds & 0xFFFFu) * WS : 0.f;
+      s4[i] = (mo < M) ? h2f(ds >> 16) : 0.f;
     }
     da[p] = f32x4{d4[0], d4[1], d4[2], d4[3]};
+    sa[p] = f32x4{s4[0], s4[1], s4[2], s4[3]};
   }
 }
 
@@ -479,10 +486,12 @@ __device__ inline void mf_stage_q8p(const MfArgs& a, uint32_t* area, uint32_t bl
 // slot: the tile's LDS slot (rows of RB payload bytes, mf_swz chunk order,
 // then 16 rows of SRS scale bytes); RR: result rows per lane that can be
 // output rows.  On return every lane holds the full sums of rows 4 (g % 2) ..
-// 4 (g % 2) + 3 of column c.
-template <class G, int BPW, int RR>
+// 4 (g % 2) + 3 of column c.  KQ (q4_K): the scale bytes of a row are its 16
+// super-block headers {d, dmin, 12 scale bytes}, the codes enter as 0..15,
+// and block j of a super-block adds d sc_j dA S - dmin m_j s.
+template <class G, int BPW, int RR, bool KQ = false>
 __device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, int c, const i32x4 (&aq)[BPW / 2],
-                                   const f32x4 (&da)[BPW / 2], float (&acc)[4]) {
+                                   const f32x4 (&da)[BPW / 2], const f32x4 (&sa)[BPW / 2], float (&acc)[4]) {
   uint32_t scw[BPW / 2];
 #pragma unroll
   for (int k = 0; k < BPW / 8; ++k) {
@@ -499,7 +508,12 @@ __device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, in
   for (int p = 0; p < BPW / 2; ++p) {
     const int b = int(blk0) + 2 * p + e;
     i32x4 bv;
-    if constexpr (G::NP == 1) {
+    if constexpr (KQ) {
+      // codes 0..15 as int8
+      const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(b, c) * 16 + 8 * h);
+      bv = i32x4{int(u.x & 0x0F0F0F0Fu), int((u.x >> 4) & 0x0F0F0F0Fu), int(u.y & 0x0F0F0F0Fu),
+                 int((u.y >> 4) & 0x0F0F0F0Fu)};
+    } else if constexpr (G::NP == 1) {
       // 16 (code - 8) as int8: the nibble moved to the high half of its
       // byte, sign bit flipped
       const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(b, c) * 16 + 8 * h);
@@ -509,9 +523,21 @@ __device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, in
       bv = *reinterpret_cast<const i32x4*>(row + mf_swz(h * G::NB + b, c) * 16);
     }
     const i32x4 sdot = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[p], bv, i32x4{0, 0, 0, 0}, 0, 0, 0);
-    const float s = h2f(scw[p] >> sh);
+    if constexpr (KQ) {
+      // header of super-block (2 p + e) / 8 of the wave's span (= p / 4),
+      // sub-block (2 p + e) % 8; both products exact in fp32
+      const int hb = 4 * (p >> 2);
+      uint32_t sc, mn;
+      q4_K_sc_m(scw[hb + 1], scw[hb + 2], scw[hb + 3], uint32_t((2 * p + e) & 7), sc, mn);
+      const float aw = h2f(scw[hb] & 0xFFFFu) * float(sc);
+      const float bw = h2f(scw[hb] >> 16) * float(mn);
 #pragma unroll
-    for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, da[p][i] * float(sdot[i]), acc[i]);
+      for (int i = 0; i < RR; ++i) acc[i] = fmaf(aw, da[p][i] * float(sdot[i]), fmaf(-bw, sa[p][i], acc[i]));
+    } else {
+      const float s = h2f(scw[p] >> sh);
+#pragma unroll
+      for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, da[p][i] * float(sdot[i]), acc[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < RR; ++i) {
@@ -1130,8 +1156,9 @@ struct MfDmaGeom {
 // mf_stage_grp).
 template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
-  constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1);
+  constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1 || FMT == SKG_Q4_K_Q8_1);
   static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
+  constexpr int WKQ = FMT == SKG_Q4_0_Q8_1 ? WK_Q4_0 : FMT == SKG_Q4_K_Q8_1 ? WK_Q4_K : WK_Q8_0;
   static_assert(!Q8 || XT == 1, "Q8_1 activations: one integer term");
   static_assert(E == 0 || (!Q8 && (XT == 1 || E == 2)), "grouped blocks: fp32 activations");
   static_assert(R >= 2 && R <= MF_DMA_TILES, "ring slots");
@@ -1207,7 +1234,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   uint8_t* stage_area = ALIAS ? (R == 4 ? slot3 : R == 3 ? slot2 : slot1) : stage_own;
   f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
   i32x4 aq[Q8 ? BPW / 2 : 1];
-  f32x4 da[Q8 ? BPW / 2 : 1];
+  f32x4 da[Q8 ? BPW / 2 : 1], sa[Q8 ? BPW / 2 : 1];
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};
   f16x8 ksum = {};  // unused: no q4_K here
   // The first R tiles' transfers are unconditional (a workgroup with fewer
@@ -1221,8 +1248,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if constexpr (R == 4 && !ALIAS) dma_tile(slot3, clamp(3));
   };
   if constexpr (Q8)
-    mf_stage_q8p<M, BPW, FMT == SKG_Q4_0_Q8_1, QRP>(
-        a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq, da, [] {}, first_dma);
+    mf_stage_q8p<M, BPW, WKQ, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane,
+                                   aq, da, sa, [] {}, first_dma);
   else if constexpr (E > 0)
     mf_stage_grp<M, BPW, E, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {},
                                 first_dma);
@@ -1268,7 +1295,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   auto run = [&](uint8_t* slot, int i) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (Q8) {
-      mf_tile_q8p<G, BPW, (M > 4 ? 4 : M)>(slot, blk0, g, c, aq, da, acc);
+      mf_tile_q8p<G, BPW, (M > 4 ? 4 : M), FMT == SKG_Q4_K_Q8_1>(slot, blk0, g, c, aq, da, sa, acc);
     } else if constexpr (E > 0) {
       constexpr bool LOROWS = XT == 2 && M <= 4, LOCHAIN = XT == 2 && !LOROWS;
       mf_tile_grp<G, BPW, E, RR, LOROWS, LOCHAIN>(slot, blk0, g, c, ah, al, acc, mlo, mhi, magic);

@@ -11,6 +11,17 @@
 
 namespace skg {
 void register_gemv_q4_K(std::vector<GemvEntry>& out) {
+  // q4_K x Q8_1 at M = 3..8: the integer matrix cores with the weights
+  // streamed into an LDS ring (two sub-blocks per 64-deep MFMA, the d sc_j
+  // scaling and the dmin m_j s min term per sub-block on the vector ALU;
+  // K = 4096 only, other K fall through to the vector kernels below).
+  // Alternating timings, us (ring / vector default before): M = 3 10.10 /
+  // 10.38, 4 10.49 / 11.67, 5 10.35 / 13.46, 6 10.54 / 15.05, 7 10.56 /
+  // 16.51, 8 10.53 / 17.87.
+  for (auto e : {gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 3, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 4, 1, 2, true>(),
+                 gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 5, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 6, 1, 2, true>(),
+                 gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 7, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 8, 1, 2, true>()})
+    out.push_back(e);
   // q4_K x fp32 at M = 2..8 on the matrix cores (K a multiple of 256 up to
   // 4096; others fall through to the vector kernels below): the activation
   // as two fp16 terms at M = 2, 3 (13.01 / 14.11 us against 13.28 / 17.62 for
@@ -87,5 +98,8 @@ void register_gemv_q4_K(std::vector<GemvEntry>& out) {
   SKG_MFK(8, 8, 16, 1, 1)
   SKG_MFK(8, 8, 16, 1, 2)
   SKG_MFK(8, 8, 16, 2, 1)
+  // q4_K x Q8_1 on the integer matrix cores at M = 2: slower than the
+  // vector kernel (9.50 against 9.30 us)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 2, 1, 2, true>());
 }
 }  // namespace skg
