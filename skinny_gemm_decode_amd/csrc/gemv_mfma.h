@@ -598,9 +598,16 @@ constexpr int GRP_ROW = 8 * 32 * 2 + 16;
 // second set of operands (al), a second MFMA chain against the same B
 // operand into the same result.  The area holds the hi rows, then the lo
 // rows (2 M x GRP_ROW bytes).
-template <int M, int BPW, int E, int XT = 1, class Between, class AfterX>
+//
+// KQ (q4_K): ks[gi] receives the block sums S of the activation values the
+// MFMAs see (hi + lo with two terms) for the lane's result rows of its block
+// in group gi (the min term -dmin m_j S), zero where a result row is not an
+// activation row or (lo rows of the M <= 4 two-term layout) would count it
+// twice; the sums go through M x BPW floats after the staging rows.
+template <int M, int BPW, int E, int XT = 1, bool KQ = false, class Between, class AfterX>
 __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ap)[BPW],
-                                    f16x8 (&al)[BPW], float (&unscale)[4], Between between, AfterX after_x) {
+                                    f16x8 (&al)[BPW], float (&unscale)[4], f32x4 (&ks)[BPW / E], Between between,
+                                    AfterX after_x) {
   static_assert((E == 2 && M <= 8) || (E == 4 && M <= 4), "result rows per block of a group");
   static_assert(XT == 1 || E == 2, "two terms: two blocks per chain");
   static_assert(BPW % 8 == 0, "whole staging passes");
@@ -658,10 +665,21 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
       const f16x2 p01 = __builtin_convertvector((f32x2{v.x, v.y}), f16x2);
       const f16x2 p23 = __builtin_convertvector((f32x2{v.z, v.w}), f16x2);
       *reinterpret_cast<u32x2*>(area + m * GRP_ROW + 8 * lane) = u32x2{bits(p01), bits(p23)};
+      float part = (float(p01[0]) + float(p01[1])) + (float(p23[0]) + float(p23[1]));
       if constexpr (XT == 2) {
         const f16x2 l01 = __builtin_convertvector((f32x2{v.x, v.y} - __builtin_convertvector(p01, f32x2)), f16x2);
         const f16x2 l23 = __builtin_convertvector((f32x2{v.z, v.w} - __builtin_convertvector(p23, f32x2)), f16x2);
         *reinterpret_cast<u32x2*>(area + (M + m) * GRP_ROW + 8 * lane) = u32x2{bits(l01), bits(l23)};
+        part += (float(l01[0]) + float(l01[1])) + (float(l23[0]) + float(l23[1]));
+      }
+      if constexpr (KQ) {
+        // the 8 lanes of a block (lane / 8) add their shares; lane 8 bl keeps
+        // row m's sum of block 8 e + bl
+        part += dpp_f<SKG_DPP_QUAD_XOR1>(part);
+        part += dpp_f<SKG_DPP_QUAD_XOR2>(part);
+        part += dpp_f<SKG_DPP_ROW_HALF_MIRROR>(part);
+        if ((lane & 7) == 0)
+          reinterpret_cast<float*>(area + XT * M * GRP_ROW)[m * BPW + 8 * e + (lane >> 3)] = part;
       }
     }
 #pragma unroll
@@ -679,6 +697,23 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
         if constexpr (LOCHAIN) al[E * (e * (8 / E) + gl) + j] = slots(rdl);
       }
   }
+  if constexpr (KQ) {
+    // the wave's own LDS writes are visible to its later reads
+    const float* sums = reinterpret_cast<const float*>(area + XT * M * GRP_ROW);
+    const int gb = (E == 2) ? (g >> 1) : g;
+    const int base = (E == 2 && !LOROWS) ? 4 * (g & 1) : 0;
+    const bool live = !(LOROWS && (g & 1));
+#pragma unroll
+    for (int gi = 0; gi < BPW / E; ++gi) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = base + i;
+        v[i] = (live && m < M) ? sums[(m < M ? m : 0) * BPW + E * gi + gb] : 0.f;
+      }
+      ks[gi] = f32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
 }
 
 // One tile of the weight-ring kernel with grouped blocks (layout above); RR:
@@ -686,12 +721,16 @@ __device__ inline void mf_stage_grp(const MfArgs& a, uint8_t* area, uint32_t blk
 // the full sums of its result rows (lane groups holding the same activation
 // rows have been added).
 // LOCHAIN: the lo operands al are a second chain (two terms, M = 5..8).
-template <class G, int BPW, int E, int RR, bool LOROWS = false, bool LOCHAIN = false>
+// KQ (q4_K): the slot's scale rows hold the 16-byte super-block headers; the
+// codes enter as the exact fp16 subnormals c 2^-24 (one AND per pair, no
+// offset to cancel), and sub-block j of a super-block adds
+// 2^24 d sc_j D - dmin m_j S with S the block sums of ks.
+template <class G, int BPW, int E, int RR, bool LOROWS = false, bool LOCHAIN = false, bool KQ = false>
 __device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, int c, const f16x8 (&ap)[BPW],
-                                   const f16x8 (&al)[BPW], float (&acc)[4], uint32_t mlo, uint32_t mhi,
-                                   uint32_t magic) {
-  uint32_t scw[E == 2 ? BPW / 2 : 1];
-  if constexpr (E == 2) {
+                                   const f16x8 (&al)[BPW], const f32x4 (&ks)[BPW / E], float (&acc)[4], uint32_t mlo,
+                                   uint32_t mhi, uint32_t magic) {
+  uint32_t scw[(E == 2 || KQ) ? BPW / 2 : 1];
+  if constexpr (E == 2 || KQ) {
 #pragma unroll
     for (int k = 0; k < BPW / 8; ++k) {
       const u32x4 s4 =
@@ -725,7 +764,19 @@ __device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, in
   for (int gi = 0; gi < BPW / E; ++gi) {
     const int b = int(blk0) + E * gi + gb;
     f16x8 bw[E];
-    if constexpr (G::NP == 1) {
+    if constexpr (KQ) {
+      if constexpr (E == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(b, c) * 16 + 8 * (g & 1));
+        bw[0] = __builtin_bit_cast(f16x8, u32x4{u.x & mlo, (u.x >> 8) & mlo, u.y & mlo, (u.y >> 8) & mlo});
+        bw[1] = __builtin_bit_cast(f16x8, u32x4{(u.x >> 4) & mlo, (u.x >> 12) & mlo, (u.y >> 4) & mlo, (u.y >> 12) & mlo});
+      } else {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(row + mf_swz(b, c) * 16);
+        bw[0] = __builtin_bit_cast(f16x8, u32x4{u.x & mlo, (u.x >> 8) & mlo, u.y & mlo, (u.y >> 8) & mlo});
+        bw[1] = __builtin_bit_cast(f16x8, u32x4{u.z & mlo, (u.z >> 8) & mlo, u.w & mlo, (u.w >> 8) & mlo});
+        bw[2] = __builtin_bit_cast(f16x8, u32x4{(u.x >> 4) & mlo, (u.x >> 12) & mlo, (u.y >> 4) & mlo, (u.y >> 12) & mlo});
+        bw[3] = __builtin_bit_cast(f16x8, u32x4{(u.z >> 4) & mlo, (u.z >> 12) & mlo, (u.w >> 4) & mlo, (u.w >> 12) & mlo});
+      }
+    } else if constexpr (G::NP == 1) {
       if constexpr (E == 2) {
         const uint2 u = *reinterpret_cast<const uint2*>(row + mf_swz(b, c) * 16 + 8 * (g & 1));
         bw[0] = q4lo(u.x, u.y);
@@ -760,17 +811,29 @@ __device__ inline void mf_tile_grp(const uint8_t* slot, uint32_t blk0, int g, in
 #pragma unroll
       for (int j = 0; j < E; ++j) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[E * gi + j], bw[j], d, 0, 0, 0);
     }
-    // fp16 scale of block b: with E = 2 half gb of word gi of the quads read
-    // above; with E = 4 the lane's own 2-byte read (a word chosen per lane
-    // would go through scratch)
-    uint32_t sw;
-    if constexpr (E == 2)
-      sw = scw[gi] >> (16u * uint32_t(gb));
-    else
-      sw = *reinterpret_cast<const uint16_t*>(slot + 16 * G::RB + c * G::SRS + mf_swz(b >> 3, c) * 16 + (b & 7) * 2);
-    const float s = h2f(sw & 0xFFFFu);
+    if constexpr (KQ) {
+      // header of super-block (E gi + gb) / 8 of the span (E gi / 8: the
+      // group never straddles two), sub-block (E gi + gb) % 8
+      const int hb = 4 * ((E * gi) >> 3);
+      uint32_t sc, mn;
+      q4_K_sc_m(scw[hb + 1], scw[hb + 2], scw[hb + 3], uint32_t((E * gi + gb) & 7), sc, mn);
+      const float aw = h2f(scw[hb] & 0xFFFFu) * float(sc) * 16777216.0f;  // exact: 2^24 d sc_j
+      const float bw = h2f(scw[hb] >> 16) * float(mn);
 #pragma unroll
-    for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, d[i], acc[i]);
+      for (int i = 0; i < RR; ++i) acc[i] = fmaf(aw, d[i], fmaf(-bw, ks[gi][i], acc[i]));
+    } else {
+      // fp16 scale of block b: with E = 2 half gb of word gi of the quads
+      // read above; with E = 4 the lane's own 2-byte read (a word chosen per
+      // lane would go through scratch)
+      uint32_t sw;
+      if constexpr (E == 2)
+        sw = scw[gi] >> (16u * uint32_t(gb));
+      else
+        sw = *reinterpret_cast<const uint16_t*>(slot + 16 * G::RB + c * G::SRS + mf_swz(b >> 3, c) * 16 + (b & 7) * 2);
+      const float s = h2f(sw & 0xFFFFu);
+#pragma unroll
+      for (int i = 0; i < RR; ++i) acc[i] = fmaf(s, d[i], acc[i]);
+    }
   }
   // lane groups g and g + 2 (and, with E = 4 or two terms, g ^ 1) hold
   // parts of the same sums
@@ -1157,7 +1220,10 @@ struct MfDmaGeom {
 template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1 || FMT == SKG_Q4_K_Q8_1);
-  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || Q8, "quantised weight formats only");
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || FMT == SKG_Q4_K_F32 || Q8,
+                "quantised weight formats only");
+  constexpr bool KQF = FMT == SKG_Q4_K_F32;
+  static_assert(!KQF || E > 0, "q4_K x fp32: grouped blocks only");
   constexpr int WKQ = FMT == SKG_Q4_0_Q8_1 ? WK_Q4_0 : FMT == SKG_Q4_K_Q8_1 ? WK_Q4_K : WK_Q8_0;
   static_assert(!Q8 || XT == 1, "Q8_1 activations: one integer term");
   static_assert(E == 0 || (!Q8 && (XT == 1 || E == 2)), "grouped blocks: fp32 activations");
@@ -1171,7 +1237,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr int MSO = (XT * M) | 1;
   constexpr int MSD = (!ALIAS || WAVES * (8 * 4 * MSO * 16) <= G::SLOT) ? MSO : XT * M;
   constexpr int QRP = (!ALIAS || WAVES * M * q8_stage_row<BPW>() * 4 <= G::SLOT) ? q8_stage_row<BPW>() : 9 * BPW;
-  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : E > 0 ? XT * M * GRP_ROW : 8 * 4 * MSD * 16;
+  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : E > 0 ? XT * M * GRP_ROW + (KQF ? M * BPW * 4 : 0) : 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   // one LDS array, carved: R slots, the own staging area, the partial sums
   constexpr int RED_BYTES = 2 * WAVES * MF_ROWS * M * 4;
@@ -1235,6 +1301,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
   i32x4 aq[Q8 ? BPW / 2 : 1];
   f32x4 da[Q8 ? BPW / 2 : 1], sa[Q8 ? BPW / 2 : 1];
+  f32x4 ks[E > 0 ? BPW / (E > 0 ? E : 1) : 1];  // q4_K block sums (grouped kernel)
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};
   f16x8 ksum = {};  // unused: no q4_K here
   // The first R tiles' transfers are unconditional (a workgroup with fewer
@@ -1251,8 +1318,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     mf_stage_q8p<M, BPW, WKQ, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane,
                                    aq, da, sa, [] {}, first_dma);
   else if constexpr (E > 0)
-    mf_stage_grp<M, BPW, E, XT>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, [] {},
-                                first_dma);
+    mf_stage_grp<M, BPW, E, XT, KQF>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, ks,
+                                     [] {}, first_dma);
   else
     mf_stage<M, BPW, XT, MSD>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ah, al, unscale, ksum, [] {},
                               first_dma);
@@ -1298,7 +1365,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       mf_tile_q8p<G, BPW, (M > 4 ? 4 : M), FMT == SKG_Q4_K_Q8_1>(slot, blk0, g, c, aq, da, sa, acc);
     } else if constexpr (E > 0) {
       constexpr bool LOROWS = XT == 2 && M <= 4, LOCHAIN = XT == 2 && !LOROWS;
-      mf_tile_grp<G, BPW, E, RR, LOROWS, LOCHAIN>(slot, blk0, g, c, ah, al, acc, mlo, mhi, magic);
+      mf_tile_grp<G, BPW, E, RR, LOROWS, LOCHAIN, KQF>(slot, blk0, g, c, ah, al, ks, acc, mlo, mhi, magic);
     } else {
       MfW<NP, BPW> w;
 #pragma unroll

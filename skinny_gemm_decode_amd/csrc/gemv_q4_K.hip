@@ -11,6 +11,20 @@
 
 namespace skg {
 void register_gemv_q4_K(std::vector<GemvEntry>& out) {
+  // q4_K x fp32 at M = 2..8: the LDS-ring kernel with grouped blocks (four
+  // sub-blocks per MFMA chain for M <= 4, two for M = 5..8; codes as exact
+  // fp16 subnormals, d sc_j per sub-block, the min term from block sums of
+  // the staged activation), the activation as one fp16 term; K = 4096 only,
+  // other K take the register-fed kernels below.  Alternating timings, us
+  // (grouped / previous default, register-fed): M = 2 10.05 / 12.61 (two
+  // terms), 3 10.51 / 13.92 (two terms), 4 10.69 / 13.04, 5 11.97 / 13.89,
+  // 6 12.03 / 14.04, 7 12.46 / 14.42, 8 12.63 / 14.48; grouped with two
+  // terms 10.73 / 11.69 / 12.40 / 13.53 / 13.68 / 14.37 / 14.44.
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_K_F32, 2, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 3, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 5, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 6, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 7, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 8, 2, false>()})
+    out.push_back(e);
   // q4_K x Q8_1 at M = 3..8: the integer matrix cores with the weights
   // streamed into an LDS ring (two sub-blocks per 64-deep MFMA, the d sc_j
   // scaling and the dmin m_j s min term per sub-block on the vector ALU;
@@ -98,6 +112,13 @@ void register_gemv_q4_K(std::vector<GemvEntry>& out) {
   SKG_MFK(8, 8, 16, 1, 1)
   SKG_MFK(8, 8, 16, 1, 2)
   SKG_MFK(8, 8, 16, 2, 1)
+  // q4_K x fp32 on the LDS-ring kernel with grouped blocks, two fp16
+  // activation terms (measurement variants)
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_K_F32, 2, 2, false, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 3, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 2, false, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 5, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 6, 2, false, 2>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 7, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 8, 2, false, 2>()})
+    out.push_back(e);
   // q4_K x Q8_1 on the integer matrix cores at M = 2: slower than the
   // vector kernel (9.50 against 9.30 us)
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 2, 1, 2, true>());
