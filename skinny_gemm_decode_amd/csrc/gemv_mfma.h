@@ -548,6 +548,123 @@ __device__ inline void mf_tile_q8p(const uint8_t* slot, uint32_t blk0, int g, in
 }
 
 // ---------------------------------------------------------------------------
+// q6_K weights against Q8_1 activations (weight-ring kernel).  A q6_K block
+// scales each 16-element half by its own int8 scale, so a block's two halves
+// must not meet in one result row: the 64-deep integer MFMA takes two blocks
+// as four block-halves, lane group g holding half g % 2 of block b + g / 2
+// (16 codes), and A rows 4 g .. 4 g + 3 carry activation rows 0..3 (a second
+// chain: rows 4..7) of that block-half in group g only.  Result row r is then
+// block-half r / 4's dot with activation row r % 4, and each lane's four
+// results share one weight scale d sc.  The codes enter as 0..63; the -32 of
+// the format is a chained MFMA against a constant B of int8 -32, so
+// sum (q - 32) qa is exact in int32 with no vector-ALU work.  The four lane
+// groups hold parts of the same sums, added once per tile.
+
+// A operands (two chains for M > 4) and the activation scales of each lane's
+// four result rows (zero for rows >= M) of the wave's BPW / 2 block pairs.
+template <int M, int BPW, int RWP = q8_stage_row<BPW>(), class Between, class AfterX>
+__device__ inline void mf_stage_q6q8(const MfArgs& a, uint32_t* area, uint32_t blk0, int lane,
+                                     i32x4 (&aq)[2][BPW / 2], f32x4 (&da)[2][BPW / 2], Between between,
+                                     AfterX after_x) {
+  static_assert(M <= 8 && BPW % 2 == 0, "two chains of four rows");
+  mf_copy_q8<M, BPW, RWP>(a, area, blk0, lane, between);
+  after_x();
+  const int g = lane >> 4, c = lane & 15;
+  const int h = g & 1, e = g >> 1;
+#pragma unroll
+  for (int ch = 0; ch < (M > 4 ? 2 : 1); ++ch) {
+    const int m = (c & 3) + 4 * ch;
+    const bool on = (c >> 2) == g && m < M;
+    const uint32_t* row = area + (on ? m : 0) * RWP;
+#pragma unroll
+    for (int p = 0; p < BPW / 2; ++p) {
+      // elements 16 h .. 16 h + 15 of the block: dwords 1 + 4 h .. 4 + 4 h
+      const uint32_t* blk = row + (2 * p + e) * 9 + 1 + 4 * h;
+      aq[ch][p] = on ? i32x4{int(blk[0]), int(blk[1]), int(blk[2]), int(blk[3])} : i32x4{0, 0, 0, 0};
+      float d4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mo = 4 * ch + i;
+        d4[i] = (mo < M) ? h2f(area[(mo < M ? mo : 0) * RWP + (2 * p + e) * 9] & 0xFFFFu) : 0.f;
+      }
+      da[ch][p] = f32x4{d4[0], d4[1], d4[2], d4[3]};
+    }
+  }
+}
+
+// One tile against Q8_1 activations in that layout.  The slot holds per row
+// the low units (16 bytes per block, q4_0 nibble order) then the high units
+// (8 bytes per block), in mf_swz chunk order; then 16 rows of int8 scale
+// pairs; then the rows' fp16 super-block d (G::DOFF, 32 bytes per row).  On
+// return every lane holds the full sums of activation rows 0..3 (acc[0]) and
+// 4..7 (acc[1]) of column c.
+template <class G, int BPW, int M>
+__device__ inline void mf_tile_q6q8(const uint8_t* slot, uint32_t blk0, int g, int c, const i32x4 (&aq)[2][BPW / 2],
+                                    const f32x4 (&da)[2][BPW / 2], float (&acc)[2][4]) {
+  constexpr int NCH = M > 4 ? 2 : 1;
+  constexpr int RR0 = M < 4 ? M : 4;
+  uint32_t scw[BPW / 2];
+#pragma unroll
+  for (int k = 0; k < BPW / 8; ++k) {
+    const u32x4 s4 = *reinterpret_cast<const u32x4*>(slot + 16 * G::RB + c * G::SRS + mf_swz(int(blk0) / 8 + k, c) * 16);
+    scw[4 * k + 0] = s4.x;
+    scw[4 * k + 1] = s4.y;
+    scw[4 * k + 2] = s4.z;
+    scw[4 * k + 3] = s4.w;
+  }
+  static_assert(BPW == 16, "two super-blocks per wave span");
+  // d of the span's two super-blocks (row c)
+  const uint32_t dw = *reinterpret_cast<const uint32_t*>(slot + G::DOFF + c * 32 + (int(blk0) / 8) * 2);
+  const float dsb[2] = {h2f(dw & 0xFFFFu), h2f(dw >> 16)};
+  const uint8_t* row = slot + c * G::RB;
+  const int h = g & 1, e = g >> 1;
+  // per-lane shifts: the half's nibbles, and where its top two bits sit in
+  // the high unit's dword (even k: bits 4h..; odd k: shifted up)
+  const uint32_t sl = 4u * uint32_t(h), sre = 2u * uint32_t(h), slo = 4u - 2u * uint32_t(h);
+  const i32x4 m32 = {int(0xE0E0E0E0u), int(0xE0E0E0E0u), int(0xE0E0E0E0u), int(0xE0E0E0E0u)};  // int8 -32
+#pragma unroll
+  for (int p = 0; p < BPW / 2; ++p) {
+    const int b = int(blk0) + 2 * p + e;
+    const u32x4 lw = *reinterpret_cast<const u32x4*>(row + mf_swz(b, c) * 16);
+    const uint2 hw = *reinterpret_cast<const uint2*>(row + mf_swz(G::NB + (b >> 1), c) * 16 + 8 * (b & 1));
+    const uint32_t w[4] = {lw.x, lw.y, lw.z, lw.w};
+    uint32_t q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t H = (k >> 1) ? hw.y : hw.x;
+      const uint32_t hx = (k & 1) ? (H << slo) : (H >> sre);
+      q[k] = ((w[k] >> sl) & 0x0F0F0F0Fu) | (hx & 0x30303030u);
+    }
+    const i32x4 bv = {int(q[0]), int(q[1]), int(q[2]), int(q[3])};
+    // d sc of the lane's block-half (int8 scale: byte g of word p).  A plain
+    // int8_t cast: the sign-extending bit-field builtin followed by the
+    // conversion compiled to an unsigned int -> float conversion (every
+    // negative scale became ~4.3e9).
+    const float ds = dsb[p >> 2] * float(int(int8_t(uint8_t(scw[p] >> (8u * uint32_t(g))))));
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      i32x4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[ch][p], m32, i32x4{0, 0, 0, 0}, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[ch][p], bv, d, 0, 0, 0);
+      const int rr = ch == 0 ? RR0 : M - 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < rr) acc[ch][i] = fmaf(ds, da[ch][p][i] * float(d[i]), acc[ch][i]);
+    }
+  }
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = __float_as_uint(acc[ch][i]);
+      const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      acc[ch][i] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+      v = __float_as_uint(acc[ch][i]);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      acc[ch][i] = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Grouped blocks for fp16 activations (weight-ring kernel, one fp16 term).
 // With one term, A rows M..15 of the one-block-per-MFMA layout are padding.
 // Here E = 16 / RB blocks share a chain of E v_mfma_f32_16x16x32_f16, RB = 8
@@ -1202,14 +1319,20 @@ constexpr int MF_DMA_TILES = 4;  // most tiles one workgroup processes
 template <int FMT>
 struct MfDmaGeom {
   static constexpr int NP = (FMT == SKG_Q8_0_F32 || FMT == SKG_Q8_0_Q8_1) ? 2 : 1;
+  static constexpr bool Q6 = FMT == SKG_Q6_K_Q8_1;    // low + high units per row, d rows
   static constexpr int NB = 128;                     // blocks per row (K = 4096)
-  static constexpr int RB = NB * 16 * NP;            // payload bytes per row (LDS row stride)
+  static constexpr int RB = Q6 ? NB * 24 : NB * 16 * NP;  // payload bytes per row (LDS row stride)
   static constexpr int SRS = NB * 2;                 // scale bytes per row (16 chunks)
+  // q6_K: the rows' fp16 super-block d (32 bytes per row), copied by one
+  // 64-lane transfer whose upper half repeats the lower into a pad
+  static constexpr int DOFF = 16 * RB + 16 * SRS;
+  static constexpr int DREG = Q6 ? 1024 : 0;
   // one tile, plus 256 bytes so that the aliased Q8_1 staging of 8 rows keeps
   // its bank-spreading row stride (8 waves x 8 rows x 145 dwords)
-  static constexpr int SLOT = 16 * RB + 16 * SRS + 256;
+  static constexpr int SLOT = 16 * RB + 16 * SRS + DREG + 256;
   static constexpr int CH = RB / 1024;               // 1 KB transfers per row
-  static constexpr int P = 2 * CH + 1;               // transfers per wave per tile (2 rows + 4 scale rows)
+  // transfers per wave per tile (2 rows + 4 scale rows [+ the d rows])
+  static constexpr int P = 2 * CH + 1 + (Q6 ? 1 : 0);
 };
 
 
@@ -1219,7 +1342,8 @@ struct MfDmaGeom {
 // mf_stage_grp).
 template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
-  constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1 || FMT == SKG_Q4_K_Q8_1);
+  constexpr bool Q6 = FMT == SKG_Q6_K_Q8_1;
+  constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1 || FMT == SKG_Q4_K_Q8_1 || Q6);
   static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || FMT == SKG_Q4_K_F32 || Q8,
                 "quantised weight formats only");
   constexpr bool KQF = FMT == SKG_Q4_K_F32;
@@ -1295,12 +1419,22 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       const uint16_t* srow = sg.w0.scales + size_t(n) * sg.w0.nb;
       dma16_stream(srow + mf_swz(lane & 15, r) * 8, lds_addr(slot) + uint32_t(16 * G::RB + 4 * (wave & 3) * G::SRS));
     }
+    if constexpr (G::Q6) {
+      // d rows: lane l copies 16 bytes (chunk l % 2) of row (l / 2) % 16; every
+      // wave issues the same copy
+      const int r = (lane >> 1) & 15;
+      const int64_t n = (rbase + r < sg.N) ? rbase + r : sg.N - 1;
+      const uint16_t* drow = sg.w0.dsup + size_t(n) * (sg.w0.nb / 8);
+      dma16_stream(drow + 8 * (lane & 1), lds_addr(slot) + uint32_t(G::DOFF));
+    }
   };
 
   uint8_t* stage_area = ALIAS ? (R == 4 ? slot3 : R == 3 ? slot2 : slot1) : stage_own;
   f16x8 ah[Q8 ? 1 : BPW], al[Q8 ? 1 : BPW];
   i32x4 aq[Q8 ? BPW / 2 : 1];
   f32x4 da[Q8 ? BPW / 2 : 1], sa[Q8 ? BPW / 2 : 1];
+  i32x4 aq6[Q6 ? 2 : 1][Q6 ? BPW / 2 : 1];
+  f32x4 da6[Q6 ? 2 : 1][Q6 ? BPW / 2 : 1];
   f32x4 ks[E > 0 ? BPW / (E > 0 ? E : 1) : 1];  // q4_K block sums (grouped kernel)
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};
   f16x8 ksum = {};  // unused: no q4_K here
@@ -1314,7 +1448,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if constexpr ((R == 3 && !ALIAS) || R == 4) dma_tile(slot2, clamp(2));
     if constexpr (R == 4 && !ALIAS) dma_tile(slot3, clamp(3));
   };
-  if constexpr (Q8)
+  if constexpr (Q6)
+    mf_stage_q6q8<M, BPW, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq6,
+                               da6, [] {}, first_dma);
+  else if constexpr (Q8)
     mf_stage_q8p<M, BPW, WKQ, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane,
                                    aq, da, sa, [] {}, first_dma);
   else if constexpr (E > 0)
@@ -1361,7 +1498,13 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   int parity = 0;
   auto run = [&](uint8_t* slot, int i) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Q8) {
+    if constexpr (Q6) {
+      float a6[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      mf_tile_q6q8<G, BPW, M>(slot, blk0, g, c, aq6, da6, a6);
+      // lane group 0 writes rows 0..3, group 1 rows 4..7 (below)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = (g == 1) ? a6[1][i] : a6[0][i];
+    } else if constexpr (Q8) {
       mf_tile_q8p<G, BPW, (M > 4 ? 4 : M), FMT == SKG_Q4_K_Q8_1>(slot, blk0, g, c, aq, da, sa, acc);
     } else if constexpr (E > 0) {
       constexpr bool LOROWS = XT == 2 && M <= 4, LOCHAIN = XT == 2 && !LOROWS;

@@ -3,9 +3,21 @@
 // chosen by measurement on MI355X at K = 4096, N = 14336 under cold-cache
 // rotation.
 #include "gemv_instances.h"
+#include "gemv_mfma.h"
 
 namespace skg {
 void register_gemv_q6_K(std::vector<GemvEntry>& out) {
+  // q6_K x Q8_1 at M = 4..8: the integer matrix cores with the weights
+  // streamed into an LDS ring (low units, high units, int8 scale pairs and d
+  // per row; block-halves per 64-deep MFMA, the -32 of the codes as a chained
+  // MFMA against constant -32; K = 4096 only, other K fall through to the
+  // vector kernels below).  Alternating timings, us (ring / vector default
+  // before): M = 4 13.45 / 14.03, 5 15.89 / 16.58, 6 16.08 / 18.29,
+  // 7 16.32 / 19.78, 8 15.88 / 21.39.
+  for (auto e : {gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 4, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 5, 1, 2, true>(),
+                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 6, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 7, 1, 2, true>(),
+                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 8, 1, 2, true>()})
+    out.push_back(e);
   // q6_K x fp32, activation in LDS: 2 rows per wave (M = 1: 2 units per
   // lane, 11.09 us against 11.83-12.20; M = 6 27.29 against 40.19 with 4
   // rows), 4 rows at M = 3, 5 (M = 5 22.44 against 24.46)
@@ -46,5 +58,9 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   SKG_M12(SKG_Q6_K_Q8_1, 4, 2, 4, 1, 2, 2)
   SKG_M3_8(SKG_Q6_K_Q8_1, 4, 1, false, 2)
   SKG_N3_8(SKG_Q6_K_Q8_1, 4, 1, true)
+  // q6_K x Q8_1 on the integer matrix cores at M = 2, 3: slower than the
+  // vector kernels (12.67 / 13.51 against 11.40 / 12.63 us)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 2, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 3, 1, 2, true>());
 }
 }  // namespace skg
