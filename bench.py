@@ -919,7 +919,7 @@ def main():
             # fp32-activation matrix-core defaults that round the activation to
             # one fp16 term are timed beside the two-term (~22-bit) kernel
             dv = skg.gemv_default_variant(fmt, M, skg.EPI_NONE, 4096)
-            mf_f32 = fmt in (skg.Q8_0_F32, skg.Q4_0_F32, skg.Q4_K_F32)
+            mf_f32 = fmt in (skg.Q8_0_F32, skg.Q4_0_F32, skg.Q4_K_F32, skg.Q6_K_F32)
             extra = (two_term_variants(skg, fmt, M) if mf_f32 and dv["x_lds"] in (2, 3, 5) and dv["j"] == 1 else [])
             r = bench_gemv_arm(skg, si, torch, timer, f"{skg.FMT_NAMES[fmt]}_m{M}_k4096_n14336", kind, fmt, M,
                                14336, 4096, xh, warm_s=warm, graph=True, variants=extra)

@@ -664,6 +664,162 @@ __device__ inline void mf_tile_q6q8(const uint8_t* slot, uint32_t blk0, int g, i
     }
 }
 
+// Bytes of one activation row in a staging pass (8 blocks of fp16, plus 16 so
+// that the rows a fragment read takes start 4 banks apart).
+constexpr int GRP_ROW = 8 * 32 * 2 + 16;
+
+// ---------------------------------------------------------------------------
+// q6_K weights against fp32 activations (weight-ring kernel, the activation
+// as one fp16 term with a power of two per row and wave, as mf_stage_grp).
+// The block-half layout of the integer kernel above on
+// v_mfma_f32_16x16x32_f16: lane group g holds eight elements of half g % 2 of
+// block b + g / 2 per MFMA (two MFMAs per pair of blocks and chain), A rows
+// 4 g .. 4 g + 3 carry activation rows 0..3 (second chain: 4..7) in group g
+// only, and the codes enter as the exact fp16 values q - 32 (a byte under the
+// exponent of 1024 by one mask-and-or, one packed subtraction of 1056), so a
+// zero weight contributes exactly zero.  ap[ch][2 p + j]: chain ch, pair p,
+// elements 16 h + 8 j .. + 7 in the decode's slot order.
+template <int M, int BPW, class Between, class AfterX>
+__device__ inline void mf_stage_q6f(const MfArgs& a, uint8_t* area, uint32_t blk0, int lane, f16x8 (&ap)[2][BPW],
+                                    float (&unscale)[4], Between between, AfterX after_x) {
+  static_assert(M <= 8 && BPW % 8 == 0, "two chains of four rows, whole staging passes");
+  const int g = lane >> 4, c = lane & 15;
+  const int h = g & 1, e = g >> 1;
+  f32x4 xv[M][BPW / 8];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int ee = 0; ee < BPW / 8; ++ee)
+      xv[m][ee] = *reinterpret_cast<const f32x4*>(a.x + size_t(m) * size_t(a.K) + size_t(blk0) * 32 + 256 * ee + 4 * lane);
+  __builtin_amdgcn_sched_barrier(0);
+  between();
+  __builtin_amdgcn_sched_barrier(0);
+  float sc[M], us[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float mx = 0.f;
+#pragma unroll
+    for (int ee = 0; ee < BPW / 8; ++ee)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[m][ee].x), fabsf(xv[m][ee].y)), fmaxf(fabsf(xv[m][ee].z), fabsf(xv[m][ee].w))));
+    mx = wave_max(mx);
+    int se = 15 - __builtin_amdgcn_frexp_expf(mx);
+    se = se > 126 ? 126 : (se < -126 ? -126 : se);
+    sc[m] = __builtin_ldexpf(1.0f, se);
+    us[m] = __builtin_ldexpf(1.0f, -se);
+  }
+  // the lane's written rows (below): group 1 rows 4..7, else rows 0..3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u0 = (i < M) ? us[i < M ? i : 0] : 1.f;
+    const float u1 = (4 + i < M) ? us[4 + i < M ? 4 + i : 0] : 1.f;
+    unscale[i] = (g == 1) ? u1 : u0;
+  }
+  after_x();
+#pragma unroll
+  for (int ee = 0; ee < BPW / 8; ++ee) {
+    // a wave's LDS accesses complete in order: this pass's writes are seen by
+    // its reads, and its reads finish before the next pass writes
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const f32x4 v = xv[m][ee] * sc[m];
+      const f16x2 p01 = __builtin_convertvector((f32x2{v.x, v.y}), f16x2);
+      const f16x2 p23 = __builtin_convertvector((f32x2{v.z, v.w}), f16x2);
+      *reinterpret_cast<u32x2*>(area + m * GRP_ROW + 8 * lane) = u32x2{bits(p01), bits(p23)};
+    }
+#pragma unroll
+    for (int ch = 0; ch < (M > 4 ? 2 : 1); ++ch) {
+      const int m = (c & 3) + 4 * ch;
+      const bool on = (c >> 2) == g && m < M;
+      const uint8_t* rd = area + (on ? m : 0) * GRP_ROW;
+#pragma unroll
+      for (int gl = 0; gl < 4; ++gl)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 r = *reinterpret_cast<const u32x4*>(rd + 2 * (32 * (2 * gl + e) + 16 * h + 8 * j));
+          const u32x4 sl = {__builtin_amdgcn_perm(r.y, r.x, 0x05040100u), __builtin_amdgcn_perm(r.y, r.x, 0x07060302u),
+                            __builtin_amdgcn_perm(r.w, r.z, 0x05040100u), __builtin_amdgcn_perm(r.w, r.z, 0x07060302u)};
+          ap[ch][2 * (4 * ee + gl) + j] = __builtin_bit_cast(f16x8, on ? sl : u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+  }
+}
+
+// One tile of q6_K against the fp16 operands above; slot as mf_tile_q6q8.  On
+// return every lane holds the full (still scaled) sums of activation rows
+// 0..3 (acc[0]) and 4..7 (acc[1]) of column c.
+template <class G, int BPW, int M>
+__device__ inline void mf_tile_q6f(const uint8_t* slot, uint32_t blk0, int g, int c, const f16x8 (&ap)[2][BPW],
+                                   float (&acc)[2][4], uint32_t magic, uint32_t mbyte) {
+  constexpr int NCH = M > 4 ? 2 : 1;
+  constexpr int RR0 = M < 4 ? M : 4;
+  uint32_t scw[BPW / 2];
+#pragma unroll
+  for (int k = 0; k < BPW / 8; ++k) {
+    const u32x4 s4 = *reinterpret_cast<const u32x4*>(slot + 16 * G::RB + c * G::SRS + mf_swz(int(blk0) / 8 + k, c) * 16);
+    scw[4 * k + 0] = s4.x;
+    scw[4 * k + 1] = s4.y;
+    scw[4 * k + 2] = s4.z;
+    scw[4 * k + 3] = s4.w;
+  }
+  static_assert(BPW == 16, "two super-blocks per wave span");
+  const uint32_t dw = *reinterpret_cast<const uint32_t*>(slot + G::DOFF + c * 32 + (int(blk0) / 8) * 2);
+  const float dsb[2] = {h2f(dw & 0xFFFFu), h2f(dw >> 16)};
+  const uint8_t* row = slot + c * G::RB;
+  const int h = g & 1, e = g >> 1;
+  const uint32_t sl = 4u * uint32_t(h), sre = 2u * uint32_t(h), slo = 4u - 2u * uint32_t(h);
+  const f16x2 off = {(_Float16)-1056.0f, (_Float16)-1056.0f};
+  // codes of one dword (bytes 0..3) as fp16 q - 32 in slot order 0, 2, 1, 3
+  auto dec = [&](uint32_t q, f16x2& r02, f16x2& r13) {
+    r02 = half2_of((q & mbyte) | magic) + off;
+    r13 = half2_of(((q >> 8) & mbyte) | magic) + off;
+  };
+#pragma unroll
+  for (int p = 0; p < BPW / 2; ++p) {
+    const int b = int(blk0) + 2 * p + e;
+    const u32x4 lw = *reinterpret_cast<const u32x4*>(row + mf_swz(b, c) * 16);
+    const uint2 hw = *reinterpret_cast<const uint2*>(row + mf_swz(G::NB + (b >> 1), c) * 16 + 8 * (b & 1));
+    const uint32_t w[4] = {lw.x, lw.y, lw.z, lw.w};
+    uint32_t q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t H = (k >> 1) ? hw.y : hw.x;
+      const uint32_t hx = (k & 1) ? (H << slo) : (H >> sre);
+      q[k] = ((w[k] >> sl) & 0x0F0F0F0Fu) | (hx & 0x30303030u);
+    }
+    f16x8 bw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f16x2 a02, a13, b02, b13;
+      dec(q[2 * j], a02, a13);
+      dec(q[2 * j + 1], b02, b13);
+      bw[j] = f16x8{a02[0], a02[1], a13[0], a13[1], b02[0], b02[1], b13[0], b13[1]};
+    }
+    // d sc of the lane's block-half: a plain int8_t cast (see mf_tile_q6q8)
+    const float ds = dsb[p >> 2] * float(int(int8_t(uint8_t(scw[p] >> (8u * uint32_t(g))))));
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[ch][2 * p], bw[0], d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap[ch][2 * p + 1], bw[1], d, 0, 0, 0);
+      const int rr = ch == 0 ? RR0 : M - 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < rr) acc[ch][i] = fmaf(ds, d[i], acc[ch][i]);
+    }
+  }
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = __float_as_uint(acc[ch][i]);
+      const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      acc[ch][i] = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+      v = __float_as_uint(acc[ch][i]);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      acc[ch][i] = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Grouped blocks for fp16 activations (weight-ring kernel, one fp16 term).
 // With one term, A rows M..15 of the one-block-per-MFMA layout are padding.
@@ -698,9 +854,6 @@ __device__ inline int grp_elem(int gl, int g, int j) {
     return 32 * (4 * gl + g) + 8 * j;
 }
 
-// Bytes of one activation row in a staging pass (8 blocks of fp16, plus 16 so
-// that the rows a fragment read takes start 4 banks apart).
-constexpr int GRP_ROW = 8 * 32 * 2 + 16;
 
 // A operands of the wave's BPW blocks in the grouped layout (ap[E gi + j] is
 // chain step j of group gi) and the power-of-two unscale of each lane's
@@ -1319,7 +1472,7 @@ constexpr int MF_DMA_TILES = 4;  // most tiles one workgroup processes
 template <int FMT>
 struct MfDmaGeom {
   static constexpr int NP = (FMT == SKG_Q8_0_F32 || FMT == SKG_Q8_0_Q8_1) ? 2 : 1;
-  static constexpr bool Q6 = FMT == SKG_Q6_K_Q8_1;    // low + high units per row, d rows
+  static constexpr bool Q6 = FMT == SKG_Q6_K_Q8_1 || FMT == SKG_Q6_K_F32;  // low + high units per row, d rows
   static constexpr int NB = 128;                     // blocks per row (K = 4096)
   static constexpr int RB = Q6 ? NB * 24 : NB * 16 * NP;  // payload bytes per row (LDS row stride)
   static constexpr int SRS = NB * 2;                 // scale bytes per row (16 chunks)
@@ -1344,8 +1497,10 @@ template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr bool Q6 = FMT == SKG_Q6_K_Q8_1;
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1 || FMT == SKG_Q4_K_Q8_1 || Q6);
-  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || FMT == SKG_Q4_K_F32 || Q8,
+  constexpr bool Q6F = FMT == SKG_Q6_K_F32;
+  static_assert(FMT == SKG_Q4_0_F32 || FMT == SKG_Q8_0_F32 || FMT == SKG_Q4_K_F32 || Q6F || Q8,
                 "quantised weight formats only");
+  static_assert(!Q6F || XT == 1, "q6_K x fp32: one fp16 term");
   constexpr bool KQF = FMT == SKG_Q4_K_F32;
   static_assert(!KQF || E > 0, "q4_K x fp32: grouped blocks only");
   constexpr int WKQ = FMT == SKG_Q4_0_Q8_1 ? WK_Q4_0 : FMT == SKG_Q4_K_Q8_1 ? WK_Q4_K : WK_Q8_0;
@@ -1361,7 +1516,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr int MSO = (XT * M) | 1;
   constexpr int MSD = (!ALIAS || WAVES * (8 * 4 * MSO * 16) <= G::SLOT) ? MSO : XT * M;
   constexpr int QRP = (!ALIAS || WAVES * M * q8_stage_row<BPW>() * 4 <= G::SLOT) ? q8_stage_row<BPW>() : 9 * BPW;
-  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4 : E > 0 ? XT * M * GRP_ROW + (KQF ? M * BPW * 4 : 0) : 8 * 4 * MSD * 16;
+  constexpr int WAVE_STAGE = Q8 ? M * QRP * 4
+                             : (E > 0 || Q6F) ? XT * M * GRP_ROW + (KQF ? M * BPW * 4 : 0)
+                                              : 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   // one LDS array, carved: R slots, the own staging area, the partial sums
   constexpr int RED_BYTES = 2 * WAVES * MF_ROWS * M * 4;
@@ -1435,6 +1592,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   f32x4 da[Q8 ? BPW / 2 : 1], sa[Q8 ? BPW / 2 : 1];
   i32x4 aq6[Q6 ? 2 : 1][Q6 ? BPW / 2 : 1];
   f32x4 da6[Q6 ? 2 : 1][Q6 ? BPW / 2 : 1];
+  f16x8 ap6[Q6F ? 2 : 1][Q6F ? BPW : 1];
   f32x4 ks[E > 0 ? BPW / (E > 0 ? E : 1) : 1];  // q4_K block sums (grouped kernel)
   float unscale[4] = {1.f, 1.f, 1.f, 1.f};
   f16x8 ksum = {};  // unused: no q4_K here
@@ -1448,7 +1606,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if constexpr ((R == 3 && !ALIAS) || R == 4) dma_tile(slot2, clamp(2));
     if constexpr (R == 4 && !ALIAS) dma_tile(slot3, clamp(3));
   };
-  if constexpr (Q6)
+  if constexpr (Q6F)
+    mf_stage_q6f<M, BPW>(a, stage_area + size_t(wave) * WAVE_STAGE, blk0, lane, ap6, unscale, [] {}, first_dma);
+  else if constexpr (Q6)
     mf_stage_q6q8<M, BPW, QRP>(a, reinterpret_cast<uint32_t*>(stage_area + size_t(wave) * WAVE_STAGE), blk0, lane, aq6,
                                da6, [] {}, first_dma);
   else if constexpr (Q8)
@@ -1498,7 +1658,13 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   int parity = 0;
   auto run = [&](uint8_t* slot, int i) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Q6) {
+    if constexpr (Q6F) {
+      float a6[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      mf_tile_q6f<G, BPW, M>(slot, blk0, g, c, ap6, a6, magic, 0x00FF00FFu);
+      // lane group 0 writes rows 0..3, group 1 rows 4..7 (below, times unscale)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = (g == 1) ? a6[1][k] : a6[0][k];
+    } else if constexpr (Q6) {
       float a6[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       mf_tile_q6q8<G, BPW, M>(slot, blk0, g, c, aq6, da6, a6);
       // lane group 0 writes rows 0..3, group 1 rows 4..7 (below)
@@ -1579,6 +1745,18 @@ inline GemvEntry gemv_mfma_dma_entry() {
 // The ring kernel with grouped blocks (x_lds = 5): one fp16 activation term
 // with two blocks per MFMA chain for M = 5..8 and four for M <= 4, or two
 // terms (XT = 2) with two blocks per chain.
+// q6_K x fp32 on the ring kernel (block-halves; x_lds = 5 like the grouped
+// kernels, one fp16 term).
+template <int M, int R, bool ALIAS>
+inline GemvEntry gemv_mfma_q6f_entry() {
+  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<SKG_Q6_K_F32, M, 1, R, ALIAS>),
+              SKG_Q6_K_F32, M, SKG_EPI_NONE, MF_ROWS, 1, 5, 8, 16};
+  e.lds = 0;
+  e.max_nb = MfDmaGeom<SKG_Q6_K_F32>::NB;
+  e.depth = R;
+  return e;
+}
+
 template <int FMT, int M, int R, bool ALIAS, int XT = 1>
 inline GemvEntry gemv_mfma_grp_entry() {
   constexpr int E = (M <= 4 && XT == 1) ? 4 : 2;

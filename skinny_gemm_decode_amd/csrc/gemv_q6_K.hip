@@ -7,6 +7,16 @@
 
 namespace skg {
 void register_gemv_q6_K(std::vector<GemvEntry>& out) {
+  // q6_K x fp32 at M = 3..8: the matrix cores with the weights streamed into
+  // an LDS ring (block-halves per MFMA so each result row has one int8 scale,
+  // codes as the exact fp16 q - 32, the activation as one fp16 term with a
+  // power of two per row and wave; K = 4096 only, other K take the vector
+  // kernels below).  Alternating timings, us (ring / vector default
+  // before): M = 3 15.83 / 18.98, 4 15.92 / 20.68, 5 18.05 / 25.27,
+  // 6 18.42 / 25.76, 7 18.67 / 33.53, 8 18.70 / 36.58.
+  for (auto e : {gemv_mfma_q6f_entry<3, 2, false>(), gemv_mfma_q6f_entry<4, 2, false>(), gemv_mfma_q6f_entry<5, 2, false>(),
+                 gemv_mfma_q6f_entry<6, 2, false>(), gemv_mfma_q6f_entry<7, 2, false>(), gemv_mfma_q6f_entry<8, 2, false>()})
+    out.push_back(e);
   // q6_K x Q8_1 at M = 4..8: the integer matrix cores with the weights
   // streamed into an LDS ring (low units, high units, int8 scale pairs and d
   // per row; block-halves per 64-deep MFMA, the -32 of the codes as a chained
@@ -62,5 +72,8 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   // vector kernels (12.67 / 13.51 against 11.40 / 12.63 us)
   out.push_back(gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 2, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 3, 1, 2, true>());
+  // q6_K x fp32 on the LDS-ring kernel at M = 2: slower than the vector
+  // kernel (15.25 against 13.97 us)
+  out.push_back(gemv_mfma_q6f_entry<2, 2, false>());
 }
 }  // namespace skg

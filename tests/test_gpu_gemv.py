@@ -313,7 +313,7 @@ def mfma_variants(skg, fmt, M):
             if v["fmt"] == fmt and v["M"] == M and v["epi"] == skg.EPI_NONE and v["x_lds"] in (2, 3, 4, 5)]
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 7, 9, 10])
+@pytest.mark.parametrize("fmt", [1, 2, 3, 4, 7, 8, 9, 10])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemv_mfma_shapes(skg, fmt, M):
     """Default path at the shapes the matrix-core kernel takes, then every
