@@ -316,24 +316,28 @@ skg_status skg_empty_launch(int64_t grid, int block, hipStream_t stream);
  *   variant is not compiled; a later call returns SKG_E_UNSUPPORTED if the
  *   selected variant does not take its K.
  *   x_lds = 2 names the matrix-core kernel of the fp32-activation quantised
- *   formats (SKG_Q8_0_F32, SKG_Q4_0_F32): ro = 16 output rows per tile, j =
+ *   formats (SKG_Q8_0_F32, SKG_Q4_0_F32, SKG_Q4_K_F32; also the Q8_1 formats
+ *   of q4_0 and q8_0 on the integer matrix cores): ro = 16 output rows per tile, j =
  *   fp16 terms carrying each activation (2: ~22 bits; 1: one rounding to
  *   fp16, relative error 2^-11), waves = most waves per workgroup, kw =
  *   quantisation blocks per wave; it takes K with (K / 32) % kw == 0 and
  *   K / 32 <= waves * kw.
  *   x_lds = 3 names the same matrix-core computation with the weight tiles
  *   copied by direct global-to-LDS transfers into a ring of two or three
- *   16-row slots (the activation as for x_lds = 2); compiled for K = 4096 only
+ *   16-row slots (the activation as for x_lds = 2; formats q4_0 / q8_0 x fp32
+ *   and q4_0 / q8_0 / q4_K / q6_K x Q8_1); compiled for K = 4096 only
  *   (waves * kw = 128 blocks), so a call with any other K returns
  *   SKG_E_UNSUPPORTED while it is selected.
  *   x_lds = 4 names the same matrix-core computation with a private weight
  *   ring per wave (each wave copies its own 16-block slice of every tile into
  *   `depth` LDS slots; no workgroup barrier until the last tile); it takes K
  *   with (K / 32) % 16 == 0 and K / 32 <= 128.
- *   x_lds = 5 names the ring kernel of x_lds = 3 with several quantisation
- *   blocks per chain of MFMAs (a block-diagonal A operand: four blocks for
- *   M <= 4 and two for M = 5..8 with j = 1; two blocks of four hi and four lo
- *   rows with j = 2, M <= 4); compiled for K = 4096 only, like x_lds = 3.
+ *   x_lds = 5 names the ring kernel of x_lds = 3 for fp32 activations with
+ *   several quantisation blocks per chain of MFMAs (a block-diagonal A
+ *   operand: four blocks for M <= 4 and two for M = 5..8 with j = 1; two
+ *   blocks of four hi and four lo rows, or a second chain of lo operands,
+ *   with j = 2; q4_0, q8_0, q4_K, and q6_K by block-halves); compiled for
+ *   K = 4096 only, like x_lds = 3.
  *   depth: weight tiles in flight (1 for the vector kernels; the prefetch
  *   depth of x_lds = 2, 1 or 2; the ring slots of x_lds = 3 or 5, 2 or 3, or
  *   4 for q4_0 weights); 0 matches any depth.

@@ -1,5 +1,9 @@
 // Small-batch GEMV on the matrix cores: y[m][n] = sum_k W[n][k] x[m][k] for
-// q4_0 / q8_0 weights and fp32 activations, 1 <= M <= 8.
+// q4_0 / q8_0 / q4_K / q6_K weights against fp32 activations (fp16 MFMAs) or
+// Q8_1 activations (int8 MFMAs), 1 <= M <= 8.  The register-fed kernel below
+// is described first; the weight-ring kernel (gemv_mfma_dma_kernel, the
+// defaults at K = 4096) and its operand layouts (block pairs, grouped blocks,
+// q6_K block-halves) follow further down.
 //
 // With fp32 activations every weight element costs M fused multiply-adds on
 // the vector ALU, so the vector kernel stops being bound by HBM as soon as
