@@ -11,16 +11,23 @@ namespace skg {
 // measured on MI355X under cold-cache rotation (K = 4096, N = 14336).
 void register_gemv_mfma_q4_0(std::vector<GemvEntry>& out) {
   // M = 2..8: the LDS-ring kernel with grouped blocks (four per MFMA chain
-  // for M <= 4, two for M = 5..8), two ring slots, the activation as one
-  // fp16 term (one rounding, 2^-11, inside the accuracy bound).  Alternating
-  // timings against the kernels below, us (grouped / previous default):
-  // M = 2 10.25 / 11.35 (ring, two terms), 3 10.64 / 11.57, 4 10.70 /
-  // 11.76, 5 11.12 / 12.44, 6 11.16 / 12.40, 7 11.39 / 11.78, 8 11.39 /
-  // 11.78 (ring, one block per MFMA); three slots: 10.8-12.3.
-  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 2, false>(),
-                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 2, false>(),
+  // for M <= 4, two for M = 5..8), the activation as one fp16 term (one
+  // rounding, 2^-11, inside the accuracy bound).  Alternating timings against
+  // the kernels below, us (grouped / previous default): M = 2 10.25 / 11.35
+  // (ring, two terms), 3 10.64 / 11.57, 4 10.70 / 11.76, 5 11.12 / 12.44,
+  // 6 11.16 / 12.40, 7 11.39 / 11.78, 8 11.39 / 11.78 (ring, one block per
+  // MFMA).  M = 2..4 take three slots with the staging in the last (two
+  // tiles requested at the start, the third once the activation is staged):
+  // 9.98-10.08 / 10.39-10.41 / 10.36-10.44 us against 10.24-10.25 /
+  // 10.62-10.63 / 10.69 with two slots and their own staging area; at
+  // M = 5, 6, 8 they trail by 0.5-1% (11.16-11.22, 11.25-11.29, 11.47).
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 3, true>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 2, false>(),
                  gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 2, false>(),
                  gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 2, false>()})
+    out.push_back(e);
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 2, false>()})
     out.push_back(e);
   // Before them: M = 2: the LDS-ring kernel with two fp16 activation terms, 11.35 us
   // against 11.82 (register-fed, two terms); M = 3 / 5: the ring with one
@@ -57,11 +64,12 @@ void register_gemv_mfma_q4_0_alt(std::vector<GemvEntry>& out) {
                  gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 2, false, 2>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 2, false, 2>(),
                  gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 2, false, 2>()})
     out.push_back(e);
-  // grouped blocks with three ring slots
-  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 2, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 3, 3, false>(),
-                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 4, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 3, false>(),
-                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 3, false>(),
-                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 3, false>()})
+  // grouped blocks with three ring slots and their own staging area (all
+  // three tiles requested at the start): 0.6-0.8 us slower than two slots
+  // (M = 2 / 3 / 4: 10.82 / 11.44 / 11.50 us; 8: 12.18-12.20).  At M = 2..4
+  // the three-slot defaults (staging in the last slot) hold their keys.
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_0_F32, 5, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 6, 3, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_0_F32, 7, 3, false>(), gemv_mfma_grp_entry<SKG_Q4_0_F32, 8, 3, false>()})
     out.push_back(e);
   // per-wave weight rings (measurement variants)
   out.push_back(gemv_mfma_pw_entry<SKG_Q4_0_F32, 2, 1, 3>());

@@ -19,14 +19,23 @@ namespace skg {
 // 12.19 for the vector kernel, q8_0 14.43 / 14.65 against 14.73 / 15.89; at
 // M = 2 / 3 the vector kernel stays ahead (q4_0 8.77 / 9.62 against 9.33 /
 // 10.18, q8_0 12.18 / 13.49 against 13.38 / 13.98).
+// q4_0 at M = 3..8 takes three ring slots with the staging in the last (two
+// tiles requested at the start, the third once the activation is staged):
+// M = 3 / 4 / 5 / 6 / 7 / 8 9.32-9.33 / 9.67-9.69 / 9.95-9.99 /
+// 10.00-10.03 / 10.04 / 9.96-9.99 us against 9.41 / 9.90-9.91 / 10.02 /
+// 10.14-10.16 / 10.18-10.19 / 10.11-10.13 with two slots (and 9.60-9.62
+// for the vector kernel at M = 3); without the aliasing (two slots and an
+// own staging area) 10.25 / 10.47 / 10.52 at M = 4 / 6 / 8.  q8_0's slots
+// fit the LDS only twice.
 void register_gemv_mfma_q8_1(std::vector<GemvEntry>& out) {
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 4, 1, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 5, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 3, 1, 3, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 4, 1, 3, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 5, 1, 3, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 4, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 5, 1, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 2, true>());
-  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 2, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 3, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 3, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 3, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q8_0_Q8_1, 6, 1, 2, true>());
   SKG_MF8(SKG_Q4_0_Q8_1, 7, 16, 8, 1)
   SKG_MF8(SKG_Q4_0_Q8_1, 8, 16, 8, 1)
@@ -65,5 +74,10 @@ void register_gemv_mfma_q8_1_alt(std::vector<GemvEntry>& out) {
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 4, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 4, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 4, true>());
+  // q4_0 with two slots (the defaults before the three-slot ones)
+  for (auto e : {gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 4, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 5, 1, 2, true>(),
+                 gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 6, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 7, 1, 2, true>(),
+                 gemv_mfma_dma_entry<SKG_Q4_0_Q8_1, 8, 1, 2, true>()})
+    out.push_back(e);
 }
 }  // namespace skg

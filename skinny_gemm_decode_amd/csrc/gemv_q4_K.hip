@@ -19,11 +19,18 @@ void register_gemv_q4_K(std::vector<GemvEntry>& out) {
   // (grouped / previous default, register-fed): M = 2 10.05 / 12.61 (two
   // terms), 3 10.51 / 13.92 (two terms), 4 10.69 / 13.04, 5 11.97 / 13.89,
   // 6 12.03 / 14.04, 7 12.46 / 14.42, 8 12.63 / 14.48; grouped with two
-  // terms 10.73 / 11.69 / 12.40 / 13.53 / 13.68 / 14.37 / 14.44.
-  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_K_F32, 2, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 3, 2, false>(),
-                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 5, 2, false>(),
+  // terms 10.73 / 11.69 / 12.40 / 13.53 / 13.68 / 14.37 / 14.44.  M = 2..4
+  // take three slots with the staging in the last (two tiles requested at
+  // the start, the third once the activation is staged): 9.73-9.81 /
+  // 10.39-10.47 / 10.58-10.61 us against 10.10-10.11 / 10.54 / 10.69-10.72
+  // with two slots and their own staging area; at M = 7 12.53 against 12.46.
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_K_F32, 2, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 3, 3, true>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 5, 2, false>(),
                  gemv_mfma_grp_entry<SKG_Q4_K_F32, 6, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 7, 2, false>(),
                  gemv_mfma_grp_entry<SKG_Q4_K_F32, 8, 2, false>()})
+    out.push_back(e);
+  for (auto e : {gemv_mfma_grp_entry<SKG_Q4_K_F32, 2, 2, false>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 3, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 2, false>()})
     out.push_back(e);
   // q4_K x Q8_1 at M = 3..8: the integer matrix cores with the weights
   // streamed into an LDS ring (two sub-blocks per 64-deep MFMA, the d sc_j
@@ -122,5 +129,11 @@ void register_gemv_q4_K(std::vector<GemvEntry>& out) {
   // q4_K x Q8_1 on the integer matrix cores at M = 2: slower than the
   // vector kernel (9.50 against 9.30 us)
   out.push_back(gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 2, 1, 2, true>());
+  // q4_K x Q8_1 with three slots (staging in the last): slower than two at
+  // M = 4 / 6 / 8 (10.53-10.54 / 10.90-10.91 / 11.04-11.05 against 10.42 /
+  // 10.53-10.54 / 10.50-10.55 us)
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 4, 1, 3, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 6, 1, 3, true>());
+  out.push_back(gemv_mfma_dma_entry<SKG_Q4_K_Q8_1, 8, 1, 3, true>());
 }
 }  // namespace skg
