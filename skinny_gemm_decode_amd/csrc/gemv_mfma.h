@@ -1496,8 +1496,10 @@ struct MfDmaGeom {
 // R: ring slots; ALIAS: the activation staging area shares the last slot
 // (its first load is issued after staging); E: 0 for one block per MFMA, or
 // 2 / 4 blocks per chain of MFMAs (fp32 activations as one fp16 term; see
-// mf_stage_grp).
-template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0>
+// mf_stage_grp); DEFER: the partial sums of all the workgroup's tiles stay
+// in LDS and meet once after the last tile, instead of after each tile's
+// barrier (faster for the q6_K kernels, slower for the others).
+template <int FMT, int M, int XT, int R, bool ALIAS, int E = 0, bool DEFER = false>
 __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
   constexpr bool Q6 = FMT == SKG_Q6_K_Q8_1;
   constexpr bool Q8 = (FMT == SKG_Q4_0_Q8_1 || FMT == SKG_Q8_0_Q8_1 || FMT == SKG_Q4_K_Q8_1 || Q6);
@@ -1525,7 +1527,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
                                               : 8 * 4 * MSD * 16;
   static_assert(!ALIAS || WAVES * WAVE_STAGE <= G::SLOT, "staging must fit the shared slot");
   // one LDS array, carved: R slots, the own staging area, the partial sums
-  constexpr int RED_BYTES = 2 * WAVES * MF_ROWS * M * 4;
+  constexpr int RED_BYTES = (DEFER ? MF_DMA_TILES : 2) * WAVES * MF_ROWS * M * 4;
   constexpr int STAGE_BYTES = ALIAS ? 0 : WAVES * WAVE_STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[R * G::SLOT + STAGE_BYTES + RED_BYTES];
   uint8_t* const slot0 = lds_all;
@@ -1692,7 +1694,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
       const MfNext none{};
       mf_tile<NP, BPW, RR, XT, false>(w, ah, al, acc, mlo, mhi, magic, none, blk0, g);
     }
-    float* rb = red + parity * (WAVES * MF_ROWS * M);
+    float* rb = red + (DEFER ? i : parity) * (WAVES * MF_ROWS * M);
     parity ^= 1;
 #pragma unroll
     for (int k = 0; k < RR; ++k) {
@@ -1704,6 +1706,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if (i + 1 < nmine) wait_tile(i + 1, i + R);
     sync();
     if (i + R < nmine) dma_tile(slot, i + R);
+    if constexpr (DEFER) return;
     const int t = t0 + i * step;
     for (int o = int(threadIdx.x); o < MF_ROWS * M; o += 512) {
       const int cc = o / M, m = o % M;
@@ -1731,14 +1734,27 @@ __global__ __launch_bounds__(512) void gemv_mfma_dma_kernel(const MfArgs a) {
     if (2 < nmine) run(slot0, 2);
     if (3 < nmine) run(slot1, 3);
   }
+  if constexpr (DEFER) {
+    for (int o = int(threadIdx.x); o < nmine * MF_ROWS * M; o += 512) {
+      const int i = o / (MF_ROWS * M), cc = (o / M) % MF_ROWS, m = o % M;
+      const float* rb = red + i * (WAVES * MF_ROWS * M);
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WAVES; ++ww) v += rb[(ww * MF_ROWS + cc) * M + m];
+      const int t = t0 + i * step;
+      const MfSeg sg = seg_of(t);
+      const int64_t n = int64_t(t - sg.tile_begin) * MF_ROWS + cc;
+      if (n < sg.N) sg.y[size_t(m) * size_t(sg.N) + size_t(n)] = v;
+    }
+  }
   // a workgroup with fewer tiles than slots still has its repeated first
   // transfers in flight: none may outlive the workgroup's LDS
   wait_vmcnt<0>();
 }
 
-template <int FMT, int M, int XT, int R, bool ALIAS>
+template <int FMT, int M, int XT, int R, bool ALIAS, bool DEFER = false>
 inline GemvEntry gemv_mfma_dma_entry() {
-  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<FMT, M, XT, R, ALIAS>),
+  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<FMT, M, XT, R, ALIAS, 0, DEFER>),
               FMT, M, SKG_EPI_NONE, MF_ROWS, XT, 3, 8, 16};
   e.lds = 0;
   e.max_nb = MfDmaGeom<FMT>::NB;
@@ -1751,9 +1767,9 @@ inline GemvEntry gemv_mfma_dma_entry() {
 // terms (XT = 2) with two blocks per chain.
 // q6_K x fp32 on the ring kernel (block-halves; x_lds = 5 like the grouped
 // kernels, one fp16 term).
-template <int M, int R, bool ALIAS>
+template <int M, int R, bool ALIAS, bool DEFER = false>
 inline GemvEntry gemv_mfma_q6f_entry() {
-  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<SKG_Q6_K_F32, M, 1, R, ALIAS>),
+  GemvEntry e{reinterpret_cast<const void*>(&gemv_mfma_dma_kernel<SKG_Q6_K_F32, M, 1, R, ALIAS, 0, DEFER>),
               SKG_Q6_K_F32, M, SKG_EPI_NONE, MF_ROWS, 1, 5, 8, 16};
   e.lds = 0;
   e.max_nb = MfDmaGeom<SKG_Q6_K_F32>::NB;

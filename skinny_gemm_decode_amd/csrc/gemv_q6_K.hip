@@ -13,9 +13,14 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   // power of two per row and wave; K = 4096 only, other K take the vector
   // kernels below).  Alternating timings, us (ring / vector default
   // before): M = 3 15.83 / 18.98, 4 15.92 / 20.68, 5 18.05 / 25.27,
-  // 6 18.42 / 25.76, 7 18.67 / 33.53, 8 18.70 / 36.58.
-  for (auto e : {gemv_mfma_q6f_entry<3, 2, false>(), gemv_mfma_q6f_entry<4, 2, false>(), gemv_mfma_q6f_entry<5, 2, false>(),
-                 gemv_mfma_q6f_entry<6, 2, false>(), gemv_mfma_q6f_entry<7, 2, false>(), gemv_mfma_q6f_entry<8, 2, false>()})
+  // 6 18.42 / 25.76, 7 18.67 / 33.53, 8 18.70 / 36.58.  The partial sums of
+  // a workgroup's tiles meet once after its last tile (instead of after each
+  // tile's barrier): M = 3 / 4 / 6 / 8 15.13-15.16 / 15.31-15.32 /
+  // 17.35-17.37 / 17.85-17.91 us against 15.85-15.86 / 15.87-15.88 /
+  // 18.41-18.42 / 18.70-18.72.
+  for (auto e : {gemv_mfma_q6f_entry<3, 2, false, true>(), gemv_mfma_q6f_entry<4, 2, false, true>(),
+                 gemv_mfma_q6f_entry<5, 2, false, true>(), gemv_mfma_q6f_entry<6, 2, false, true>(),
+                 gemv_mfma_q6f_entry<7, 2, false, true>(), gemv_mfma_q6f_entry<8, 2, false, true>()})
     out.push_back(e);
   // q6_K x Q8_1 at M = 4..8: the integer matrix cores with the weights
   // streamed into an LDS ring (low units, high units, int8 scale pairs and d
@@ -23,10 +28,14 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   // MFMA against constant -32; K = 4096 only, other K fall through to the
   // vector kernels below).  Alternating timings, us (ring / vector default
   // before): M = 4 13.45 / 14.03, 5 15.89 / 16.58, 6 16.08 / 18.29,
-  // 7 16.32 / 19.78, 8 15.88 / 21.39.
-  for (auto e : {gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 4, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 5, 1, 2, true>(),
-                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 6, 1, 2, true>(), gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 7, 1, 2, true>(),
-                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 8, 1, 2, true>()})
+  // 7 16.32 / 19.78, 8 15.88 / 21.39.  With the partial sums reduced once
+  // after the last tile: M = 4 / 6 / 8 12.92 / 15.07 / 15.59-15.60 us
+  // against 13.47-13.48 / 16.09-16.10 / 15.93.
+  for (auto e : {gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 4, 1, 2, true, true>(),
+                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 5, 1, 2, true, true>(),
+                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 6, 1, 2, true, true>(),
+                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 7, 1, 2, true, true>(),
+                 gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 8, 1, 2, true, true>()})
     out.push_back(e);
   // q6_K x fp32, activation in LDS: 2 rows per wave (M = 1: 2 units per
   // lane, 11.09 us against 11.83-12.20; M = 6 27.29 against 40.19 with 4
