@@ -17,10 +17,12 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   // a workgroup's tiles meet once after its last tile (instead of after each
   // tile's barrier): M = 3 / 4 / 6 / 8 15.13-15.16 / 15.31-15.32 /
   // 17.35-17.37 / 17.85-17.91 us against 15.85-15.86 / 15.87-15.88 /
-  // 18.41-18.42 / 18.70-18.72.
-  for (auto e : {gemv_mfma_q6f_entry<3, 2, false, true>(), gemv_mfma_q6f_entry<4, 2, false, true>(),
-                 gemv_mfma_q6f_entry<5, 2, false, true>(), gemv_mfma_q6f_entry<6, 2, false, true>(),
-                 gemv_mfma_q6f_entry<7, 2, false, true>(), gemv_mfma_q6f_entry<8, 2, false, true>()})
+  // 18.41-18.42 / 18.70-18.72; with the activation staged in the second
+  // slot too (its tile requested once the staging is read): M = 4 / 8
+  // 14.77-14.79 / 17.13-17.16 against 15.28-15.30 / 17.88-17.91.
+  for (auto e : {gemv_mfma_q6f_entry<3, 2, true, true>(), gemv_mfma_q6f_entry<4, 2, true, true>(),
+                 gemv_mfma_q6f_entry<5, 2, true, true>(), gemv_mfma_q6f_entry<6, 2, true, true>(),
+                 gemv_mfma_q6f_entry<7, 2, true, true>(), gemv_mfma_q6f_entry<8, 2, true, true>()})
     out.push_back(e);
   // q6_K x Q8_1 at M = 4..8: the integer matrix cores with the weights
   // streamed into an LDS ring (low units, high units, int8 scale pairs and d
