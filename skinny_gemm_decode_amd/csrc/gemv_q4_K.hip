@@ -24,11 +24,12 @@ void register_gemv_q4_K(std::vector<GemvEntry>& out) {
   // the start, the third once the activation is staged): 9.73-9.81 /
   // 10.39-10.47 / 10.58-10.61 us against 10.10-10.11 / 10.54 / 10.69-10.72
   // with two slots and their own staging area; at M = 7 12.53 against 12.46.
-  // M = 6, 7 take two slots with the staging in the last (tile 1 requested
-  // once the activation is staged): 11.84-11.85 / 12.22-12.24 us against
-  // 12.06-12.08 / 12.49 (at M = 8 the staging and block sums outgrow a slot).
+  // M = 5, 6, 7 take two slots with the staging in the last (tile 1
+  // requested once the activation is staged): 11.61-11.62 / 11.84-11.85 /
+  // 12.22-12.24 us against 11.99-12.00 / 12.06-12.08 / 12.49 (at M = 8 the
+  // staging and block sums outgrow a slot).
   for (auto e : {gemv_mfma_grp_entry<SKG_Q4_K_F32, 2, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 3, 3, true>(),
-                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 5, 2, false>(),
+                 gemv_mfma_grp_entry<SKG_Q4_K_F32, 4, 3, true>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 5, 2, true>(),
                  gemv_mfma_grp_entry<SKG_Q4_K_F32, 6, 2, true>(), gemv_mfma_grp_entry<SKG_Q4_K_F32, 7, 2, true>(),
                  gemv_mfma_grp_entry<SKG_Q4_K_F32, 8, 2, false>()})
     out.push_back(e);

@@ -20,7 +20,11 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   // 18.41-18.42 / 18.70-18.72; with the activation staged in the second
   // slot too (its tile requested once the staging is read): M = 4 / 8
   // 14.77-14.79 / 17.13-17.16 against 15.28-15.30 / 17.88-17.91.
-  for (auto e : {gemv_mfma_q6f_entry<3, 2, true, true>(), gemv_mfma_q6f_entry<4, 2, true, true>(),
+  // At M = 2 the same kernel (activation as one fp16 term) takes 13.92-13.94
+  // us against 14.27-14.51 for the vector kernels (fp32 activation), and
+  // 15.23-15.24 with its own staging area and a reduction per tile.
+  for (auto e : {gemv_mfma_q6f_entry<2, 2, true, true>(), gemv_mfma_q6f_entry<3, 2, true, true>(),
+                 gemv_mfma_q6f_entry<4, 2, true, true>(),
                  gemv_mfma_q6f_entry<5, 2, true, true>(), gemv_mfma_q6f_entry<6, 2, true, true>(),
                  gemv_mfma_q6f_entry<7, 2, true, true>(), gemv_mfma_q6f_entry<8, 2, true, true>()})
     out.push_back(e);
@@ -83,8 +87,6 @@ void register_gemv_q6_K(std::vector<GemvEntry>& out) {
   // vector kernels (12.67 / 13.51 against 11.40 / 12.63 us)
   out.push_back(gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 2, 1, 2, true>());
   out.push_back(gemv_mfma_dma_entry<SKG_Q6_K_Q8_1, 3, 1, 2, true>());
-  // q6_K x fp32 on the LDS-ring kernel at M = 2: slower than the vector
-  // kernel (15.25 against 13.97 us)
-  out.push_back(gemv_mfma_q6f_entry<2, 2, false>());
+
 }
 }  // namespace skg
